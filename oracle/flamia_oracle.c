@@ -1,0 +1,745 @@
+/*
+ * flamia_oracle.c -- plain FP64 CPU oracle for causal, packed, variable-length
+ * attention over microscaled E4M3 operands (the FLAMIA method).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is used by the test-suite, by the
+ * package's smoke check and by the benchmark's CPU-baseline leg.  The HIP
+ * library never links, loads or calls it, and it shares no code, header or
+ * table with the HIP sources.  Everything here is written from the method's
+ * description, slow and direct on purpose, so that it can be read against it.
+ *
+ * Sources (pages and sections):
+ *   [R]  "FLAMIA ... technical review" (zhongzhuzhou.org, 2026-11-08)
+ *        S2  "Prerequisites"           attention, backward products, D identity,
+ *                                       online softmax recurrence
+ *        S3  "Reusable scales"         document-local 32-token blocks, one
+ *                                       exponent over the block x full head dim
+ *        S4  "A causal mask must include scale selection"
+ *                                       conservative (ceil) exponent, 448 bound,
+ *                                       floor rule as the leaking alternative,
+ *                                       causal dQ accumulator prescale
+ *        S5  "Reconstructing the forward in the backward", Algorithm 1,
+ *                                       "A range budget for probability
+ *                                       quantization" (boost 256)
+ *        S6  "Packed documents and GPU scheduling" (+inf LSE sentinel,
+ *                                       masked keys outside the document)
+ *   [K]  jaehun.me review of arXiv 2611.03344, S1.2 (S, P, O and the five
+ *        backward products), S2 (floor-rule group exponent), S3.1-S3.3
+ *        (32x32 dS blocks, per-query-row dS exponent option, D from the
+ *        quantized dO).
+ *   [F]  richardcheam.github.io "efficient execution", "Attention without the
+ *        score matrix" (blockwise online softmax), "Lower precision" (E4M3
+ *        OCP max 448).
+ *
+ * Readings where the pages are silent or garbled (their formulas were lost in
+ * extraction) are listed in the repository's design notes; the ones that
+ * change arithmetic are restated next to the code that implements them.
+ *
+ * Parity pins: every function here is pinned by tests under tests/ that check
+ * it against values the pages print, closed forms, invariants or brute force.
+ * The dQ prescale exponent (orc_bwd_prep, kpre) has no printed value on the
+ * pages: it is pinned only by its defining inequality ("parity unpinned"
+ * against the pages).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_EBADSEQ (-1)
+#define ORC_EBADARG (-2)
+
+/* ------------------------------------------------------------------------- */
+/* Number formats                                                             */
+/* ------------------------------------------------------------------------- */
+
+/* Nearest integer to a non-negative q, ties to the even integer. */
+static double rne_nonneg(double q)
+{
+    double f = floor(q);
+    double r = q - f;
+    if (r > 0.5) return f + 1.0;
+    if (r < 0.5) return f;
+    return (fmod(f, 2.0) == 0.0) ? f : f + 1.0;
+}
+
+/* OCP E4M3FN ([F] "Lower precision": max 448; spacing 0.125 just above 1):
+ * bias 7, subnormals m/8 * 2^-6, largest finite 1.75 * 2^8 = 448 (0x7E);
+ * 0x7F / 0xFF are NaN and never produced.  Round to nearest, ties to even,
+ * saturating to +-448; the sign is kept, so -0 encodes as 0x80. */
+uint8_t orc_e4m3_encode(double y)
+{
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    double a = fabs(y);
+    uint8_t mag;
+    if (a >= 448.0) {
+        mag = 0x7E;
+    } else if (a < ldexp(1.0, -6)) {
+        /* subnormal lattice: integer multiples of 2^-9; 8 * 2^-9 is the
+           smallest normal, whose code is 0x08, so the count is the code */
+        mag = (uint8_t)rne_nonneg(ldexp(a, 9));
+    } else {
+        int E;
+        frexp(a, &E);
+        E -= 1; /* a in [2^E, 2^(E+1)) */
+        double q = rne_nonneg(ldexp(a, 3 - E)); /* in [8, 16] */
+        if (q == 16.0) {
+            q = 8.0;
+            E += 1;
+        }
+        mag = (uint8_t)(((E + 7) << 3) | ((int)q - 8));
+    }
+    return (uint8_t)(sign | mag);
+}
+
+double orc_e4m3_decode(uint8_t c)
+{
+    int E = (c >> 3) & 15, M = c & 7;
+    double v = (E == 0) ? ldexp((double)M, -9) : ldexp((double)(8 + M), E - 10);
+    return (c & 0x80) ? -v : v;
+}
+
+double orc_bf16_to_f64(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Round a double to bfloat16 (8 significant bits, FP32 exponent range),
+ * nearest, ties to even. */
+uint16_t orc_f64_to_bf16(double x)
+{
+    if (isnan(x)) return 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0x0000;
+    double a = fabs(x);
+    if (a == 0.0) return sign;
+    int E;
+    frexp(a, &E);
+    E -= 1;
+    int qexp = (E < -126 ? -126 : E) - 7; /* weight of the last kept bit */
+    double v = ldexp(rne_nonneg(ldexp(a, -qexp)), qexp);
+    if (v >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80);
+    float f = (float)v; /* exact: v lies on the bf16 lattice */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+void orc_f64_to_bf16_array(int64_t n, const double* x, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f64_to_bf16(x[i]);
+}
+
+/* Conservative exponent ([R] S4 "Why doubling the scale often preserves E4M3
+ * values"; [K] S3.2): the smallest integer e with amax / 2^e <= 448.
+ * With amax = m * 2^E, m in [1, 2), and 448 = 1.75 * 2^8 this is
+ * E - 8 + [m > 1.75].  A zero block takes e = 0 (a conventional finite scale).
+ * The result is clamped to the UE8M0 range [-127, 127]. */
+int orc_ceil_exponent(double amax)
+{
+    if (!(amax > 0.0)) return 0;
+    int E;
+    double f = frexp(amax, &E); /* amax = f * 2^E, f in [0.5, 1) */
+    double m = 2.0 * f;
+    E -= 1;
+    int e = E - 8 + (m > 1.75 ? 1 : 0);
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/* The floor rule of the reference MX conversion ([K] S2): e = floor(log2
+ * amax) - 8, where 8 is E4M3's largest exponent.  It can push amax / 2^e past
+ * 448, and is kept only as a negative control for the causality tests. */
+int orc_floor_exponent(double amax)
+{
+    if (!(amax > 0.0)) return 0;
+    int E;
+    frexp(amax, &E);
+    E -= 1;
+    int e = E - 8;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/* Smallest E4M3 value >= t for t in (0, 448]; 448 when t > 448. */
+static double e4m3_ceil_value(double t)
+{
+    for (int c = 1; c <= 0x7E; ++c) {
+        double v = orc_e4m3_decode((uint8_t)c);
+        if (v >= t) return v;
+    }
+    return 448.0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Packed-document helpers                                                    */
+/* ------------------------------------------------------------------------- */
+
+/* cu_seqlens must start at 0, never decrease and end at or below T. */
+int orc_check_seqlens(int T, int B, const int32_t* cu)
+{
+    if (B < 1 || T < 0) return ORC_EBADSEQ;
+    if (cu[0] != 0) return ORC_EBADSEQ;
+    for (int b = 0; b < B; ++b)
+        if (cu[b + 1] < cu[b]) return ORC_EBADSEQ;
+    if (cu[B] > T) return ORC_EBADSEQ;
+    return ORC_OK;
+}
+
+/* Document holding token t, or -1 for padding rows (t >= cu[B]). */
+static int doc_of(int B, const int32_t* cu, int t)
+{
+    if (t < 0 || t >= cu[B]) return -1;
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (cu[mid] <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    while (cu[lo + 1] <= t) ++lo; /* skip empty documents */
+    return lo;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Token-block quantizer ([R] S3; [K] S3.1)                                   */
+/* ------------------------------------------------------------------------- */
+
+/* x: bf16 [T][H][d].  For every head and every document-local block of at most
+ * `block` consecutive tokens (blocks start at each document start; the last
+ * one may be partial), one exponent e over the block's tokens x all d
+ * features; codes = E4M3(x * 2^-e); exps[h][t] = e + 127 replicated on every
+ * token of the block (dense per-token scale table, [R] S6).
+ * block = 32 is the default policy, block = 1 the per-token exact option.
+ * rule 0: conservative ceil exponent; rule 1: floor exponent (control only).
+ * Padding rows: codes 0, exponent byte 127. */
+int orc_quantize(int T, int B, const int32_t* cu, int H, int d, const uint16_t* x, int block,
+                 int rule, uint8_t* codes, uint8_t* exps)
+{
+    if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
+    if (H < 1 || d < 1 || block < 1) return ORC_EBADARG;
+    memset(codes, 0, (size_t)T * H * d);
+    memset(exps, 127, (size_t)H * T);
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int h = 0; h < H; ++h) {
+        for (int b = 0; b < B; ++b) {
+            for (int s0 = cu[b]; s0 < cu[b + 1]; s0 += block) {
+                int s1 = s0 + block < cu[b + 1] ? s0 + block : cu[b + 1];
+                double amax = 0.0;
+                for (int t = s0; t < s1; ++t)
+                    for (int c = 0; c < d; ++c) {
+                        double v = fabs(orc_bf16_to_f64(x[((size_t)t * H + h) * d + c]));
+                        if (v > amax) amax = v;
+                    }
+                int e = rule == 0 ? orc_ceil_exponent(amax) : orc_floor_exponent(amax);
+                for (int t = s0; t < s1; ++t) {
+                    exps[(size_t)h * T + t] = (uint8_t)(e + 127);
+                    for (int c = 0; c < d; ++c) {
+                        size_t k = ((size_t)t * H + h) * d + c;
+                        codes[k] = orc_e4m3_encode(ldexp(orc_bf16_to_f64(x[k]), -e));
+                    }
+                }
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/* Dequantized operand values: decode(code) * 2^(byte - 127), [T][H][d]. */
+void orc_dequantize(int T, int H, int d, const uint8_t* codes, const uint8_t* exps, double* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t)
+        for (int h = 0; h < H; ++h)
+            for (int c = 0; c < d; ++c) {
+                size_t k = ((size_t)t * H + h) * d + c;
+                out[k] = ldexp(orc_e4m3_decode(codes[k]), (int)exps[(size_t)h * T + t] - 127);
+            }
+}
+
+/* ------------------------------------------------------------------------- */
+/* E2M1 score view with an E4M3 scale per 16 in-token features ([R] S2 "Codes,
+ * scales, and hardware layout"; [K] S3.1), without a tensor-level scale.     */
+/* ------------------------------------------------------------------------- */
+
+/* E2M1 magnitudes by code 0..7. */
+static const double e2m1_val[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* |x| rounded to the E2M1 lattice scaled by s, nearest with ties to the even
+ * code, by comparing |x| with the midpoints times s (exact products). */
+static int e2m1_code(double ax, double s)
+{
+    int best = 7;
+    for (int c = 0; c < 7; ++c) {
+        double mid = 0.5 * (e2m1_val[c] + e2m1_val[c + 1]) * s;
+        if (ax < mid) {
+            best = c;
+            break;
+        }
+        if (ax == mid) {
+            best = (c % 2 == 0) ? c : c + 1;
+            break;
+        }
+    }
+    return best;
+}
+
+/* x bf16 [T][H][d] -> codes [T][H][d/2] (element 2k in the low nibble),
+ * scales [T][H][d/16] E4M3.  The group scale is the smallest E4M3 value s
+ * with amax / s <= 6 (the no-clipping rule applied to E2M1's maximum 6); a
+ * zero group takes s = 1.  Padding rows are zero codes with scale 1. */
+int orc_quantize_nvfp4(int T, int B, const int32_t* cu, int H, int d, const uint16_t* x,
+                       uint8_t* codes, uint8_t* scales)
+{
+    if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
+    if (d % 16 != 0) return ORC_EBADARG;
+    memset(codes, 0, (size_t)T * H * (d / 2));
+    for (size_t i = 0; i < (size_t)T * H * (d / 16); ++i) scales[i] = orc_e4m3_encode(1.0);
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < cu[B]; ++t) {
+        for (int h = 0; h < H; ++h) {
+            for (int g = 0; g < d / 16; ++g) {
+                const uint16_t* xs = x + ((size_t)t * H + h) * d + 16 * g;
+                double amax = 0.0;
+                for (int c = 0; c < 16; ++c) {
+                    double v = fabs(orc_bf16_to_f64(xs[c]));
+                    if (v > amax) amax = v;
+                }
+                double s = amax > 0.0 ? e4m3_ceil_value(amax / 6.0) : 1.0;
+                scales[((size_t)t * H + h) * (d / 16) + g] = orc_e4m3_encode(s);
+                for (int c = 0; c < 16; ++c) {
+                    double v = orc_bf16_to_f64(xs[c]);
+                    int code = e2m1_code(fabs(v), s) | (signbit(v) ? 8 : 0);
+                    size_t k = ((size_t)t * H + h) * (d / 2) + 8 * g + c / 2;
+                    codes[k] |= (uint8_t)(c % 2 == 0 ? code : code << 4);
+                }
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/* Dequantized E2M1 view: code value times its group's E4M3 scale, [T][H][d]. */
+void orc_dequantize_nvfp4(int T, int H, int d, const uint8_t* codes, const uint8_t* scales,
+                          double* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t)
+        for (int h = 0; h < H; ++h)
+            for (int c = 0; c < d; ++c) {
+                uint8_t byte = codes[((size_t)t * H + h) * (d / 2) + c / 2];
+                int code = (c % 2 == 0) ? (byte & 15) : (byte >> 4);
+                double v = e2m1_val[code & 7] *
+                           orc_e4m3_decode(scales[((size_t)t * H + h) * (d / 16) + c / 16]);
+                out[((size_t)t * H + h) * d + c] = (code & 8) ? -v : v;
+            }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Attention on dequantized operands                                          */
+/* ------------------------------------------------------------------------- */
+
+typedef struct {
+    int T, B, Hq, Hkv, d, causal;
+    const int32_t* cu;
+    double scale;             /* softmax scale applied to Q.K */
+    const double *Q, *K, *V;  /* dequantized operands, [T][H][d] */
+    const double *Qs, *Ks;    /* score view of Q and K (NULL: Q and K) */
+} orc_attn;
+
+static inline int kv_head(const orc_attn* a, int h) { return h * a->Hkv / a->Hq; }
+
+static inline const double* row(const double* X, int H, int d, int t, int h)
+{
+    return X + ((size_t)t * H + h) * d;
+}
+
+/* Score s_ij = scale * Q_i . K_j ([R] S2; [K] S1.2).  With a separate score
+ * view (the E2M1 route) the score uses it ([R] S2: the mixed route
+ * reconstructs scores from the selected Q/K format and re-quantizes Q and K
+ * in E4M3 for the gradient products). */
+static double score(const orc_attn* a, int h, int i, int j)
+{
+    const double* q = row(a->Qs ? a->Qs : a->Q, a->Hq, a->d, i, h);
+    const double* k = row(a->Ks ? a->Ks : a->K, a->Hkv, a->d, j, kv_head(a, h));
+    double acc = 0.0;
+    for (int c = 0; c < a->d; ++c) acc += q[c] * k[c];
+    return a->scale * acc;
+}
+
+/* Visible keys of query i in document b: [s_b, i] when causal, else the whole
+ * document ([R] S2: the keys in that document up through i). */
+static inline int key_end(const orc_attn* a, int b, int i)
+{
+    return a->causal ? i + 1 : a->cu[b + 1];
+}
+
+/* ------------------------------------------------------------------------- */
+/* Forward                                                                    */
+/* ------------------------------------------------------------------------- */
+
+/* One query row.  mode:
+ *   0  microscaled forward, rounded normaliser: base-2 logits s2 = s*log2(e);
+ *      integer row reference r = ceil(max s2); unnormalised weights
+ *      p = 2^(s2 - r) <= 1; probability operand P^ = E4M3(256 p) / 256 (the
+ *      boost 256 of [R] S5 "A range budget"); l = sum P^; O = sum P^ V / l;
+ *      LSE = (r + log2 l) ln 2.
+ *   1  as 0 with the unrounded normaliser l = sum p.
+ *   2  reference math: blockwise online softmax in FP64 over document-local
+ *      key blocks of `kblock` keys ([R] S2 "Why flash tiling recomputes
+ *      scores"; [F] "Attention without the score matrix"): running max m,
+ *      normaliser l and accumulator, rescaled by exp(m_old - m_new) whenever
+ *      the max grows; O = acc / l; LSE = m + ln l.
+ * Rows outside every document get O = 0 and LSE = +inf ([R] S6). */
+static void fwd_row(const orc_attn* a, int mode, int kblock, int h, int i, double* O, double* LSE,
+                    int32_t* n_rescale, double* s_buf)
+{
+    int d = a->d, g = kv_head(a, h);
+    int b = doc_of(a->B, a->cu, i);
+    for (int c = 0; c < d; ++c) O[c] = 0.0;
+    if (n_rescale) *n_rescale = 0;
+    if (b < 0) {
+        *LSE = INFINITY;
+        return;
+    }
+    int j0 = a->cu[b], j1 = key_end(a, b, i);
+    for (int j = j0; j < j1; ++j) s_buf[j - j0] = score(a, h, i, j);
+
+    if (mode == 0 || mode == 1) {
+        double mx = -INFINITY;
+        for (int j = j0; j < j1; ++j) {
+            double s2 = s_buf[j - j0] * M_LOG2E;
+            if (s2 > mx) mx = s2;
+        }
+        double r = ceil(mx);
+        double l = 0.0;
+        for (int j = j0; j < j1; ++j) {
+            double p = exp2(s_buf[j - j0] * M_LOG2E - r);
+            double ph = orc_e4m3_decode(orc_e4m3_encode(256.0 * p)) / 256.0;
+            l += (mode == 0) ? ph : p;
+            const double* v = row(a->V, a->Hkv, d, j, g);
+            for (int c = 0; c < d; ++c) O[c] += ph * v[c];
+        }
+        for (int c = 0; c < d; ++c) O[c] /= l;
+        *LSE = (r + log2(l)) * M_LN2;
+        return;
+    }
+
+    /* mode 2: online recurrence over document-local key blocks */
+    double m = -INFINITY, l = 0.0;
+    int nres = 0;
+    for (int k0 = j0; k0 < j1; k0 += kblock) {
+        int k1 = k0 + kblock < j1 ? k0 + kblock : j1;
+        double mb = -INFINITY;
+        for (int j = k0; j < k1; ++j)
+            if (s_buf[j - j0] > mb) mb = s_buf[j - j0];
+        double m_new = mb > m ? mb : m;
+        if (m != -INFINITY && m_new > m) {
+            double alpha = exp(m - m_new);
+            l *= alpha;
+            for (int c = 0; c < d; ++c) O[c] *= alpha;
+            ++nres;
+        }
+        for (int j = k0; j < k1; ++j) {
+            double w = exp(s_buf[j - j0] - m_new);
+            l += w;
+            const double* v = row(a->V, a->Hkv, d, j, g);
+            for (int c = 0; c < d; ++c) O[c] += w * v[c];
+        }
+        m = m_new;
+    }
+    for (int c = 0; c < d; ++c) O[c] /= l;
+    *LSE = m + log(l);
+    if (n_rescale) *n_rescale = nres;
+}
+
+/* Q, K, V: dequantized operands; Qs, Ks: optional score view (else NULL).
+ * rows: n_rows pairs (h, t); NULL means every (h, t).  O: [T][Hq][d],
+ * LSE: [Hq][T], n_rescale: [Hq][T] or NULL.  Unlisted rows are untouched. */
+int orc_attn_fwd(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale,
+                 int causal, const double* Q, const double* K, const double* V, const double* Qs,
+                 const double* Ks, int mode, int kblock, int64_t n_rows, const int32_t* rows,
+                 double* O, double* LSE, int32_t* n_rescale)
+{
+    if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d < 1 || kblock < 1 || mode < 0 || mode > 2)
+        return ORC_EBADARG;
+    orc_attn a = {T, B, Hq, Hkv, d, causal, cu, scale, Q, K, V, Qs, Ks};
+    int64_t n = rows ? n_rows : (int64_t)Hq * T;
+    int Tn = T > 0 ? T : 1;
+#pragma omp parallel
+    {
+        double* s_buf = (double*)malloc(sizeof(double) * Tn);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t k = 0; k < n; ++k) {
+            int h = rows ? rows[2 * k] : (int)(k / Tn);
+            int t = rows ? rows[2 * k + 1] : (int)(k % Tn);
+            fwd_row(&a, mode, kblock, h, t, O + ((size_t)t * Hq + h) * d, LSE + (size_t)h * T + t,
+                    n_rescale ? n_rescale + (size_t)h * T + t : NULL, s_buf);
+        }
+        free(s_buf);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Backward                                                                   */
+/* ------------------------------------------------------------------------- */
+
+/* Backward preparation ([R] Algorithm 1 steps "Encode G once; compute D from
+ * reconstructed G and saved O" and "Select ... causal row dQ accumulator
+ * boosts"; [K] S3.3):
+ *   - dO (bf16 [T][Hq][d]) is quantized with the operand rule (block 32 or the
+ *     per-token option);
+ *   - D_i = dO^_i . O_i with the dequantized dO and the saved bf16 O;
+ *   - kpre_i, the power-of-two prescale exponent of row i's FP16 dQ partials.
+ *     It must depend only on what row i may see ([R] S4 "Forward locality and
+ *     backward locality differ": the row's own dO and running maxima of the
+ *     visible key and value magnitudes).  Reading: with e_dO the row's dO
+ *     exponent and maxV, maxK the largest V and K exponents over the visible
+ *     keys, every partial sum of dQ_i is bounded by
+ *         2 * scale * d * 448^3 * 2^(e_dO + maxV + maxK),
+ *     so with C = ceil(log2(4 * scale * d * 448^3)) (a factor 2 of margin)
+ *     kpre_i = 14 - C - (e_dO + maxV + maxK) keeps boosted partials below
+ *     2^14, inside FP16's finite range.  Clamped to [-60, 60]; 0 for padding
+ *     rows and rows whose quantized dO is all zero.  (Parity unpinned against
+ *     the pages: their formula is lost; pinned by the inequality only.) */
+int orc_bwd_prep(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale,
+                 int causal, int block, const uint16_t* dO, const uint16_t* O, const uint8_t* ke,
+                 const uint8_t* ve, uint8_t* do_codes, uint8_t* do_exps, double* D, int32_t* kpre)
+{
+    if (Hkv < 1 || Hq % Hkv != 0) return ORC_EBADARG;
+    int rc = orc_quantize(T, B, cu, Hq, d, dO, block, 0, do_codes, do_exps);
+    if (rc != ORC_OK) return rc;
+    int C = (int)ceil(log2(4.0 * scale * d * 448.0 * 448.0 * 448.0));
+#pragma omp parallel for collapse(2) schedule(dynamic, 64)
+    for (int h = 0; h < Hq; ++h) {
+        for (int t = 0; t < T; ++t) {
+            int g = h * Hkv / Hq;
+            int b = doc_of(B, cu, t);
+            size_t r = (size_t)t * Hq + h;
+            if (b < 0) {
+                D[(size_t)h * T + t] = 0.0;
+                kpre[(size_t)h * T + t] = 0;
+                continue;
+            }
+            double acc = 0.0;
+            int nonzero = 0;
+            int eg = (int)do_exps[(size_t)h * T + t] - 127;
+            for (int c = 0; c < d; ++c) {
+                double g_hat = ldexp(orc_e4m3_decode(do_codes[r * d + c]), eg);
+                acc += g_hat * orc_bf16_to_f64(O[r * d + c]);
+                if (g_hat != 0.0) nonzero = 1;
+            }
+            D[(size_t)h * T + t] = acc;
+            int j0 = cu[b], j1 = causal ? t + 1 : cu[b + 1];
+            int maxv = -1000, maxk = -1000;
+            for (int j = j0; j < j1; ++j) {
+                int ev = (int)ve[(size_t)g * T + j] - 127, ek = (int)ke[(size_t)g * T + j] - 127;
+                if (ev > maxv) maxv = ev;
+                if (ek > maxk) maxk = ek;
+            }
+            int E = eg + maxv + maxk;
+            int k = 14 - C - E;
+            if (k < -60) k = -60;
+            if (k > 60) k = 60;
+            kpre[(size_t)h * T + t] = nonzero ? k : 0;
+        }
+    }
+    return ORC_OK;
+}
+
+typedef struct {
+    const orc_attn* a;
+    const double* G;   /* dequantized dO, [T][Hq][d] */
+    const double* D;   /* [Hq][T] */
+    const double* LSE; /* [Hq][T], natural log, as saved by a forward */
+    int mode;          /* 0: E4M3 P^ and dS^; 1: reference math, no rounding */
+    int per_row_ds;    /* dS exponent per (query row, key block) for dQ */
+} orc_bwd;
+
+/* One document-local 32x32 block (queries [q0,q1) x keys [k0,k1) of one
+ * document, head h) of the recomputed backward ([R] Algorithm 1 steps
+ * 11-15; [K] S1.2, S3.3), row-major [32][32] outputs:
+ *   P   = exp(s_ij - LSE_i)       probabilities rebuilt from the saved LSE
+ *   dP  = dO^_i . V^_j
+ *   dS  = P (dP - D_i)
+ *   Pq  the probability operand of dV: E4M3(256 P) / 256 (mode 0) or P;
+ *   dSk dS quantized on the 32x32 block ([K] S3.1: one scale per 32x32 dS
+ *       block, from the block's largest |dS| over visible entries, with the
+ *       conservative exponent), used for dK, and for dQ unless per_row_ds;
+ *   dSq with per_row_ds: dS quantized with one exponent per query row of the
+ *       block (the per-query-row option, [R] S4, [K] S3.2), used for dQ.
+ * Entries with j > i (causal) and entries outside the block are zero. */
+static void bwd_block(const orc_bwd* w, int h, int q0, int q1, int k0, int k1, double* P,
+                      double* dP, double* dS, double* Pq, double* dSk, double* dSq)
+{
+    const orc_attn* a = w->a;
+    int T = a->T, d = a->d, g = kv_head(a, h);
+    for (int k = 0; k < 1024; ++k) P[k] = dP[k] = dS[k] = Pq[k] = dSk[k] = dSq[k] = 0.0;
+    double amax = 0.0;
+    for (int i = q0; i < q1; ++i) {
+        const double* gi = row(w->G, a->Hq, d, i, h);
+        for (int j = k0; j < k1; ++j) {
+            if (a->causal && j > i) continue;
+            int e = (i - q0) * 32 + (j - k0);
+            const double* vj = row(a->V, a->Hkv, d, j, g);
+            P[e] = exp(score(a, h, i, j) - w->LSE[(size_t)h * T + i]);
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c) acc += gi[c] * vj[c];
+            dP[e] = acc;
+            dS[e] = P[e] * (dP[e] - w->D[(size_t)h * T + i]);
+            if (fabs(dS[e]) > amax) amax = fabs(dS[e]);
+            Pq[e] = w->mode == 0 ? orc_e4m3_decode(orc_e4m3_encode(256.0 * P[e])) / 256.0 : P[e];
+        }
+    }
+    int eb = orc_ceil_exponent(amax);
+    for (int i = q0; i < q1; ++i) {
+        int base = (i - q0) * 32;
+        double ramax = 0.0;
+        for (int j = k0; j < k1; ++j)
+            if (fabs(dS[base + j - k0]) > ramax) ramax = fabs(dS[base + j - k0]);
+        int er = orc_ceil_exponent(ramax);
+        for (int j = k0; j < k1; ++j) {
+            int e = base + (j - k0);
+            if (a->causal && j > i) continue;
+            if (w->mode == 0) {
+                dSk[e] = ldexp(orc_e4m3_decode(orc_e4m3_encode(ldexp(dS[e], -eb))), eb);
+                dSq[e] = w->per_row_ds
+                             ? ldexp(orc_e4m3_decode(orc_e4m3_encode(ldexp(dS[e], -er))), er)
+                             : dSk[e];
+            } else {
+                dSk[e] = dSq[e] = dS[e];
+            }
+        }
+    }
+}
+
+static int check_blocks(int B, const int32_t* cu, int64_t n, const int32_t* blocks, int nheads)
+{
+    for (int64_t k = 0; k < n; ++k) {
+        int b = doc_of(B, cu, blocks[2 * k + 1]);
+        if (b < 0 || (blocks[2 * k + 1] - cu[b]) % 32 != 0) return ORC_EBADARG;
+        if (blocks[2 * k] < 0 || blocks[2 * k] >= nheads) return ORC_EBADARG;
+    }
+    return ORC_OK;
+}
+
+/* Exposes one block of the recomputed backward (for the invariant checks). */
+int orc_bwd_block(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale,
+                  int causal, const double* Q, const double* K, const double* V,
+                  const double* Qs, const double* Ks, const double* G, const double* D,
+                  const double* LSE, int mode, int per_row_ds, int h, int q0, int k0, double* P,
+                  double* dP, double* dS, double* Pq, double* dSk, double* dSq)
+{
+    if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
+    int b = doc_of(B, cu, q0);
+    if (b < 0 || doc_of(B, cu, k0) != b || (q0 - cu[b]) % 32 || (k0 - cu[b]) % 32)
+        return ORC_EBADARG;
+    orc_attn a = {T, B, Hq, Hkv, d, causal, cu, scale, Q, K, V, Qs, Ks};
+    orc_bwd w = {&a, G, D, LSE, mode, per_row_ds};
+    int q1 = q0 + 32 < cu[b + 1] ? q0 + 32 : cu[b + 1];
+    int k1 = k0 + 32 < cu[b + 1] ? k0 + 32 : cu[b + 1];
+    bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq);
+    return ORC_OK;
+}
+
+/* dQ_i = scale * sum_j dS^_ij K^_j for every query of the listed
+ * document-local 32-query blocks.  qblocks: n pairs (q head, t0), t0 the
+ * first token of a block.  dQ: [T][Hq][d], accumulated into. */
+int orc_bwd_dq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale, int causal,
+               const double* Q, const double* K, const double* V, const double* Qs,
+               const double* Ks, const double* G, const double* D, const double* LSE, int mode,
+               int per_row_ds, int64_t n, const int32_t* qblocks, double* dQ)
+{
+    if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
+    if (Hkv < 1 || Hq % Hkv != 0) return ORC_EBADARG;
+    if (check_blocks(B, cu, n, qblocks, Hq) != ORC_OK) return ORC_EBADARG;
+    orc_attn a = {T, B, Hq, Hkv, d, causal, cu, scale, Q, K, V, Qs, Ks};
+    orc_bwd w = {&a, G, D, LSE, mode, per_row_ds};
+#pragma omp parallel
+    {
+        double* buf = (double*)malloc(sizeof(double) * 6 * 1024);
+#pragma omp for schedule(dynamic)
+        for (int64_t k = 0; k < n; ++k) {
+            int h = qblocks[2 * k], q0 = qblocks[2 * k + 1];
+            int b = doc_of(B, cu, q0), g = h * Hkv / Hq;
+            int q1 = q0 + 32 < cu[b + 1] ? q0 + 32 : cu[b + 1];
+            int kend = causal ? q1 : cu[b + 1];
+            double *P = buf, *dP = buf + 1024, *dS = buf + 2048, *Pq = buf + 3072,
+                   *dSk = buf + 4096, *dSq = buf + 5120;
+            for (int k0 = cu[b]; k0 < kend; k0 += 32) {
+                int k1 = k0 + 32 < cu[b + 1] ? k0 + 32 : cu[b + 1];
+                bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq);
+                for (int i = q0; i < q1; ++i) {
+                    double* out = dQ + ((size_t)i * Hq + h) * d;
+                    for (int c = 0; c < d; ++c) {
+                        double acc = 0.0;
+                        for (int j = k0; j < k1; ++j)
+                            acc += dSq[(i - q0) * 32 + (j - k0)] * row(K, Hkv, d, j, g)[c];
+                        out[c] += scale * acc;
+                    }
+                }
+            }
+        }
+        free(buf);
+    }
+    return ORC_OK;
+}
+
+/* dV_j = sum over the group's q heads and visible queries of P^_ij dO^_i and
+ * dK_j = scale * sum dS^_ij Q^_i, for every key of the listed document-local
+ * 32-key blocks.  kblocks: n pairs (kv head, t0).  GQA: q head h reads kv
+ * head floor(h * Hkv / Hq) (contiguous groups).  dK, dV: [T][Hkv][d],
+ * accumulated into. */
+int orc_bwd_dkdv(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale,
+                 int causal, const double* Q, const double* K, const double* V, const double* Qs,
+                 const double* Ks, const double* G, const double* D, const double* LSE, int mode,
+                 int per_row_ds, int64_t n, const int32_t* kblocks, double* dK, double* dV)
+{
+    if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
+    if (Hkv < 1 || Hq % Hkv != 0) return ORC_EBADARG;
+    if (check_blocks(B, cu, n, kblocks, Hkv) != ORC_OK) return ORC_EBADARG;
+    orc_attn a = {T, B, Hq, Hkv, d, causal, cu, scale, Q, K, V, Qs, Ks};
+    orc_bwd w = {&a, G, D, LSE, mode, per_row_ds};
+    int Gr = Hq / Hkv;
+#pragma omp parallel
+    {
+        double* buf = (double*)malloc(sizeof(double) * 6 * 1024);
+#pragma omp for schedule(dynamic)
+        for (int64_t k = 0; k < n; ++k) {
+            int g = kblocks[2 * k], k0 = kblocks[2 * k + 1];
+            int b = doc_of(B, cu, k0);
+            int k1 = k0 + 32 < cu[b + 1] ? k0 + 32 : cu[b + 1];
+            double *P = buf, *dP = buf + 1024, *dS = buf + 2048, *Pq = buf + 3072,
+                   *dSk = buf + 4096, *dSq = buf + 5120;
+            for (int h = g * Gr; h < (g + 1) * Gr; ++h) {
+                int qstart = causal ? k0 : cu[b];
+                for (int q0 = qstart; q0 < cu[b + 1]; q0 += 32) {
+                    int q1 = q0 + 32 < cu[b + 1] ? q0 + 32 : cu[b + 1];
+                    bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq);
+                    for (int j = k0; j < k1; ++j) {
+                        double* ov = dV + ((size_t)j * Hkv + g) * d;
+                        double* ok = dK + ((size_t)j * Hkv + g) * d;
+                        for (int c = 0; c < d; ++c) {
+                            double av = 0.0, ak = 0.0;
+                            for (int i = q0; i < q1; ++i) {
+                                int e = (i - q0) * 32 + (j - k0);
+                                av += Pq[e] * row(G, Hq, d, i, h)[c];
+                                ak += dSk[e] * row(Q, Hq, d, i, h)[c];
+                            }
+                            ov[c] += av;
+                            ok[c] += scale * ak;
+                        }
+                    }
+                }
+            }
+        }
+        free(buf);
+    }
+    return ORC_OK;
+}
