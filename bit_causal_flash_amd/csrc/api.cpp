@@ -1,0 +1,348 @@
+// api.cpp -- the C ABI declared in include/flamia.h: host-side validation,
+// workspace layout and kernel launches.  No device memory is allocated and no
+// device memory is read on the host; every call only enqueues kernels.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "flamia.h"
+#include "kernels.hpp"
+
+namespace {
+
+using namespace flamia;
+
+constexpr size_t kAlign = 256;
+constexpr int kFwdTile = 128;  // queries per forward work item
+constexpr int kBwdTile = 128;  // keys per backward work item
+constexpr uint32_t kKnownFlags =
+    FLAMIA_CAUSAL | FLAMIA_EXACT | FLAMIA_FP4_SCORE | FLAMIA_DETERMINISTIC;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Dims {
+    int64_t T, B, Hq, Hkv, d;
+    float scale;
+    bool causal;
+};
+
+flamia_status check_seq(const flamia_problem* p)
+{
+    if (p == nullptr) return FLAMIA_ERR_INVALID_ARG;
+    if (p->total_tokens < 0 || p->num_seqs < 1 || p->cu_seqlens == nullptr)
+        return FLAMIA_ERR_INVALID_ARG;
+    return FLAMIA_OK;
+}
+
+flamia_status check_head_dim(int32_t d)
+{
+    if (d <= 0) return FLAMIA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FLAMIA_ERR_UNSUPPORTED;
+    return FLAMIA_OK;
+}
+
+flamia_status check_attn(const flamia_problem* p, Dims* out)
+{
+    flamia_status st = check_seq(p);
+    if (st != FLAMIA_OK) return st;
+    if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->num_q_heads % p->num_kv_heads != 0)
+        return FLAMIA_ERR_INVALID_ARG;
+    if (p->num_q_heads > 65535) return FLAMIA_ERR_UNSUPPORTED;  // grid.y of the dO preparation
+    st = check_head_dim(p->head_dim);
+    if (st != FLAMIA_OK) return st;
+    if (p->flags & ~kKnownFlags) return FLAMIA_ERR_INVALID_ARG;
+    if ((p->flags & FLAMIA_FP4_SCORE) && !(p->flags & FLAMIA_EXACT)) return FLAMIA_ERR_INVALID_ARG;
+    if (p->flags & (FLAMIA_EXACT | FLAMIA_FP4_SCORE | FLAMIA_DETERMINISTIC))
+        return FLAMIA_ERR_UNSUPPORTED;
+    if (std::isnan(p->softmax_scale) || std::isinf(p->softmax_scale)) return FLAMIA_ERR_INVALID_ARG;
+    out->T = p->total_tokens;
+    out->B = p->num_seqs;
+    out->Hq = p->num_q_heads;
+    out->Hkv = p->num_kv_heads;
+    out->d = p->head_dim;
+    out->scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+    out->causal = (p->flags & FLAMIA_CAUSAL) != 0;
+    // grid limits: items x heads must fit a 1-D launch
+    const int64_t items = out->T / 128 + std::min(out->B, out->T) + 1;
+    if (items * out->Hq >= (int64_t)INT32_MAX) return FLAMIA_ERR_UNSUPPORTED;
+    return FLAMIA_OK;
+}
+
+int64_t max_items(const Dims& d, int tile) { return d.T / tile + std::min(d.B, d.T) + 1; }
+int64_t max_cost(const Dims& d) { return (d.T + 63) / 64 + 1; }
+
+struct WorklistLayout {
+    size_t doc_off, hist, cursor, count, items, total;
+};
+
+WorklistLayout worklist_layout(const Dims& d, int tile, size_t base)
+{
+    WorklistLayout w;
+    size_t o = base;
+    w.doc_off = o;
+    o = align_up(o + 4 * (size_t)(d.B + 1));
+    w.hist = o;
+    o = align_up(o + 4 * (size_t)(max_cost(d) + 1));
+    w.cursor = o;
+    o = align_up(o + 4 * (size_t)(max_cost(d) + 1));
+    w.count = o;
+    o = align_up(o + 4);
+    w.items = o;
+    o = align_up(o + 8 * (size_t)max_items(d, tile));
+    w.total = o;
+    return w;
+}
+
+// The public part of the backward workspace layout, plus where its work list
+// starts.
+flamia_bwd_workspace_layout bwd_layout(const Dims& d, size_t* worklist_base = nullptr)
+{
+    flamia_bwd_workspace_layout l;
+    const size_t rows = (size_t)d.T * d.Hq;
+    size_t o = 0;
+    l.do_codes = o;
+    o = align_up(o + rows * d.d);
+    l.do_exps = o;
+    o = align_up(o + rows);
+    l.delta = o;
+    o = align_up(o + 4 * rows);
+    l.dq_prescale = o;
+    o = align_up(o + rows);
+    l.dq_accum = o;
+    o = align_up(o + 2 * rows * d.d);
+    if (worklist_base) *worklist_base = o;
+    l.total = worklist_layout(d, kBwdTile, o).total;
+    return l;
+}
+
+WorklistArgs make_worklist_args(const Dims& d, const flamia_problem* p, int tile, bool backward,
+                                uint8_t* ws, const WorklistLayout& w)
+{
+    WorklistArgs a;
+    a.B = (int)d.B;
+    a.T = (int)d.T;
+    a.tile = tile;
+    a.causal = d.causal ? 1 : 0;
+    a.backward = backward ? 1 : 0;
+    a.max_items = (int)max_items(d, tile);
+    a.max_cost = (int)max_cost(d);
+    a.cu = p->cu_seqlens;
+    a.doc_off = (int32_t*)(ws + w.doc_off);
+    a.hist = (int32_t*)(ws + w.hist);
+    a.cursor = (int32_t*)(ws + w.cursor);
+    a.count = (int32_t*)(ws + w.count);
+    a.items = (int32_t*)(ws + w.items);
+    return a;
+}
+
+// C of the dQ prescale: ceil(log2(4 * scale * d * 448^3)).
+int prescale_c(const Dims& d)
+{
+    return (int)std::ceil(std::log2(4.0 * (double)d.scale * (double)d.d * 448.0 * 448.0 * 448.0));
+}
+
+flamia_status hip_status(hipError_t e) { return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* flamia_status_string(flamia_status s)
+{
+    switch (s) {
+    case FLAMIA_OK: return "ok";
+    case FLAMIA_ERR_INVALID_ARG: return "invalid argument";
+    case FLAMIA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FLAMIA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FLAMIA_ERR_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_heads,
+                                       int32_t scale_mode, const uint16_t* x, uint8_t* codes,
+                                       uint8_t* exps, void* stream)
+{
+    flamia_status st = check_seq(p);
+    if (st != FLAMIA_OK) return st;
+    st = check_head_dim(p->head_dim);
+    if (st != FLAMIA_OK) return st;
+    if (num_heads < 1) return FLAMIA_ERR_INVALID_ARG;
+    if (scale_mode == FLAMIA_SCALE_NVFP4_16) return FLAMIA_ERR_UNSUPPORTED;
+    if (scale_mode != FLAMIA_SCALE_TOKBLOCK32 && scale_mode != FLAMIA_SCALE_PER_TOKEN)
+        return FLAMIA_ERR_INVALID_ARG;
+    if ((int64_t)(p->total_tokens + 31) / 32 * num_heads >= (int64_t)INT32_MAX * 64)
+        return FLAMIA_ERR_UNSUPPORTED;
+    if (num_heads > 65535) return FLAMIA_ERR_UNSUPPORTED;
+    if (p->total_tokens == 0) return FLAMIA_OK;
+    if (x == nullptr || codes == nullptr || exps == nullptr) return FLAMIA_ERR_INVALID_ARG;
+    QuantArgs a = {};
+    a.T = p->total_tokens;
+    a.B = p->num_seqs;
+    a.H = num_heads;
+    a.block = scale_mode == FLAMIA_SCALE_PER_TOKEN ? 1 : 32;
+    a.cu = p->cu_seqlens;
+    a.x = x;
+    a.codes = codes;
+    a.exps = exps;
+    return hip_status(launch_quant(a, p->head_dim, false, (hipStream_t)stream));
+}
+
+size_t flamia_attn_fwd_workspace_size(const flamia_problem* p)
+{
+    Dims d;
+    if (check_attn(p, &d) != FLAMIA_OK) return 0;
+    return worklist_layout(d, kFwdTile, 0).total;
+}
+
+flamia_status flamia_attn_fwd(const flamia_problem* p, const uint8_t* q_codes,
+                              const uint8_t* q_exps, const uint8_t* k_codes,
+                              const uint8_t* k_exps, const uint8_t* v_codes,
+                              const uint8_t* v_exps, const uint8_t* q_fp4,
+                              const uint8_t* q_fp4_scales, const uint8_t* k_fp4,
+                              const uint8_t* k_fp4_scales, uint16_t* o, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream)
+{
+    Dims d;
+    flamia_status st = check_attn(p, &d);
+    if (st != FLAMIA_OK) return st;
+    if (q_fp4 || q_fp4_scales || k_fp4 || k_fp4_scales) return FLAMIA_ERR_INVALID_ARG;
+    if (d.T == 0) return FLAMIA_OK;
+    if (!q_codes || !q_exps || !k_codes || !k_exps || !v_codes || !v_exps || !o || !lse)
+        return FLAMIA_ERR_INVALID_ARG;
+    const WorklistLayout wl = worklist_layout(d, kFwdTile, 0);
+    if (workspace == nullptr || workspace_bytes < wl.total) return FLAMIA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+
+    WorklistArgs w = make_worklist_args(d, p, kFwdTile, false, ws, wl);
+    hipError_t e = launch_worklist(w, s);
+    if (e != hipSuccess) return FLAMIA_ERR_HIP;
+
+    AttnArgs a = {};
+    a.T = (int)d.T;
+    a.B = (int)d.B;
+    a.Hq = (int)d.Hq;
+    a.Hkv = (int)d.Hkv;
+    a.causal = d.causal ? 1 : 0;
+    a.scale = d.scale;
+    a.c2 = d.scale * 1.4426950408889634f;
+    a.cu = p->cu_seqlens;
+    a.count = w.count;
+    a.items = w.items;
+    a.q_codes = q_codes;
+    a.q_exps = q_exps;
+    a.k_codes = k_codes;
+    a.k_exps = k_exps;
+    a.v_codes = v_codes;
+    a.v_exps = v_exps;
+    a.o = o;
+    a.lse = lse;
+    e = launch_fwd(a, (int)d.d, w.max_items, s);
+    if (e != hipSuccess) return FLAMIA_ERR_HIP;
+    return hip_status(launch_fwd_padding(a, (int)d.d, s));
+}
+
+size_t flamia_attn_bwd_workspace_size(const flamia_problem* p)
+{
+    Dims d;
+    if (check_attn(p, &d) != FLAMIA_OK) return 0;
+    return bwd_layout(d).total;
+}
+
+flamia_status flamia_attn_bwd_workspace_layout(const flamia_problem* p,
+                                               flamia_bwd_workspace_layout* out)
+{
+    Dims d;
+    flamia_status st = check_attn(p, &d);
+    if (st != FLAMIA_OK) return st;
+    if (out == nullptr) return FLAMIA_ERR_INVALID_ARG;
+    *out = bwd_layout(d);
+    return FLAMIA_OK;
+}
+
+flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
+                              const uint8_t* q_exps, const uint8_t* k_codes,
+                              const uint8_t* k_exps, const uint8_t* v_codes,
+                              const uint8_t* v_exps, const uint8_t* q_fp4,
+                              const uint8_t* q_fp4_scales, const uint8_t* k_fp4,
+                              const uint8_t* k_fp4_scales, const uint16_t* o, const float* lse,
+                              const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                              void* workspace, size_t workspace_bytes, void* stream)
+{
+    Dims d;
+    flamia_status st = check_attn(p, &d);
+    if (st != FLAMIA_OK) return st;
+    if (q_fp4 || q_fp4_scales || k_fp4 || k_fp4_scales) return FLAMIA_ERR_INVALID_ARG;
+    if (d.T == 0) return FLAMIA_OK;
+    if (!q_codes || !q_exps || !k_codes || !k_exps || !v_codes || !v_exps || !o || !lse ||
+        !dout || !dq || !dk || !dv)
+        return FLAMIA_ERR_INVALID_ARG;
+    size_t wl_base = 0;
+    const flamia_bwd_workspace_layout L = bwd_layout(d, &wl_base);
+    if (workspace == nullptr || workspace_bytes < L.total) return FLAMIA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+
+    // dO quantization, D, prescale exponents, accumulator zeroing
+    QuantArgs q = {};
+    q.T = (int)d.T;
+    q.B = (int)d.B;
+    q.H = (int)d.Hq;
+    q.block = 32;
+    q.cu = p->cu_seqlens;
+    q.x = dout;
+    q.codes = ws + L.do_codes;
+    q.exps = ws + L.do_exps;
+    q.Hkv = (int)d.Hkv;
+    q.causal = d.causal ? 1 : 0;
+    q.prescale_c = prescale_c(d);
+    q.o = o;
+    q.k_exps = k_exps;
+    q.v_exps = v_exps;
+    q.delta = (float*)(ws + L.delta);
+    q.prescale = (int8_t*)(ws + L.dq_prescale);
+    q.dq_acc = (_Float16*)(ws + L.dq_accum);
+    hipError_t e = launch_quant(q, (int)d.d, true, s);
+    if (e != hipSuccess) return FLAMIA_ERR_HIP;
+
+    const WorklistLayout wl = worklist_layout(d, kBwdTile, wl_base);
+    WorklistArgs w = make_worklist_args(d, p, kBwdTile, true, ws, wl);
+    e = launch_worklist(w, s);
+    if (e != hipSuccess) return FLAMIA_ERR_HIP;
+
+    AttnArgs a = {};
+    a.T = (int)d.T;
+    a.B = (int)d.B;
+    a.Hq = (int)d.Hq;
+    a.Hkv = (int)d.Hkv;
+    a.causal = d.causal ? 1 : 0;
+    a.scale = d.scale;
+    a.c2 = d.scale * 1.4426950408889634f;
+    a.cu = p->cu_seqlens;
+    a.count = w.count;
+    a.items = w.items;
+    a.q_codes = q_codes;
+    a.q_exps = q_exps;
+    a.k_codes = k_codes;
+    a.k_exps = k_exps;
+    a.v_codes = v_codes;
+    a.v_exps = v_exps;
+    a.lse_in = lse;
+    a.do_codes = q.codes;
+    a.do_exps = q.exps;
+    a.delta = q.delta;
+    a.prescale = q.prescale;
+    a.dq_acc = q.dq_acc;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    e = launch_bwd(a, (int)d.d, w.max_items, s);
+    if (e != hipSuccess) return FLAMIA_ERR_HIP;
+    return hip_status(launch_bwd_finalize(a, (int)d.d, s));
+}
+
+}  // extern "C"

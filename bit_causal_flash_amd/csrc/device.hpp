@@ -1,0 +1,183 @@
+// device.hpp -- gfx950 device helpers shared by the attention kernels:
+// E4M3 / UE8M0 conversions, the conservative exponent, bf16 packing, FP8 MFMA
+// and LDS transpose-read wrappers.
+//
+// Hardware behaviour relied on here was measured on gfx950 (MI355X):
+//   * v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands: lane i holds row
+//     (A) / column (B) i % 32; operand bytes 0..15 are k = 16 * (i / 32) + s
+//     and bytes 16..31 are k = 32 + 16 * (i / 32) + (s - 16).  Lane i supplies
+//     the E8M0 scale of row/column i % 32 for the 32-wide k block i / 32.
+//     Accumulator: lane i holds column i % 32, rows 8 (v / 4) + 4 (i / 32) +
+//     v % 4 for v = 0..15.
+//   * v_cvt_pk_fp8_f32 rounds to nearest, ties to even, onto the OCP E4M3FN
+//     lattice and keeps the sign of zero; it saturates to 448 only up to 464
+//     and returns NaN beyond, so callers keep inputs within [-448, 448].
+//   * ds_read_b64_tr_b8: in each group of 16 lanes, lane j receives byte
+//     j % 8 of the 8-byte rows read by lanes 2r + j / 8, r = 0..7 (an 8 x 16
+//     byte transpose).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flamia {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int lds_i32x2;
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// E8M0 byte of the probability operand's 2^-8 (the boost 256 undone in the
+// MFMA).
+constexpr int kScaleMinus8 = 127 - 8;
+
+__device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c, int scale_a,
+                                        int scale_b)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+
+// Conservative exponent of a non-negative finite float amax: the smallest e
+// with amax / 2^e <= 448 (448 = 1.75 * 2^8), 0 for amax == 0, clamped to
+// [-127, 127].  Pure integer work on the float's bits.
+__device__ __forceinline__ int ceil_exp448(float amax)
+{
+    uint32_t u = __float_as_uint(amax) & 0x7fffffffu;
+    if (u == 0) return 0;
+    int E;
+    uint32_t frac;
+    uint32_t bexp = u >> 23;
+    if (bexp != 0) {
+        E = (int)bexp - 127;
+        frac = u & 0x7fffffu;
+    } else {  // float subnormal: normalise the mantissa
+        int lz = __clz(u) - 8;  // leading zeros inside the 24-bit field
+        E = -126 - lz;
+        frac = (u << lz) & 0x7fffffu;
+    }
+    int e = E - 8 + (frac > 0x600000u ? 1 : 0);
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Two floats -> two E4M3 codes in the low 16 bits (x in byte 0).
+__device__ __forceinline__ uint32_t cvt2_fp8(float x, float y)
+{
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, y, 0, false) & 0xffffu;
+}
+
+// Four floats -> four E4M3 codes packed little-endian.
+__device__ __forceinline__ uint32_t cvt4_fp8(float a, float b, float c, float d)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// Sum of the four E4M3 values packed in w.
+__device__ __forceinline__ float sum4_fp8(uint32_t w)
+{
+    v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    return (lo.x + lo.y) + (hi.x + hi.y);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// float -> bf16, nearest with ties to even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+}
+
+// One 8-byte transposed LDS read (see the header note).
+__device__ __forceinline__ v2i lds_read_tr8(const uint8_t* lds_addr)
+{
+    lds_i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) lds_i32x2*)(lds_addr));
+    v2i out;
+    out.x = r[0];
+    out.y = r[1];
+    return out;
+}
+
+// MFMA operand (32 bytes per lane) whose k axis runs over 32 consecutive
+// tokens of a token-major LDS tile.  The tile holds rows of `pitch` bytes;
+// `row0` is the first of the 64 tokens the k axis covers and `col0` the first
+// of the 32 columns this operand's rows cover (lane i -> column col0 + i % 32).
+// k layout: bytes 0..15 tokens 16g + (0..15), bytes 16..31 tokens
+// 32 + 16g + (0..15), g = lane / 32.
+__device__ __forceinline__ v8i lds_tr_operand(const uint8_t* tile, int pitch, int row0, int col0,
+                                              int lane)
+{
+    const int grp = lane >> 4;  // 16-lane group
+    const int l16 = lane & 15;
+    const int g = grp >> 1;
+    const int col = col0 + 16 * (grp & 1) + 8 * (l16 & 1);
+    const int r = l16 >> 1;
+    const uint8_t* base = tile + (size_t)(row0 + r) * pitch + col;
+    v2i a = lds_read_tr8(base + (size_t)(16 * g) * pitch);
+    v2i b = lds_read_tr8(base + (size_t)(16 * g + 8) * pitch);
+    v2i c = lds_read_tr8(base + (size_t)(32 + 16 * g) * pitch);
+    v2i d = lds_read_tr8(base + (size_t)(40 + 16 * g) * pitch);
+    v8i o;
+    o[0] = a.x; o[1] = a.y; o[2] = b.x; o[3] = b.y;
+    o[4] = c.x; o[5] = c.y; o[6] = d.x; o[7] = d.y;
+    return o;
+}
+
+// MFMA operand whose k axis runs over 64 consecutive bytes of one row (the
+// head dim, or keys of a dS row): bytes 0..15 = row[16g .. 16g+16),
+// bytes 16..31 = row[32 + 16g .. 32 + 16g + 16).
+__device__ __forceinline__ v8i row_operand(const uint8_t* row, int lane)
+{
+    const int g = lane >> 5;
+    v4i a = *(const v4i*)(row + 16 * g);
+    v4i b = *(const v4i*)(row + 32 + 16 * g);
+    v8i o;
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    return o;
+}
+
+// Token of the 64-token step held by accumulator row `rho` of tile t when
+// the rows are permuted so that, in the accumulator, lane group g holds the
+// tokens whose positions match the k layout above: VGPR v of tile t in lane
+// group g <-> token 32 t + 16 g + v.
+__device__ __forceinline__ int perm_row(int t, int rho)
+{
+    return 32 * t + 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3);
+}
+
+__device__ __forceinline__ float wave_max(float x)
+{
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+    return x;
+}
+
+__device__ __forceinline__ int doc_of(const int32_t* cu, int B, int t)
+{
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+}  // namespace flamia

@@ -1,0 +1,224 @@
+// fwd.hip -- causal packed microscaled attention forward for gfx950.
+//
+// Method (FLAMIA review section 2 "Why flash tiling recomputes scores",
+// section 3 "Factoring the scales out of the score MMA", section 5
+// Algorithm 1 steps 04-08 and "A range budget for probability
+// quantization"; jaehun.me section 3.1):
+//   S = Q^ K^T as an E4M3 MFMA on the stored codes, the Q and K token-block
+//   exponents entering as per-row / per-column E8M0 operand scales (exact
+//   powers of two); base-2 logits s2 = scale * log2(e) * S; an integer running
+//   reference r = ceil(max s2); weights p = 2^(s2 - r) <= 1 boosted by 256
+//   and rounded to E4M3 (the probability operand P^); l accumulates the
+//   rounded weights; O += P^ V^ with V's per-32-key-block exponent and the
+//   2^-8 un-boost as MFMA operand scales.  When r rises, O and l are
+//   multiplied by the exact power of two 2^(r_old - r_new).
+//   End: O = O / l (bf16), LSE = (r + log2 l) ln 2.
+//
+// Tiling: a workgroup (4 waves) owns one work-list item, a 128-query tile of
+// one document and one q head; wave w owns 32 queries.  Keys are visited in
+// document-relative 64-key steps staged in LDS, so every 32-key MFMA scale
+// block is exactly one document-local token block.  S is computed transposed
+// (S^T = K Q^T, lane = query) with the key rows permuted so that the
+// accumulator layout already is the k layout the P^ V MFMA expects: P^ never
+// leaves registers.  V is read k-major straight from its token-major LDS tile
+// with ds_read_b64_tr_b8, so no transposed copy of V exists anywhere.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace flamia {
+
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void fwd_kernel(AttnArgs a)
+{
+    constexpr int PITCH = D + 16;  // LDS row pitch (bytes): spreads rows over banks
+    constexpr int NKS = D / 64;    // k steps over the head dim
+    constexpr int NDT = D / 32;    // 32-wide head-dim tiles of O
+    constexpr int CPR = D / 16;    // 16-byte chunks per row
+    __shared__ __attribute__((aligned(16))) uint8_t s_k[64 * PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_v[64 * PITCH];
+    __shared__ int s_ek[64];
+    __shared__ int s_ev[2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+    const int Hq = a.Hq, Hkv = a.Hkv;
+    const size_t T = (size_t)a.T;
+    const int item = blockIdx.x / Hq, h = blockIdx.x % Hq;
+    if (item >= *a.count) return;
+    const int b = a.items[2 * item], m = a.items[2 * item + 1];
+    const int s = a.cu[b], e = a.cu[b + 1];
+    const int hk = h * Hkv / Hq;
+    const int q0 = s + 128 * m;
+    const int qw = q0 + 32 * wave;
+    const int qi = qw + (lane & 31);
+    const bool qvalid = qi < e;
+    const float c2 = a.c2;
+
+    // Q fragments: B operand of S^T = K Q^T (lane = query column, k = head dim)
+    v8i qf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        if (qvalid) qf[ks] = row_operand(a.q_codes + ((size_t)qi * Hq + h) * D + 64 * ks, lane);
+        else qf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    const int eq = qvalid ? (int)a.q_exps[(size_t)h * T + qi] : 127;
+
+    const int kend = a.causal ? min(q0 + 128, e) : e;
+    const int nsteps = (kend - s + 63) / 64;
+    const int kend_w = a.causal ? min(qw + 32, e) : e;
+
+    v16f oacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
+    float r = -INFINITY;  // integer base-2 row reference
+    float l = 0.f;        // sum of rounded weights
+
+    for (int st = 0; st < nsteps; ++st) {
+        const int kt0 = s + 64 * st;
+        __syncthreads();
+        for (int c = tid; c < 64 * CPR; c += 256) {
+            const int row = c / CPR, col = 16 * (c % CPR);
+            const int t = kt0 + row;
+            v4i kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+            if (t < e) {
+                kv = *(const v4i*)(a.k_codes + ((size_t)t * Hkv + hk) * D + col);
+                vv = *(const v4i*)(a.v_codes + ((size_t)t * Hkv + hk) * D + col);
+            }
+            *(v4i*)(s_k + row * PITCH + col) = kv;
+            *(v4i*)(s_v + row * PITCH + col) = vv;
+        }
+        if (tid < 64) {
+            const int t = kt0 + tid;
+            s_ek[tid] = t < e ? (int)a.k_exps[(size_t)hk * T + t] : 127;
+        }
+        if (tid < 2) {
+            const int t = kt0 + 32 * tid;
+            s_ev[tid] = t < e ? (int)a.v_exps[(size_t)hk * T + t] : 127;
+        }
+        __syncthreads();
+        if (kt0 >= kend_w) continue;  // no key of this step is visible to this wave
+
+        // S^T tiles: tile t row rho <-> key perm_row(t, rho) of the step
+        v16f sacc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int krow = perm_row(t, lane & 31);
+            const int ek = s_ek[krow];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sacc[t][v] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                sacc[t] = mfma_f8(row_operand(s_k + krow * PITCH + 64 * ks, lane), qf[ks], sacc[t],
+                                  ek, eq);
+        }
+
+        // masking and the running integer reference
+        const bool full = (kt0 + 64 <= e) && (!a.causal || kt0 + 63 <= qw);
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int key = kt0 + 32 * t + 16 * g + v;
+                const bool vis = full || (key < e && (!a.causal || key <= qi));
+                if (!vis) sacc[t][v] = -INFINITY;
+                mloc = fmaxf(mloc, sacc[t][v]);
+            }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+        const float rn = fmaxf(r, ceilf(mloc * c2));
+        if (__any(rn > r)) {
+            float alpha = 1.f;
+            if (rn > r) alpha = (r == -INFINITY) ? 0.f : ldexpf(1.f, (int)fmaxf(r - rn, -200.f));
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+        }
+        r = rn;
+
+        // probability operand: E4M3(256 * 2^(s2 - r)), byte 16 t + v <-> key 32 t + 16 g + v
+        const float off = (r == -INFINITY) ? 0.f : 8.f - r;
+        v8i pf;
+        float lsum = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float p[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    p[k] = __builtin_amdgcn_exp2f(fmaf(sacc[t][4 * q + k], c2, off));
+                const uint32_t w = cvt4_fp8(p[0], p[1], p[2], p[3]);
+                pf[4 * t + q] = (int)w;
+                lsum += sum4_fp8(w);
+            }
+        l += lsum * 0.00390625f;
+
+        // O^T += V^T P^T: V^T read k-major from the token-major LDS tile
+        const int sv = s_ev[g];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            oacc[dt] = mfma_f8(lds_tr_operand(s_v, PITCH, 0, 32 * dt, lane), pf, oacc[dt], sv,
+                               kScaleMinus8);
+    }
+
+    l += __shfl_xor(l, 32, kWave);
+    if (qvalid) {
+        const float inv = 1.f / l;
+        uint16_t* orow = a.o + ((size_t)qi * Hq + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v2i w;
+                w.x = (int)pack_bf16x2(oacc[dt][4 * q] * inv, oacc[dt][4 * q + 1] * inv);
+                w.y = (int)pack_bf16x2(oacc[dt][4 * q + 2] * inv, oacc[dt][4 * q + 3] * inv);
+                *(v2i*)(orow + 32 * dt + 8 * q + 4 * g) = w;
+            }
+        if (g == 0) a.lse[(size_t)h * T + qi] = (r + __log2f(l)) * kLn2;
+    }
+}
+
+// Rows after the last document: O = 0, LSE = +inf.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_padding_kernel(AttnArgs a)
+{
+    const int ntok = a.cu[a.B];
+    const size_t T = (size_t)a.T;
+    const size_t nchunks = (size_t)a.T * a.Hq * (D / 8);
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < nchunks;
+         i += (size_t)gridDim.x * 256) {
+        const size_t row = i / (D / 8);
+        const int t = (int)(row / a.Hq), h = (int)(row % a.Hq);
+        if (t < ntok) continue;
+        *(v4i*)(a.o + row * D + 8 * (i % (D / 8))) = v4i{0, 0, 0, 0};
+        if (i % (D / 8) == 0) a.lse[(size_t)h * T + t] = INFINITY;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const AttnArgs& a, int D, int max_items, hipStream_t stream)
+{
+    if (max_items <= 0) return hipSuccess;
+    const dim3 grid((unsigned)max_items * a.Hq);
+    if (D == 128) hipLaunchKernelGGL(fwd_kernel<128>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(fwd_kernel<64>, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_padding(const AttnArgs& a, int D, hipStream_t stream)
+{
+    if (a.T == 0) return hipSuccess;
+    const size_t nchunks = (size_t)a.T * a.Hq * (D / 8);
+    const unsigned blocks = (unsigned)min((size_t)4096, (nchunks + 255) / 256);
+    if (D == 128) hipLaunchKernelGGL(fwd_padding_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(fwd_padding_kernel<64>, dim3(blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace flamia

@@ -1,0 +1,67 @@
+// kernels.hpp -- argument blocks and launchers of the HIP kernels (internal;
+// the public interface is include/flamia.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flamia {
+
+struct QuantArgs {
+    int T, B, H, block;
+    const int32_t* cu;
+    const uint16_t* x;   // bf16 [T][H][D]
+    uint8_t* codes;      // [T][H][D]
+    uint8_t* exps;       // [H][T]
+    // backward preparation only
+    int Hkv, causal, prescale_c;
+    const uint16_t* o;        // bf16 [T][H][D]
+    const uint8_t* k_exps;    // [Hkv][T]
+    const uint8_t* v_exps;    // [Hkv][T]
+    float* delta;             // [H][T]
+    int8_t* prescale;         // [H][T]
+    _Float16* dq_acc;         // [T][H][D]
+};
+
+hipError_t launch_quant(const QuantArgs& a, int D, bool prep, hipStream_t stream);
+
+// Work list of (document, tile) items sorted by decreasing cost.
+struct WorklistArgs {
+    int B, T, tile, causal, backward;
+    int max_items, max_cost;
+    const int32_t* cu;
+    int32_t* doc_off;    // [B + 1]
+    int32_t* hist;       // [max_cost + 1]
+    int32_t* cursor;     // [max_cost + 1]
+    int32_t* count;      // [1]
+    int32_t* items;      // [max_items][2] = (doc, tile)
+};
+
+hipError_t launch_worklist(const WorklistArgs& a, hipStream_t stream);
+
+struct AttnArgs {
+    int T, B, Hq, Hkv, causal;
+    float scale;      // softmax scale
+    float c2;         // scale * log2(e)
+    const int32_t* cu;
+    const int32_t* count;
+    const int32_t* items;
+    const uint8_t *q_codes, *q_exps, *k_codes, *k_exps, *v_codes, *v_exps;
+    // forward
+    uint16_t* o;
+    float* lse;
+    // backward
+    const float* lse_in;
+    const uint8_t *do_codes, *do_exps;
+    const float* delta;
+    const int8_t* prescale;
+    _Float16* dq_acc;
+    uint16_t *dq, *dk, *dv;
+};
+
+hipError_t launch_fwd(const AttnArgs& a, int D, int max_items, hipStream_t stream);
+hipError_t launch_fwd_padding(const AttnArgs& a, int D, hipStream_t stream);
+hipError_t launch_bwd(const AttnArgs& a, int D, int max_items, hipStream_t stream);
+hipError_t launch_bwd_finalize(const AttnArgs& a, int D, hipStream_t stream);
+
+}  // namespace flamia

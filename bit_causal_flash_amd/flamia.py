@@ -1,0 +1,210 @@
+"""ctypes binding of libflamia.so (the C ABI in include/flamia.h).
+
+Argument marshalling only: torch supplies device memory and the current
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is missing or a call fails, an exception
+is raised."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libflamia.so")
+
+FLAMIA_OK = 0
+FLAMIA_ERR_INVALID_ARG = 1
+FLAMIA_ERR_UNSUPPORTED = 2
+FLAMIA_ERR_WORKSPACE = 3
+FLAMIA_ERR_HIP = 4
+
+FLAMIA_CAUSAL = 1 << 0
+FLAMIA_EXACT = 1 << 1
+FLAMIA_FP4_SCORE = 1 << 2
+FLAMIA_DETERMINISTIC = 1 << 3
+
+FLAMIA_SCALE_TOKBLOCK32 = 0
+FLAMIA_SCALE_PER_TOKEN = 1
+FLAMIA_SCALE_NVFP4_16 = 2
+
+EXPORTED = [
+    "flamia_quantize_tokblock",
+    "flamia_attn_fwd_workspace_size",
+    "flamia_attn_fwd",
+    "flamia_attn_bwd_workspace_size",
+    "flamia_attn_bwd",
+    "flamia_attn_bwd_workspace_layout",
+    "flamia_status_string",
+]
+
+
+class FlamiaError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (fn, status_string(status), status))
+
+
+class flamia_problem(ctypes.Structure):
+    _fields_ = [
+        ("total_tokens", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class flamia_bwd_workspace_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("do_codes", "do_exps", "delta", "dq_prescale", "dq_accum", "total")]
+
+
+_lib = None
+
+
+def load():
+    """Load libflamia.so (built by bit_causal_flash_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libflamia.so is not built: run `python -m bit_causal_flash_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(flamia_problem)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.flamia_quantize_tokblock.restype = ctypes.c_int
+    lib.flamia_quantize_tokblock.argtypes = [P, i32, i32, vp, vp, vp, vp]
+    lib.flamia_attn_fwd_workspace_size.restype = sz
+    lib.flamia_attn_fwd_workspace_size.argtypes = [P]
+    lib.flamia_attn_fwd.restype = ctypes.c_int
+    lib.flamia_attn_fwd.argtypes = [P] + [vp] * 12 + [vp, sz, vp]
+    lib.flamia_attn_bwd_workspace_size.restype = sz
+    lib.flamia_attn_bwd_workspace_size.argtypes = [P]
+    lib.flamia_attn_bwd.restype = ctypes.c_int
+    lib.flamia_attn_bwd.argtypes = [P] + [vp] * 16 + [vp, sz, vp]
+    lib.flamia_attn_bwd_workspace_layout.restype = ctypes.c_int
+    lib.flamia_attn_bwd_workspace_layout.argtypes = [P, ctypes.POINTER(flamia_bwd_workspace_layout)]
+    lib.flamia_status_string.restype = ctypes.c_char_p
+    lib.flamia_status_string.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().flamia_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != FLAMIA_OK:
+        raise FlamiaError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_problem(cu_seqlens, total_tokens: int, num_q_heads: int, num_kv_heads: int,
+                 head_dim: int, softmax_scale: float = 0.0, flags: int = FLAMIA_CAUSAL):
+    """cu_seqlens: device int32 tensor [B + 1] (kept alive by the problem)."""
+    p = flamia_problem(int(total_tokens), int(cu_seqlens.numel()) - 1,
+                       ctypes.c_void_p(cu_seqlens.data_ptr()), int(num_q_heads),
+                       int(num_kv_heads), int(head_dim), float(softmax_scale), int(flags))
+    p._cu = cu_seqlens
+    return p
+
+
+def softmax_scale_of(p) -> float:
+    return p.softmax_scale if p.softmax_scale > 0 else 1.0 / math.sqrt(p.head_dim)
+
+
+def flamia_quantize_tokblock(p, num_heads, scale_mode, x, codes, exps, stream=None):
+    _check("flamia_quantize_tokblock",
+           load().flamia_quantize_tokblock(ctypes.byref(p), int(num_heads), int(scale_mode),
+                                           _ptr(x), _ptr(codes), _ptr(exps), _stream(stream)))
+
+
+def flamia_attn_fwd_workspace_size(p) -> int:
+    return int(load().flamia_attn_fwd_workspace_size(ctypes.byref(p)))
+
+
+def flamia_attn_bwd_workspace_size(p) -> int:
+    return int(load().flamia_attn_bwd_workspace_size(ctypes.byref(p)))
+
+
+def flamia_attn_bwd_workspace_layout(p) -> flamia_bwd_workspace_layout:
+    out = flamia_bwd_workspace_layout()
+    _check("flamia_attn_bwd_workspace_layout",
+           load().flamia_attn_bwd_workspace_layout(ctypes.byref(p), ctypes.byref(out)))
+    return out
+
+
+def flamia_attn_fwd(p, q_codes, q_exps, k_codes, k_exps, v_codes, v_exps, o, lse, workspace,
+                    fp4=None, stream=None):
+    q4, q4s, k4, k4s = fp4 if fp4 is not None else (None, None, None, None)
+    _check("flamia_attn_fwd", load().flamia_attn_fwd(
+        ctypes.byref(p), _ptr(q_codes), _ptr(q_exps), _ptr(k_codes), _ptr(k_exps), _ptr(v_codes),
+        _ptr(v_exps), _ptr(q4), _ptr(q4s), _ptr(k4), _ptr(k4s), _ptr(o), _ptr(lse),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def flamia_attn_bwd(p, q_codes, q_exps, k_codes, k_exps, v_codes, v_exps, o, lse, dout, dq, dk,
+                    dv, workspace, fp4=None, stream=None):
+    q4, q4s, k4, k4s = fp4 if fp4 is not None else (None, None, None, None)
+    _check("flamia_attn_bwd", load().flamia_attn_bwd(
+        ctypes.byref(p), _ptr(q_codes), _ptr(q_exps), _ptr(k_codes), _ptr(k_exps), _ptr(v_codes),
+        _ptr(v_exps), _ptr(q4), _ptr(q4s), _ptr(k4), _ptr(k4s), _ptr(o), _ptr(lse), _ptr(dout),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# torch-facing conveniences (allocation only)
+# ---------------------------------------------------------------------------
+
+def quantize(p, x, num_heads, scale_mode=FLAMIA_SCALE_TOKBLOCK32, stream=None):
+    """x: bf16 (or int16 bit patterns) [T][H][d] on the GPU -> (codes uint8, exps uint8)."""
+    import torch
+    T, H, d = x.shape
+    codes = torch.empty((T, H, d), dtype=torch.uint8, device=x.device)
+    exps = torch.empty((H, T), dtype=torch.uint8, device=x.device)
+    flamia_quantize_tokblock(p, num_heads, scale_mode, x, codes, exps, stream)
+    return codes, exps
+
+
+def attn_fwd(p, q, k, v, stream=None):
+    """q, k, v: (codes, exps) pairs.  Returns (o bf16 [T][Hq][d], lse [Hq][T])."""
+    import torch
+    dev = q[0].device
+    T, Hq, d = q[0].shape
+    o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(flamia_attn_fwd_workspace_size(p), 1), dtype=torch.uint8, device=dev)
+    flamia_attn_fwd(p, q[0], q[1], k[0], k[1], v[0], v[1], o, lse, ws, stream=stream)
+    return o, lse
+
+
+def attn_bwd(p, q, k, v, o, lse, dout, stream=None, workspace=None):
+    """Returns (dq, dk, dv, workspace)."""
+    import torch
+    dev = q[0].device
+    T, Hq, d = q[0].shape
+    Hkv = k[0].shape[1]
+    dq = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
+    dk = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
+    dv = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(flamia_attn_bwd_workspace_size(p), 1), dtype=torch.uint8,
+                                device=dev)
+    flamia_attn_bwd(p, q[0], q[1], k[0], k[1], v[0], v[1], o, lse, dout, dq, dk, dv, workspace,
+                    stream=stream)
+    return dq, dk, dv, workspace

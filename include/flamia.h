@@ -1,0 +1,185 @@
+/*
+ * flamia.h -- C ABI of the MI355X (gfx950) causal packed microscaled attention
+ * library: document-local token-block E4M3 quantization, the online-softmax
+ * forward and the recomputed backward of the FLAMIA method.
+ *
+ * Method references (pages and sections):
+ *   "FLAMIA ... technical review" (zhongzhuzhou.org, 2026-11-08):
+ *     section 2 "Prerequisites" (attention, backward products, D identity,
+ *     online softmax), section 3 "Reusable scales and score formation"
+ *     (document-local 32-token blocks x full head dim, separable score
+ *     scaling), section 4 "A causal mask must include scale selection"
+ *     (conservative exponent, causal dQ accumulator scale), section 5
+ *     Algorithm 1 and "A range budget for probability quantization",
+ *     section 6 "Packed documents and GPU scheduling" and Algorithm 2.
+ *   jaehun.me review of arXiv 2611.03344, sections 3.1-3.4 (E4M3 token
+ *     blocks for Q, K, V, dO; one scale per 32x32 dS block; FP16 dQ
+ *     partials with a power-of-two prescale; BF16 outputs).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates device memory, never synchronises and never
+ *     reads device memory on the host: every call is asynchronous on
+ *     `stream` (a hipStream_t; NULL is the default stream) and consists only
+ *     of kernel launches.
+ *   - Errors are returned as status codes, never raised.  Host-side arguments
+ *     are validated before any launch; FLAMIA_ERR_HIP reports a launch
+ *     failure (hipGetLastError).  Device-side preconditions on cu_seqlens are
+ *     documented, not checked: violating them is undefined behaviour.
+ *   - Layouts (row-major, packed along tokens):
+ *       bf16 activations   uint16 [T][H][d]
+ *       E4M3 codes         uint8  [T][H][d]     (OCP E4M3FN)
+ *       exponent tables    uint8  [H][T]        (UE8M0 byte e + 127, one per
+ *                                                token, replicated over its
+ *                                                block)
+ *       LSE                float  [Hq][T]       (natural log)
+ *   - Rows t >= cu_seqlens[B] are padding: codes 0, exponent byte 127,
+ *     O = 0, LSE = +inf, dQ = dK = dV = 0.
+ *   - GQA: q head h reads kv head floor(h * Hkv / Hq) (contiguous groups).
+ *   - Thread-safety: no global mutable state; concurrent calls on different
+ *     streams with disjoint outputs and workspaces are safe.
+ */
+#ifndef FLAMIA_H
+#define FLAMIA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FLAMIA_OK = 0,
+    FLAMIA_ERR_INVALID_ARG = 1, /* a host-side argument is out of range or NULL */
+    FLAMIA_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. head_dim 96) */
+    FLAMIA_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required */
+    FLAMIA_ERR_HIP = 4          /* a kernel launch failed */
+} flamia_status;
+
+/* Problem flags. */
+enum {
+    FLAMIA_CAUSAL = 1u << 0,        /* keys j <= i of the query's document */
+    FLAMIA_EXACT = 1u << 1,         /* per-token operand exponents + per-row dS
+                                       exponents (not available in this build) */
+    FLAMIA_FP4_SCORE = 1u << 2,     /* E2M1 score view; requires FLAMIA_EXACT
+                                       (not available in this build) */
+    FLAMIA_DETERMINISTIC = 1u << 3  /* bitwise run-to-run repeatable backward */
+};
+
+/* Quantizer scale policies. */
+enum {
+    FLAMIA_SCALE_TOKBLOCK32 = 0, /* one exponent per document-local block of
+                                    <= 32 tokens x full head dim */
+    FLAMIA_SCALE_PER_TOKEN = 1,  /* one exponent per token x full head dim */
+    FLAMIA_SCALE_NVFP4_16 = 2    /* E2M1 + E4M3 per 16 features (not available
+                                    in this build) */
+};
+
+typedef struct {
+    int32_t total_tokens;       /* T >= 0: rows of every packed buffer */
+    int32_t num_seqs;           /* B >= 1 */
+    const int32_t* cu_seqlens;  /* DEVICE int32 [B + 1]; cu[0] = 0, nondecreasing,
+                                   cu[B] <= T (unchecked: UB if violated) */
+    int32_t num_q_heads;        /* Hq >= 1 */
+    int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0 */
+    int32_t head_dim;           /* d in {64, 128} */
+    float softmax_scale;        /* <= 0 selects 1 / sqrt(d) */
+    uint32_t flags;             /* FLAMIA_* flags */
+} flamia_problem;
+
+/*
+ * Token-block quantizer (review section 3 "Why one shared exponent can serve
+ * two reductions"; section 4 conservative exponent; jaehun.me section 3.1).
+ * For each head and each document-local block of up to 32 consecutive tokens
+ * (blocks start at every document start; the last may be partial), with amax
+ * the block's largest |x| over all d features:
+ *     e = smallest integer with amax / 2^e <= 448   (e = 0 for amax = 0),
+ *         clamped to [-127, 127];
+ *     codes = E4M3(x * 2^-e), nearest with ties to even;
+ *     exps[h][t] = e + 127 on every token of the block.
+ *   p          problem; only total_tokens, num_seqs and cu_seqlens are read
+ *   num_heads  H >= 1 of this tensor (Hq for Q, Hkv for K and V)
+ *   scale_mode FLAMIA_SCALE_TOKBLOCK32 or FLAMIA_SCALE_PER_TOKEN
+ *   x          bf16 [T][H][d] (device, read)
+ *   codes      uint8 [T][H][d] (device, written)
+ *   exps       uint8 [H][T] (device, written)
+ */
+flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_heads,
+                                       int32_t scale_mode, const uint16_t* x, uint8_t* codes,
+                                       uint8_t* exps, void* stream);
+
+/*
+ * Forward (review section 2 online softmax, section 3 separable score
+ * scaling, section 5 Algorithm 1 steps 04-08 and the range budget):
+ *   s2_ij = softmax_scale * log2(e) * Q^_i . K^_j over visible keys, with the
+ *   Q/K token-block exponents applied as row and column factors;
+ *   per row an integer base-2 reference r = ceil(max s2) (running), weights
+ *   p = 2^(s2 - r), probability operand P^ = E4M3(256 p) / 256,
+ *   l = sum P^, O = sum P^ V^ / l (bf16), LSE = (r + log2 l) ln 2.
+ * Inputs are the quantizer's outputs for Q (Hq heads), K and V (Hkv heads).
+ *   o          bf16 [T][Hq][d] (written)
+ *   lse        float [Hq][T] (written)
+ *   workspace  device scratch of at least flamia_attn_fwd_workspace_size(p)
+ *              bytes; its contents are overwritten.
+ * The fp4 pointers are reserved for FLAMIA_FP4_SCORE and must be NULL.
+ */
+size_t flamia_attn_fwd_workspace_size(const flamia_problem* p);
+flamia_status flamia_attn_fwd(const flamia_problem* p, const uint8_t* q_codes,
+                              const uint8_t* q_exps, const uint8_t* k_codes,
+                              const uint8_t* k_exps, const uint8_t* v_codes,
+                              const uint8_t* v_exps, const uint8_t* q_fp4,
+                              const uint8_t* q_fp4_scales, const uint8_t* k_fp4,
+                              const uint8_t* k_fp4_scales, uint16_t* o, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward (review section 5 Algorithm 1 steps 09-16; jaehun.me sections
+ * 3.1-3.4).  dO is quantized inside the call with the operand rule;
+ * D_i = dO^_i . O_i; P is rebuilt from the saved LSE; dP = dO^ V^T;
+ * dS = P (dP - D); P^ = E4M3(256 P) / 256; dS is quantized with one
+ * conservative exponent per document-local 32x32 block;
+ *   dV = P^T dO^,  dK = scale dS^T Q^,  dQ = scale dS^ K^.
+ * dQ partials are accumulated in FP16 after a per-row power-of-two prescale
+ * 2^k_i that depends only on what row i may see (k_i = 14 - C - (e_dO(i) +
+ * max visible V exponent + max visible K exponent), C = ceil(log2(4 scale d
+ * 448^3))), and unscaled at the end; with FLAMIA_DETERMINISTIC dQ is instead
+ * accumulated in FP32 registers by query-major blocks, so repeated calls are
+ * bitwise identical.  dK and dV sum over the q heads of each kv group.
+ *   o, lse     the forward's outputs
+ *   dout       bf16 [T][Hq][d]
+ *   dq         bf16 [T][Hq][d] (written)
+ *   dk, dv     bf16 [T][Hkv][d] (written)
+ *   workspace  at least flamia_attn_bwd_workspace_size(p) bytes; it holds the
+ *              quantized dO, D, k_i, the FP16 dQ accumulator and work lists,
+ *              at the offsets flamia_attn_bwd_workspace_layout reports.
+ */
+size_t flamia_attn_bwd_workspace_size(const flamia_problem* p);
+flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
+                              const uint8_t* q_exps, const uint8_t* k_codes,
+                              const uint8_t* k_exps, const uint8_t* v_codes,
+                              const uint8_t* v_exps, const uint8_t* q_fp4,
+                              const uint8_t* q_fp4_scales, const uint8_t* k_fp4,
+                              const uint8_t* k_fp4_scales, const uint16_t* o, const float* lse,
+                              const uint16_t* dout, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Byte offsets, inside the backward workspace, of what a backward call left
+ * there: dO codes uint8 [T][Hq][d], dO exponents uint8 [Hq][T], D float
+ * [Hq][T], prescale exponents int8 [Hq][T] and the FP16 dQ accumulator
+ * [T][Hq][d] (scaled by 2^k_i).  Returns FLAMIA_ERR_INVALID_ARG for an
+ * invalid problem. */
+typedef struct {
+    size_t do_codes, do_exps, delta, dq_prescale, dq_accum, total;
+} flamia_bwd_workspace_layout;
+flamia_status flamia_attn_bwd_workspace_layout(const flamia_problem* p,
+                                               flamia_bwd_workspace_layout* out);
+
+/* Static string for a status code. */
+const char* flamia_status_string(flamia_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLAMIA_H */

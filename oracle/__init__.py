@@ -162,6 +162,7 @@ def quantize_nvfp4(x, cu):
 MODE_ROUNDED = 0      # microscaled forward, l = sum of rounded weights
 MODE_UNROUNDED = 1    # microscaled forward, l = sum of unrounded weights
 MODE_REFERENCE = 2    # FP64 online softmax without probability rounding
+MODE_TILED = 3        # microscaled forward in the tile loop (running reference)
 
 
 def dequantize(codes, exps):
@@ -223,7 +224,7 @@ class Operands:
 
 
 def attn_fwd(cu, ops: Operands, scale=None, causal=True, mode=MODE_ROUNDED, kblock=32,
-             rows=None, want_rescale=False):
+             rows=None, want_rescale=False, want_flags=False):
     """Forward.  rows: None (all) or int array [n][2] of (q head, token).
     Returns (O float64 [T][Hq][d], LSE float64 [Hq][T][, n_rescale])."""
     cu = _c(cu, np.int32)
@@ -232,12 +233,19 @@ def attn_fwd(cu, ops: Operands, scale=None, causal=True, mode=MODE_ROUNDED, kblo
     O = np.zeros((T, Hq, d), dtype=np.float64)
     LSE = np.zeros((Hq, T), dtype=np.float64)
     nres = np.zeros((Hq, T), dtype=np.int32) if want_rescale else None
+    ties = np.zeros((Hq, T, 2), dtype=np.float64) if want_flags else None
     r = None if rows is None else _c(rows, np.int32).reshape(-1, 2)
     n = 0 if r is None else r.shape[0]
     _check(_load().orc_attn_fwd(
         T, len(cu) - 1, _p(cu), Hq, Hkv, d, ctypes.c_double(scale), int(bool(causal)),
-        *ops.ptrs(), mode, kblock, ctypes.c_int64(n), _p(r), _p(O), _p(LSE), _p(nres)))
-    return (O, LSE, nres) if want_rescale else (O, LSE)
+        *ops.ptrs(), mode, kblock, ctypes.c_int64(n), _p(r), _p(O), _p(LSE), _p(nres),
+        _p(ties)))
+    out = (O, LSE)
+    if want_rescale:
+        out += (nres,)
+    if want_flags:
+        out += (ties,)
+    return out
 
 
 def bwd_prep(cu, dO, O, k_exps, v_exps, Hkv, scale=None, causal=True, block=32):
@@ -284,7 +292,7 @@ def _pairs(heads, starts):
 
 
 def bwd_dq(cu, ops: Operands, G, D, LSE, scale=None, causal=True, mode=MODE_ROUNDED,
-           per_row_ds=False, qblocks=None):
+           per_row_ds=False, qblocks=None, want_flags=False):
     """dQ (float64 [T][Hq][d]) for the listed (q head, block start) pairs
     (default: every block of every head).  G: dequantized dO; D: [Hq][T];
     LSE: [Hq][T] natural log as saved by a forward."""
@@ -295,15 +303,19 @@ def bwd_dq(cu, ops: Operands, G, D, LSE, scale=None, causal=True, mode=MODE_ROUN
         qblocks = _pairs(range(Hq), doc_blocks(cu))
     qblocks = _c(qblocks, np.int32).reshape(-1, 2)
     dQ = np.zeros((T, Hq, d), dtype=np.float64)
+    tie = np.zeros((T, Hq), dtype=np.float64)
+    acc = np.zeros((T, Hq), dtype=np.float64)
+    absm = np.zeros((T, Hq), dtype=np.float64)
     _check(_load().orc_bwd_dq(
         T, len(cu) - 1, _p(cu), Hq, Hkv, d, ctypes.c_double(scale), int(bool(causal)),
         *ops.ptrs(), _p(_c(G, np.float64)), _p(_c(D, np.float64)), _p(_c(LSE, np.float64)),
-        mode, int(bool(per_row_ds)), ctypes.c_int64(qblocks.shape[0]), _p(qblocks), _p(dQ)))
-    return dQ
+        mode, int(bool(per_row_ds)), ctypes.c_int64(qblocks.shape[0]), _p(qblocks), _p(dQ),
+        _p(tie), _p(acc), _p(absm)))
+    return (dQ, tie, acc, absm) if want_flags else dQ
 
 
 def bwd_dkdv(cu, ops: Operands, G, D, LSE, scale=None, causal=True, mode=MODE_ROUNDED,
-             per_row_ds=False, kblocks=None):
+             per_row_ds=False, kblocks=None, want_flags=False):
     """dK, dV (float64 [T][Hkv][d]) for the listed (kv head, block start)
     pairs (default: every block of every kv head)."""
     cu = _c(cu, np.int32)
@@ -314,25 +326,33 @@ def bwd_dkdv(cu, ops: Operands, G, D, LSE, scale=None, causal=True, mode=MODE_RO
     kblocks = _c(kblocks, np.int32).reshape(-1, 2)
     dK = np.zeros((T, Hkv, d), dtype=np.float64)
     dV = np.zeros((T, Hkv, d), dtype=np.float64)
+    tie_k = np.zeros((T, Hkv), dtype=np.float64)
+    tie_v = np.zeros((T, Hkv), dtype=np.float64)
+    abs_k = np.zeros((T, Hkv), dtype=np.float64)
+    abs_v = np.zeros((T, Hkv), dtype=np.float64)
     _check(_load().orc_bwd_dkdv(
         T, len(cu) - 1, _p(cu), Hq, Hkv, d, ctypes.c_double(scale), int(bool(causal)),
         *ops.ptrs(), _p(_c(G, np.float64)), _p(_c(D, np.float64)), _p(_c(LSE, np.float64)),
         mode, int(bool(per_row_ds)), ctypes.c_int64(kblocks.shape[0]), _p(kblocks), _p(dK),
-        _p(dV)))
-    return dK, dV
+        _p(dV), _p(tie_k), _p(tie_v), _p(abs_k), _p(abs_v)))
+    return (dK, dV, tie_k, tie_v, abs_k, abs_v) if want_flags else (dK, dV)
 
 
 def bwd_block(cu, ops: Operands, G, D, LSE, h, q0, k0, scale=None, causal=True,
               mode=MODE_ROUNDED, per_row_ds=False):
     """One document-local 32x32 block of the recomputed backward.  Returns a
-    dict of [32][32] float64 arrays: P, dP, dS, Pq, dSk, dSq."""
+    dict of [32][32] float64 arrays: P, dP, dS, Pq, dSk, dSq, and the flip
+    steps stepP, stepSk, stepSq (nonzero where a GPU's FP32 evaluation may
+    round P^ or dS^ to the neighbouring E4M3 value)."""
     cu = _c(cu, np.int32)
     T, Hq, Hkv, d = ops.T, ops.Hq, ops.Hkv, ops.d
     scale = default_scale(d) if scale is None else scale
     out = {k: np.zeros((32, 32), dtype=np.float64) for k in ("P", "dP", "dS", "Pq", "dSk", "dSq")}
+    steps = np.zeros((3, 32, 32), dtype=np.float64)
     _check(_load().orc_bwd_block(
         T, len(cu) - 1, _p(cu), Hq, Hkv, d, ctypes.c_double(scale), int(bool(causal)),
         *ops.ptrs(), _p(_c(G, np.float64)), _p(_c(D, np.float64)), _p(_c(LSE, np.float64)),
         mode, int(bool(per_row_ds)), int(h), int(q0), int(k0),
-        *[_p(out[k]) for k in ("P", "dP", "dS", "Pq", "dSk", "dSq")]))
+        *[_p(out[k]) for k in ("P", "dP", "dS", "Pq", "dSk", "dSq")], _p(steps)))
+    out["stepP"], out["stepSk"], out["stepSq"] = steps[0], steps[1], steps[2]
     return out

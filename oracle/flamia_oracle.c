@@ -35,6 +35,23 @@
  * extraction) are listed in the repository's design notes; the ones that
  * change arithmetic are restated next to the code that implements them.
  *
+ * Rounding-tie flags: the GPU evaluates P and dS in FP32 and this oracle in
+ * FP64, so an element lying within FP32 evaluation noise of an E4M3 rounding
+ * midpoint (or a dS block whose max lies that close to an exponent
+ * threshold) can legitimately round either way; a row with few contributors
+ * then moves by one E4M3 step of one term.  The forward and backward routines
+ * report, per output row, a bound on how far such flips could move it (the
+ * sum over near-tie elements of their step times the magnitude of the
+ * companion operand row), so that comparisons can allow exactly that and
+ * report it instead of silently excluding rows.  The evaluation noise assumed
+ * is 2^-11 of the sum of the absolute terms of each dot product (the GPU's
+ * FP8 matrix cores round inside each instruction at about that level).  The
+ * gradient routines also report, per row, the largest sum of absolute terms
+ * of the gradient product itself, which bounds that rounding in the output.  orc_bwd_dq also reports,
+ * per row, the sum over the 128-key tiles of the largest partial-sum
+ * magnitude: dQ partials are accumulated in FP16 on the GPU, and that sum
+ * bounds the accumulation error.
+ *
  * Parity pins: every function here is pinned by tests under tests/ that check
  * it against values the pages print, closed forms, invariants or brute force.
  * The dQ prescale exponent (orc_bwd_prep, kpre) has no printed value on the
@@ -362,13 +379,31 @@ static inline const double* row(const double* X, int H, int d, int t, int h)
  * view (the E2M1 route) the score uses it ([R] S2: the mixed route
  * reconstructs scores from the selected Q/K format and re-quantizes Q and K
  * in E4M3 for the gradient products). */
-static double score(const orc_attn* a, int h, int i, int j)
+static double score_abs(const orc_attn* a, int h, int i, int j, double* sabs)
 {
     const double* q = row(a->Qs ? a->Qs : a->Q, a->Hq, a->d, i, h);
     const double* k = row(a->Ks ? a->Ks : a->K, a->Hkv, a->d, j, kv_head(a, h));
-    double acc = 0.0;
-    for (int c = 0; c < a->d; ++c) acc += q[c] * k[c];
+    double acc = 0.0, ab = 0.0;
+    for (int c = 0; c < a->d; ++c) {
+        acc += q[c] * k[c];
+        ab += fabs(q[c] * k[c]);
+    }
+    if (sabs) *sabs = a->scale * ab;
     return a->scale * acc;
+}
+
+/* Evaluation noise assumed for a GPU dot product of E4M3 codes: 2^-11 of the
+ * sum of the absolute values of its terms.  (gfx950's FP8 matrix cores keep
+ * about 12 bits below the largest product inside one instruction: measured
+ * deviations from FP64 reach 2^-12.6 of that sum.) */
+#define ORC_FP32_NOISE 4.8828125e-04
+
+/* Size of the jump between the E4M3 values y - tol and y + tol round to (0
+ * when both round alike), in code units. */
+static double tie_step(double y, double tol)
+{
+    return fabs(orc_e4m3_decode(orc_e4m3_encode(y + tol)) -
+                orc_e4m3_decode(orc_e4m3_encode(y - tol)));
 }
 
 /* Visible keys of query i in document b: [s_b, i] when causal, else the whole
@@ -389,6 +424,14 @@ static inline int key_end(const orc_attn* a, int b, int i)
  *      boost 256 of [R] S5 "A range budget"); l = sum P^; O = sum P^ V / l;
  *      LSE = (r + log2 l) ln 2.
  *   1  as 0 with the unrounded normaliser l = sum p.
+ *   3  the same microscaled forward following the tile loop of the review's
+ *      Algorithm 1 (steps 04-08): over document-local key tiles of `kblock`
+ *      keys, the row reference r rises to ceil(max s2) of the keys seen so far;
+ *      when it rises, l and the accumulator are multiplied by the exact power
+ *      of two 2^(r_old - r_new); each tile's weights are rounded against the
+ *      current r, P^ = E4M3(256 * 2^(s2 - r)) / 256, and added to l and to the
+ *      accumulator.  Equal to mode 0 except for weights that are E4M3
+ *      subnormal (256 p < 2^-6) against one of the references.
  *   2  reference math: blockwise online softmax in FP64 over document-local
  *      key blocks of `kblock` keys ([R] S2 "Why flash tiling recomputes
  *      scores"; [F] "Attention without the score matrix"): running max m,
@@ -396,18 +439,19 @@ static inline int key_end(const orc_attn* a, int b, int i)
  *      the max grows; O = acc / l; LSE = m + ln l.
  * Rows outside every document get O = 0 and LSE = +inf ([R] S6). */
 static void fwd_row(const orc_attn* a, int mode, int kblock, int h, int i, double* O, double* LSE,
-                    int32_t* n_rescale, double* s_buf)
+                    int32_t* n_rescale, double* tie, double* s_buf, double* a_buf)
 {
     int d = a->d, g = kv_head(a, h);
     int b = doc_of(a->B, a->cu, i);
     for (int c = 0; c < d; ++c) O[c] = 0.0;
     if (n_rescale) *n_rescale = 0;
+    if (tie) tie[0] = tie[1] = 0.0;
     if (b < 0) {
         *LSE = INFINITY;
         return;
     }
     int j0 = a->cu[b], j1 = key_end(a, b, i);
-    for (int j = j0; j < j1; ++j) s_buf[j - j0] = score(a, h, i, j);
+    for (int j = j0; j < j1; ++j) s_buf[j - j0] = score_abs(a, h, i, j, &a_buf[j - j0]);
 
     if (mode == 0 || mode == 1) {
         double mx = -INFINITY;
@@ -417,15 +461,77 @@ static void fwd_row(const orc_attn* a, int mode, int kblock, int h, int i, doubl
         }
         double r = ceil(mx);
         double l = 0.0;
+        double tie_w = 0.0, tie_wv = 0.0; /* sum of flip steps, and times |V_j| */
         for (int j = j0; j < j1; ++j) {
             double p = exp2(s_buf[j - j0] * M_LOG2E - r);
             double ph = orc_e4m3_decode(orc_e4m3_encode(256.0 * p)) / 256.0;
+            double tol = 256.0 * p * (ORC_FP32_NOISE * a_buf[j - j0] + ldexp(1.0, -20));
+            double step = tie_step(256.0 * p, tol) / 256.0;
+            if (step > 0.0) {
+                const double* vj = row(a->V, a->Hkv, d, j, g);
+                double vm = 0.0;
+                for (int c = 0; c < d; ++c) vm = fabs(vj[c]) > vm ? fabs(vj[c]) : vm;
+                tie_w += step;
+                tie_wv += step * vm;
+            }
             l += (mode == 0) ? ph : p;
             const double* v = row(a->V, a->Hkv, d, j, g);
             for (int c = 0; c < d; ++c) O[c] += ph * v[c];
         }
         for (int c = 0; c < d; ++c) O[c] /= l;
         *LSE = (r + log2(l)) * M_LN2;
+        if (tie) {
+            /* a flip of weight j by step changes O by step (V_j - O) / l and l
+               by step: bounds on |dO| and on the relative change of l */
+            double om = 0.0;
+            for (int c = 0; c < d; ++c) om = fabs(O[c]) > om ? fabs(O[c]) : om;
+            tie[0] = (tie_wv + tie_w * om) / l;
+            tie[1] = tie_w / l;
+        }
+        return;
+    }
+
+    if (mode == 3) {
+        double r = -INFINITY, l = 0.0, tie_w = 0.0, tie_wv = 0.0;
+        for (int k0 = j0; k0 < j1; k0 += kblock) {
+            int k1 = k0 + kblock < j1 ? k0 + kblock : j1;
+            double mb = -INFINITY;
+            for (int j = k0; j < k1; ++j)
+                if (s_buf[j - j0] * M_LOG2E > mb) mb = s_buf[j - j0] * M_LOG2E;
+            double r_new = ceil(mb) > r ? ceil(mb) : r;
+            if (r != -INFINITY && r_new > r) {
+                double alpha = exp2(r - r_new);
+                l *= alpha;
+                tie_w *= alpha;
+                tie_wv *= alpha;
+                for (int c = 0; c < d; ++c) O[c] *= alpha;
+                if (n_rescale) ++*n_rescale;
+            }
+            r = r_new;
+            for (int j = k0; j < k1; ++j) {
+                double p = exp2(s_buf[j - j0] * M_LOG2E - r);
+                double ph = orc_e4m3_decode(orc_e4m3_encode(256.0 * p)) / 256.0;
+                double tol = 256.0 * p * (ORC_FP32_NOISE * a_buf[j - j0] + ldexp(1.0, -20));
+                double step = tie_step(256.0 * p, tol) / 256.0;
+                const double* vj = row(a->V, a->Hkv, d, j, g);
+                if (step > 0.0) {
+                    double vm = 0.0;
+                    for (int c = 0; c < d; ++c) vm = fabs(vj[c]) > vm ? fabs(vj[c]) : vm;
+                    tie_w += step;
+                    tie_wv += step * vm;
+                }
+                l += ph;
+                for (int c = 0; c < d; ++c) O[c] += ph * vj[c];
+            }
+        }
+        for (int c = 0; c < d; ++c) O[c] /= l;
+        *LSE = (r + log2(l)) * M_LN2;
+        if (tie) {
+            double om = 0.0;
+            for (int c = 0; c < d; ++c) om = fabs(O[c]) > om ? fabs(O[c]) : om;
+            tie[0] = (tie_wv + tie_w * om) / l;
+            tie[1] = tie_w / l;
+        }
         return;
     }
 
@@ -463,10 +569,10 @@ static void fwd_row(const orc_attn* a, int mode, int kblock, int h, int i, doubl
 int orc_attn_fwd(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale,
                  int causal, const double* Q, const double* K, const double* V, const double* Qs,
                  const double* Ks, int mode, int kblock, int64_t n_rows, const int32_t* rows,
-                 double* O, double* LSE, int32_t* n_rescale)
+                 double* O, double* LSE, int32_t* n_rescale, double* ties)
 {
     if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
-    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d < 1 || kblock < 1 || mode < 0 || mode > 2)
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d < 1 || kblock < 1 || mode < 0 || mode > 3)
         return ORC_EBADARG;
     orc_attn a = {T, B, Hq, Hkv, d, causal, cu, scale, Q, K, V, Qs, Ks};
     int64_t n = rows ? n_rows : (int64_t)Hq * T;
@@ -474,14 +580,17 @@ int orc_attn_fwd(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double
 #pragma omp parallel
     {
         double* s_buf = (double*)malloc(sizeof(double) * Tn);
+        double* a_buf = (double*)malloc(sizeof(double) * Tn);
 #pragma omp for schedule(dynamic, 4)
         for (int64_t k = 0; k < n; ++k) {
             int h = rows ? rows[2 * k] : (int)(k / Tn);
             int t = rows ? rows[2 * k + 1] : (int)(k % Tn);
             fwd_row(&a, mode, kblock, h, t, O + ((size_t)t * Hq + h) * d, LSE + (size_t)h * T + t,
-                    n_rescale ? n_rescale + (size_t)h * T + t : NULL, s_buf);
+                    n_rescale ? n_rescale + (size_t)h * T + t : NULL,
+                    ties ? ties + 2 * ((size_t)h * T + t) : NULL, s_buf, a_buf);
         }
         free(s_buf);
+        free(a_buf);
     }
     return ORC_OK;
 }
@@ -516,6 +625,30 @@ int orc_bwd_prep(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double
     int rc = orc_quantize(T, B, cu, Hq, d, dO, block, 0, do_codes, do_exps);
     if (rc != ORC_OK) return rc;
     int C = (int)ceil(log2(4.0 * scale * d * 448.0 * 448.0 * 448.0));
+    /* largest V and K exponents over the keys each row may see: a running
+       maximum along each document (causal), or the document maximum */
+    int* vis_v = (int*)malloc(sizeof(int) * ((size_t)Hkv * T + 1));
+    int* vis_k = (int*)malloc(sizeof(int) * ((size_t)Hkv * T + 1));
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int g = 0; g < Hkv; ++g) {
+        for (int b = 0; b < B; ++b) {
+            int mv = -1000, mk = -1000;
+            for (int j = cu[b]; j < cu[b + 1]; ++j) {
+                int ev = (int)ve[(size_t)g * T + j] - 127, ek = (int)ke[(size_t)g * T + j] - 127;
+                if (ev > mv) mv = ev;
+                if (ek > mk) mk = ek;
+                if (causal) {
+                    vis_v[(size_t)g * T + j] = mv;
+                    vis_k[(size_t)g * T + j] = mk;
+                }
+            }
+            if (!causal)
+                for (int j = cu[b]; j < cu[b + 1]; ++j) {
+                    vis_v[(size_t)g * T + j] = mv;
+                    vis_k[(size_t)g * T + j] = mk;
+                }
+        }
+    }
 #pragma omp parallel for collapse(2) schedule(dynamic, 64)
     for (int h = 0; h < Hq; ++h) {
         for (int t = 0; t < T; ++t) {
@@ -536,20 +669,15 @@ int orc_bwd_prep(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double
                 if (g_hat != 0.0) nonzero = 1;
             }
             D[(size_t)h * T + t] = acc;
-            int j0 = cu[b], j1 = causal ? t + 1 : cu[b + 1];
-            int maxv = -1000, maxk = -1000;
-            for (int j = j0; j < j1; ++j) {
-                int ev = (int)ve[(size_t)g * T + j] - 127, ek = (int)ke[(size_t)g * T + j] - 127;
-                if (ev > maxv) maxv = ev;
-                if (ek > maxk) maxk = ek;
-            }
-            int E = eg + maxv + maxk;
+            int E = eg + vis_v[(size_t)g * T + t] + vis_k[(size_t)g * T + t];
             int k = 14 - C - E;
             if (k < -60) k = -60;
             if (k > 60) k = 60;
             kpre[(size_t)h * T + t] = nonzero ? k : 0;
         }
     }
+    free(vis_v);
+    free(vis_k);
     return ORC_OK;
 }
 
@@ -576,11 +704,17 @@ typedef struct {
  *       block (the per-query-row option, [R] S4, [K] S3.2), used for dQ.
  * Entries with j > i (causal) and entries outside the block are zero. */
 static void bwd_block(const orc_bwd* w, int h, int q0, int q1, int k0, int k1, double* P,
-                      double* dP, double* dS, double* Pq, double* dSk, double* dSq)
+                      double* dP, double* dS, double* Pq, double* dSk, double* dSq, double* stp)
 {
+    /* stp: [3][1024] flip steps of P^ (P units), dS^ on the 32x32 grid and
+       dS^ of the dQ product (dS units); 0 where the rounding is settled */
     const orc_attn* a = w->a;
     int T = a->T, d = a->d, g = kv_head(a, h);
-    for (int k = 0; k < 1024; ++k) P[k] = dP[k] = dS[k] = Pq[k] = dSk[k] = dSq[k] = 0.0;
+    double tolv[1024];
+    for (int k = 0; k < 1024; ++k) {
+        P[k] = dP[k] = dS[k] = Pq[k] = dSk[k] = dSq[k] = tolv[k] = 0.0;
+        stp[k] = stp[1024 + k] = stp[2048 + k] = 0.0;
+    }
     double amax = 0.0;
     for (int i = q0; i < q1; ++i) {
         const double* gi = row(w->G, a->Hq, d, i, h);
@@ -588,22 +722,61 @@ static void bwd_block(const orc_bwd* w, int h, int q0, int q1, int k0, int k1, d
             if (a->causal && j > i) continue;
             int e = (i - q0) * 32 + (j - k0);
             const double* vj = row(a->V, a->Hkv, d, j, g);
-            P[e] = exp(score(a, h, i, j) - w->LSE[(size_t)h * T + i]);
-            double acc = 0.0;
-            for (int c = 0; c < d; ++c) acc += gi[c] * vj[c];
+            double sabs;
+            P[e] = exp(score_abs(a, h, i, j, &sabs) - w->LSE[(size_t)h * T + i]);
+            double acc = 0.0, pabs = 0.0;
+            for (int c = 0; c < d; ++c) {
+                acc += gi[c] * vj[c];
+                pabs += fabs(gi[c] * vj[c]);
+            }
             dP[e] = acc;
             dS[e] = P[e] * (dP[e] - w->D[(size_t)h * T + i]);
             if (fabs(dS[e]) > amax) amax = fabs(dS[e]);
             Pq[e] = w->mode == 0 ? orc_e4m3_decode(orc_e4m3_encode(256.0 * P[e])) / 256.0 : P[e];
+            /* FP32 evaluation noise of P (through the score) and of dP - D,
+               which can cancel */
+            double ds_rel = ORC_FP32_NOISE * sabs + ldexp(1.0, -20);
+            tolv[e] = fabs(dS[e]) * ds_rel + P[e] * ORC_FP32_NOISE * 2.0 * (pabs + fabs(dP[e]));
+            if (w->mode == 0) stp[e] = tie_step(256.0 * P[e], 256.0 * P[e] * ds_rel) / 256.0;
         }
     }
     int eb = orc_ceil_exponent(amax);
+    if (w->mode == 0) {
+        double tmax = 0.0;
+        for (int k = 0; k < 1024; ++k) tmax = tolv[k] > tmax ? tolv[k] : tmax;
+        int e_hi = orc_ceil_exponent(amax + tmax);
+        int block_shift = orc_ceil_exponent(amax - tmax) != e_hi;
+        for (int i = q0; i < q1; ++i)
+            for (int j = k0; j < k1; ++j) {
+                int e = (i - q0) * 32 + (j - k0);
+                if (a->causal && j > i) continue;
+                double st = ldexp(tie_step(ldexp(dS[e], -eb), ldexp(tolv[e], -eb)), eb);
+                /* an exponent shift moves values below the coarser normal
+                   range by up to one subnormal step of the larger scale */
+                if (block_shift && fabs(dS[e]) < ldexp(1.0, e_hi - 6)) st += ldexp(1.0, e_hi - 9);
+                stp[1024 + e] = st;
+                stp[2048 + e] = st;
+            }
+    }
     for (int i = q0; i < q1; ++i) {
         int base = (i - q0) * 32;
         double ramax = 0.0;
         for (int j = k0; j < k1; ++j)
             if (fabs(dS[base + j - k0]) > ramax) ramax = fabs(dS[base + j - k0]);
         int er = orc_ceil_exponent(ramax);
+        if (w->mode == 0 && w->per_row_ds) {
+            double rt = 0.0;
+            for (int j = k0; j < k1; ++j) rt = tolv[base + j - k0] > rt ? tolv[base + j - k0] : rt;
+            int r_hi = orc_ceil_exponent(ramax + rt);
+            int shift = orc_ceil_exponent(ramax - rt) != r_hi;
+            for (int j = k0; j < k1; ++j) {
+                int e = base + (j - k0);
+                if (a->causal && j > i) continue;
+                double st = ldexp(tie_step(ldexp(dS[e], -er), ldexp(tolv[e], -er)), er);
+                if (shift && fabs(dS[e]) < ldexp(1.0, r_hi - 6)) st += ldexp(1.0, r_hi - 9);
+                stp[2048 + e] = st;
+            }
+        }
         for (int j = k0; j < k1; ++j) {
             int e = base + (j - k0);
             if (a->causal && j > i) continue;
@@ -634,7 +807,7 @@ int orc_bwd_block(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, doubl
                   int causal, const double* Q, const double* K, const double* V,
                   const double* Qs, const double* Ks, const double* G, const double* D,
                   const double* LSE, int mode, int per_row_ds, int h, int q0, int k0, double* P,
-                  double* dP, double* dS, double* Pq, double* dSk, double* dSq)
+                  double* dP, double* dS, double* Pq, double* dSk, double* dSq, double* stp)
 {
     if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
     int b = doc_of(B, cu, q0);
@@ -644,7 +817,7 @@ int orc_bwd_block(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, doubl
     orc_bwd w = {&a, G, D, LSE, mode, per_row_ds};
     int q1 = q0 + 32 < cu[b + 1] ? q0 + 32 : cu[b + 1];
     int k1 = k0 + 32 < cu[b + 1] ? k0 + 32 : cu[b + 1];
-    bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq);
+    bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq, stp);
     return ORC_OK;
 }
 
@@ -654,7 +827,8 @@ int orc_bwd_block(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, doubl
 int orc_bwd_dq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale, int causal,
                const double* Q, const double* K, const double* V, const double* Qs,
                const double* Ks, const double* G, const double* D, const double* LSE, int mode,
-               int per_row_ds, int64_t n, const int32_t* qblocks, double* dQ)
+               int per_row_ds, int64_t n, const int32_t* qblocks, double* dQ, double* tie,
+               double* acc_mag, double* abs_mag)
 {
     if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
     if (Hkv < 1 || Hq % Hkv != 0) return ORC_EBADARG;
@@ -664,6 +838,9 @@ int orc_bwd_dq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double s
 #pragma omp parallel
     {
         double* buf = (double*)malloc(sizeof(double) * 6 * 1024);
+        double* stp = (double*)malloc(sizeof(double) * 3 * 1024);
+        double* part = (double*)malloc(sizeof(double) * 32 * d);
+        double* absp = (double*)malloc(sizeof(double) * 32 * d);
 #pragma omp for schedule(dynamic)
         for (int64_t k = 0; k < n; ++k) {
             int h = qblocks[2 * k], q0 = qblocks[2 * k + 1];
@@ -672,21 +849,58 @@ int orc_bwd_dq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double s
             int kend = causal ? q1 : cu[b + 1];
             double *P = buf, *dP = buf + 1024, *dS = buf + 2048, *Pq = buf + 3072,
                    *dSk = buf + 4096, *dSq = buf + 5120;
+            for (int x = 0; x < 32 * d; ++x) part[x] = absp[x] = 0.0;
             for (int k0 = cu[b]; k0 < kend; k0 += 32) {
                 int k1 = k0 + 32 < cu[b + 1] ? k0 + 32 : cu[b + 1];
-                bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq);
+                bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq, stp);
                 for (int i = q0; i < q1; ++i) {
                     double* out = dQ + ((size_t)i * Hq + h) * d;
+                    if (tie)
+                        for (int j = k0; j < k1; ++j) {
+                            double st = stp[2048 + (i - q0) * 32 + (j - k0)];
+                            if (st == 0.0) continue;
+                            double km = 0.0;
+                            for (int c = 0; c < d; ++c)
+                                km = fabs(row(K, Hkv, d, j, g)[c]) > km ? fabs(row(K, Hkv, d, j, g)[c]) : km;
+                            tie[(size_t)i * Hq + h] += scale * st * km;
+                        }
                     for (int c = 0; c < d; ++c) {
-                        double acc = 0.0;
-                        for (int j = k0; j < k1; ++j)
-                            acc += dSq[(i - q0) * 32 + (j - k0)] * row(K, Hkv, d, j, g)[c];
+                        double acc = 0.0, ab = 0.0;
+                        for (int j = k0; j < k1; ++j) {
+                            double t = dSq[(i - q0) * 32 + (j - k0)] * row(K, Hkv, d, j, g)[c];
+                            acc += t;
+                            ab += fabs(t);
+                        }
                         out[c] += scale * acc;
+                        part[(i - q0) * d + c] += scale * acc;
+                        absp[(i - q0) * d + c] += scale * ab;
+                    }
+                }
+                if (abs_mag && k0 + 32 >= kend)
+                    for (int i = q0; i < q1; ++i) {
+                        double m = 0.0;
+                        for (int c = 0; c < d; ++c) m = absp[(i - q0) * d + c] > m ? absp[(i - q0) * d + c] : m;
+                        abs_mag[(size_t)i * Hq + h] = m;
+                    }
+                /* per 128-key tile (document-relative): add the tile partial's
+                   largest magnitude to the row's accumulation magnitude */
+                if (acc_mag && (((k0 - cu[b]) / 32) % 4 == 3 || k0 + 32 >= kend)) {
+                    for (int i = q0; i < q1; ++i) {
+                        double m = 0.0;
+                        for (int c = 0; c < d; ++c) {
+                            double v = fabs(part[(i - q0) * d + c]);
+                            m = v > m ? v : m;
+                            part[(i - q0) * d + c] = 0.0;
+                        }
+                        acc_mag[(size_t)i * Hq + h] += m;
                     }
                 }
             }
         }
         free(buf);
+        free(stp);
+        free(part);
+        free(absp);
     }
     return ORC_OK;
 }
@@ -699,7 +913,8 @@ int orc_bwd_dq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double s
 int orc_bwd_dkdv(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale,
                  int causal, const double* Q, const double* K, const double* V, const double* Qs,
                  const double* Ks, const double* G, const double* D, const double* LSE, int mode,
-                 int per_row_ds, int64_t n, const int32_t* kblocks, double* dK, double* dV)
+                 int per_row_ds, int64_t n, const int32_t* kblocks, double* dK, double* dV,
+                 double* tie_k, double* tie_v, double* abs_k, double* abs_v)
 {
     if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
     if (Hkv < 1 || Hq % Hkv != 0) return ORC_EBADARG;
@@ -710,36 +925,72 @@ int orc_bwd_dkdv(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double
 #pragma omp parallel
     {
         double* buf = (double*)malloc(sizeof(double) * 6 * 1024);
+        double* stp = (double*)malloc(sizeof(double) * 3 * 1024);
+        double* ak_sum = (double*)malloc(sizeof(double) * 32 * d);
+        double* av_sum = (double*)malloc(sizeof(double) * 32 * d);
 #pragma omp for schedule(dynamic)
         for (int64_t k = 0; k < n; ++k) {
             int g = kblocks[2 * k], k0 = kblocks[2 * k + 1];
             int b = doc_of(B, cu, k0);
             int k1 = k0 + 32 < cu[b + 1] ? k0 + 32 : cu[b + 1];
+            for (int x = 0; x < 32 * d; ++x) ak_sum[x] = av_sum[x] = 0.0;
             double *P = buf, *dP = buf + 1024, *dS = buf + 2048, *Pq = buf + 3072,
                    *dSk = buf + 4096, *dSq = buf + 5120;
             for (int h = g * Gr; h < (g + 1) * Gr; ++h) {
                 int qstart = causal ? k0 : cu[b];
                 for (int q0 = qstart; q0 < cu[b + 1]; q0 += 32) {
                     int q1 = q0 + 32 < cu[b + 1] ? q0 + 32 : cu[b + 1];
-                    bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq);
+                    bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq, stp);
                     for (int j = k0; j < k1; ++j) {
                         double* ov = dV + ((size_t)j * Hkv + g) * d;
-                        double* ok = dK + ((size_t)j * Hkv + g) * d;
-                        for (int c = 0; c < d; ++c) {
-                            double av = 0.0, ak = 0.0;
+                        if (tie_k && tie_v)
                             for (int i = q0; i < q1; ++i) {
                                 int e = (i - q0) * 32 + (j - k0);
-                                av += Pq[e] * row(G, Hq, d, i, h)[c];
-                                ak += dSk[e] * row(Q, Hq, d, i, h)[c];
+                                if (stp[e] == 0.0 && stp[1024 + e] == 0.0) continue;
+                                double qm = 0.0, gm = 0.0;
+                                for (int c = 0; c < d; ++c) {
+                                    double qv = fabs(row(Q, Hq, d, i, h)[c]), gv = fabs(row(G, Hq, d, i, h)[c]);
+                                    qm = qv > qm ? qv : qm;
+                                    gm = gv > gm ? gv : gm;
+                                }
+                                tie_v[(size_t)j * Hkv + g] += stp[e] * gm;
+                                tie_k[(size_t)j * Hkv + g] += scale * stp[1024 + e] * qm;
+                            }
+                        double* ok = dK + ((size_t)j * Hkv + g) * d;
+                        for (int c = 0; c < d; ++c) {
+                            double av = 0.0, ak = 0.0, bv = 0.0, bk = 0.0;
+                            for (int i = q0; i < q1; ++i) {
+                                int e = (i - q0) * 32 + (j - k0);
+                                double tv = Pq[e] * row(G, Hq, d, i, h)[c];
+                                double tk = dSk[e] * row(Q, Hq, d, i, h)[c];
+                                av += tv;
+                                ak += tk;
+                                bv += fabs(tv);
+                                bk += fabs(tk);
                             }
                             ov[c] += av;
                             ok[c] += scale * ak;
+                            av_sum[(j - k0) * d + c] += bv;
+                            ak_sum[(j - k0) * d + c] += scale * bk;
                         }
                     }
                 }
             }
+            if (abs_k && abs_v)
+                for (int j = k0; j < k1; ++j) {
+                    double mk = 0.0, mv = 0.0;
+                    for (int c = 0; c < d; ++c) {
+                        mk = ak_sum[(j - k0) * d + c] > mk ? ak_sum[(j - k0) * d + c] : mk;
+                        mv = av_sum[(j - k0) * d + c] > mv ? av_sum[(j - k0) * d + c] : mv;
+                    }
+                    abs_k[(size_t)j * Hkv + g] = mk;
+                    abs_v[(size_t)j * Hkv + g] = mv;
+                }
         }
         free(buf);
+        free(stp);
+        free(ak_sum);
+        free(av_sum);
     }
     return ORC_OK;
 }

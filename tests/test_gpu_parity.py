@@ -1,0 +1,89 @@
+"""GPU parity: the HIP path through the C ABI against the FP64 oracle on the
+same seeded inputs.  Codes, exponents and prescale exponents bit-exact;
+forward and backward within the stated tolerances."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_helpers import check_fwd, check_grad, dq_tiles, log, oracle_operands, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # name, lens, capacity, Hq, Hkv, d, causal
+    ("one_doc_d64", [256], 256, 1, 1, 64, True),
+    ("ragged_d128", [300, 7, 129, 1, 64], 520, 2, 2, 128, True),
+    ("gqa_d128", [190, 333], 560, 4, 2, 128, True),
+    ("gqa_d64_tail", [45, 250, 97], 400, 6, 2, 64, True),
+    ("noncausal_d128", [150, 80, 33], 300, 2, 1, 128, False),
+]
+
+
+def _workload(name, lens, cap, Hq, Hkv, d, causal, seed=0):
+    return workloads.make(name, seed, cap, lens, Hq, Hkv, d,
+                          flags=workloads.FLAG_CAUSAL if causal else 0)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_forward_backward(case):
+    name, lens, cap, Hq, Hkv, d, causal = case
+    log("case %s" % name)
+    w = _workload(*case)
+    g = run_gpu(w)
+    # quantizer: bit-exact
+    q, k, v = oracle_operands(w)
+    for tag, (c, e) in (("q", q), ("k", k), ("v", v)):
+        assert np.array_equal(g[tag + "c"], c), tag + " codes"
+        assert np.array_equal(g[tag + "e"], e), tag + " exps"
+    # forward against the microscaled oracle
+    ops = oracle.Operands.from_codes(q, k, v)
+    O, L, ties = oracle.attn_fwd(w.cu, ops, causal=causal, mode=oracle.MODE_TILED, kblock=64,
+                                   want_flags=True)
+    check_fwd(g["O"].reshape(-1, d), g["LSE"].T.ravel(), O.reshape(-1, d), L.T.ravel(),
+              ties.transpose(1, 0, 2).reshape(-1, 2), tag=name)
+    # causal: the first token of every document sees only itself, so O equals
+    # its dequantized V row exactly
+    for s, e_ in zip(w.cu[:-1], w.cu[1:]):
+        if e_ > s and causal:
+            for h in range(Hq):
+                assert np.array_equal(g["O"][s, h], oracle.to_bf16(ops.V[s, h * Hkv // Hq]))
+    # backward, from the GPU's saved O and LSE
+    gc, ge, D, kpre = oracle.bwd_prep(w.cu, w.do, g["O"], k[1], v[1], Hkv, causal=causal)
+    assert np.array_equal(g["gc"], gc) and np.array_equal(g["ge"], ge)
+    assert np.array_equal(g["kpre"].astype(np.int32), kpre)
+    assert np.allclose(g["D"], D, rtol=1e-4, atol=1e-6 * np.abs(D).max())
+    G = oracle.dequantize(gc, ge)
+    lse = g["LSE"].astype(np.float64)
+    dQ, tq, acc, aq = oracle.bwd_dq(w.cu, ops, G, D, lse, causal=causal, want_flags=True)
+    dK, dV, tk, tv, ak, av = oracle.bwd_dkdv(w.cu, ops, G, D, lse, causal=causal, want_flags=True)
+    nt = np.repeat(dq_tiles(w.cu, w.T, causal)[:, None], Hq, axis=1)
+    check_grad(g["dQ"], dQ, name + " dQ", tq, acc=acc, ntiles=nt, absm=aq)
+    check_grad(g["dK"], dK, name + " dK", tk, absm=ak)
+    check_grad(g["dV"], dV, name + " dV", tv, absm=av)
+    # padding rows
+    n = int(w.cu[-1])
+    assert np.all(g["O"][n:] == 0) and np.all(np.isinf(g["LSE"][:, n:]))
+    assert np.all(g["dQ"][n:] == 0) and np.all(g["dK"][n:] == 0) and np.all(g["dV"][n:] == 0)
+
+
+def test_quantizer_per_token_mode_bit_exact():
+    w = _workload("pt", [100, 61], 170, 3, 1, 128, True)
+    g = run_gpu(w, backward=False, scale_mode=1)
+    c, e = oracle.quantize(w.q, w.cu, block=1)
+    assert np.array_equal(g["qc"], c) and np.array_equal(g["qe"], e)
+
+
+def test_quantizer_edge_values_bit_exact():
+    # zero blocks, a huge outlier, bf16 subnormals and negative zeros
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((96, 2, 64)).astype(np.float32)
+    x[0:32] = 0.0
+    x[40, 1, 5] = 3.0e38
+    x[70:80] *= np.float32(1e-39)
+    x[81, 0, :] = -0.0
+    w = workloads.make("edge", 0, 96, [37, 59], 2, 2, 64)
+    w.q = workloads.f32_to_bf16_bits(x)
+    g = run_gpu(w, backward=False)
+    c, e = oracle.quantize(w.q, w.cu)
+    assert np.array_equal(g["qc"], c) and np.array_equal(g["qe"], e)

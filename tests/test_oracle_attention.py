@@ -155,3 +155,48 @@ def test_mirror_within_rounding_bound_of_reference():
     # and on typical data it is far inside the bound
     cos = np.dot(Om.ravel(), Or.ravel()) / np.linalg.norm(Om) / np.linalg.norm(Or)
     assert cos > 0.999
+
+
+def test_tiled_mode_equals_final_reference_on_normal_weights():
+    # with every weight exactly representable the tile loop (any tile size)
+    # equals the final-reference definition and the FP64 reference
+    rng = np.random.default_rng(4)
+    T, d = 90, 4
+    Q = np.zeros((T, 1, d))
+    Q[:, 0, 0] = 1.0
+    K = np.zeros((T, 1, d))
+    K[:, 0, 0] = rng.integers(-12, 1, T)
+    V = rng.integers(-8, 9, (T, 1, d)).astype(np.float64)
+    cu = np.array([0, 17, 90], dtype=np.int32)
+    ops = oracle.Operands(Q, K, V)
+    Or, Lr = oracle.attn_fwd(cu, ops, scale=math.log(2), mode=oracle.MODE_REFERENCE)
+    rises = 0
+    for kb in (1, 7, 64):
+        Ot, Lt, nres = oracle.attn_fwd(cu, ops, scale=math.log(2), mode=oracle.MODE_TILED,
+                                       kblock=kb, want_rescale=True)
+        assert np.allclose(Ot, Or, rtol=1e-12, atol=1e-12)
+        assert np.allclose(Lt, Lr, rtol=1e-12, atol=1e-12)
+        rises += int(nres.max())
+    assert rises > 0  # the running reference did rise in this data
+
+
+def test_tiled_mode_differs_only_by_subnormal_weights():
+    # per weight the tile loop and the final reference differ by at most half
+    # an E4M3 subnormal step (2^-10 of the boosted weight, i.e. 2^-18 of the
+    # row reference), so |dl| <= n 2^-18 and |dO| <= n 2^-18 max|V| / l
+    w = small_problem(13, [300, 77], 2, 1, 64, capacity=400, scale_q=3.0)
+    q, k, v = quantized_operands(w)
+    ops = oracle.Operands.from_codes(q, k, v)
+    O0, L0 = oracle.attn_fwd(w.cu, ops, mode=oracle.MODE_ROUNDED)
+    for kb in (64, 128):
+        O3, L3 = oracle.attn_fwd(w.cu, ops, mode=oracle.MODE_TILED, kblock=kb)
+        for b in range(2):
+            s, e = int(w.cu[b]), int(w.cu[b + 1])
+            n = np.arange(1, e - s + 1)[:, None]
+            bound = n * 2.0 ** -18 * np.abs(ops.V).max() * 4
+            assert np.all(np.abs(O3[s:e] - O0[s:e]).max(axis=2) <= bound)
+        assert np.nanmax(np.abs(L3 - L0)[np.isfinite(L0)]) < 1e-2
+    # the first token of each document is still exactly its value row
+    O3, _ = oracle.attn_fwd(w.cu, ops, mode=oracle.MODE_TILED, kblock=64)
+    for s in w.cu[:-1]:
+        assert np.array_equal(oracle.to_bf16(O3[s, 0]), oracle.to_bf16(ops.V[s, 0]))
