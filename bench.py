@@ -1,0 +1,229 @@
+"""Benchmark of the causal packed microscaled attention hot path on one MI355X.
+
+One step = quantize Q, K, V (token-block E4M3) + forward + backward (dO
+quantization, D, prescale, recomputed P/dP/dS, dK/dV/dQ, dQ finalize), the
+full training call, on seeded synthetic inputs already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload packed_mha]
+
+Prints one JSON line.  value = algorithmic FLOPs of attention fwd+bwd
+(14 d Hq x visible pairs; a multiply-add counts 2) per second of the step.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t pairs through the HIP runtime (plumbing for kernel timing)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
+                                            ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def cpu_baseline(w, flop_target=3e11):
+    """The FP64 oracle on a bounded sample of the same workload: the first q
+    heads (whole kv groups), every document, quantize + forward + backward,
+    sized to about `flop_target` algorithmic FLOPs (10-30 s on a host)."""
+    import oracle
+    oracle.build()
+    G = w.Hq // w.Hkv
+    per_head = 14.0 * w.d * w.visible_pairs()
+    nh = int(round(flop_target / per_head / G)) * G
+    nh = min(w.Hq, max(G, nh))
+    nkv = nh // G
+    sub = workloads.Workload("sample", w.T, w.cu, nh, nkv, w.d, w.flags,
+                             np.ascontiguousarray(w.q[:, :nh]), np.ascontiguousarray(w.k[:, :nkv]),
+                             np.ascontiguousarray(w.v[:, :nkv]), np.ascontiguousarray(w.do[:, :nh]))
+    t0 = time.time()
+    q, k, v = (oracle.quantize(x, sub.cu) for x in (sub.q, sub.k, sub.v))
+    ops = oracle.Operands.from_codes(q, k, v)
+    O, L = oracle.attn_fwd(sub.cu, ops, mode=oracle.MODE_TILED, kblock=64)
+    gc, ge, D, _ = oracle.bwd_prep(sub.cu, sub.do, oracle.to_bf16(O), k[1], v[1], nkv)
+    Gd = oracle.dequantize(gc, ge)
+    oracle.bwd_dq(sub.cu, ops, Gd, D, L)
+    oracle.bwd_dkdv(sub.cu, ops, Gd, D, L)
+    dt = time.time() - t0
+    flop = 14.0 * w.d * nh * w.visible_pairs()
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "q heads 0..%d of %d (all documents): quantize + fwd + bwd in FP64, %.1f s"
+                      % (nh - 1, w.Hq, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="packed_mha", choices=sorted(workloads.NAMED))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_causal_flash_amd import flamia as F
+    F.load()
+    dev = torch.device("cuda:0")
+    w = workloads.NAMED[args.workload](args.seed)
+    log("workload %s: T=%d docs=%d Hq=%d Hkv=%d d=%d" % (w.name, w.T, len(w.cu) - 1, w.Hq, w.Hkv,
+                                                         w.d))
+    T, Hq, Hkv, d = w.T, w.Hq, w.Hkv, w.d
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    cu = torch.from_numpy(w.cu.astype(np.int32)).to(dev)
+    xq, xk, xv, xdo = up(w.q), up(w.k), up(w.v), up(w.do).view(torch.bfloat16)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    qc, kc, vc = (torch.empty((T, h, d), **u8) for h in (Hq, Hkv, Hkv))
+    qe, ke, ve = (torch.empty((h, T), **u8) for h in (Hq, Hkv, Hkv))
+    o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    dq = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
+    dk = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
+    dv = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
+    pf = F.make_problem(cu, T, Hq, Hkv, d, 0.0, F.FLAMIA_CAUSAL)
+    pb = F.make_problem(cu, T, Hq, Hkv, d, 0.0, F.FLAMIA_CAUSAL)
+    wsf = torch.empty(F.flamia_attn_fwd_workspace_size(pf), **u8)
+    wsb = torch.empty(F.flamia_attn_bwd_workspace_size(pb), **u8)
+
+    def quant():
+        F.flamia_quantize_tokblock(pf, Hq, 0, xq, qc, qe)
+        F.flamia_quantize_tokblock(pf, Hkv, 0, xk, kc, ke)
+        F.flamia_quantize_tokblock(pf, Hkv, 0, xv, vc, ve)
+
+    def fwd():
+        F.flamia_attn_fwd(pf, qc, qe, kc, ke, vc, ve, o, lse, wsf)
+
+    def bwd():
+        F.flamia_attn_bwd(pb, qc, qe, kc, ke, vc, ve, o, lse, xdo, dq, dk, dv, wsb)
+
+    def step():
+        quant()
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    K = args.steps
+    evf = [(hip.create(), hip.create()) for _ in range(K)]
+    evb = [(hip.create(), hip.create()) for _ in range(K)]
+    t_start, t_stop = hip.create(), hip.create()
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    hip.lib.hipEventRecord(ctypes.c_void_p(t_start), ctypes.c_void_p(stream))
+    for i in range(K):
+        F.set_events(pf, *evf[i])
+        F.set_events(pb, *evb[i])
+        step()
+    hip.lib.hipEventRecord(ctypes.c_void_p(t_stop), ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    F.set_events(pf, None, None)
+    F.set_events(pb, None, None)
+    ms_step = hip.elapsed_ms(t_start, t_stop) / K
+    ms_fwd = sum(hip.elapsed_ms(a, b) for a, b in evf) / K
+    ms_bwd = sum(hip.elapsed_ms(a, b) for a, b in evb) / K
+
+    # stage timings (same launches, separately bracketed)
+    def timed(fn, reps):
+        torch.cuda.synchronize()
+        hip.lib.hipEventRecord(ctypes.c_void_p(t_start), ctypes.c_void_p(stream))
+        for _ in range(reps):
+            fn()
+        hip.lib.hipEventRecord(ctypes.c_void_p(t_stop), ctypes.c_void_p(stream))
+        torch.cuda.synchronize()
+        return hip.elapsed_ms(t_start, t_stop) / reps
+
+    ms_quant = timed(quant, K)
+    ms_attn = timed(lambda: (fwd(), bwd()), K)
+
+    pairs = w.visible_pairs()
+    flop = 14.0 * d * Hq * pairs
+    flop_bwd = 10.0 * d * Hq * pairs
+    flop_fwd = 4.0 * d * Hq * pairs
+    value = flop / (ms_step * 1e-3) / 1e12
+    bwd_tflops = flop_bwd / (ms_bwd * 1e-3) / 1e12
+    qbytes = (T * (Hq + 2 * Hkv)) * (3 * d + 1)  # read bf16, write codes + exponent byte
+    out = {
+        "metric": "causal packed attn fwd+bwd TFLOP/s at 1 MI355X; % of FP8 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "documents": int(len(w.cu) - 1),
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "causal": True,
+                   "visible_pairs": int(pairs), "seed": args.seed,
+                   "step": "quantize Q,K,V + attn fwd + attn bwd"},
+        "pct_fp8_peak": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
+        "roofline": {"kernel": "bwd_kernel", "bound": "mfma", "achieved": round(bwd_tflops, 2),
+                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(bwd_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None},
+        "kernels": {
+            "fwd_kernel_ms": round(ms_fwd, 4),
+            "fwd_kernel_tflops": round(flop_fwd / (ms_fwd * 1e-3) / 1e12, 2),
+            "bwd_kernel_ms": round(ms_bwd, 4),
+            "bwd_kernel_tflops": round(bwd_tflops, 2),
+            "attn_fwd_bwd_ms": round(ms_attn, 4),
+            "attn_fwd_bwd_tflops": round(flop / (ms_attn * 1e-3) / 1e12, 2),
+            "quantize_qkv_ms": round(ms_quant, 4),
+            "quantize_qkv_gbps": round(qbytes / (ms_quant * 1e-3) / 1e9, 1),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample ...")
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -146,6 +146,13 @@ int prescale_c(const Dims& d)
 
 flamia_status hip_status(hipError_t e) { return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP; }
 
+hipError_t record(const flamia_problem* p, bool start, hipStream_t s)
+{
+    if (p->events == nullptr) return hipSuccess;
+    void* ev = start ? p->events->attn_start : p->events->attn_stop;
+    return ev ? hipEventRecord((hipEvent_t)ev, s) : hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -241,8 +248,10 @@ flamia_status flamia_attn_fwd(const flamia_problem* p, const uint8_t* q_codes,
     a.v_exps = v_exps;
     a.o = o;
     a.lse = lse;
+    if (record(p, true, s) != hipSuccess) return FLAMIA_ERR_HIP;
     e = launch_fwd(a, (int)d.d, w.max_items, s);
     if (e != hipSuccess) return FLAMIA_ERR_HIP;
+    if (record(p, false, s) != hipSuccess) return FLAMIA_ERR_HIP;
     return hip_status(launch_fwd_padding(a, (int)d.d, s));
 }
 
@@ -340,8 +349,10 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
+    if (record(p, true, s) != hipSuccess) return FLAMIA_ERR_HIP;
     e = launch_bwd(a, (int)d.d, w.max_items, s);
     if (e != hipSuccess) return FLAMIA_ERR_HIP;
+    if (record(p, false, s) != hipSuccess) return FLAMIA_ERR_HIP;
     return hip_status(launch_bwd_finalize(a, (int)d.d, s));
 }
 

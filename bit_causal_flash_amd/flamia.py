@@ -45,6 +45,10 @@ class FlamiaError(RuntimeError):
         super().__init__("%s failed: %s (%d)" % (fn, status_string(status), status))
 
 
+class flamia_kernel_events(ctypes.Structure):
+    _fields_ = [("attn_start", ctypes.c_void_p), ("attn_stop", ctypes.c_void_p)]
+
+
 class flamia_problem(ctypes.Structure):
     _fields_ = [
         ("total_tokens", ctypes.c_int32),
@@ -55,6 +59,7 @@ class flamia_problem(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("flags", ctypes.c_uint32),
+        ("events", ctypes.POINTER(flamia_kernel_events)),
     ]
 
 
@@ -118,9 +123,21 @@ def make_problem(cu_seqlens, total_tokens: int, num_q_heads: int, num_kv_heads: 
     """cu_seqlens: device int32 tensor [B + 1] (kept alive by the problem)."""
     p = flamia_problem(int(total_tokens), int(cu_seqlens.numel()) - 1,
                        ctypes.c_void_p(cu_seqlens.data_ptr()), int(num_q_heads),
-                       int(num_kv_heads), int(head_dim), float(softmax_scale), int(flags))
+                       int(num_kv_heads), int(head_dim), float(softmax_scale), int(flags), None)
     p._cu = cu_seqlens
     return p
+
+
+def set_events(p, start, stop):
+    """Make the next attention calls with `p` record hipEvent_t handles
+    `start` / `stop` (ints) around their main kernel; None clears them."""
+    if start is None and stop is None:
+        p.events = None
+        p._ev = None
+        return
+    ev = flamia_kernel_events(ctypes.c_void_p(start), ctypes.c_void_p(stop))
+    p._ev = ev
+    p.events = ctypes.pointer(ev)
 
 
 def softmax_scale_of(p) -> float:

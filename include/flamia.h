@@ -76,6 +76,15 @@ enum {
                                     in this build) */
 };
 
+/* Optional timing hook: hipEvent_t handles the library records on the call's
+ * stream immediately before and after the main attention kernel of
+ * flamia_attn_fwd (the forward kernel) or flamia_attn_bwd (the backward main
+ * kernel).  Either may be NULL.  The caller owns the events. */
+typedef struct {
+    void* attn_start;
+    void* attn_stop;
+} flamia_kernel_events;
+
 typedef struct {
     int32_t total_tokens;       /* T >= 0: rows of every packed buffer */
     int32_t num_seqs;           /* B >= 1 */
@@ -86,6 +95,7 @@ typedef struct {
     int32_t head_dim;           /* d in {64, 128} */
     float softmax_scale;        /* <= 0 selects 1 / sqrt(d) */
     uint32_t flags;             /* FLAMIA_* flags */
+    const flamia_kernel_events* events; /* optional timing events, or NULL */
 } flamia_problem;
 
 /*

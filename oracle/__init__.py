@@ -120,6 +120,11 @@ def bf16_to_float(h) -> np.ndarray:
     return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(_load().orc_num_threads())
+
+
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 

@@ -59,6 +59,7 @@
  * against the pages).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -66,6 +67,9 @@
 #define ORC_OK 0
 #define ORC_EBADSEQ (-1)
 #define ORC_EBADARG (-2)
+
+/* Threads the oracle's parallel loops use. */
+int orc_num_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------- */
 /* Number formats                                                             */

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "flamia.h")).read()
-    names = re.findall(r"\b(flamia_[a-z0-9_]+)\s*\(", text)
+    names = re.findall(r"^[A-Za-z_ *]*?\b(flamia_[a-z0-9_]+)\s*\(", text, flags=re.M)
     return sorted(set(names))
 
 
@@ -26,7 +26,7 @@ def test_header_declarations_are_exported():
 
 
 def _problem(T=64, B=1, Hq=2, Hkv=1, d=128, flags=F.FLAMIA_CAUSAL, cu=8):
-    return F.flamia_problem(T, B, ctypes.c_void_p(cu), Hq, Hkv, d, 0.0, flags)
+    return F.flamia_problem(T, B, ctypes.c_void_p(cu), Hq, Hkv, d, 0.0, flags, None)
 
 
 def test_invalid_arguments_rejected_before_launch():
