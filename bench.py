@@ -179,6 +179,10 @@ def main():
 
     ms_quant = timed(quant, K)
     ms_attn = timed(lambda: (fwd(), bwd()), K)
+    pdet = F.make_problem(cu, T, Hq, Hkv, d, 0.0, F.FLAMIA_CAUSAL | F.FLAMIA_DETERMINISTIC)
+    wsd = torch.empty(F.flamia_attn_bwd_workspace_size(pdet), **u8)
+    ms_bwd_det = timed(lambda: F.flamia_attn_bwd(pdet, qc, qe, kc, ke, vc, ve, o, lse, xdo, dq, dk,
+                                                 dv, wsd), K)
 
     pairs = w.visible_pairs()
     flop = 14.0 * d * Hq * pairs
@@ -215,6 +219,7 @@ def main():
             "bwd_kernel_tflops": round(bwd_tflops, 2),
             "attn_fwd_bwd_ms": round(ms_attn, 4),
             "attn_fwd_bwd_tflops": round(flop / (ms_attn * 1e-3) / 1e12, 2),
+            "bwd_call_deterministic_ms": round(ms_bwd_det, 4),
             "quantize_qkv_ms": round(ms_quant, 4),
             "quantize_qkv_gbps": round(qbytes / (ms_quant * 1e-3) / 1e9, 1),
         },

@@ -26,7 +26,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Dims {
     int64_t T, B, Hq, Hkv, d;
     float scale;
-    bool causal;
+    bool causal, deterministic;
 };
 
 flamia_status check_seq(const flamia_problem* p)
@@ -55,8 +55,7 @@ flamia_status check_attn(const flamia_problem* p, Dims* out)
     if (st != FLAMIA_OK) return st;
     if (p->flags & ~kKnownFlags) return FLAMIA_ERR_INVALID_ARG;
     if ((p->flags & FLAMIA_FP4_SCORE) && !(p->flags & FLAMIA_EXACT)) return FLAMIA_ERR_INVALID_ARG;
-    if (p->flags & (FLAMIA_EXACT | FLAMIA_FP4_SCORE | FLAMIA_DETERMINISTIC))
-        return FLAMIA_ERR_UNSUPPORTED;
+    if (p->flags & (FLAMIA_EXACT | FLAMIA_FP4_SCORE)) return FLAMIA_ERR_UNSUPPORTED;
     if (std::isnan(p->softmax_scale) || std::isinf(p->softmax_scale)) return FLAMIA_ERR_INVALID_ARG;
     out->T = p->total_tokens;
     out->B = p->num_seqs;
@@ -65,6 +64,7 @@ flamia_status check_attn(const flamia_problem* p, Dims* out)
     out->d = p->head_dim;
     out->scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
     out->causal = (p->flags & FLAMIA_CAUSAL) != 0;
+    out->deterministic = (p->flags & FLAMIA_DETERMINISTIC) != 0;
     // grid limits: items x heads must fit a 1-D launch
     const int64_t items = out->T / 128 + std::min(out->B, out->T) + 1;
     if (items * out->Hq >= (int64_t)INT32_MAX) return FLAMIA_ERR_UNSUPPORTED;
@@ -114,7 +114,9 @@ flamia_bwd_workspace_layout bwd_layout(const Dims& d, size_t* worklist_base = nu
     l.dq_accum = o;
     o = align_up(o + 2 * rows * d.d);
     if (worklist_base) *worklist_base = o;
-    l.total = worklist_layout(d, kBwdTile, o).total;
+    o = worklist_layout(d, kBwdTile, o).total;
+    if (worklist_base) worklist_base[1] = o;  // query-tile list of the deterministic dQ kernel
+    l.total = worklist_layout(d, kFwdTile, o).total;
     return l;
 }
 
@@ -290,8 +292,8 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     if (!q_codes || !q_exps || !k_codes || !k_exps || !v_codes || !v_exps || !o || !lse ||
         !dout || !dq || !dk || !dv)
         return FLAMIA_ERR_INVALID_ARG;
-    size_t wl_base = 0;
-    const flamia_bwd_workspace_layout L = bwd_layout(d, &wl_base);
+    size_t wl_base[2] = {0, 0};
+    const flamia_bwd_workspace_layout L = bwd_layout(d, wl_base);
     if (workspace == nullptr || workspace_bytes < L.total) return FLAMIA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     uint8_t* ws = (uint8_t*)workspace;
@@ -318,7 +320,7 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     hipError_t e = launch_quant(q, (int)d.d, true, s);
     if (e != hipSuccess) return FLAMIA_ERR_HIP;
 
-    const WorklistLayout wl = worklist_layout(d, kBwdTile, wl_base);
+    const WorklistLayout wl = worklist_layout(d, kBwdTile, wl_base[0]);
     WorklistArgs w = make_worklist_args(d, p, kBwdTile, true, ws, wl);
     e = launch_worklist(w, s);
     if (e != hipSuccess) return FLAMIA_ERR_HIP;
@@ -350,10 +352,20 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     a.dk = dk;
     a.dv = dv;
     if (record(p, true, s) != hipSuccess) return FLAMIA_ERR_HIP;
-    e = launch_bwd(a, (int)d.d, w.max_items, s);
+    e = launch_bwd(a, (int)d.d, w.max_items, !d.deterministic, s);
     if (e != hipSuccess) return FLAMIA_ERR_HIP;
     if (record(p, false, s) != hipSuccess) return FLAMIA_ERR_HIP;
-    return hip_status(launch_bwd_finalize(a, (int)d.d, s));
+    if (d.deterministic) {
+        // dQ by query-major blocks in FP32 registers, written directly
+        const WorklistLayout wq = worklist_layout(d, kFwdTile, wl_base[1]);
+        WorklistArgs wqa = make_worklist_args(d, p, kFwdTile, false, ws, wq);
+        if (launch_worklist(wqa, s) != hipSuccess) return FLAMIA_ERR_HIP;
+        AttnArgs aq = a;
+        aq.count = wqa.count;
+        aq.items = wqa.items;
+        if (launch_bwd_dq(aq, (int)d.d, wqa.max_items, s) != hipSuccess) return FLAMIA_ERR_HIP;
+    }
+    return hip_status(launch_bwd_finalize(a, (int)d.d, !d.deterministic, s));
 }
 
 }  // extern "C"

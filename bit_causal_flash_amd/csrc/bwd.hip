@@ -23,7 +23,10 @@
 // hold P^ and dS^ in the k layout of the dV / dK MFMAs.  Q, dO and K are
 // staged token-major in LDS and read k-major with ds_read_b64_tr_b8 where the
 // contraction runs over tokens: one copy of every code tensor serves both
-// orientations.  dS^ goes through LDS once, transposed, for dQ.
+// orientations.  dS^ goes through LDS once, key-major, and is read
+// transposed for dQ.  The next Q/dO tile is fetched into registers while the
+// current one is processed (double-buffered LDS), and barriers order LDS
+// traffic only, so the FP16 dQ atomics never stall the workgroup.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -31,20 +34,57 @@ namespace flamia {
 
 namespace {
 
+// One 64-query tile of one q head, as staged for the backward: codes (two
+// 16-byte chunks per thread of Q and of dO) and per-query statistics.
+struct QTile {
+    v4i q[2], g[2];
+    int eq, edo;
+    float lse2, delta, qscale;
+};
+
 template <int D>
+__device__ __forceinline__ void load_qtile(const AttnArgs& a, QTile& r, int h, int qb, int e, int tid)
+{
+    constexpr int CPR = D / 16;
+    const int Hq = a.Hq;
+    const size_t T = (size_t)a.T;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int c = tid + 256 * k;
+        const int row = c / CPR, col = 16 * (c % CPR);
+        const int t = qb + row;
+        r.q[k] = v4i{0, 0, 0, 0};
+        r.g[k] = v4i{0, 0, 0, 0};
+        if (row < 64 && t < e) {
+            r.q[k] = *(const v4i*)(a.q_codes + ((size_t)t * Hq + h) * D + col);
+            r.g[k] = *(const v4i*)(a.do_codes + ((size_t)t * Hq + h) * D + col);
+        }
+    }
+    if (tid < 64) {
+        const int t = qb + tid;
+        const bool ok = t < e;
+        r.eq = ok ? (int)a.q_exps[(size_t)h * T + t] : 127;
+        r.edo = ok ? (int)a.do_exps[(size_t)h * T + t] : 127;
+        r.lse2 = ok ? a.lse_in[(size_t)h * T + t] * kLog2e : INFINITY;
+        r.delta = ok ? a.delta[(size_t)h * T + t] : 0.f;
+        r.qscale = ok ? ldexpf(a.scale, (int)a.prescale[(size_t)h * T + t]) : 0.f;
+    }
+}
+
+template <int D, bool WITH_DQ>
 __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
 {
-    constexpr int PITCH = D + 16;
-    constexpr int SPITCH = 128 + 16;
+    constexpr int PITCH = D + 16;   // token-major code tiles
+    constexpr int SPITCH = 64 + 16; // dS^ tile, key-major: [128 keys][64 queries]
     constexpr int NKS = D / 64;
     constexpr int NDT = D / 32;
     constexpr int CPR = D / 16;
     __shared__ __attribute__((aligned(16))) uint8_t s_kt[128 * PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t s_q[64 * PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t s_do[64 * PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t s_ds[64 * SPITCH];
-    __shared__ int s_eq[64], s_edo[64];
-    __shared__ float s_lse2[64], s_delta[64], s_qscale[64];
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[2][64 * PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_do[2][64 * PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ds[128 * SPITCH];
+    __shared__ int s_eq[2][64], s_edo[2][64];
+    __shared__ float s_lse2[2][64], s_delta[2][64], s_qscale[2][64];
     __shared__ int s_dsexp[2][4];
     __shared__ int s_ekb[4];
 
@@ -93,146 +133,167 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
 #pragma unroll
         for (int v = 0; v < 16; ++v) dk[dt][v] = dv[dt][v] = 0.f;
 
+    // iterations: q heads of the group (outer) x 64-query tiles that see the keys
     const int qt_lo = a.causal ? 2 * kt : 0;
-    const int qt_hi = (e - s + 63) / 64;
-    for (int hh = 0; hh < G; ++hh) {
-        const int h = hk * G + hh;
-        for (int qt = qt_lo; qt < qt_hi; ++qt) {
-            const int qb = s + 64 * qt;
-            __syncthreads();
-            for (int c = tid; c < 64 * CPR; c += 256) {
-                const int row = c / CPR, col = 16 * (c % CPR);
-                const int t = qb + row;
-                v4i qv = {0, 0, 0, 0}, gv = {0, 0, 0, 0};
-                if (t < e) {
-                    qv = *(const v4i*)(a.q_codes + ((size_t)t * Hq + h) * D + col);
-                    gv = *(const v4i*)(a.do_codes + ((size_t)t * Hq + h) * D + col);
-                }
-                *(v4i*)(s_q + row * PITCH + col) = qv;
-                *(v4i*)(s_do + row * PITCH + col) = gv;
-            }
-            if (tid < 64) {
-                const int t = qb + tid;
-                const bool ok = t < e;
-                s_eq[tid] = ok ? (int)a.q_exps[(size_t)h * T + t] : 127;
-                s_edo[tid] = ok ? (int)a.do_exps[(size_t)h * T + t] : 127;
-                s_lse2[tid] = ok ? a.lse_in[(size_t)h * T + t] * kLog2e : INFINITY;
-                s_delta[tid] = ok ? a.delta[(size_t)h * T + t] : 0.f;
-                s_qscale[tid] = ok ? ldexpf(a.scale, (int)a.prescale[(size_t)h * T + t]) : 0.f;
-            }
-            __syncthreads();
+    const int nqt = (e - s + 63) / 64 - qt_lo;
+    const int niter = G * nqt;
 
-            const bool active = wave_keys && (!a.causal || qb + 63 >= kw0);
-            v8i pf = {0, 0, 0, 0, 0, 0, 0, 0}, df = {0, 0, 0, 0, 0, 0, 0, 0};
-            int dse[2] = {127, 127};
-            if (active) {
-                v16f sacc[2], pacc[2];
+    auto stage = [&](const QTile& r, int buf) {
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int qr = perm_row(t, lane & 31);
+        for (int k = 0; k < 2; ++k) {
+            const int c = tid + 256 * k;
+            const int row = c / CPR, col = 16 * (c % CPR);
+            if (row < 64) {
+                *(v4i*)(&s_q[buf][row * PITCH + col]) = r.q[k];
+                *(v4i*)(&s_do[buf][row * PITCH + col]) = r.g[k];
+            }
+        }
+        if (tid < 64) {
+            s_eq[buf][tid] = r.eq;
+            s_edo[buf][tid] = r.edo;
+            s_lse2[buf][tid] = r.lse2;
+            s_delta[buf][tid] = r.delta;
+            s_qscale[buf][tid] = r.qscale;
+        }
+    };
+
+    QTile nxt;
+    if (niter > 0) {
+        load_qtile<D>(a, nxt, hk * G, s + 64 * qt_lo, e, tid);
+        stage(nxt, 0);
+    }
+    lds_barrier();
+
+    for (int it = 0; it < niter; ++it) {
+        const int cur = it & 1;
+        const int h = hk * G + it / nqt;
+        const int qb = s + 64 * (qt_lo + it % nqt);
+        const bool more = it + 1 < niter;
+        if (more) {
+            const int h1 = hk * G + (it + 1) / nqt;
+            const int qb1 = s + 64 * (qt_lo + (it + 1) % nqt);
+            load_qtile<D>(a, nxt, h1, qb1, e, tid);
+        }
+        const uint8_t* sq = s_q[cur];
+        const uint8_t* sg = s_do[cur];
+
+        const bool active = wave_keys && (!a.causal || qb + 63 >= kw0);
+        v8i pf = {0, 0, 0, 0, 0, 0, 0, 0}, df = {0, 0, 0, 0, 0, 0, 0, 0};
+        int dse[2] = {127, 127};
+        if (active) {
+            v16f sacc[2], pacc[2];
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) sacc[t][v] = pacc[t][v] = 0.f;
+            for (int t = 0; t < 2; ++t) {
+                const int qr = perm_row(t, lane & 31);
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) {
-                        sacc[t] = mfma_f8(row_operand(s_q + qr * PITCH + 64 * ks, lane), kf[ks],
-                                          sacc[t], s_eq[qr], ek);
-                        pacc[t] = mfma_f8(row_operand(s_do + qr * PITCH + 64 * ks, lane), vf[ks],
-                                          pacc[t], s_edo[qr], ev);
-                    }
-                }
-                // P, dS; element (t, v) of lane group g <-> query 32 t + 16 g + v
-                float amax[2] = {0.f, 0.f};
+                for (int v = 0; v < 16; ++v) sacc[t][v] = pacc[t][v] = 0.f;
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int qq = 32 * t + 16 * g + v;
-                        const int qi = qb + qq;
-                        const bool vis = kvalid && qi < e && (!a.causal || kj <= qi);
-                        const float p =
-                            vis ? __builtin_amdgcn_exp2f(fmaf(sacc[t][v], c2, -s_lse2[qq])) : 0.f;
-                        const float ds = p * (pacc[t][v] - s_delta[qq]);
-                        sacc[t][v] = p;
-                        pacc[t][v] = ds;
-                        amax[t] = fmaxf(amax[t], fabsf(ds));
-                    }
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int et = ceil_exp448(wave_max(amax[t]));
-                    dse[t] = et + 127;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        pf[4 * t + q] = (int)cvt4_fp8(fminf(256.f * sacc[t][4 * q], 448.f),
-                                                      fminf(256.f * sacc[t][4 * q + 1], 448.f),
-                                                      fminf(256.f * sacc[t][4 * q + 2], 448.f),
-                                                      fminf(256.f * sacc[t][4 * q + 3], 448.f));
-                        df[4 * t + q] = (int)cvt4_fp8(
-                            ldexpf(pacc[t][4 * q], -et), ldexpf(pacc[t][4 * q + 1], -et),
-                            ldexpf(pacc[t][4 * q + 2], -et), ldexpf(pacc[t][4 * q + 3], -et));
-                    }
-                }
-                // dV^T += dO^T P^ and dK^T += Q^T dS^ (k = the tile's 64 queries)
-                const int sdo = s_edo[32 * g];
-                const int sq = s_eq[32 * g];
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    dv[dt] = mfma_f8(lds_tr_operand(s_do, PITCH, 0, 32 * dt, lane), pf, dv[dt], sdo,
-                                     kScaleMinus8);
-                    dk[dt] = mfma_f8(lds_tr_operand(s_q, PITCH, 0, 32 * dt, lane), df, dk[dt], sq,
-                                     dse[g]);
+                for (int ks = 0; ks < NKS; ++ks) {
+                    sacc[t] = mfma_f8(row_operand(sq + qr * PITCH + 64 * ks, lane), kf[ks], sacc[t],
+                                      s_eq[cur][qr], ek);
+                    pacc[t] = mfma_f8(row_operand(sg + qr * PITCH + 64 * ks, lane), vf[ks], pacc[t],
+                                      s_edo[cur][qr], ev);
                 }
             }
-
-            // dS^ to LDS, query-major, for the dQ product
-            {
-                const int kcol = 32 * wave + (lane & 31);
+            // P, dS; element (t, v) of lane group g <-> query 32 t + 16 g + v
+            float amax[2] = {0.f, 0.f};
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const uint32_t w = (uint32_t)df[4 * t + v / 4];
-                        s_ds[(32 * t + 16 * g + v) * SPITCH + kcol] = (uint8_t)(w >> (8 * (v % 4)));
-                    }
-                if (lane == 0) {
-                    s_dsexp[0][wave] = dse[0];
-                    s_dsexp[1][wave] = dse[1];
+                for (int v = 0; v < 16; ++v) {
+                    const int qq = 32 * t + 16 * g + v;
+                    const int qi = qb + qq;
+                    const bool vis = kvalid && qi < e && (!a.causal || kj <= qi);
+                    const float p =
+                        vis ? __builtin_amdgcn_exp2f(fmaf(sacc[t][v], c2, -s_lse2[cur][qq])) : 0.f;
+                    const float ds = p * (pacc[t][v] - s_delta[cur][qq]);
+                    sacc[t][v] = p;
+                    pacc[t][v] = ds;
+                    amax[t] = fmaxf(amax[t], fabsf(ds));
+                }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int et = ceil_exp448(wave_max(amax[t]));
+                dse[t] = et + 127;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    pf[4 * t + q] = (int)cvt4_fp8(fminf(256.f * sacc[t][4 * q], 448.f),
+                                                  fminf(256.f * sacc[t][4 * q + 1], 448.f),
+                                                  fminf(256.f * sacc[t][4 * q + 2], 448.f),
+                                                  fminf(256.f * sacc[t][4 * q + 3], 448.f));
+                    df[4 * t + q] = (int)cvt4_fp8(
+                        ldexpf(pacc[t][4 * q], -et), ldexpf(pacc[t][4 * q + 1], -et),
+                        ldexpf(pacc[t][4 * q + 2], -et), ldexpf(pacc[t][4 * q + 3], -et));
                 }
             }
-            __syncthreads();
+            // dV^T += dO^T P^ and dK^T += Q^T dS^ (k = the tile's 64 queries)
+            const int sdo = s_edo[cur][32 * g];
+            const int sqe = s_eq[cur][32 * g];
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                dv[dt] = mfma_f8(lds_tr_operand(sg, PITCH, 0, 32 * dt, lane), pf, dv[dt], sdo,
+                                 kScaleMinus8);
+                dk[dt] = mfma_f8(lds_tr_operand(sq, PITCH, 0, 32 * dt, lane), df, dk[dt], sqe,
+                                 dse[g]);
+            }
+        }
 
-            // dQ^T = K^T dS^T over the tile's 128 keys, 32 x 32 output tiles
-            for (int j = wave; j < 2 * NDT; j += 4) {
-                const int dt = j % NDT, ct = j / NDT;
-                if (qb + 32 * ct >= e) continue;
-                if (a.causal && qb + 32 * ct + 31 < k0) continue;
-                const int qcol = 32 * ct + (lane & 31);
-                v16f acc;
+        if constexpr (WITH_DQ) {
+        // dS^ to LDS key-major (row = this lane's key): two 16-byte chunks
+        {
+            const int krow = 32 * wave + (lane & 31);
+            *(v4i*)(s_ds + krow * SPITCH + 16 * g) = v4i{df[0], df[1], df[2], df[3]};
+            *(v4i*)(s_ds + krow * SPITCH + 32 + 16 * g) = v4i{df[4], df[5], df[6], df[7]};
+            if (lane == 0) {
+                s_dsexp[0][wave] = dse[0];
+                s_dsexp[1][wave] = dse[1];
+            }
+        }
+        lds_barrier();
+
+        // dQ = dS^ K^ over the tile's 128 keys, 32 x 32 output tiles (rows =
+        // queries, columns = head dim).  Lanes hold consecutive columns, so
+        // after pairing neighbour lanes each packed FP16 atomic instruction
+        // covers 64 contiguous bytes of 4 dQ rows.
+        for (int j = wave; j < 2 * NDT; j += 4) {
+            const int dt = j % NDT, ct = j / NDT;
+            if (qb + 32 * ct >= e) continue;
+            v16f acc;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+            for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (k0 + 64 * ks >= e) break;
-                    acc = mfma_f8(lds_tr_operand(s_kt + 64 * ks * PITCH, PITCH, 0, 32 * dt, lane),
-                                  row_operand(s_ds + qcol * SPITCH + 64 * ks, lane), acc,
-                                  s_ekb[2 * ks + g], s_dsexp[ct][2 * ks + g]);
-                }
-                const int qi = qb + qcol;
+            for (int ks = 0; ks < 2; ++ks) {
+                if (k0 + 64 * ks >= e) break;
+                acc = mfma_f8(lds_tr_operand(s_ds + 64 * ks * SPITCH, SPITCH, 0, 32 * ct, lane),
+                              lds_tr_operand(s_kt + 64 * ks * PITCH, PITCH, 0, 32 * dt, lane), acc,
+                              s_dsexp[ct][2 * ks + g], s_ekb[2 * ks + g]);
+            }
+            // row of accumulator v: query 32 ct + 8 (v / 4) + 4 g + v % 4
+            const bool odd = lane & 1;
+            const int dcol = 32 * dt + (lane & 30);
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+                const int qq0 = 32 * ct + 8 * (v / 4) + 4 * g + (v % 4);  // row of v
+                const int qq1 = qq0 + 1;                                   // row of v + 1
+                // even lanes keep rows of v, odd lanes rows of v + 1
+                const float mine = odd ? acc[v + 1] : acc[v];
+                const float give = odd ? acc[v] : acc[v + 1];
+                const float other = __shfl_xor(give, 1, kWave);
+                const int qq = odd ? qq1 : qq0;
+                const int qi = qb + qq;
                 if (qi < e) {
-                    const float f = s_qscale[qcol];
-                    _Float16* dst = a.dq_acc + ((size_t)qi * Hq + h) * D + 32 * dt + 4 * g;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-#pragma unroll
-                        for (int pr = 0; pr < 2; ++pr) {
-                            h2 val;
-                            val.x = (_Float16)(acc[4 * q + 2 * pr] * f);
-                            val.y = (_Float16)(acc[4 * q + 2 * pr + 1] * f);
-                            __builtin_amdgcn_global_atomic_fadd_v2f16((h2*)(dst + 8 * q + 2 * pr),
-                                                                      val);
-                        }
+                    const float f = s_qscale[cur][qq];
+                    h2 val;
+                    val.x = (_Float16)((odd ? other : mine) * f);
+                    val.y = (_Float16)((odd ? mine : other) * f);
+                    __builtin_amdgcn_global_atomic_fadd_v2f16(
+                        (h2*)(a.dq_acc + ((size_t)qi * Hq + h) * D + dcol), val);
                 }
             }
         }
+        }  // WITH_DQ
+        if (more) stage(nxt, cur ^ 1);
+        lds_barrier();
     }
 
     if (kvalid) {
@@ -254,8 +315,199 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
     }
 }
 
-// dQ = acc * 2^-k_i -> bf16 for every row; dK = dV = 0 on padding rows.
+// Query-major dQ for the deterministic backward: a workgroup (4 waves x 32
+// queries) owns a 128-query tile of one document and one q head and walks
+// the visible keys in 64-key steps, recomputing S and dP exactly as the
+// key-major kernel does but with lanes on queries (S^T = K Q^T with the key
+// rows permuted).  dS^ then already sits in registers in the k layout of the
+// dQ^T = K^T dS^T MFMA, and dQ accumulates in FP32 registers in a fixed
+// order: no atomics, bitwise repeatable.  The 32 x 32 dS blocks (the wave's
+// 32 queries x 32 keys) and their exponents are the same as in the key-major
+// kernel.
+struct KVStep {
+    v4i k[2], v[2];
+    int ek, ev;
+};
+
 template <int D>
+__device__ __forceinline__ void load_kvstep(const AttnArgs& a, KVStep& r, int hk, int kt0, int e,
+                                            int tid)
+{
+    constexpr int CPR = D / 16;
+    const int Hkv = a.Hkv;
+    const size_t T = (size_t)a.T;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int c = tid + 256 * k;
+        const int row = c / CPR, col = 16 * (c % CPR);
+        const int t = kt0 + row;
+        r.k[k] = v4i{0, 0, 0, 0};
+        r.v[k] = v4i{0, 0, 0, 0};
+        if (row < 64 && t < e) {
+            r.k[k] = *(const v4i*)(a.k_codes + ((size_t)t * Hkv + hk) * D + col);
+            r.v[k] = *(const v4i*)(a.v_codes + ((size_t)t * Hkv + hk) * D + col);
+        }
+    }
+    r.ek = 127;
+    r.ev = 127;
+    if (tid < 64) {
+        const int t = kt0 + tid;
+        if (t < e) {
+            r.ek = (int)a.k_exps[(size_t)hk * T + t];
+            r.ev = (int)a.v_exps[(size_t)hk * T + t];
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a)
+{
+    constexpr int PITCH = D + 16;
+    constexpr int NKS = D / 64;
+    constexpr int NDT = D / 32;
+    constexpr int CPR = D / 16;
+    __shared__ __attribute__((aligned(16))) uint8_t s_k[2][64 * PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_v[2][64 * PITCH];
+    __shared__ int s_ek[2][64], s_ev[2][64];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+    const int Hq = a.Hq, Hkv = a.Hkv;
+    const size_t T = (size_t)a.T;
+    const int item = blockIdx.x / Hq, h = blockIdx.x % Hq;
+    if (item >= *a.count) return;
+    const int b = a.items[2 * item], m = a.items[2 * item + 1];
+    const int s = a.cu[b], e = a.cu[b + 1];
+    const int hk = h * Hkv / Hq;
+    const int q0 = s + 128 * m;
+    const int qw = q0 + 32 * wave;
+    const int qi = qw + (lane & 31);
+    const bool qvalid = qi < e;
+    const float c2 = a.c2;
+
+    // Q and dO rows of this lane's query: B operands of S^T and dP^T
+    v8i qf[NKS], gf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        if (qvalid) {
+            qf[ks] = row_operand(a.q_codes + ((size_t)qi * Hq + h) * D + 64 * ks, lane);
+            gf[ks] = row_operand(a.do_codes + ((size_t)qi * Hq + h) * D + 64 * ks, lane);
+        } else {
+            qf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            gf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    }
+    const int eq = qvalid ? (int)a.q_exps[(size_t)h * T + qi] : 127;
+    const int edo = qvalid ? (int)a.do_exps[(size_t)h * T + qi] : 127;
+    const float lse2 = qvalid ? a.lse_in[(size_t)h * T + qi] * kLog2e : INFINITY;
+    const float delta = qvalid ? a.delta[(size_t)h * T + qi] : 0.f;
+
+    const int kend = a.causal ? min(q0 + 128, e) : e;
+    const int nsteps = (kend - s + 63) / 64;
+    const int kend_w = a.causal ? min(qw + 32, e) : e;
+
+    v16f dq[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dq[dt][v] = 0.f;
+
+    auto stage = [&](const KVStep& t, int buf) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int c = tid + 256 * k;
+            const int row = c / CPR, col = 16 * (c % CPR);
+            if (row < 64) {
+                *(v4i*)(&s_k[buf][row * PITCH + col]) = t.k[k];
+                *(v4i*)(&s_v[buf][row * PITCH + col]) = t.v[k];
+            }
+        }
+        if (tid < 64) {
+            s_ek[buf][tid] = t.ek;
+            s_ev[buf][tid] = t.ev;
+        }
+    };
+
+    KVStep nxt;
+    if (nsteps > 0) {
+        load_kvstep<D>(a, nxt, hk, s, e, tid);
+        stage(nxt, 0);
+    }
+    lds_barrier();
+
+    for (int st = 0; st < nsteps; ++st) {
+        const int cur = st & 1;
+        const int kt0 = s + 64 * st;
+        const bool more = st + 1 < nsteps;
+        if (more) load_kvstep<D>(a, nxt, hk, kt0 + 64, e, tid);
+        if (kt0 < kend_w) {
+            const uint8_t* sk = s_k[cur];
+            const uint8_t* sv = s_v[cur];
+            v16f sacc[2], pacc[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int krow = perm_row(t, lane & 31);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sacc[t][v] = pacc[t][v] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    sacc[t] = mfma_f8(row_operand(sk + krow * PITCH + 64 * ks, lane), qf[ks],
+                                      sacc[t], s_ek[cur][krow], eq);
+                    pacc[t] = mfma_f8(row_operand(sv + krow * PITCH + 64 * ks, lane), gf[ks],
+                                      pacc[t], s_ev[cur][krow], edo);
+                }
+            }
+            // element (t, v) of lane group g <-> key kt0 + 32 t + 16 g + v
+            float amax[2] = {0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = kt0 + 32 * t + 16 * g + v;
+                    const bool vis = qvalid && key < e && (!a.causal || key <= qi);
+                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[t][v], c2, -lse2)) : 0.f;
+                    const float ds = p * (pacc[t][v] - delta);
+                    pacc[t][v] = ds;
+                    amax[t] = fmaxf(amax[t], fabsf(ds));
+                }
+            int dse[2];
+            v8i df;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int et = ceil_exp448(wave_max(amax[t]));
+                dse[t] = et + 127;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    df[4 * t + q] = (int)cvt4_fp8(
+                        ldexpf(pacc[t][4 * q], -et), ldexpf(pacc[t][4 * q + 1], -et),
+                        ldexpf(pacc[t][4 * q + 2], -et), ldexpf(pacc[t][4 * q + 3], -et));
+            }
+            // dQ^T += K^T dS^T: K read k-major from the token-major LDS tile
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                dq[dt] = mfma_f8(lds_tr_operand(sk, PITCH, 0, 32 * dt, lane), df, dq[dt],
+                                 s_ek[cur][32 * g], dse[g]);
+        }
+        if (more) stage(nxt, cur ^ 1);
+        lds_barrier();
+    }
+
+    if (qvalid) {
+        uint16_t* row = a.dq + ((size_t)qi * Hq + h) * D;
+        const float sc = a.scale;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v2i w;
+                w.x = (int)pack_bf16x2(dq[dt][4 * q] * sc, dq[dt][4 * q + 1] * sc);
+                w.y = (int)pack_bf16x2(dq[dt][4 * q + 2] * sc, dq[dt][4 * q + 3] * sc);
+                *(v2i*)(row + 32 * dt + 8 * q + 4 * g) = w;
+            }
+    }
+}
+
+// dQ = acc * 2^-k_i -> bf16 for every row; dK = dV = 0 on padding rows.
+template <int D, bool FROM_ACC>
 __global__ __launch_bounds__(256) void bwd_finalize_kernel(AttnArgs a)
 {
     const int ntok = a.cu[a.B];
@@ -265,14 +517,18 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(AttnArgs a)
         const size_t row = i / (D / 8);
         const int c = (int)(i % (D / 8));
         const int t = (int)(row / a.Hq), h = (int)(row % a.Hq);
-        const int k = (int)a.prescale[(size_t)h * T + t];
-        const h8 raw = *(const h8*)(a.dq_acc + row * D + 8 * c);
-        v4i out;
-        out.x = (int)pack_bf16x2(ldexpf((float)raw.s0, -k), ldexpf((float)raw.s1, -k));
-        out.y = (int)pack_bf16x2(ldexpf((float)raw.s2, -k), ldexpf((float)raw.s3, -k));
-        out.z = (int)pack_bf16x2(ldexpf((float)raw.s4, -k), ldexpf((float)raw.s5, -k));
-        out.w = (int)pack_bf16x2(ldexpf((float)raw.s6, -k), ldexpf((float)raw.s7, -k));
-        *(v4i*)(a.dq + row * D + 8 * c) = out;
+        if constexpr (FROM_ACC) {
+            const int k = (int)a.prescale[(size_t)h * T + t];
+            const h8 raw = *(const h8*)(a.dq_acc + row * D + 8 * c);
+            v4i out;
+            out.x = (int)pack_bf16x2(ldexpf((float)raw.s0, -k), ldexpf((float)raw.s1, -k));
+            out.y = (int)pack_bf16x2(ldexpf((float)raw.s2, -k), ldexpf((float)raw.s3, -k));
+            out.z = (int)pack_bf16x2(ldexpf((float)raw.s4, -k), ldexpf((float)raw.s5, -k));
+            out.w = (int)pack_bf16x2(ldexpf((float)raw.s6, -k), ldexpf((float)raw.s7, -k));
+            *(v4i*)(a.dq + row * D + 8 * c) = out;
+        } else if (t >= ntok) {
+            *(v4i*)(a.dq + row * D + 8 * c) = v4i{0, 0, 0, 0};
+        }
         if (row < T * a.Hkv) {
             const int t2 = (int)(row / a.Hkv);
             if (t2 >= ntok) {
@@ -285,22 +541,41 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(AttnArgs a)
 
 }  // namespace
 
-hipError_t launch_bwd(const AttnArgs& a, int D, int max_items, hipStream_t stream)
+hipError_t launch_bwd(const AttnArgs& a, int D, int max_items, bool with_dq, hipStream_t stream)
 {
     if (max_items <= 0) return hipSuccess;
     const dim3 grid((unsigned)max_items * a.Hkv);
-    if (D == 128) hipLaunchKernelGGL(bwd_kernel<128>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(bwd_kernel<64>, grid, dim3(256), 0, stream, a);
+    if (D == 128) {
+        if (with_dq) hipLaunchKernelGGL((bwd_kernel<128, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((bwd_kernel<128, false>), grid, dim3(256), 0, stream, a);
+    } else {
+        if (with_dq) hipLaunchKernelGGL((bwd_kernel<64, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((bwd_kernel<64, false>), grid, dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_finalize(const AttnArgs& a, int D, hipStream_t stream)
+hipError_t launch_bwd_dq(const AttnArgs& a, int D, int max_items, hipStream_t stream)
+{
+    if (max_items <= 0) return hipSuccess;
+    const dim3 grid((unsigned)max_items * a.Hq);
+    if (D == 128) hipLaunchKernelGGL(bwd_dq_kernel<128>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(bwd_dq_kernel<64>, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_finalize(const AttnArgs& a, int D, bool dq_from_acc, hipStream_t stream)
 {
     if (a.T == 0) return hipSuccess;
     const size_t n = (size_t)a.T * a.Hq * (D / 8);
     const unsigned blocks = (unsigned)min((size_t)8192, (n + 255) / 256);
-    if (D == 128) hipLaunchKernelGGL(bwd_finalize_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(bwd_finalize_kernel<64>, dim3(blocks), dim3(256), 0, stream, a);
+    if (D == 128) {
+        if (dq_from_acc) hipLaunchKernelGGL((bwd_finalize_kernel<128, true>), dim3(blocks), dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((bwd_finalize_kernel<128, false>), dim3(blocks), dim3(256), 0, stream, a);
+    } else {
+        if (dq_from_acc) hipLaunchKernelGGL((bwd_finalize_kernel<64, true>), dim3(blocks), dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((bwd_finalize_kernel<64, false>), dim3(blocks), dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

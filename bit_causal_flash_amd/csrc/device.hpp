@@ -163,6 +163,15 @@ __device__ __forceinline__ int perm_row(int t, int rho)
     return 32 * t + 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3);
 }
 
+// Workgroup barrier that orders LDS traffic only: global loads, stores and
+// atomics in flight are not waited for.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float wave_max(float x)
 {
     for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));

@@ -21,7 +21,9 @@
 // (S^T = K Q^T, lane = query) with the key rows permuted so that the
 // accumulator layout already is the k layout the P^ V MFMA expects: P^ never
 // leaves registers.  V is read k-major straight from its token-major LDS tile
-// with ds_read_b64_tr_b8, so no transposed copy of V exists anywhere.
+// with ds_read_b64_tr_b8, so no transposed copy of V exists anywhere.  The
+// next step's K/V tile is fetched into registers while the current one is
+// processed (double-buffered LDS, one LDS-only barrier per step).
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -29,17 +31,54 @@ namespace flamia {
 
 namespace {
 
+// One 64-key step of K and V codes (two 16-byte chunks per thread of each)
+// and their exponents, as staged for the forward.
+struct KVTile {
+    v4i k[2], v[2];
+    int ek, ev;
+};
+
 template <int D>
-__global__ __launch_bounds__(256, 1) void fwd_kernel(AttnArgs a)
+__device__ __forceinline__ void load_kvtile(const AttnArgs& a, KVTile& r, int hk, int kt0, int e,
+                                            int tid)
+{
+    constexpr int CPR = D / 16;
+    const int Hkv = a.Hkv;
+    const size_t T = (size_t)a.T;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int c = tid + 256 * k;
+        const int row = c / CPR, col = 16 * (c % CPR);
+        const int t = kt0 + row;
+        r.k[k] = v4i{0, 0, 0, 0};
+        r.v[k] = v4i{0, 0, 0, 0};
+        if (row < 64 && t < e) {
+            r.k[k] = *(const v4i*)(a.k_codes + ((size_t)t * Hkv + hk) * D + col);
+            r.v[k] = *(const v4i*)(a.v_codes + ((size_t)t * Hkv + hk) * D + col);
+        }
+    }
+    r.ek = 127;
+    r.ev = 127;
+    if (tid < 64) {
+        const int t = kt0 + tid;
+        if (t < e) r.ek = (int)a.k_exps[(size_t)hk * T + t];
+    } else if (tid < 66) {
+        const int t = kt0 + 32 * (tid - 64);
+        if (t < e) r.ev = (int)a.v_exps[(size_t)hk * T + t];
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
 {
     constexpr int PITCH = D + 16;  // LDS row pitch (bytes): spreads rows over banks
     constexpr int NKS = D / 64;    // k steps over the head dim
     constexpr int NDT = D / 32;    // 32-wide head-dim tiles of O
     constexpr int CPR = D / 16;    // 16-byte chunks per row
-    __shared__ __attribute__((aligned(16))) uint8_t s_k[64 * PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t s_v[64 * PITCH];
-    __shared__ int s_ek[64];
-    __shared__ int s_ev[2];
+    __shared__ __attribute__((aligned(16))) uint8_t s_k[2][64 * PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_v[2][64 * PITCH];
+    __shared__ int s_ek[2][64];
+    __shared__ int s_ev[2][2];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
     const int Hq = a.Hq, Hkv = a.Hkv;
@@ -76,94 +115,102 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(AttnArgs a)
     float r = -INFINITY;  // integer base-2 row reference
     float l = 0.f;        // sum of rounded weights
 
-    for (int st = 0; st < nsteps; ++st) {
-        const int kt0 = s + 64 * st;
-        __syncthreads();
-        for (int c = tid; c < 64 * CPR; c += 256) {
+    auto stage = [&](const KVTile& t, int buf) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int c = tid + 256 * k;
             const int row = c / CPR, col = 16 * (c % CPR);
-            const int t = kt0 + row;
-            v4i kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-            if (t < e) {
-                kv = *(const v4i*)(a.k_codes + ((size_t)t * Hkv + hk) * D + col);
-                vv = *(const v4i*)(a.v_codes + ((size_t)t * Hkv + hk) * D + col);
+            if (row < 64) {
+                *(v4i*)(&s_k[buf][row * PITCH + col]) = t.k[k];
+                *(v4i*)(&s_v[buf][row * PITCH + col]) = t.v[k];
             }
-            *(v4i*)(s_k + row * PITCH + col) = kv;
-            *(v4i*)(s_v + row * PITCH + col) = vv;
         }
-        if (tid < 64) {
-            const int t = kt0 + tid;
-            s_ek[tid] = t < e ? (int)a.k_exps[(size_t)hk * T + t] : 127;
-        }
-        if (tid < 2) {
-            const int t = kt0 + 32 * tid;
-            s_ev[tid] = t < e ? (int)a.v_exps[(size_t)hk * T + t] : 127;
-        }
-        __syncthreads();
-        if (kt0 >= kend_w) continue;  // no key of this step is visible to this wave
+        if (tid < 64) s_ek[buf][tid] = t.ek;
+        else if (tid < 66) s_ev[buf][tid - 64] = t.ev;
+    };
 
-        // S^T tiles: tile t row rho <-> key perm_row(t, rho) of the step
-        v16f sacc[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int krow = perm_row(t, lane & 31);
-            const int ek = s_ek[krow];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) sacc[t][v] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                sacc[t] = mfma_f8(row_operand(s_k + krow * PITCH + 64 * ks, lane), qf[ks], sacc[t],
-                                  ek, eq);
-        }
+    KVTile nxt;
+    if (nsteps > 0) {
+        load_kvtile<D>(a, nxt, hk, s, e, tid);
+        stage(nxt, 0);
+    }
+    lds_barrier();
 
-        // masking and the running integer reference
-        const bool full = (kt0 + 64 <= e) && (!a.causal || kt0 + 63 <= qw);
-        float mloc = -INFINITY;
+    for (int st = 0; st < nsteps; ++st) {
+        const int cur = st & 1;
+        const int kt0 = s + 64 * st;
+        const bool more = st + 1 < nsteps;
+        if (more) load_kvtile<D>(a, nxt, hk, kt0 + 64, e, tid);
+        const uint8_t* sk = s_k[cur];
+        const uint8_t* sv = s_v[cur];
+
+        if (kt0 < kend_w) {
+            // S^T tiles: tile t row rho <-> key perm_row(t, rho) of the step
+            v16f sacc[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t) {
+                const int krow = perm_row(t, lane & 31);
+                const int ek = s_ek[cur][krow];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = kt0 + 32 * t + 16 * g + v;
-                const bool vis = full || (key < e && (!a.causal || key <= qi));
-                if (!vis) sacc[t][v] = -INFINITY;
-                mloc = fmaxf(mloc, sacc[t][v]);
+                for (int v = 0; v < 16; ++v) sacc[t][v] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    sacc[t] = mfma_f8(row_operand(sk + krow * PITCH + 64 * ks, lane), qf[ks],
+                                      sacc[t], ek, eq);
             }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-        const float rn = fmaxf(r, ceilf(mloc * c2));
-        if (__any(rn > r)) {
-            float alpha = 1.f;
-            if (rn > r) alpha = (r == -INFINITY) ? 0.f : ldexpf(1.f, (int)fmaxf(r - rn, -200.f));
-            l *= alpha;
+
+            // masking and the running integer reference
+            const bool full = (kt0 + 64 <= e) && (!a.causal || kt0 + 63 <= qw);
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = kt0 + 32 * t + 16 * g + v;
+                    const bool vis = full || (key < e && (!a.causal || key <= qi));
+                    if (!vis) sacc[t][v] = -INFINITY;
+                    mloc = fmaxf(mloc, sacc[t][v]);
+                }
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+            const float rn = fmaxf(r, ceilf(mloc * c2));
+            if (__any(rn > r)) {
+                float alpha = 1.f;
+                if (rn > r) alpha = (r == -INFINITY) ? 0.f : ldexpf(1.f, (int)fmaxf(r - rn, -200.f));
+                l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+            }
+            r = rn;
+
+            // probability operand: E4M3(256 * 2^(s2 - r)), byte 16 t + v <-> key 32 t + 16 g + v
+            const float off = (r == -INFINITY) ? 0.f : 8.f - r;
+            v8i pf;
+            float lsum = 0.f;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float p[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        p[k] = __builtin_amdgcn_exp2f(fmaf(sacc[t][4 * q + k], c2, off));
+                    const uint32_t w = cvt4_fp8(p[0], p[1], p[2], p[3]);
+                    pf[4 * t + q] = (int)w;
+                    lsum += sum4_fp8(w);
+                }
+            l += lsum * 0.00390625f;
+
+            // O^T += V^T P^T: V^T read k-major from the token-major LDS tile
+            const int sv_exp = s_ev[cur][g];
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+                oacc[dt] = mfma_f8(lds_tr_operand(sv, PITCH, 0, 32 * dt, lane), pf, oacc[dt],
+                                   sv_exp, kScaleMinus8);
         }
-        r = rn;
-
-        // probability operand: E4M3(256 * 2^(s2 - r)), byte 16 t + v <-> key 32 t + 16 g + v
-        const float off = (r == -INFINITY) ? 0.f : 8.f - r;
-        v8i pf;
-        float lsum = 0.f;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float p[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    p[k] = __builtin_amdgcn_exp2f(fmaf(sacc[t][4 * q + k], c2, off));
-                const uint32_t w = cvt4_fp8(p[0], p[1], p[2], p[3]);
-                pf[4 * t + q] = (int)w;
-                lsum += sum4_fp8(w);
-            }
-        l += lsum * 0.00390625f;
-
-        // O^T += V^T P^T: V^T read k-major from the token-major LDS tile
-        const int sv = s_ev[g];
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-            oacc[dt] = mfma_f8(lds_tr_operand(s_v, PITCH, 0, 32 * dt, lane), pf, oacc[dt], sv,
-                               kScaleMinus8);
+        if (more) stage(nxt, cur ^ 1);
+        lds_barrier();
     }
 
     l += __shfl_xor(l, 32, kWave);

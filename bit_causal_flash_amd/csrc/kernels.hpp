@@ -61,7 +61,8 @@ struct AttnArgs {
 
 hipError_t launch_fwd(const AttnArgs& a, int D, int max_items, hipStream_t stream);
 hipError_t launch_fwd_padding(const AttnArgs& a, int D, hipStream_t stream);
-hipError_t launch_bwd(const AttnArgs& a, int D, int max_items, hipStream_t stream);
-hipError_t launch_bwd_finalize(const AttnArgs& a, int D, hipStream_t stream);
+hipError_t launch_bwd(const AttnArgs& a, int D, int max_items, bool with_dq, hipStream_t stream);
+hipError_t launch_bwd_dq(const AttnArgs& a, int D, int max_items, hipStream_t stream);
+hipError_t launch_bwd_finalize(const AttnArgs& a, int D, bool dq_from_acc, hipStream_t stream);
 
 }  // namespace flamia
