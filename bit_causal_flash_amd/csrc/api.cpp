@@ -333,6 +333,12 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     a.causal = d.causal ? 1 : 0;
     a.scale = d.scale;
     a.c2 = d.scale * 1.4426950408889634f;
+    {
+        int ex = 0;
+        const float m = std::frexp(d.scale, &ex);  // scale = m 2^ex, m in [0.5, 1)
+        a.scale_exp = ex - 1;
+        a.scale_res = 2.0f * m;
+    }
     a.cu = p->cu_seqlens;
     a.count = w.count;
     a.items = w.items;

@@ -38,8 +38,8 @@ namespace {
 // 16-byte chunks per thread of Q and of dO) and per-query statistics.
 struct QTile {
     v4i q[2], g[2];
-    int eq, edo;
-    float lse2, delta, qscale;
+    int eq, edo, kq;
+    float nlse, delta;
 };
 
 template <int D>
@@ -65,9 +65,54 @@ __device__ __forceinline__ void load_qtile(const AttnArgs& a, QTile& r, int h, i
         const bool ok = t < e;
         r.eq = ok ? (int)a.q_exps[(size_t)h * T + t] : 127;
         r.edo = ok ? (int)a.do_exps[(size_t)h * T + t] : 127;
-        r.lse2 = ok ? a.lse_in[(size_t)h * T + t] * kLog2e : INFINITY;
+        // exponent argument offset: 8 - LSE log2 e, so that exp2 yields 256 P
+        r.nlse = ok ? 8.f - a.lse_in[(size_t)h * T + t] * kLog2e : -INFINITY;
         r.delta = ok ? a.delta[(size_t)h * T + t] : 0.f;
-        r.qscale = ok ? ldexpf(a.scale, (int)a.prescale[(size_t)h * T + t]) : 0.f;
+        r.kq = ok ? (int)a.prescale[(size_t)h * T + t] + a.scale_exp : 0;
+    }
+}
+
+// 256 P and 256 dS of one wave's 32 keys x 64 queries, in place, and the
+// largest |256 dS| of each 32 x 32 block.  Element (t, v) of lane group g is
+// query 32 t + 16 g + v of the tile; with MASK it is kept only if
+// 32 t + v >= lim (causal visibility and key validity folded into lim).
+template <bool MASK>
+__device__ __forceinline__ void softmax_grad(v16f (&sacc)[2], v16f (&pacc)[2], const float* nl,
+                                             const float* dl, float c2, int lim, float (&amax)[2])
+{
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][v], c2, nl[32 * t + v]));
+            if (MASK) p = (32 * t + v >= lim) ? p : 0.f;
+            const float ds = p * (pacc[t][v] - dl[32 * t + v]);
+            sacc[t][v] = p;
+            pacc[t][v] = ds;
+            amax[t] = fmaxf(amax[t], fabsf(ds));
+        }
+}
+
+// Adds one 32 x 32 dQ tile (accumulator of a 32x32x64 MFMA: lane = column,
+// VGPR v = row 8 (v / 4) + 4 g + v % 4) into the FP16 accumulator.  Neighbour
+// lanes exchange halves so that each lane adds two adjacent columns of one
+// row: the even lane of a pair takes the even rows of each VGPR pair, the odd
+// lane the odd rows.  `tile` is the tile's first element, `rs` the row
+// stride in elements; rows >= nrows are skipped.
+template <bool CHECK>
+__device__ __forceinline__ void dq_tile_atomics(const v16f& acc, _Float16* tile, size_t rs,
+                                                uint32_t lane_off, uint32_t sel, int row0, int nrows)
+{
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int roff = 8 * (p / 2) + 2 * (p % 2);
+        const h2 mine = __builtin_convertvector(v2f{acc[2 * p], acc[2 * p + 1]}, h2);
+        const uint32_t w = __builtin_bit_cast(uint32_t, mine);
+        const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0xB1, 0xF, 0xF, false);
+        const uint32_t out = __builtin_amdgcn_perm(y, w, sel);
+        if (!CHECK || row0 + roff < nrows)
+            __builtin_amdgcn_global_atomic_fadd_v2f16(
+                (h2*)((char*)(tile + (size_t)roff * rs) + lane_off), __builtin_bit_cast(h2, out));
     }
 }
 
@@ -83,8 +128,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(16))) uint8_t s_q[2][64 * PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t s_do[2][64 * PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t s_ds[128 * SPITCH];
-    __shared__ int s_eq[2][64], s_edo[2][64];
-    __shared__ float s_lse2[2][64], s_delta[2][64], s_qscale[2][64];
+    __shared__ int s_eq[2][64], s_edo[2][64], s_kq[2][64];
+    __shared__ __attribute__((aligned(16))) float s_nlse[2][64];
+    __shared__ __attribute__((aligned(16))) float s_delta[2][64];
     __shared__ int s_dsexp[2][4];
     __shared__ int s_ekb[4];
 
@@ -138,6 +184,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
     const int nqt = (e - s + 63) / 64 - qt_lo;
     const int niter = G * nqt;
 
+    // dQ atomics: per-lane byte offset inside a 32 x 32 tile (row 4 g + odd,
+    // column pair lane & 30) and the byte selector that assembles the pair
+    const bool odd = lane & 1;
+    const uint32_t dq_sel = odd ? 0x03020706u : 0x05040100u;
+    const size_t dq_rs = (size_t)Hq * D;
+
     auto stage = [&](const QTile& r, int buf) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -151,9 +203,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
         if (tid < 64) {
             s_eq[buf][tid] = r.eq;
             s_edo[buf][tid] = r.edo;
-            s_lse2[buf][tid] = r.lse2;
+            s_kq[buf][tid] = r.kq;
+            s_nlse[buf][tid] = r.nlse;
             s_delta[buf][tid] = r.delta;
-            s_qscale[buf][tid] = r.qscale;
         }
     };
 
@@ -195,35 +247,31 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
                                       s_edo[cur][qr], ev);
                 }
             }
-            // P, dS; element (t, v) of lane group g <-> query 32 t + 16 g + v
+            // Masking is needed only where some key is invalid or, causally,
+            // some query precedes some key; queries past the document end have
+            // 256 P = exp2(-inf) = 0 and D = 0.
             float amax[2] = {0.f, 0.f};
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int qq = 32 * t + 16 * g + v;
-                    const int qi = qb + qq;
-                    const bool vis = kvalid && qi < e && (!a.causal || kj <= qi);
-                    const float p =
-                        vis ? __builtin_amdgcn_exp2f(fmaf(sacc[t][v], c2, -s_lse2[cur][qq])) : 0.f;
-                    const float ds = p * (pacc[t][v] - s_delta[cur][qq]);
-                    sacc[t][v] = p;
-                    pacc[t][v] = ds;
-                    amax[t] = fmaxf(amax[t], fabsf(ds));
-                }
+            const float* nl = &s_nlse[cur][16 * g];
+            const float* dl = &s_delta[cur][16 * g];
+            const bool full = kw0 + 32 <= e && (!a.causal || qb >= kw0 + 31);
+            if (full) {
+                softmax_grad<false>(sacc, pacc, nl, dl, c2, 0, amax);
+            } else {
+                const int lim = a.causal ? kj - qb - 16 * g : (kvalid ? -1 : 64);
+                softmax_grad<true>(sacc, pacc, nl, dl, c2, lim, amax);
+            }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const int et = ceil_exp448(wave_max(amax[t]));
+                // block exponent of dS = 2^-8 (256 dS); the scaling is exact
+                const int et = ceil_exp448(wave_max_nonneg(amax[t]) * 0.00390625f);
                 dse[t] = et + 127;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    pf[4 * t + q] = (int)cvt4_fp8(fminf(256.f * sacc[t][4 * q], 448.f),
-                                                  fminf(256.f * sacc[t][4 * q + 1], 448.f),
-                                                  fminf(256.f * sacc[t][4 * q + 2], 448.f),
-                                                  fminf(256.f * sacc[t][4 * q + 3], 448.f));
+                    pf[4 * t + q] = (int)cvt4_fp8(sacc[t][4 * q], sacc[t][4 * q + 1],
+                                                  sacc[t][4 * q + 2], sacc[t][4 * q + 3]);
                     df[4 * t + q] = (int)cvt4_fp8(
-                        ldexpf(pacc[t][4 * q], -et), ldexpf(pacc[t][4 * q + 1], -et),
-                        ldexpf(pacc[t][4 * q + 2], -et), ldexpf(pacc[t][4 * q + 3], -et));
+                        ldexpf(pacc[t][4 * q], -et - 8), ldexpf(pacc[t][4 * q + 1], -et - 8),
+                        ldexpf(pacc[t][4 * q + 2], -et - 8), ldexpf(pacc[t][4 * q + 3], -et - 8));
                 }
             }
             // dV^T += dO^T P^ and dK^T += Q^T dS^ (k = the tile's 64 queries)
@@ -237,6 +285,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
                                  dse[g]);
             }
         }
+        // keep the loop-carried dK / dV accumulators in AGPRs
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
 
         if constexpr (WITH_DQ) {
         // dS^ to LDS key-major (row = this lane's key): two 16-byte chunks
@@ -252,44 +303,34 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
         lds_barrier();
 
         // dQ = dS^ K^ over the tile's 128 keys, 32 x 32 output tiles (rows =
-        // queries, columns = head dim).  Lanes hold consecutive columns, so
-        // after pairing neighbour lanes each packed FP16 atomic instruction
-        // covers 64 contiguous bytes of 4 dQ rows.
-        for (int j = wave; j < 2 * NDT; j += 4) {
+        // queries, columns = head dim).  The row's prescale 2^(k_i + f)
+        // (2^f <= softmax scale < 2^(f + 1)) rides in the A operand's block
+        // scale; the finalize applies the remaining scale 2^-(k_i + f).
+#pragma unroll
+        for (int jj = 0; jj < (2 * NDT + 3) / 4; ++jj) {
+            const int j = wave + 4 * jj;
+            if (j >= 2 * NDT) break;
             const int dt = j % NDT, ct = j / NDT;
-            if (qb + 32 * ct >= e) continue;
+            const int nrows = e - (qb + 32 * ct);
+            if (nrows <= 0) continue;
+            const int kq = s_kq[cur][32 * ct + (lane & 31)];
             v16f acc;
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (k0 + 64 * ks >= e) break;
-                acc = mfma_f8(lds_tr_operand(s_ds + 64 * ks * SPITCH, SPITCH, 0, 32 * ct, lane),
-                              lds_tr_operand(s_kt + 64 * ks * PITCH, PITCH, 0, 32 * dt, lane), acc,
-                              s_dsexp[ct][2 * ks + g], s_ekb[2 * ks + g]);
-            }
-            // row of accumulator v: query 32 ct + 8 (v / 4) + 4 g + v % 4
-            const bool odd = lane & 1;
-            const int dcol = 32 * dt + (lane & 30);
-#pragma unroll
-            for (int v = 0; v < 16; v += 2) {
-                const int qq0 = 32 * ct + 8 * (v / 4) + 4 * g + (v % 4);  // row of v
-                const int qq1 = qq0 + 1;                                   // row of v + 1
-                // even lanes keep rows of v, odd lanes rows of v + 1
-                const float mine = odd ? acc[v + 1] : acc[v];
-                const float give = odd ? acc[v] : acc[v + 1];
-                const float other = __shfl_xor(give, 1, kWave);
-                const int qq = odd ? qq1 : qq0;
-                const int qi = qb + qq;
-                if (qi < e) {
-                    const float f = s_qscale[cur][qq];
-                    h2 val;
-                    val.x = (_Float16)((odd ? other : mine) * f);
-                    val.y = (_Float16)((odd ? mine : other) * f);
-                    __builtin_amdgcn_global_atomic_fadd_v2f16(
-                        (h2*)(a.dq_acc + ((size_t)qi * Hq + h) * D + dcol), val);
-                }
-            }
+            acc = mfma_f8(lds_tr_operand(s_ds, SPITCH, 0, 32 * ct, lane),
+                          lds_tr_operand(s_kt, PITCH, 0, 32 * dt, lane), acc,
+                          min(max(s_dsexp[ct][g] + kq, 0), 254), s_ekb[g]);
+            if (k0 + 64 < e)
+                acc = mfma_f8(lds_tr_operand(s_ds + 64 * SPITCH, SPITCH, 0, 32 * ct, lane),
+                              lds_tr_operand(s_kt + 64 * PITCH, PITCH, 0, 32 * dt, lane), acc,
+                              min(max(s_dsexp[ct][2 + g] + kq, 0), 254), s_ekb[2 + g]);
+            _Float16* tile = a.dq_acc + ((size_t)(qb + 32 * ct) * Hq + h) * D + 32 * dt;
+            const int row0 = 4 * g + (odd ? 1 : 0);
+            const uint32_t lane_off = (uint32_t)(((size_t)row0 * dq_rs + (lane & 30)) * 2);
+            if (nrows >= 32)
+                dq_tile_atomics<false>(acc, tile, dq_rs, lane_off, dq_sel, row0, nrows);
+            else
+                dq_tile_atomics<true>(acc, tile, dq_rs, lane_off, dq_sel, row0, nrows);
         }
         }  // WITH_DQ
         if (more) stage(nxt, cur ^ 1);
@@ -506,7 +547,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a)
     }
 }
 
-// dQ = acc * 2^-k_i -> bf16 for every row; dK = dV = 0 on padding rows.
+// dQ = acc * (scale 2^-f) * 2^-k_i -> bf16 for every row, the accumulator
+// holding 2^(k_i + f) sum dS^ K^ (2^f <= scale < 2^(f + 1)); dK = dV = 0 on
+// padding rows.
 template <int D, bool FROM_ACC>
 __global__ __launch_bounds__(256) void bwd_finalize_kernel(AttnArgs a)
 {
@@ -518,13 +561,13 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(AttnArgs a)
         const int c = (int)(i % (D / 8));
         const int t = (int)(row / a.Hq), h = (int)(row % a.Hq);
         if constexpr (FROM_ACC) {
-            const int k = (int)a.prescale[(size_t)h * T + t];
+            const float f = ldexpf(a.scale_res, -(int)a.prescale[(size_t)h * T + t]);
             const h8 raw = *(const h8*)(a.dq_acc + row * D + 8 * c);
             v4i out;
-            out.x = (int)pack_bf16x2(ldexpf((float)raw.s0, -k), ldexpf((float)raw.s1, -k));
-            out.y = (int)pack_bf16x2(ldexpf((float)raw.s2, -k), ldexpf((float)raw.s3, -k));
-            out.z = (int)pack_bf16x2(ldexpf((float)raw.s4, -k), ldexpf((float)raw.s5, -k));
-            out.w = (int)pack_bf16x2(ldexpf((float)raw.s6, -k), ldexpf((float)raw.s7, -k));
+            out.x = (int)pack_bf16x2((float)raw.s0 * f, (float)raw.s1 * f);
+            out.y = (int)pack_bf16x2((float)raw.s2 * f, (float)raw.s3 * f);
+            out.z = (int)pack_bf16x2((float)raw.s4 * f, (float)raw.s5 * f);
+            out.w = (int)pack_bf16x2((float)raw.s6 * f, (float)raw.s7 * f);
             *(v4i*)(a.dq + row * D + 8 * c) = out;
         } else if (t >= ntok) {
             *(v4i*)(a.dq + row * D + 8 * c) = v4i{0, 0, 0, 0};

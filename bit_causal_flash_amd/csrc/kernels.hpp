@@ -43,6 +43,8 @@ struct AttnArgs {
     int T, B, Hq, Hkv, causal;
     float scale;      // softmax scale
     float c2;         // scale * log2(e)
+    int scale_exp;    // f = floor(log2 scale)
+    float scale_res;  // scale * 2^-f, in [1, 2)
     const int32_t* cu;
     const int32_t* count;
     const int32_t* items;
