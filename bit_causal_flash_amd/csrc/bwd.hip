@@ -34,42 +34,42 @@ namespace flamia {
 
 namespace {
 
-// One 64-query tile of one q head, as staged for the backward: codes (two
-// 16-byte chunks per thread of Q and of dO) and per-query statistics.
+// One 64-query tile of one q head, as staged for the backward: codes (D / 64
+// 16-byte chunks per thread of Q and of dO) and the raw per-query values of
+// row tid % 64.  Every load is unconditional, with rows past the document end
+// clamped to its last row (their statistics are replaced at staging, which
+// makes their P, and so their dS, exactly zero), so that the only wait on the
+// prefetch is where it is staged.
+template <int D>
 struct QTile {
-    v4i q[2], g[2];
-    int eq, edo, kq;
-    float nlse, delta;
+    static constexpr int NC = D / 64;
+    v4i q[NC], g[NC];
+    int eq, edo, pre, ok;
+    float lse, delta;
 };
 
 template <int D>
-__device__ __forceinline__ void load_qtile(const AttnArgs& a, QTile& r, int h, int qb, int e, int tid)
+__device__ __forceinline__ void load_qtile(const AttnArgs& a, QTile<D>& r, int h, int qb, int e, int tid)
 {
     constexpr int CPR = D / 16;
     const int Hq = a.Hq;
     const size_t T = (size_t)a.T;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < QTile<D>::NC; ++k) {
         const int c = tid + 256 * k;
         const int row = c / CPR, col = 16 * (c % CPR);
-        const int t = qb + row;
-        r.q[k] = v4i{0, 0, 0, 0};
-        r.g[k] = v4i{0, 0, 0, 0};
-        if (row < 64 && t < e) {
-            r.q[k] = *(const v4i*)(a.q_codes + ((size_t)t * Hq + h) * D + col);
-            r.g[k] = *(const v4i*)(a.do_codes + ((size_t)t * Hq + h) * D + col);
-        }
+        const int t = min(qb + row, e - 1);
+        r.q[k] = *(const v4i*)(a.q_codes + ((size_t)t * Hq + h) * D + col);
+        r.g[k] = *(const v4i*)(a.do_codes + ((size_t)t * Hq + h) * D + col);
     }
-    if (tid < 64) {
-        const int t = qb + tid;
-        const bool ok = t < e;
-        r.eq = ok ? (int)a.q_exps[(size_t)h * T + t] : 127;
-        r.edo = ok ? (int)a.do_exps[(size_t)h * T + t] : 127;
-        // exponent argument offset: 8 - LSE log2 e, so that exp2 yields 256 P
-        r.nlse = ok ? 8.f - a.lse_in[(size_t)h * T + t] * kLog2e : -INFINITY;
-        r.delta = ok ? a.delta[(size_t)h * T + t] : 0.f;
-        r.kq = ok ? (int)a.prescale[(size_t)h * T + t] + a.scale_exp : 0;
-    }
+    const int t = qb + (tid & 63);
+    r.ok = t < e;
+    const size_t i = (size_t)h * T + min(t, e - 1);
+    r.eq = a.q_exps[i];
+    r.edo = a.do_exps[i];
+    r.lse = a.lse_in[i];
+    r.delta = a.delta[i];
+    r.pre = a.prescale[i];
 }
 
 // 256 P and 256 dS of one wave's 32 keys x 64 queries, in place, and the
@@ -190,40 +190,44 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
     const uint32_t dq_sel = odd ? 0x03020706u : 0x05040100u;
     const size_t dq_rs = (size_t)Hq * D;
 
-    auto stage = [&](const QTile& r, int buf) {
+    // every thread writes (the four waves write identical statistics), so
+    // that every prefetched register is consumed on every path
+    auto stage = [&](const QTile<D>& r, int buf) {
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < QTile<D>::NC; ++k) {
             const int c = tid + 256 * k;
             const int row = c / CPR, col = 16 * (c % CPR);
-            if (row < 64) {
-                *(v4i*)(&s_q[buf][row * PITCH + col]) = r.q[k];
-                *(v4i*)(&s_do[buf][row * PITCH + col]) = r.g[k];
-            }
+            *(v4i*)(&s_q[buf][row * PITCH + col]) = r.q[k];
+            *(v4i*)(&s_do[buf][row * PITCH + col]) = r.g[k];
         }
-        if (tid < 64) {
-            s_eq[buf][tid] = r.eq;
-            s_edo[buf][tid] = r.edo;
-            s_kq[buf][tid] = r.kq;
-            s_nlse[buf][tid] = r.nlse;
-            s_delta[buf][tid] = r.delta;
-        }
+        const int row = tid & 63;
+        s_eq[buf][row] = r.ok ? r.eq : 127;
+        s_edo[buf][row] = r.ok ? r.edo : 127;
+        s_kq[buf][row] = r.ok ? r.pre + a.scale_exp : 0;
+        // 8 - LSE log2 e: exp2 of the score term then yields 256 P; rows past
+        // the document end get -inf, so their P is exactly zero
+        s_nlse[buf][row] = r.ok ? 8.f - r.lse * kLog2e : -INFINITY;
+        s_delta[buf][row] = r.ok ? r.delta : 0.f;
     };
 
-    QTile nxt;
-    if (niter > 0) {
-        load_qtile<D>(a, nxt, hk * G, s + 64 * qt_lo, e, tid);
-        stage(nxt, 0);
-    }
+    QTile<D> nxt;
+    load_qtile<D>(a, nxt, hk * G, s + 64 * qt_lo, e, tid);
+    stage(nxt, 0);
+    // every load issued so far has landed (vmcnt(0)), so that inside the loop
+    // only the prefetch of the next tile is outstanding
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
 
     for (int it = 0; it < niter; ++it) {
         const int cur = it & 1;
         const int h = hk * G + it / nqt;
         const int qb = s + 64 * (qt_lo + it % nqt);
-        const bool more = it + 1 < niter;
-        if (more) {
-            const int h1 = hk * G + (it + 1) / nqt;
-            const int qb1 = s + 64 * (qt_lo + (it + 1) % nqt);
+        // prefetch the next tile (the last iteration reloads its own, unused):
+        // unconditional, so the only wait on these loads is at staging
+        {
+            const int it1 = min(it + 1, niter - 1);
+            const int h1 = hk * G + it1 / nqt;
+            const int qb1 = s + 64 * (qt_lo + it1 % nqt);
             load_qtile<D>(a, nxt, h1, qb1, e, tid);
         }
         const uint8_t* sq = s_q[cur];
@@ -290,8 +294,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
         for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
 
         if constexpr (WITH_DQ) {
-        // dS^ to LDS key-major (row = this lane's key): two 16-byte chunks
-        {
+            // dS^ to LDS key-major (row = this lane's key): two 16-byte chunks
             const int krow = 32 * wave + (lane & 31);
             *(v4i*)(s_ds + krow * SPITCH + 16 * g) = v4i{df[0], df[1], df[2], df[3]};
             *(v4i*)(s_ds + krow * SPITCH + 32 + 16 * g) = v4i{df[4], df[5], df[6], df[7]};
@@ -300,6 +303,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
                 s_dsexp[1][wave] = dse[1];
             }
         }
+        // Stage the prefetched tile into the other buffer now, ahead of this
+        // tile's dQ atomics: the wait on its loads then also covers only the
+        // previous tile's atomics, which have had a whole tile to complete.
+        stage(nxt, cur ^ 1);
+
+        if constexpr (WITH_DQ) {
         lds_barrier();
 
         // dQ = dS^ K^ over the tile's 128 keys, 32 x 32 output tiles (rows =
@@ -333,7 +342,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
                 dq_tile_atomics<true>(acc, tile, dq_rs, lane_off, dq_sel, row0, nrows);
         }
         }  // WITH_DQ
-        if (more) stage(nxt, cur ^ 1);
         lds_barrier();
     }
 
