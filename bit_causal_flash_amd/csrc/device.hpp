@@ -179,6 +179,25 @@ __device__ __forceinline__ float swap_adjacent(float x)
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
 }
 
+// Combining a value with the one of lane i ^ 32.  v_permlane32_swap
+// exchanges the upper half of its first operand with the lower half of its
+// second; with both operands x, each lane receives, across the two results,
+// its own x and the x of lane i ^ 32, so symmetric combinations of the two
+// results need no knowledge of which is which.
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                     false);
+    return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+
+__device__ __forceinline__ float sum_xor32(float x)
+{
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                     false);
+    return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+}
+
 __device__ __forceinline__ float wave_max(float x)
 {
     for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));

@@ -31,41 +31,89 @@ namespace flamia {
 
 namespace {
 
-// One 64-key step of K and V codes (two 16-byte chunks per thread of each)
-// and their exponents, as staged for the forward.
+// One 64-key step of K and V codes (D / 64 16-byte chunks per thread of
+// each) and the raw exponents of key tid % 64 and of the V block of tid % 2.
+// Every load is unconditional, rows past the document end clamped to its last
+// row (staging replaces their exponents, and the masks zero their weights),
+// so that the only wait on the prefetch is where it is staged.
+template <int D>
 struct KVTile {
-    v4i k[2], v[2];
-    int ek, ev;
+    static constexpr int NC = D / 64;
+    v4i k[NC], v[NC];
+    int ek, ev, kok, vok;
 };
 
 template <int D>
-__device__ __forceinline__ void load_kvtile(const AttnArgs& a, KVTile& r, int hk, int kt0, int e,
+__device__ __forceinline__ void load_kvtile(const AttnArgs& a, KVTile<D>& r, int hk, int kt0, int e,
                                             int tid)
 {
     constexpr int CPR = D / 16;
     const int Hkv = a.Hkv;
     const size_t T = (size_t)a.T;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < KVTile<D>::NC; ++k) {
         const int c = tid + 256 * k;
         const int row = c / CPR, col = 16 * (c % CPR);
-        const int t = kt0 + row;
-        r.k[k] = v4i{0, 0, 0, 0};
-        r.v[k] = v4i{0, 0, 0, 0};
-        if (row < 64 && t < e) {
-            r.k[k] = *(const v4i*)(a.k_codes + ((size_t)t * Hkv + hk) * D + col);
-            r.v[k] = *(const v4i*)(a.v_codes + ((size_t)t * Hkv + hk) * D + col);
+        const int t = min(kt0 + row, e - 1);
+        r.k[k] = *(const v4i*)(a.k_codes + ((size_t)t * Hkv + hk) * D + col);
+        r.v[k] = *(const v4i*)(a.v_codes + ((size_t)t * Hkv + hk) * D + col);
+    }
+    const int tk = kt0 + (tid & 63);
+    const int tv = kt0 + 32 * (tid & 1);
+    r.kok = tk < e;
+    r.vok = tv < e;
+    r.ek = a.k_exps[(size_t)hk * T + min(tk, e - 1)];
+    r.ev = a.v_exps[(size_t)hk * T + min(tv, e - 1)];
+}
+
+// Online-softmax update of one wave's 32 queries x 64 keys: the running
+// integer reference r, the rescale of O and l when it rises, and the
+// probability operand P^ (byte 16 t + v <-> key 32 t + 16 g + v) with its
+// rounded row sum.  Unless `full`, element (t, v) is kept only if
+// 32 t + v < lim.
+template <int NDT>
+__device__ __forceinline__ void online_softmax(v16f (&sacc)[2], v16f (&oacc)[NDT], float& r,
+                                               float& l, v8i& pf, float c2, bool full, int lim)
+{
+    if (!full) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                if (!(32 * t + v < lim)) sacc[t][v] = -INFINITY;
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, sacc[t][v]);
+    // the other half of the keys sits in the lane 32 away
+    mloc = max_xor32(mloc);
+    const float rn = fmaxf(r, ceilf(mloc * c2));
+    if (__any(rn > r)) {
+        float alpha = 1.f;
+        if (rn > r) alpha = (r == -INFINITY) ? 0.f : ldexpf(1.f, (int)fmaxf(r - rn, -200.f));
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+    }
+    r = rn;
+    const float off = (r == -INFINITY) ? 0.f : 8.f - r;
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float p[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) p[k] = __builtin_amdgcn_exp2f(fmaf(sacc[t][4 * q + k], c2, off));
+            const uint32_t w = cvt4_fp8(p[0], p[1], p[2], p[3]);
+            pf[4 * t + q] = (int)w;
+            lsum += sum4_fp8(w);
         }
-    }
-    r.ek = 127;
-    r.ev = 127;
-    if (tid < 64) {
-        const int t = kt0 + tid;
-        if (t < e) r.ek = (int)a.k_exps[(size_t)hk * T + t];
-    } else if (tid < 66) {
-        const int t = kt0 + 32 * (tid - 64);
-        if (t < e) r.ev = (int)a.v_exps[(size_t)hk * T + t];
-    }
+    l += lsum * 0.00390625f;
 }
 
 template <int D>
@@ -115,32 +163,33 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
     float r = -INFINITY;  // integer base-2 row reference
     float l = 0.f;        // sum of rounded weights
 
-    auto stage = [&](const KVTile& t, int buf) {
+    // every thread writes (the four waves write identical exponents), so
+    // that every prefetched register is consumed on every path
+    auto stage = [&](const KVTile<D>& t, int buf) {
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < KVTile<D>::NC; ++k) {
             const int c = tid + 256 * k;
             const int row = c / CPR, col = 16 * (c % CPR);
-            if (row < 64) {
-                *(v4i*)(&s_k[buf][row * PITCH + col]) = t.k[k];
-                *(v4i*)(&s_v[buf][row * PITCH + col]) = t.v[k];
-            }
+            *(v4i*)(&s_k[buf][row * PITCH + col]) = t.k[k];
+            *(v4i*)(&s_v[buf][row * PITCH + col]) = t.v[k];
         }
-        if (tid < 64) s_ek[buf][tid] = t.ek;
-        else if (tid < 66) s_ev[buf][tid - 64] = t.ev;
+        s_ek[buf][tid & 63] = t.kok ? t.ek : 127;
+        s_ev[buf][tid & 1] = t.vok ? t.ev : 127;
     };
 
-    KVTile nxt;
-    if (nsteps > 0) {
-        load_kvtile<D>(a, nxt, hk, s, e, tid);
-        stage(nxt, 0);
-    }
+    KVTile<D> nxt;
+    load_kvtile<D>(a, nxt, hk, s, e, tid);
+    stage(nxt, 0);
+    // every load issued so far has landed (vmcnt(0)), so that inside the loop
+    // only the prefetch of the next step is outstanding
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
 
     for (int st = 0; st < nsteps; ++st) {
         const int cur = st & 1;
         const int kt0 = s + 64 * st;
-        const bool more = st + 1 < nsteps;
-        if (more) load_kvtile<D>(a, nxt, hk, kt0 + 64, e, tid);
+        // prefetch the next step (the last step reloads its own, unused)
+        load_kvtile<D>(a, nxt, hk, min(kt0 + 64, s + 64 * (nsteps - 1)), e, tid);
         const uint8_t* sk = s_k[cur];
         const uint8_t* sv = s_v[cur];
 
@@ -159,48 +208,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
                                       sacc[t], ek, eq);
             }
 
-            // masking and the running integer reference
-            const bool full = (kt0 + 64 <= e) && (!a.causal || kt0 + 63 <= qw);
-            float mloc = -INFINITY;
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int key = kt0 + 32 * t + 16 * g + v;
-                    const bool vis = full || (key < e && (!a.causal || key <= qi));
-                    if (!vis) sacc[t][v] = -INFINITY;
-                    mloc = fmaxf(mloc, sacc[t][v]);
-                }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-            const float rn = fmaxf(r, ceilf(mloc * c2));
-            if (__any(rn > r)) {
-                float alpha = 1.f;
-                if (rn > r) alpha = (r == -INFINITY) ? 0.f : ldexpf(1.f, (int)fmaxf(r - rn, -200.f));
-                l *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
-            }
-            r = rn;
-
-            // probability operand: E4M3(256 * 2^(s2 - r)), byte 16 t + v <-> key 32 t + 16 g + v
-            const float off = (r == -INFINITY) ? 0.f : 8.f - r;
+            // masking is needed only where the step runs past the document
+            // end or, causally, some key follows some query of the wave;
+            // element (t, v) is key kt0 + 32 t + 16 g + v
             v8i pf;
-            float lsum = 0.f;
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float p[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        p[k] = __builtin_amdgcn_exp2f(fmaf(sacc[t][4 * q + k], c2, off));
-                    const uint32_t w = cvt4_fp8(p[0], p[1], p[2], p[3]);
-                    pf[4 * t + q] = (int)w;
-                    lsum += sum4_fp8(w);
-                }
-            l += lsum * 0.00390625f;
+            const bool full = (kt0 + 64 <= e) && (!a.causal || kt0 + 63 <= qw);
+            const int lim = min(e, a.causal ? qi + 1 : e) - kt0 - 16 * g;
+            online_softmax<NDT>(sacc, oacc, r, l, pf, c2, full, lim);
 
             // O^T += V^T P^T: V^T read k-major from the token-major LDS tile
             const int sv_exp = s_ev[cur][g];
@@ -209,11 +223,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
                 oacc[dt] = mfma_f8(lds_tr_operand(sv, PITCH, 0, 32 * dt, lane), pf, oacc[dt],
                                    sv_exp, kScaleMinus8);
         }
-        if (more) stage(nxt, cur ^ 1);
+        stage(nxt, cur ^ 1);
         lds_barrier();
     }
 
-    l += __shfl_xor(l, 32, kWave);
+    l = sum_xor32(l);
     if (qvalid) {
         const float inv = 1.f / l;
         uint16_t* orow = a.o + ((size_t)qi * Hq + h) * D;
