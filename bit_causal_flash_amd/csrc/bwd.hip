@@ -522,7 +522,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a)
             v8i df;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const int et = ceil_exp448(wave_max(amax[t]));
+                const int et = ceil_exp448(wave_max_nonneg(amax[t]));
                 dse[t] = et + 127;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)

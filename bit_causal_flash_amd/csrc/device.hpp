@@ -198,19 +198,10 @@ __device__ __forceinline__ float sum_xor32(float x)
     return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
 }
 
-__device__ __forceinline__ float wave_max(float x)
+// Largest unsigned value over the wave, returned wave-uniform: DPP within
+// each 16-lane row, then the four row maxima through v_readlane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t u)
 {
-    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
-    return x;
-}
-
-// Largest value over the wave of a non-negative float, returned wave-uniform.
-// Non-negative floats order like their bit patterns, so the reduction runs on
-// integers: DPP within each 16-lane row, then the four row maxima through
-// v_readlane.
-__device__ __forceinline__ float wave_max_nonneg(float x)
-{
-    uint32_t u = __float_as_uint(x);
     u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
     u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
     u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, false));  // row_half_mirror
@@ -219,7 +210,14 @@ __device__ __forceinline__ float wave_max_nonneg(float x)
     const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)u, 16);
     const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)u, 32);
     const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)u, 48);
-    return __uint_as_float(max(max(r0, r1), max(r2, r3)));
+    return max(max(r0, r1), max(r2, r3));
+}
+
+// Largest value over the wave of a non-negative float, returned wave-uniform
+// (non-negative floats order like their bit patterns).
+__device__ __forceinline__ float wave_max_nonneg(float x)
+{
+    return __uint_as_float(wave_max_u32(__float_as_uint(x)));
 }
 
 __device__ __forceinline__ int doc_of(const int32_t* cu, int B, int t)
