@@ -34,16 +34,17 @@ namespace flamia {
 
 namespace {
 
-// One 64-query tile of one q head, as staged for the backward: codes (D / 64
-// 16-byte chunks per thread of Q and of dO) and the raw per-query values of
-// row tid % 64.  Every load is unconditional, with rows past the document end
-// clamped to its last row (their statistics are replaced at staging, which
-// makes their P, and so their dS, exactly zero), so that the only wait on the
-// prefetch is where it is staged.
+// One 64-query tile of one q head, as staged for the backward by the 512
+// threads of a workgroup: D / 64 16-byte chunks per thread of the Q and dO
+// code tiles (chunk c < 4 D of Q, the rest of dO) and the raw per-query
+// values of row tid % 64.  Every load is unconditional, with rows past the
+// document end clamped to its last row (their statistics are replaced at
+// staging, which makes their P, and so their dS, exactly zero), so that the
+// only wait on the prefetch is where it is staged.
 template <int D>
 struct QTile {
     static constexpr int NC = D / 64;
-    v4i q[NC], g[NC];
+    v4i c[NC];
     int eq, edo, pre, ok;
     float lse, delta;
 };
@@ -56,11 +57,13 @@ __device__ __forceinline__ void load_qtile(const AttnArgs& a, QTile<D>& r, int h
     const size_t T = (size_t)a.T;
 #pragma unroll
     for (int k = 0; k < QTile<D>::NC; ++k) {
-        const int c = tid + 256 * k;
-        const int row = c / CPR, col = 16 * (c % CPR);
+        const int c = tid + 512 * k;
+        const bool isq = c < 4 * D;
+        const int cc = isq ? c : c - 4 * D;
+        const int row = cc / CPR, col = 16 * (cc % CPR);
         const int t = min(qb + row, e - 1);
-        r.q[k] = *(const v4i*)(a.q_codes + ((size_t)t * Hq + h) * D + col);
-        r.g[k] = *(const v4i*)(a.do_codes + ((size_t)t * Hq + h) * D + col);
+        const uint8_t* src = isq ? a.q_codes : a.do_codes;
+        r.c[k] = *(const v4i*)(src + ((size_t)t * Hq + h) * D + col);
     }
     const int t = qb + (tid & 63);
     r.ok = t < e;
@@ -72,25 +75,25 @@ __device__ __forceinline__ void load_qtile(const AttnArgs& a, QTile<D>& r, int h
     r.pre = a.prescale[i];
 }
 
-// 256 P and 256 dS of one wave's 32 keys x 64 queries, in place, and the
-// largest |256 dS| of each 32 x 32 block.  Element (t, v) of lane group g is
-// query 32 t + 16 g + v of the tile; with MASK it is kept only if
-// 32 t + v >= lim (causal visibility and key validity folded into lim).
+// 256 P and 256 dS of one wave's 32 keys x 32 queries, in place, and the
+// largest |256 dS|.  Element v of lane group g is query 16 g + v of the
+// wave's 32 (the statistics nl, dl start at that query); with MASK it is
+// kept only if v >= lim (causal visibility and key validity folded into lim).
 template <bool MASK>
-__device__ __forceinline__ void softmax_grad(v16f (&sacc)[2], v16f (&pacc)[2], const float* nl,
-                                             const float* dl, float c2, int lim, float (&amax)[2])
+__device__ __forceinline__ float softmax_grad(v16f& sacc, v16f& pacc, const float* nl,
+                                              const float* dl, float c2, int lim)
 {
+    float amax = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][v], c2, nl[32 * t + v]));
-            if (MASK) p = (32 * t + v >= lim) ? p : 0.f;
-            const float ds = p * (pacc[t][v] - dl[32 * t + v]);
-            sacc[t][v] = p;
-            pacc[t][v] = ds;
-            amax[t] = fmaxf(amax[t], fabsf(ds));
-        }
+    for (int v = 0; v < 16; ++v) {
+        float p = __builtin_amdgcn_exp2f(fmaf(sacc[v], c2, nl[v]));
+        if (MASK) p = (v >= lim) ? p : 0.f;
+        const float ds = p * (pacc[v] - dl[v]);
+        sacc[v] = p;
+        pacc[v] = ds;
+        amax = fmaxf(amax, fabsf(ds));
+    }
+    return amax;
 }
 
 // Adds one 32 x 32 dQ tile (accumulator of a 32x32x64 MFMA: lane = column,
@@ -116,25 +119,35 @@ __device__ __forceinline__ void dq_tile_atomics(const v16f& acc, _Float16* tile,
     }
 }
 
+// Workgroup of 8 waves: wave w serves the keys 32 (w % 4) .. + 31 of the
+// 128-key tile and the query half w / 4 of each 64-query tile.  It computes
+// S and dP of its 32 x 32 block (which is exactly one dS scale block) and
+// shares its P^ and dS^ codes with the other half through key-major LDS
+// tiles; then both waves of a key group contract all 64 queries, each for
+// half of the head dim of dV and dK.  Per wave this keeps 32 keys x d / 2
+// of each accumulator, so two waves fit on every SIMD.
 template <int D, bool WITH_DQ>
-__global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
+__global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
 {
     constexpr int PITCH = D + 16;   // token-major code tiles
-    constexpr int SPITCH = 64 + 16; // dS^ tile, key-major: [128 keys][64 queries]
+    constexpr int SPITCH = 64 + 16; // P^ / dS^ tiles, key-major: [128 keys][64 queries]
     constexpr int NKS = D / 64;
     constexpr int NDT = D / 32;
+    constexpr int NDH = NDT / 2;    // head-dim tiles of dV / dK per wave
     constexpr int CPR = D / 16;
     __shared__ __attribute__((aligned(16))) uint8_t s_kt[128 * PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t s_q[2][64 * PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t s_do[2][64 * PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_p[128 * SPITCH];
     __shared__ __attribute__((aligned(16))) uint8_t s_ds[128 * SPITCH];
     __shared__ int s_eq[2][64], s_edo[2][64], s_kq[2][64];
     __shared__ __attribute__((aligned(16))) float s_nlse[2][64];
     __shared__ __attribute__((aligned(16))) float s_delta[2][64];
-    __shared__ int s_dsexp[2][4];
+    __shared__ int s_dsexp[2][4];   // [query half][key group]
     __shared__ int s_ekb[4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+    const int kg = wave & 3, half = wave >> 2;
     const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
     const size_t T = (size_t)a.T;
     const int item = blockIdx.x / Hkv, hk = blockIdx.x % Hkv;
@@ -142,14 +155,14 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
     const int b = a.items[2 * item], kt = a.items[2 * item + 1];
     const int s = a.cu[b], e = a.cu[b + 1];
     const int k0 = s + 128 * kt;
-    const int kw0 = k0 + 32 * wave;
+    const int kw0 = k0 + 32 * kg;
     const int kj = kw0 + (lane & 31);
     const bool kvalid = kj < e;
     const bool wave_keys = kw0 < e;
     const float c2 = a.c2;
 
     // the workgroup's K tile, token-major, for the dQ MFMA (k = keys)
-    for (int c = tid; c < 128 * CPR; c += 256) {
+    for (int c = tid; c < 128 * CPR; c += 512) {
         const int row = c / CPR, col = 16 * (c % CPR);
         const int t = k0 + row;
         v4i kv = {0, 0, 0, 0};
@@ -173,11 +186,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
     const int ek = kvalid ? (int)a.k_exps[(size_t)hk * T + kj] : 127;
     const int ev = kvalid ? (int)a.v_exps[(size_t)hk * T + kj] : 127;
 
-    v16f dk[NDT], dv[NDT];
+    // dK^T, dV^T of the wave's keys over head-dim tiles NDH half .. + NDH - 1
+    v16f dk[NDH], dv[NDH];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int i = 0; i < NDH; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) dk[dt][v] = dv[dt][v] = 0.f;
+        for (int v = 0; v < 16; ++v) dk[i][v] = dv[i][v] = 0.f;
 
     // iterations: q heads of the group (outer) x 64-query tiles that see the keys
     const int qt_lo = a.causal ? 2 * kt : 0;
@@ -190,15 +204,16 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
     const uint32_t dq_sel = odd ? 0x03020706u : 0x05040100u;
     const size_t dq_rs = (size_t)Hq * D;
 
-    // every thread writes (the four waves write identical statistics), so
-    // that every prefetched register is consumed on every path
+    // every thread writes (the waves write identical statistics), so that
+    // every prefetched register is consumed on every path
     auto stage = [&](const QTile<D>& r, int buf) {
 #pragma unroll
         for (int k = 0; k < QTile<D>::NC; ++k) {
-            const int c = tid + 256 * k;
-            const int row = c / CPR, col = 16 * (c % CPR);
-            *(v4i*)(&s_q[buf][row * PITCH + col]) = r.q[k];
-            *(v4i*)(&s_do[buf][row * PITCH + col]) = r.g[k];
+            const int c = tid + 512 * k;
+            const bool isq = c < 4 * D;
+            const int cc = isq ? c : c - 4 * D;
+            const int row = cc / CPR, col = 16 * (cc % CPR);
+            *(v4i*)((isq ? s_q[buf] : s_do[buf]) + row * PITCH + col) = r.c[k];
         }
         const int row = tid & 63;
         s_eq[buf][row] = r.ok ? r.eq : 127;
@@ -218,6 +233,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
     __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
 
+    const int krow = 32 * kg + (lane & 31);  // this lane's key in the key-major tiles
     for (int it = 0; it < niter; ++it) {
         const int cur = it & 1;
         const int h = hk * G + it / nqt;
@@ -233,92 +249,87 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
         const uint8_t* sq = s_q[cur];
         const uint8_t* sg = s_do[cur];
 
-        const bool active = wave_keys && (!a.causal || qb + 63 >= kw0);
-        v8i pf = {0, 0, 0, 0, 0, 0, 0, 0}, df = {0, 0, 0, 0, 0, 0, 0, 0};
-        int dse[2] = {127, 127};
+        // this wave's 32 x 32 block: queries 32 half .. + 31 of the tile
+        const bool active = wave_keys && (!a.causal || qb + 32 * half + 31 >= kw0);
+        v4i pf = {0, 0, 0, 0}, df = {0, 0, 0, 0};
+        int dse = 127;
         if (active) {
-            v16f sacc[2], pacc[2];
+            v16f sacc, pacc;
+            const int qr = perm_row(half, lane & 31);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int qr = perm_row(t, lane & 31);
+            for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = 0.f;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) sacc[t][v] = pacc[t][v] = 0.f;
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    sacc[t] = mfma_f8(row_operand(sq + qr * PITCH + 64 * ks, lane), kf[ks], sacc[t],
-                                      s_eq[cur][qr], ek);
-                    pacc[t] = mfma_f8(row_operand(sg + qr * PITCH + 64 * ks, lane), vf[ks], pacc[t],
-                                      s_edo[cur][qr], ev);
-                }
+            for (int ks = 0; ks < NKS; ++ks) {
+                sacc = mfma_f8(row_operand(sq + qr * PITCH + 64 * ks, lane), kf[ks], sacc,
+                               s_eq[cur][qr], ek);
+                pacc = mfma_f8(row_operand(sg + qr * PITCH + 64 * ks, lane), vf[ks], pacc,
+                               s_edo[cur][qr], ev);
             }
             // Masking is needed only where some key is invalid or, causally,
             // some query precedes some key; queries past the document end have
-            // 256 P = exp2(-inf) = 0 and D = 0.
-            float amax[2] = {0.f, 0.f};
-            const float* nl = &s_nlse[cur][16 * g];
-            const float* dl = &s_delta[cur][16 * g];
-            const bool full = kw0 + 32 <= e && (!a.causal || qb >= kw0 + 31);
+            // 256 P = exp2(-inf) = 0 and D = 0.  Element v of lane group g is
+            // query qb + 32 half + 16 g + v.
+            const float* nl = &s_nlse[cur][32 * half + 16 * g];
+            const float* dl = &s_delta[cur][32 * half + 16 * g];
+            const bool full = kw0 + 32 <= e && (!a.causal || qb + 32 * half >= kw0 + 31);
+            float amax;
             if (full) {
-                softmax_grad<false>(sacc, pacc, nl, dl, c2, 0, amax);
+                amax = softmax_grad<false>(sacc, pacc, nl, dl, c2, 0);
             } else {
-                const int lim = a.causal ? kj - qb - 16 * g : (kvalid ? -1 : 64);
-                softmax_grad<true>(sacc, pacc, nl, dl, c2, lim, amax);
+                const int lim = a.causal ? kj - qb - 32 * half - 16 * g : (kvalid ? -1 : 16);
+                amax = softmax_grad<true>(sacc, pacc, nl, dl, c2, lim);
             }
+            // block exponent of dS = 2^-8 (256 dS); the scaling is exact
+            const int et = ceil_exp448(wave_max_nonneg(amax) * 0.00390625f);
+            dse = et + 127;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                // block exponent of dS = 2^-8 (256 dS); the scaling is exact
-                const int et = ceil_exp448(wave_max_nonneg(amax[t]) * 0.00390625f);
-                dse[t] = et + 127;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    pf[4 * t + q] = (int)cvt4_fp8(sacc[t][4 * q], sacc[t][4 * q + 1],
-                                                  sacc[t][4 * q + 2], sacc[t][4 * q + 3]);
-                    df[4 * t + q] = (int)cvt4_fp8(
-                        ldexpf(pacc[t][4 * q], -et - 8), ldexpf(pacc[t][4 * q + 1], -et - 8),
-                        ldexpf(pacc[t][4 * q + 2], -et - 8), ldexpf(pacc[t][4 * q + 3], -et - 8));
-                }
-            }
-            // dV^T += dO^T P^ and dK^T += Q^T dS^ (k = the tile's 64 queries)
-            const int sdo = s_edo[cur][32 * g];
-            const int sqe = s_eq[cur][32 * g];
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                dv[dt] = mfma_f8(lds_tr_operand(sg, PITCH, 0, 32 * dt, lane), pf, dv[dt], sdo,
-                                 kScaleMinus8);
-                dk[dt] = mfma_f8(lds_tr_operand(sq, PITCH, 0, 32 * dt, lane), df, dk[dt], sqe,
-                                 dse[g]);
+            for (int q = 0; q < 4; ++q) {
+                pf[q] = (int)cvt4_fp8(sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]);
+                df[q] = (int)cvt4_fp8(ldexpf(pacc[4 * q], -et - 8), ldexpf(pacc[4 * q + 1], -et - 8),
+                                      ldexpf(pacc[4 * q + 2], -et - 8),
+                                      ldexpf(pacc[4 * q + 3], -et - 8));
             }
         }
-        // keep the loop-carried dK / dV accumulators in AGPRs
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
-
-        if constexpr (WITH_DQ) {
-            // dS^ to LDS key-major (row = this lane's key): two 16-byte chunks
-            const int krow = 32 * wave + (lane & 31);
-            *(v4i*)(s_ds + krow * SPITCH + 16 * g) = v4i{df[0], df[1], df[2], df[3]};
-            *(v4i*)(s_ds + krow * SPITCH + 32 + 16 * g) = v4i{df[4], df[5], df[6], df[7]};
-            if (lane == 0) {
-                s_dsexp[0][wave] = dse[0];
-                s_dsexp[1][wave] = dse[1];
-            }
-        }
+        // P^ and dS^ to LDS, key-major (row = this lane's key, 16 bytes at the
+        // wave's query half and lane group)
+        *(v4i*)(s_p + krow * SPITCH + 32 * half + 16 * g) = pf;
+        *(v4i*)(s_ds + krow * SPITCH + 32 * half + 16 * g) = df;
+        if (lane == 0) s_dsexp[half][kg] = dse;
         // Stage the prefetched tile into the other buffer now, ahead of this
         // tile's dQ atomics: the wait on its loads then also covers only the
         // previous tile's atomics, which have had a whole tile to complete.
         stage(nxt, cur ^ 1);
-
-        if constexpr (WITH_DQ) {
         lds_barrier();
 
-        // dQ = dS^ K^ over the tile's 128 keys, 32 x 32 output tiles (rows =
-        // queries, columns = head dim).  The row's prescale 2^(k_i + f)
-        // (2^f <= softmax scale < 2^(f + 1)) rides in the A operand's block
-        // scale; the finalize applies the remaining scale 2^-(k_i + f).
+        // dV^T += dO^T P^ and dK^T += Q^T dS^ over all 64 queries (k), for
+        // this wave's half of the head dim; the B operands are the key group's
+        // P^ / dS^ rows in the k layout (bytes 0-15 query half 0, 16-31 half 1)
+        if (wave_keys && (!a.causal || qb + 63 >= kw0)) {
+            const v4i p0 = *(const v4i*)(s_p + krow * SPITCH + 16 * g);
+            const v4i p1 = *(const v4i*)(s_p + krow * SPITCH + 32 + 16 * g);
+            const v4i d0 = *(const v4i*)(s_ds + krow * SPITCH + 16 * g);
+            const v4i d1 = *(const v4i*)(s_ds + krow * SPITCH + 32 + 16 * g);
+            const v8i pfull = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+            const v8i dfull = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+            const int sdo = s_edo[cur][32 * g];
+            const int sqe = s_eq[cur][32 * g];
+            const int dsg = s_dsexp[g][kg];
 #pragma unroll
-        for (int jj = 0; jj < (2 * NDT + 3) / 4; ++jj) {
-            const int j = wave + 4 * jj;
-            if (j >= 2 * NDT) break;
+            for (int i = 0; i < NDH; ++i) {
+                const int dt = NDH * half + i;
+                dv[i] = mfma_f8(lds_tr_operand(sg, PITCH, 0, 32 * dt, lane), pfull, dv[i], sdo,
+                                kScaleMinus8);
+                dk[i] = mfma_f8(lds_tr_operand(sq, PITCH, 0, 32 * dt, lane), dfull, dk[i], sqe, dsg);
+            }
+        }
+
+        if constexpr (WITH_DQ) {
+        // dQ = dS^ K^ over the tile's 128 keys, 32 x 32 output tiles (rows =
+        // queries, columns = head dim), one per wave.  The row's prescale
+        // 2^(k_i + f) (2^f <= softmax scale < 2^(f + 1)) rides in the A
+        // operand's block scale; the finalize applies the remaining scale
+        // 2^-(k_i + f).
+        for (int j = wave; j < 2 * NDT; j += 8) {
             const int dt = j % NDT, ct = j / NDT;
             const int nrows = e - (qb + 32 * ct);
             if (nrows <= 0) continue;
@@ -346,21 +357,23 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(AttnArgs a)
     }
 
     if (kvalid) {
-        uint16_t* krow = a.dk + ((size_t)kj * Hkv + hk) * D;
-        uint16_t* vrow = a.dv + ((size_t)kj * Hkv + hk) * D;
+        uint16_t* krp = a.dk + ((size_t)kj * Hkv + hk) * D;
+        uint16_t* vrp = a.dv + ((size_t)kj * Hkv + hk) * D;
         const float sc = a.scale;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+        for (int i = 0; i < NDH; ++i) {
+            const int dt = NDH * half + i;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 v2i wk, wv;
-                wk.x = (int)pack_bf16x2(dk[dt][4 * q] * sc, dk[dt][4 * q + 1] * sc);
-                wk.y = (int)pack_bf16x2(dk[dt][4 * q + 2] * sc, dk[dt][4 * q + 3] * sc);
-                wv.x = (int)pack_bf16x2(dv[dt][4 * q], dv[dt][4 * q + 1]);
-                wv.y = (int)pack_bf16x2(dv[dt][4 * q + 2], dv[dt][4 * q + 3]);
-                *(v2i*)(krow + 32 * dt + 8 * q + 4 * g) = wk;
-                *(v2i*)(vrow + 32 * dt + 8 * q + 4 * g) = wv;
+                wk.x = (int)pack_bf16x2(dk[i][4 * q] * sc, dk[i][4 * q + 1] * sc);
+                wk.y = (int)pack_bf16x2(dk[i][4 * q + 2] * sc, dk[i][4 * q + 3] * sc);
+                wv.x = (int)pack_bf16x2(dv[i][4 * q], dv[i][4 * q + 1]);
+                wv.y = (int)pack_bf16x2(dv[i][4 * q + 2], dv[i][4 * q + 3]);
+                *(v2i*)(krp + 32 * dt + 8 * q + 4 * g) = wk;
+                *(v2i*)(vrp + 32 * dt + 8 * q + 4 * g) = wv;
             }
+        }
     }
 }
 
@@ -597,11 +610,11 @@ hipError_t launch_bwd(const AttnArgs& a, int D, int max_items, bool with_dq, hip
     if (max_items <= 0) return hipSuccess;
     const dim3 grid((unsigned)max_items * a.Hkv);
     if (D == 128) {
-        if (with_dq) hipLaunchKernelGGL((bwd_kernel<128, true>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((bwd_kernel<128, false>), grid, dim3(256), 0, stream, a);
+        if (with_dq) hipLaunchKernelGGL((bwd_kernel<128, true>), grid, dim3(512), 0, stream, a);
+        else hipLaunchKernelGGL((bwd_kernel<128, false>), grid, dim3(512), 0, stream, a);
     } else {
-        if (with_dq) hipLaunchKernelGGL((bwd_kernel<64, true>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((bwd_kernel<64, false>), grid, dim3(256), 0, stream, a);
+        if (with_dq) hipLaunchKernelGGL((bwd_kernel<64, true>), grid, dim3(512), 0, stream, a);
+        else hipLaunchKernelGGL((bwd_kernel<64, false>), grid, dim3(512), 0, stream, a);
     }
     return hipGetLastError();
 }
