@@ -27,6 +27,10 @@ import workloads  # noqa: E402
 
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 HBM_PEAK_GBPS = 8000.0
+# HBM traffic of the backward main kernel, from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE runs, valid only for the sources it was measured on
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_kernel_packed_mha_traffic.json")
+KERNEL_SOURCES = ["bwd.hip", "device.hpp", "kernels.hpp"]
 
 
 def log(*a):
@@ -54,6 +58,43 @@ class HipEvents:
 
     def destroy(self, ev):
         self.lib.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def kernel_sources_sha256():
+    """Hash of the sources the backward main kernel is compiled from."""
+    import hashlib
+    hsh = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bit_causal_flash_amd", "csrc", name), "rb") as f:
+            hsh.update(f.read())
+    return hsh.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the backward main kernel on `workload`: the
+    counters' KiB per dispatch, each scaled by the factor a plain copy of
+    known size gives the same counter; None when no measurement exists for
+    the current sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    return int(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]))
+
+
+def copy_calibration(mib):
+    """A plain device copy of `mib` MiB, three times: the reference the
+    traffic counters are scaled by (read `mib`, write `mib` per copy)."""
+    import torch
+    src = torch.ones(mib * (1 << 18), dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": mib << 20, "copies": 3}), flush=True)
 
 
 def cpu_baseline(w, flop_target=3e11):
@@ -94,11 +135,16 @@ def main():
     ap.add_argument("--workload", default="packed_mha", choices=sorted(workloads.NAMED))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
+                    help="only run a plain device copy of MIB MiB (traffic counter reference)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
     from bit_causal_flash_amd import flamia as F
@@ -122,15 +168,17 @@ def main():
     dq = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
     dk = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
     dv = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
+    pq = F.make_problem(cu, T, Hq, Hkv, d, 0.0, F.FLAMIA_CAUSAL)
     pf = F.make_problem(cu, T, Hq, Hkv, d, 0.0, F.FLAMIA_CAUSAL)
     pb = F.make_problem(cu, T, Hq, Hkv, d, 0.0, F.FLAMIA_CAUSAL)
     wsf = torch.empty(F.flamia_attn_fwd_workspace_size(pf), **u8)
     wsb = torch.empty(F.flamia_attn_bwd_workspace_size(pb), **u8)
 
+    qargs = ((Hq, xq, qc, qe), (Hkv, xk, kc, ke), (Hkv, xv, vc, ve))
+
     def quant():
-        F.flamia_quantize_tokblock(pf, Hq, 0, xq, qc, qe)
-        F.flamia_quantize_tokblock(pf, Hkv, 0, xk, kc, ke)
-        F.flamia_quantize_tokblock(pf, Hkv, 0, xv, vc, ve)
+        for nh, x, c, e in qargs:
+            F.flamia_quantize_tokblock(pq, nh, 0, x, c, e)
 
     def fwd():
         F.flamia_attn_fwd(pf, qc, qe, kc, ke, vc, ve, o, lse, wsf)
@@ -178,6 +226,19 @@ def main():
         return hip.elapsed_ms(t_start, t_stop) / reps
 
     ms_quant = timed(quant, K)
+
+    # quantizer kernels alone: events recorded by the library around each
+    # kernel, with a forward queued ahead so the GPU never waits on a launch
+    evq = [[(hip.create(), hip.create()) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        fwd()
+        for j, (nh, x, c, e) in enumerate(qargs):
+            F.set_events(pq, *evq[i][j])
+            F.flamia_quantize_tokblock(pq, nh, 0, x, c, e)
+    torch.cuda.synchronize()
+    F.set_events(pq, None, None)
+    ms_qkern = sum(hip.elapsed_ms(a, b) for ev in evq for a, b in ev) / K
     ms_attn = timed(lambda: (fwd(), bwd()), K)
     pdet = F.make_problem(cu, T, Hq, Hkv, d, 0.0, F.FLAMIA_CAUSAL | F.FLAMIA_DETERMINISTIC)
     wsd = torch.empty(F.flamia_attn_bwd_workspace_size(pdet), **u8)
@@ -220,10 +281,13 @@ def main():
             "attn_fwd_bwd_ms": round(ms_attn, 4),
             "attn_fwd_bwd_tflops": round(flop / (ms_attn * 1e-3) / 1e12, 2),
             "bwd_call_deterministic_ms": round(ms_bwd_det, 4),
-            "quantize_qkv_ms": round(ms_quant, 4),
-            "quantize_qkv_gbps": round(qbytes / (ms_quant * 1e-3) / 1e9, 1),
+            "quantize_qkv_call_ms": round(ms_quant, 4),
+            "quantize_qkv_kernel_ms": round(ms_qkern, 4),
+            "quantize_kernel_gbps": round(qbytes / (ms_qkern * 1e-3) / 1e9, 1),
+            "quantize_kernel_frac_hbm_peak": round(qbytes / (ms_qkern * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         },
     }
+    out["roofline"]["traffic"] = measured_traffic(w.name)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")
         out["cpu_baseline"] = cpu_baseline(w)

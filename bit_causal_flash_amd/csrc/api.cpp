@@ -197,7 +197,10 @@ flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_head
     a.x = x;
     a.codes = codes;
     a.exps = exps;
-    return hip_status(launch_quant(a, p->head_dim, false, (hipStream_t)stream));
+    hipStream_t s = (hipStream_t)stream;
+    if (record(p, true, s) != hipSuccess) return FLAMIA_ERR_HIP;
+    if (launch_quant(a, p->head_dim, false, s) != hipSuccess) return FLAMIA_ERR_HIP;
+    return hip_status(record(p, false, s));
 }
 
 size_t flamia_attn_fwd_workspace_size(const flamia_problem* p)

@@ -119,13 +119,17 @@ __device__ __forceinline__ void dq_tile_atomics(const v16f& acc, _Float16* tile,
     }
 }
 
-// Workgroup of 8 waves: wave w serves the keys 32 (w % 4) .. + 31 of the
-// 128-key tile and the query half w / 4 of each 64-query tile.  It computes
-// S and dP of its 32 x 32 block (which is exactly one dS scale block) and
-// shares its P^ and dS^ codes with the other half through key-major LDS
-// tiles; then both waves of a key group contract all 64 queries, each for
-// half of the head dim of dV and dK.  Per wave this keeps 32 keys x d / 2
-// of each accumulator, so two waves fit on every SIMD.
+// Workgroup of 8 waves in two roles, pipelined by one query tile.  Score
+// waves (0-3) own the keys 32 w .. + 31 of the 128-key tile: for tile j they
+// compute S and dP (32 keys x 64 queries), P, dS, the two 32 x 32 dS block
+// exponents, and write P^ and dS^ key-major to LDS.  Gradient waves (4-7)
+// own the same keys and, for tile j - 1, contract those P^ / dS^ rows with
+// the staged dO and Q codes into dV and dK (all of the head dim, in
+// registers) and compute their share of the tile's dQ.  The two waves that
+// share a SIMD thus interleave an exponential-heavy and an MFMA-heavy
+// instruction stream, and one barrier per tile suffices: Q / dO tiles are
+// triple-buffered (staging j + 1, scores j, gradients j - 1) and P^ / dS^
+// double-buffered.
 template <int D, bool WITH_DQ>
 __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
 {
@@ -133,21 +137,21 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
     constexpr int SPITCH = 64 + 16; // P^ / dS^ tiles, key-major: [128 keys][64 queries]
     constexpr int NKS = D / 64;
     constexpr int NDT = D / 32;
-    constexpr int NDH = NDT / 2;    // head-dim tiles of dV / dK per wave
     constexpr int CPR = D / 16;
     __shared__ __attribute__((aligned(16))) uint8_t s_kt[128 * PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t s_q[2][64 * PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t s_do[2][64 * PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t s_p[128 * SPITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t s_ds[128 * SPITCH];
-    __shared__ int s_eq[2][64], s_edo[2][64], s_kq[2][64];
-    __shared__ __attribute__((aligned(16))) float s_nlse[2][64];
-    __shared__ __attribute__((aligned(16))) float s_delta[2][64];
-    __shared__ int s_dsexp[2][4];   // [query half][key group]
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[3][64 * PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_do[3][64 * PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_p[2][128 * SPITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ds[2][128 * SPITCH];
+    __shared__ int s_eq[3][64], s_edo[3][64], s_kq[3][64];
+    __shared__ __attribute__((aligned(16))) float s_nlse[3][64];
+    __shared__ __attribute__((aligned(16))) float s_delta[3][64];
+    __shared__ int s_dsexp[2][2][4];   // [buffer][query half][key group]
     __shared__ int s_ekb[4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
-    const int kg = wave & 3, half = wave >> 2;
+    const int kg = wave & 3;
+    const bool scorer = wave < 4;
     const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
     const size_t T = (size_t)a.T;
     const int item = blockIdx.x / Hkv, hk = blockIdx.x % Hkv;
@@ -160,6 +164,7 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
     const bool kvalid = kj < e;
     const bool wave_keys = kw0 < e;
     const float c2 = a.c2;
+    const int krow = 32 * kg + (lane & 31);  // this lane's key in the key-major tiles
 
     // the workgroup's K tile, token-major, for the dQ MFMA (k = keys)
     for (int c = tid; c < 128 * CPR; c += 512) {
@@ -171,38 +176,12 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
     }
     if (tid < 4) s_ekb[tid] = (k0 + 32 * tid < e) ? (int)a.k_exps[(size_t)hk * T + k0 + 32 * tid] : 127;
 
-    // this wave's K and V rows: B operands of S = Q K^T and dP = dO V^T
-    v8i kf[NKS], vf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        if (kvalid) {
-            kf[ks] = row_operand(a.k_codes + ((size_t)kj * Hkv + hk) * D + 64 * ks, lane);
-            vf[ks] = row_operand(a.v_codes + ((size_t)kj * Hkv + hk) * D + 64 * ks, lane);
-        } else {
-            kf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-            vf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-    }
-    const int ek = kvalid ? (int)a.k_exps[(size_t)hk * T + kj] : 127;
-    const int ev = kvalid ? (int)a.v_exps[(size_t)hk * T + kj] : 127;
-
-    // dK^T, dV^T of the wave's keys over head-dim tiles NDH half .. + NDH - 1
-    v16f dk[NDH], dv[NDH];
-#pragma unroll
-    for (int i = 0; i < NDH; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) dk[i][v] = dv[i][v] = 0.f;
-
     // iterations: q heads of the group (outer) x 64-query tiles that see the keys
     const int qt_lo = a.causal ? 2 * kt : 0;
     const int nqt = (e - s + 63) / 64 - qt_lo;
     const int niter = G * nqt;
-
-    // dQ atomics: per-lane byte offset inside a 32 x 32 tile (row 4 g + odd,
-    // column pair lane & 30) and the byte selector that assembles the pair
-    const bool odd = lane & 1;
-    const uint32_t dq_sel = odd ? 0x03020706u : 0x05040100u;
-    const size_t dq_rs = (size_t)Hq * D;
+    auto tile_head = [&](int j) { return hk * G + j / nqt; };
+    auto tile_base = [&](int j) { return s + 64 * (qt_lo + j % nqt); };
 
     // every thread writes (the waves write identical statistics), so that
     // every prefetched register is consumed on every path
@@ -224,155 +203,197 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
         s_nlse[buf][row] = r.ok ? 8.f - r.lse * kLog2e : -INFINITY;
         s_delta[buf][row] = r.ok ? r.delta : 0.f;
     };
-
+    // prefetch of tile j + 1 (clamped: the last tiles reload the final one,
+    // into a buffer nobody reads) and its staging; unconditional, so the only
+    // wait on these loads is at staging
     QTile<D> nxt;
-    load_qtile<D>(a, nxt, hk * G, s + 64 * qt_lo, e, tid);
+    auto prefetch = [&](int j) {
+        const int j1 = min(j + 1, niter - 1);
+        load_qtile<D>(a, nxt, tile_head(j1), tile_base(j1), e, tid);
+    };
+
+    load_qtile<D>(a, nxt, tile_head(0), tile_base(0), e, tid);
     stage(nxt, 0);
     // every load issued so far has landed (vmcnt(0)), so that inside the loop
     // only the prefetch of the next tile is outstanding
     __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
 
-    const int krow = 32 * kg + (lane & 31);  // this lane's key in the key-major tiles
-    for (int it = 0; it < niter; ++it) {
-        const int cur = it & 1;
-        const int h = hk * G + it / nqt;
-        const int qb = s + 64 * (qt_lo + it % nqt);
-        // prefetch the next tile (the last iteration reloads its own, unused):
-        // unconditional, so the only wait on these loads is at staging
-        {
-            const int it1 = min(it + 1, niter - 1);
-            const int h1 = hk * G + it1 / nqt;
-            const int qb1 = s + 64 * (qt_lo + it1 % nqt);
-            load_qtile<D>(a, nxt, h1, qb1, e, tid);
-        }
-        const uint8_t* sq = s_q[cur];
-        const uint8_t* sg = s_do[cur];
-
-        // this wave's 32 x 32 block: queries 32 half .. + 31 of the tile
-        const bool active = wave_keys && (!a.causal || qb + 32 * half + 31 >= kw0);
-        v4i pf = {0, 0, 0, 0}, df = {0, 0, 0, 0};
-        int dse = 127;
-        if (active) {
-            v16f sacc, pacc;
-            const int qr = perm_row(half, lane & 31);
+    if (scorer) {
+        // this wave's K and V rows: B operands of S = Q K^T and dP = dO V^T
+        v8i kf[NKS], vf[NKS];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                sacc = mfma_f8(row_operand(sq + qr * PITCH + 64 * ks, lane), kf[ks], sacc,
-                               s_eq[cur][qr], ek);
-                pacc = mfma_f8(row_operand(sg + qr * PITCH + 64 * ks, lane), vf[ks], pacc,
-                               s_edo[cur][qr], ev);
-            }
-            // Masking is needed only where some key is invalid or, causally,
-            // some query precedes some key; queries past the document end have
-            // 256 P = exp2(-inf) = 0 and D = 0.  Element v of lane group g is
-            // query qb + 32 half + 16 g + v.
-            const float* nl = &s_nlse[cur][32 * half + 16 * g];
-            const float* dl = &s_delta[cur][32 * half + 16 * g];
-            const bool full = kw0 + 32 <= e && (!a.causal || qb + 32 * half >= kw0 + 31);
-            float amax;
-            if (full) {
-                amax = softmax_grad<false>(sacc, pacc, nl, dl, c2, 0);
+        for (int ks = 0; ks < NKS; ++ks) {
+            if (kvalid) {
+                kf[ks] = row_operand(a.k_codes + ((size_t)kj * Hkv + hk) * D + 64 * ks, lane);
+                vf[ks] = row_operand(a.v_codes + ((size_t)kj * Hkv + hk) * D + 64 * ks, lane);
             } else {
-                const int lim = a.causal ? kj - qb - 32 * half - 16 * g : (kvalid ? -1 : 16);
-                amax = softmax_grad<true>(sacc, pacc, nl, dl, c2, lim);
-            }
-            // block exponent of dS = 2^-8 (256 dS); the scaling is exact
-            const int et = ceil_exp448(wave_max_nonneg(amax) * 0.00390625f);
-            dse = et + 127;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                pf[q] = (int)cvt4_fp8(sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]);
-                df[q] = (int)cvt4_fp8(ldexpf(pacc[4 * q], -et - 8), ldexpf(pacc[4 * q + 1], -et - 8),
-                                      ldexpf(pacc[4 * q + 2], -et - 8),
-                                      ldexpf(pacc[4 * q + 3], -et - 8));
+                kf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                vf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
             }
         }
-        // P^ and dS^ to LDS, key-major (row = this lane's key, 16 bytes at the
-        // wave's query half and lane group)
-        *(v4i*)(s_p + krow * SPITCH + 32 * half + 16 * g) = pf;
-        *(v4i*)(s_ds + krow * SPITCH + 32 * half + 16 * g) = df;
-        if (lane == 0) s_dsexp[half][kg] = dse;
-        // Stage the prefetched tile into the other buffer now, ahead of this
-        // tile's dQ atomics: the wait on its loads then also covers only the
-        // previous tile's atomics, which have had a whole tile to complete.
-        stage(nxt, cur ^ 1);
-        lds_barrier();
+        const int ek = kvalid ? (int)a.k_exps[(size_t)hk * T + kj] : 127;
+        const int ev = kvalid ? (int)a.v_exps[(size_t)hk * T + kj] : 127;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
 
-        // dV^T += dO^T P^ and dK^T += Q^T dS^ over all 64 queries (k), for
-        // this wave's half of the head dim; the B operands are the key group's
-        // P^ / dS^ rows in the k layout (bytes 0-15 query half 0, 16-31 half 1)
-        if (wave_keys && (!a.causal || qb + 63 >= kw0)) {
-            const v4i p0 = *(const v4i*)(s_p + krow * SPITCH + 16 * g);
-            const v4i p1 = *(const v4i*)(s_p + krow * SPITCH + 32 + 16 * g);
-            const v4i d0 = *(const v4i*)(s_ds + krow * SPITCH + 16 * g);
-            const v4i d1 = *(const v4i*)(s_ds + krow * SPITCH + 32 + 16 * g);
-            const v8i pfull = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-            const v8i dfull = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-            const int sdo = s_edo[cur][32 * g];
-            const int sqe = s_eq[cur][32 * g];
-            const int dsg = s_dsexp[g][kg];
+        for (int j = 0; j <= niter; ++j) {
+            prefetch(j);
+            if (j < niter) {
+                const int c3 = j % 3, pb = j & 1;
+                const int qb = tile_base(j);
+                const uint8_t* sq = s_q[c3];
+                const uint8_t* sg = s_do[c3];
 #pragma unroll
-            for (int i = 0; i < NDH; ++i) {
-                const int dt = NDH * half + i;
-                dv[i] = mfma_f8(lds_tr_operand(sg, PITCH, 0, 32 * dt, lane), pfull, dv[i], sdo,
-                                kScaleMinus8);
-                dk[i] = mfma_f8(lds_tr_operand(sq, PITCH, 0, 32 * dt, lane), dfull, dk[i], sqe, dsg);
+                for (int t = 0; t < 2; ++t) {
+                    // the 32 x 32 block of queries 32 t .. + 31 of the tile
+                    const bool active = wave_keys && (!a.causal || qb + 32 * t + 31 >= kw0);
+                    v4i pf = {0, 0, 0, 0}, df = {0, 0, 0, 0};
+                    int dse = 127;
+                    if (active) {
+                        v16f sacc, pacc;
+                        const int qr = perm_row(t, lane & 31);
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = 0.f;
+#pragma unroll
+                        for (int ks = 0; ks < NKS; ++ks) {
+                            sacc = mfma_f8(row_operand(sq + qr * PITCH + 64 * ks, lane), kf[ks], sacc,
+                                           s_eq[c3][qr], ek);
+                            pacc = mfma_f8(row_operand(sg + qr * PITCH + 64 * ks, lane), vf[ks], pacc,
+                                           s_edo[c3][qr], ev);
+                        }
+                        // Masking is needed only where some key is invalid or,
+                        // causally, some query precedes some key; queries past
+                        // the document end have 256 P = exp2(-inf) = 0 and
+                        // D = 0.  Element v of lane group g is query
+                        // qb + 32 t + 16 g + v.
+                        const float* nl = &s_nlse[c3][32 * t + 16 * g];
+                        const float* dl = &s_delta[c3][32 * t + 16 * g];
+                        const bool full = kw0 + 32 <= e && (!a.causal || qb + 32 * t >= kw0 + 31);
+                        float amax;
+                        if (full) {
+                            amax = softmax_grad<false>(sacc, pacc, nl, dl, c2, 0);
+                        } else {
+                            const int lim = a.causal ? kj - qb - 32 * t - 16 * g : (kvalid ? -1 : 16);
+                            amax = softmax_grad<true>(sacc, pacc, nl, dl, c2, lim);
+                        }
+                        // block exponent of dS = 2^-8 (256 dS); the scaling is exact
+                        const int et = ceil_exp448(wave_max_nonneg(amax) * 0.00390625f);
+                        dse = et + 127;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            pf[q] = (int)cvt4_fp8(sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2],
+                                                  sacc[4 * q + 3]);
+                            df[q] = (int)cvt4_fp8(
+                                ldexpf(pacc[4 * q], -et - 8), ldexpf(pacc[4 * q + 1], -et - 8),
+                                ldexpf(pacc[4 * q + 2], -et - 8), ldexpf(pacc[4 * q + 3], -et - 8));
+                        }
+                    }
+                    // key-major rows: 16 bytes at the block's queries and lane group
+                    *(v4i*)(s_p[pb] + krow * SPITCH + 32 * t + 16 * g) = pf;
+                    *(v4i*)(s_ds[pb] + krow * SPITCH + 32 * t + 16 * g) = df;
+                    if (lane == 0) s_dsexp[pb][t][kg] = dse;
+                }
             }
+            stage(nxt, (j + 1) % 3);
+            lds_barrier();
+        }
+    } else {
+        // dK^T, dV^T of the wave's keys over the whole head dim
+        v16f dk[NDT], dv[NDT];
+#pragma unroll
+        for (int i = 0; i < NDT; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dk[i][v] = dv[i][v] = 0.f;
+
+        // dQ atomics: per-lane byte offset inside a 32 x 32 tile (row 4 g +
+        // odd, column pair lane & 30) and the byte selector that assembles
+        // the pair
+        const bool odd = lane & 1;
+        const uint32_t dq_sel = odd ? 0x03020706u : 0x05040100u;
+        const size_t dq_rs = (size_t)Hq * D;
+
+        for (int j = 0; j <= niter; ++j) {
+            prefetch(j);
+            if (j >= 1) {
+                const int jp = j - 1;
+                const int c3 = jp % 3, pb = jp & 1;
+                const int qb = tile_base(jp), h = tile_head(jp);
+                const uint8_t* sq = s_q[c3];
+                const uint8_t* sg = s_do[c3];
+                // dV^T += dO^T P^ and dK^T += Q^T dS^ over the tile's 64
+                // queries (k); the B operands are the key's P^ / dS^ rows in
+                // the k layout (bytes 0-15 query half 0, 16-31 half 1)
+                if (wave_keys && (!a.causal || qb + 63 >= kw0)) {
+                    const v4i p0 = *(const v4i*)(s_p[pb] + krow * SPITCH + 16 * g);
+                    const v4i p1 = *(const v4i*)(s_p[pb] + krow * SPITCH + 32 + 16 * g);
+                    const v4i d0 = *(const v4i*)(s_ds[pb] + krow * SPITCH + 16 * g);
+                    const v4i d1 = *(const v4i*)(s_ds[pb] + krow * SPITCH + 32 + 16 * g);
+                    const v8i pfull = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+                    const v8i dfull = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                    const int sdo = s_edo[c3][32 * g];
+                    const int sqe = s_eq[c3][32 * g];
+                    const int dsg = s_dsexp[pb][g][kg];
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        dv[dt] = mfma_f8(lds_tr_operand(sg, PITCH, 0, 32 * dt, lane), pfull, dv[dt],
+                                         sdo, kScaleMinus8);
+                        dk[dt] = mfma_f8(lds_tr_operand(sq, PITCH, 0, 32 * dt, lane), dfull, dk[dt],
+                                         sqe, dsg);
+                    }
+                }
+
+                if constexpr (WITH_DQ) {
+                    // dQ = dS^ K^ over the tile's 128 keys, 32 x 32 output
+                    // tiles (rows = queries, columns = head dim).  The row's
+                    // prescale 2^(k_i + f) (2^f <= softmax scale < 2^(f + 1))
+                    // rides in the A operand's block scale; the finalize
+                    // applies the remaining scale 2^-(k_i + f).
+                    for (int jt = kg; jt < 2 * NDT; jt += 4) {
+                        const int dt = jt % NDT, ct = jt / NDT;
+                        const int nrows = e - (qb + 32 * ct);
+                        if (nrows <= 0) continue;
+                        const int kq = s_kq[c3][32 * ct + (lane & 31)];
+                        v16f acc;
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+                        acc = mfma_f8(lds_tr_operand(s_ds[pb], SPITCH, 0, 32 * ct, lane),
+                                      lds_tr_operand(s_kt, PITCH, 0, 32 * dt, lane), acc,
+                                      min(max(s_dsexp[pb][ct][g] + kq, 0), 254), s_ekb[g]);
+                        if (k0 + 64 < e)
+                            acc = mfma_f8(lds_tr_operand(s_ds[pb] + 64 * SPITCH, SPITCH, 0, 32 * ct, lane),
+                                          lds_tr_operand(s_kt + 64 * PITCH, PITCH, 0, 32 * dt, lane),
+                                          acc, min(max(s_dsexp[pb][ct][2 + g] + kq, 0), 254),
+                                          s_ekb[2 + g]);
+                        _Float16* tile = a.dq_acc + ((size_t)(qb + 32 * ct) * Hq + h) * D + 32 * dt;
+                        const int row0 = 4 * g + (odd ? 1 : 0);
+                        const uint32_t lane_off = (uint32_t)(((size_t)row0 * dq_rs + (lane & 30)) * 2);
+                        if (nrows >= 32)
+                            dq_tile_atomics<false>(acc, tile, dq_rs, lane_off, dq_sel, row0, nrows);
+                        else
+                            dq_tile_atomics<true>(acc, tile, dq_rs, lane_off, dq_sel, row0, nrows);
+                    }
+                }
+            }
+            stage(nxt, (j + 1) % 3);
+            lds_barrier();
         }
 
-        if constexpr (WITH_DQ) {
-        // dQ = dS^ K^ over the tile's 128 keys, 32 x 32 output tiles (rows =
-        // queries, columns = head dim), one per wave.  The row's prescale
-        // 2^(k_i + f) (2^f <= softmax scale < 2^(f + 1)) rides in the A
-        // operand's block scale; the finalize applies the remaining scale
-        // 2^-(k_i + f).
-        for (int j = wave; j < 2 * NDT; j += 8) {
-            const int dt = j % NDT, ct = j / NDT;
-            const int nrows = e - (qb + 32 * ct);
-            if (nrows <= 0) continue;
-            const int kq = s_kq[cur][32 * ct + (lane & 31)];
-            v16f acc;
+        if (kvalid) {
+            uint16_t* krp = a.dk + ((size_t)kj * Hkv + hk) * D;
+            uint16_t* vrp = a.dv + ((size_t)kj * Hkv + hk) * D;
+            const float sc = a.scale;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-            acc = mfma_f8(lds_tr_operand(s_ds, SPITCH, 0, 32 * ct, lane),
-                          lds_tr_operand(s_kt, PITCH, 0, 32 * dt, lane), acc,
-                          min(max(s_dsexp[ct][g] + kq, 0), 254), s_ekb[g]);
-            if (k0 + 64 < e)
-                acc = mfma_f8(lds_tr_operand(s_ds + 64 * SPITCH, SPITCH, 0, 32 * ct, lane),
-                              lds_tr_operand(s_kt + 64 * PITCH, PITCH, 0, 32 * dt, lane), acc,
-                              min(max(s_dsexp[ct][2 + g] + kq, 0), 254), s_ekb[2 + g]);
-            _Float16* tile = a.dq_acc + ((size_t)(qb + 32 * ct) * Hq + h) * D + 32 * dt;
-            const int row0 = 4 * g + (odd ? 1 : 0);
-            const uint32_t lane_off = (uint32_t)(((size_t)row0 * dq_rs + (lane & 30)) * 2);
-            if (nrows >= 32)
-                dq_tile_atomics<false>(acc, tile, dq_rs, lane_off, dq_sel, row0, nrows);
-            else
-                dq_tile_atomics<true>(acc, tile, dq_rs, lane_off, dq_sel, row0, nrows);
-        }
-        }  // WITH_DQ
-        lds_barrier();
-    }
-
-    if (kvalid) {
-        uint16_t* krp = a.dk + ((size_t)kj * Hkv + hk) * D;
-        uint16_t* vrp = a.dv + ((size_t)kj * Hkv + hk) * D;
-        const float sc = a.scale;
+            for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int i = 0; i < NDH; ++i) {
-            const int dt = NDH * half + i;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                v2i wk, wv;
-                wk.x = (int)pack_bf16x2(dk[i][4 * q] * sc, dk[i][4 * q + 1] * sc);
-                wk.y = (int)pack_bf16x2(dk[i][4 * q + 2] * sc, dk[i][4 * q + 3] * sc);
-                wv.x = (int)pack_bf16x2(dv[i][4 * q], dv[i][4 * q + 1]);
-                wv.y = (int)pack_bf16x2(dv[i][4 * q + 2], dv[i][4 * q + 3]);
-                *(v2i*)(krp + 32 * dt + 8 * q + 4 * g) = wk;
-                *(v2i*)(vrp + 32 * dt + 8 * q + 4 * g) = wv;
-            }
+                for (int q = 0; q < 4; ++q) {
+                    v2i wk, wv;
+                    wk.x = (int)pack_bf16x2(dk[dt][4 * q] * sc, dk[dt][4 * q + 1] * sc);
+                    wk.y = (int)pack_bf16x2(dk[dt][4 * q + 2] * sc, dk[dt][4 * q + 3] * sc);
+                    wv.x = (int)pack_bf16x2(dv[dt][4 * q], dv[dt][4 * q + 1]);
+                    wv.y = (int)pack_bf16x2(dv[dt][4 * q + 2], dv[dt][4 * q + 3]);
+                    *(v2i*)(krp + 32 * dt + 8 * q + 4 * g) = wk;
+                    *(v2i*)(vrp + 32 * dt + 8 * q + 4 * g) = wv;
+                }
         }
     }
 }

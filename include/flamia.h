@@ -77,9 +77,10 @@ enum {
 };
 
 /* Optional timing hook: hipEvent_t handles the library records on the call's
- * stream immediately before and after the main attention kernel of
- * flamia_attn_fwd (the forward kernel) or flamia_attn_bwd (the backward main
- * kernel).  Either may be NULL.  The caller owns the events. */
+ * stream immediately before and after the quantizer kernel of
+ * flamia_quantize_tokblock, the forward kernel of flamia_attn_fwd or the
+ * backward main kernel of flamia_attn_bwd.  Either may be NULL.  The caller
+ * owns the events. */
 typedef struct {
     void* attn_start;
     void* attn_stop;
