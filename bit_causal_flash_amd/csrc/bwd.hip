@@ -34,30 +34,31 @@ namespace flamia {
 
 namespace {
 
-// One 64-query tile of one q head, as staged for the backward by the 512
-// threads of a workgroup: D / 64 16-byte chunks per thread of the Q and dO
-// code tiles (chunk c < 4 D of Q, the rest of dO) and the raw per-query
-// values of row tid % 64.  Every load is unconditional, with rows past the
-// document end clamped to its last row (their statistics are replaced at
-// staging, which makes their P, and so their dS, exactly zero), so that the
-// only wait on the prefetch is where it is staged.
-template <int D>
+// One 64-query tile of one q head, as staged for the backward by NT threads:
+// 8 D / NT 16-byte chunks per thread of the Q and dO code tiles (chunk
+// c < 4 D of Q, the rest of dO) and the raw per-query values of row tid % 64.
+// Every load is unconditional, with rows past the document end clamped to
+// its last row (their statistics are replaced at staging, which makes their
+// P, and so their dS, exactly zero), so that the only wait on the prefetch
+// is where it is staged.
+template <int D, int NT>
 struct QTile {
-    static constexpr int NC = D / 64;
+    static constexpr int NC = 8 * D / NT;
     v4i c[NC];
     int eq, edo, pre, ok;
     float lse, delta;
 };
 
-template <int D>
-__device__ __forceinline__ void load_qtile(const AttnArgs& a, QTile<D>& r, int h, int qb, int e, int tid)
+template <int D, int NT>
+__device__ __forceinline__ void load_qtile(const AttnArgs& a, QTile<D, NT>& r, int h, int qb, int e,
+                                           int tid)
 {
     constexpr int CPR = D / 16;
     const int Hq = a.Hq;
     const size_t T = (size_t)a.T;
 #pragma unroll
-    for (int k = 0; k < QTile<D>::NC; ++k) {
-        const int c = tid + 512 * k;
+    for (int k = 0; k < QTile<D, NT>::NC; ++k) {
+        const int c = tid + NT * k;
         const bool isq = c < 4 * D;
         const int cc = isq ? c : c - 4 * D;
         const int row = cc / CPR, col = 16 * (cc % CPR);
@@ -96,26 +97,45 @@ __device__ __forceinline__ float softmax_grad(v16f& sacc, v16f& pacc, const floa
     return amax;
 }
 
-// Adds one 32 x 32 dQ tile (accumulator of a 32x32x64 MFMA: lane = column,
-// VGPR v = row 8 (v / 4) + 4 g + v % 4) into the FP16 accumulator.  Neighbour
-// lanes exchange halves so that each lane adds two adjacent columns of one
-// row: the even lane of a pair takes the even rows of each VGPR pair, the odd
-// lane the odd rows.  `tile` is the tile's first element, `rs` the row
+// Adds a 32 x 64 dQ region, the accumulators acc0 / acc1 of two
+// horizontally adjacent 32x32x64 MFMA tiles (lane = column, VGPR v = row
+// 8 (v / 4) + 4 g + v % 4), into the FP16 accumulator so that every packed
+// atomic instruction covers two whole 128-byte rows.  v_permlane32_swap
+// first regroups the halves: its first result holds the lane-group-0 rows of
+// both tiles (lanes 0-31 the left tile, 32-63 the right one), the second the
+// group-1 rows, so lane l then holds column l of its rows.  Neighbour lanes
+// then exchange halves so that each lane adds two adjacent columns of one
+// row: the even lane of a pair takes the even row of each VGPR pair, the odd
+// lane the odd one.  `region` is the region's first element, `rs` the row
 // stride in elements; rows >= nrows are skipped.
 template <bool CHECK>
-__device__ __forceinline__ void dq_tile_atomics(const v16f& acc, _Float16* tile, size_t rs,
-                                                uint32_t lane_off, uint32_t sel, int row0, int nrows)
+__device__ __forceinline__ void dq_region_atomics(const v16f& acc0, const v16f& acc1,
+                                                  _Float16* region, size_t rs, int lane, int nrows)
 {
+    const bool odd = lane & 1;
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+    const uint32_t lane_off = (uint32_t)((((size_t)(odd ? 1 : 0)) * rs + (lane & 62)) * 2);
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int roff = 8 * (p / 2) + 2 * (p % 2);
-        const h2 mine = __builtin_convertvector(v2f{acc[2 * p], acc[2 * p + 1]}, h2);
-        const uint32_t w = __builtin_bit_cast(uint32_t, mine);
-        const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0xB1, 0xF, 0xF, false);
-        const uint32_t out = __builtin_amdgcn_perm(y, w, sel);
-        if (!CHECK || row0 + roff < nrows)
-            __builtin_amdgcn_global_atomic_fadd_v2f16(
-                (h2*)((char*)(tile + (size_t)roff * rs) + lane_off), __builtin_bit_cast(h2, out));
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int v = 2 * p;
+            const auto lo = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc0[v]),
+                                                             __float_as_uint(acc1[v]), false, false);
+            const auto hi = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc0[v + 1]),
+                                                             __float_as_uint(acc1[v + 1]), false,
+                                                             false);
+            const h2 mine = __builtin_convertvector(
+                v2f{__uint_as_float(lo[half]), __uint_as_float(hi[half])}, h2);
+            const uint32_t w = __builtin_bit_cast(uint32_t, mine);
+            const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0xB1, 0xF, 0xF, false);
+            const uint32_t out = __builtin_amdgcn_perm(y, w, sel);
+            // rows of VGPR pair (v, v + 1): 8 (p / 2) + 2 (p % 2) + 4 half + {0, 1}
+            const int roff = 8 * (p / 2) + 2 * (p % 2) + 4 * half;
+            if (!CHECK || roff + (odd ? 1 : 0) < nrows)
+                __builtin_amdgcn_global_atomic_fadd_v2f16(
+                    (h2*)((char*)(region + (size_t)roff * rs) + lane_off), __builtin_bit_cast(h2, out));
+        }
     }
 }
 
@@ -149,7 +169,7 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
     __shared__ int s_dsexp[2][2][4];   // [buffer][query half][key group]
     __shared__ int s_ekb[4];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5;
     const int kg = wave & 3;
     const bool scorer = wave < 4;
     const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
@@ -183,12 +203,16 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
     auto tile_head = [&](int j) { return hk * G + j / nqt; };
     auto tile_base = [&](int j) { return s + 64 * (qt_lo + j % nqt); };
 
-    // every thread writes (the waves write identical statistics), so that
-    // every prefetched register is consumed on every path
-    auto stage = [&](const QTile<D>& r, int buf) {
+    // The score waves (threads 0-255) fetch and stage the query tiles, so
+    // the gradient waves' dQ atomics never sit ahead of a load they must wait
+    // for.  Every staging thread writes (the waves write identical
+    // statistics), so that every prefetched register is consumed on every
+    // path.
+    using Tile = QTile<D, 256>;
+    auto stage = [&](const Tile& r, int buf) {
 #pragma unroll
-        for (int k = 0; k < QTile<D>::NC; ++k) {
-            const int c = tid + 512 * k;
+        for (int k = 0; k < Tile::NC; ++k) {
+            const int c = tid + 256 * k;
             const bool isq = c < 4 * D;
             const int cc = isq ? c : c - 4 * D;
             const int row = cc / CPR, col = 16 * (cc % CPR);
@@ -206,14 +230,16 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
     // prefetch of tile j + 1 (clamped: the last tiles reload the final one,
     // into a buffer nobody reads) and its staging; unconditional, so the only
     // wait on these loads is at staging
-    QTile<D> nxt;
+    Tile nxt;
     auto prefetch = [&](int j) {
         const int j1 = min(j + 1, niter - 1);
-        load_qtile<D>(a, nxt, tile_head(j1), tile_base(j1), e, tid);
+        load_qtile<D, 256>(a, nxt, tile_head(j1), tile_base(j1), e, tid);
     };
 
-    load_qtile<D>(a, nxt, tile_head(0), tile_base(0), e, tid);
-    stage(nxt, 0);
+    if (scorer) {
+        load_qtile<D, 256>(a, nxt, tile_head(0), tile_base(0), e, tid);
+        stage(nxt, 0);
+    }
     // every load issued so far has landed (vmcnt(0)), so that inside the loop
     // only the prefetch of the next tile is outstanding
     __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -243,24 +269,32 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                 const int qb = tile_base(j);
                 const uint8_t* sq = s_q[c3];
                 const uint8_t* sg = s_do[c3];
+                // the two 32 x 32 blocks (queries 32 t .. + 31 of the tile):
+                // all eight S / dP MFMAs first, then the element-wise work
+                bool active[2];
+                v16f sacc[2], pacc[2];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    // the 32 x 32 block of queries 32 t .. + 31 of the tile
-                    const bool active = wave_keys && (!a.causal || qb + 32 * t + 31 >= kw0);
-                    v4i pf = {0, 0, 0, 0}, df = {0, 0, 0, 0};
-                    int dse = 127;
-                    if (active) {
-                        v16f sacc, pacc;
-                        const int qr = perm_row(t, lane & 31);
+                    active[t] = wave_keys && (!a.causal || qb + 32 * t + 31 >= kw0);
 #pragma unroll
-                        for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = 0.f;
+                    for (int v = 0; v < 16; ++v) sacc[t][v] = pacc[t][v] = 0.f;
+                    if (active[t]) {
+                        const int qr = perm_row(t, lane & 31);
+                        const int eqr = s_eq[c3][qr], edr = s_edo[c3][qr];
 #pragma unroll
                         for (int ks = 0; ks < NKS; ++ks) {
-                            sacc = mfma_f8(row_operand(sq + qr * PITCH + 64 * ks, lane), kf[ks], sacc,
-                                           s_eq[c3][qr], ek);
-                            pacc = mfma_f8(row_operand(sg + qr * PITCH + 64 * ks, lane), vf[ks], pacc,
-                                           s_edo[c3][qr], ev);
+                            sacc[t] = mfma_f8(row_operand(sq + qr * PITCH + 64 * ks, lane), kf[ks],
+                                              sacc[t], eqr, ek);
+                            pacc[t] = mfma_f8(row_operand(sg + qr * PITCH + 64 * ks, lane), vf[ks],
+                                              pacc[t], edr, ev);
                         }
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    v4i pf = {0, 0, 0, 0}, df = {0, 0, 0, 0};
+                    int dse = 127;
+                    if (active[t]) {
                         // Masking is needed only where some key is invalid or,
                         // causally, some query precedes some key; queries past
                         // the document end have 256 P = exp2(-inf) = 0 and
@@ -271,21 +305,22 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                         const bool full = kw0 + 32 <= e && (!a.causal || qb + 32 * t >= kw0 + 31);
                         float amax;
                         if (full) {
-                            amax = softmax_grad<false>(sacc, pacc, nl, dl, c2, 0);
+                            amax = softmax_grad<false>(sacc[t], pacc[t], nl, dl, c2, 0);
                         } else {
                             const int lim = a.causal ? kj - qb - 32 * t - 16 * g : (kvalid ? -1 : 16);
-                            amax = softmax_grad<true>(sacc, pacc, nl, dl, c2, lim);
+                            amax = softmax_grad<true>(sacc[t], pacc[t], nl, dl, c2, lim);
                         }
                         // block exponent of dS = 2^-8 (256 dS); the scaling is exact
                         const int et = ceil_exp448(wave_max_nonneg(amax) * 0.00390625f);
                         dse = et + 127;
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            pf[q] = (int)cvt4_fp8(sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2],
-                                                  sacc[4 * q + 3]);
-                            df[q] = (int)cvt4_fp8(
-                                ldexpf(pacc[4 * q], -et - 8), ldexpf(pacc[4 * q + 1], -et - 8),
-                                ldexpf(pacc[4 * q + 2], -et - 8), ldexpf(pacc[4 * q + 3], -et - 8));
+                            pf[q] = (int)cvt4_fp8(sacc[t][4 * q], sacc[t][4 * q + 1],
+                                                  sacc[t][4 * q + 2], sacc[t][4 * q + 3]);
+                            df[q] = (int)cvt4_fp8(ldexpf(pacc[t][4 * q], -et - 8),
+                                                  ldexpf(pacc[t][4 * q + 1], -et - 8),
+                                                  ldexpf(pacc[t][4 * q + 2], -et - 8),
+                                                  ldexpf(pacc[t][4 * q + 3], -et - 8));
                         }
                     }
                     // key-major rows: 16 bytes at the block's queries and lane group
@@ -305,15 +340,9 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
 #pragma unroll
             for (int v = 0; v < 16; ++v) dk[i][v] = dv[i][v] = 0.f;
 
-        // dQ atomics: per-lane byte offset inside a 32 x 32 tile (row 4 g +
-        // odd, column pair lane & 30) and the byte selector that assembles
-        // the pair
-        const bool odd = lane & 1;
-        const uint32_t dq_sel = odd ? 0x03020706u : 0x05040100u;
-        const size_t dq_rs = (size_t)Hq * D;
+        const size_t dq_rs = (size_t)Hq * D;  // row stride of the dQ accumulator
 
         for (int j = 0; j <= niter; ++j) {
-            prefetch(j);
             if (j >= 1) {
                 const int jp = j - 1;
                 const int c3 = jp % 3, pb = jp & 1;
@@ -343,38 +372,44 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                 }
 
                 if constexpr (WITH_DQ) {
-                    // dQ = dS^ K^ over the tile's 128 keys, 32 x 32 output
-                    // tiles (rows = queries, columns = head dim).  The row's
-                    // prescale 2^(k_i + f) (2^f <= softmax scale < 2^(f + 1))
-                    // rides in the A operand's block scale; the finalize
-                    // applies the remaining scale 2^-(k_i + f).
-                    for (int jt = kg; jt < 2 * NDT; jt += 4) {
-                        const int dt = jt % NDT, ct = jt / NDT;
+                    // dQ = dS^ K^ over the tile's 128 keys: wave kg computes the
+                    // 32 x 64 region (query half ct, head-dim tiles dt0, dt0 + 1).
+                    // The row's prescale 2^(k_i + f) (2^f <= softmax scale <
+                    // 2^(f + 1)) rides in the A operand's block scale; the
+                    // finalize applies the remaining scale 2^-(k_i + f).
+                    if (kg < NDT) {
+                        const int ct = kg / (NDT / 2), dt0 = 2 * (kg % (NDT / 2));
                         const int nrows = e - (qb + 32 * ct);
-                        if (nrows <= 0) continue;
-                        const int kq = s_kq[c3][32 * ct + (lane & 31)];
-                        v16f acc;
+                        if (nrows > 0) {
+                            const int kq = s_kq[c3][32 * ct + (lane & 31)];
+                            const int sa0 = min(max(s_dsexp[pb][ct][g] + kq, 0), 254);
+                            const int sa1 = min(max(s_dsexp[pb][ct][2 + g] + kq, 0), 254);
+                            const v8i a0 = lds_tr_operand(s_ds[pb], SPITCH, 0, 32 * ct, lane);
+                            v16f acc[2];
 #pragma unroll
-                        for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-                        acc = mfma_f8(lds_tr_operand(s_ds[pb], SPITCH, 0, 32 * ct, lane),
-                                      lds_tr_operand(s_kt, PITCH, 0, 32 * dt, lane), acc,
-                                      min(max(s_dsexp[pb][ct][g] + kq, 0), 254), s_ekb[g]);
-                        if (k0 + 64 < e)
-                            acc = mfma_f8(lds_tr_operand(s_ds[pb] + 64 * SPITCH, SPITCH, 0, 32 * ct, lane),
-                                          lds_tr_operand(s_kt + 64 * PITCH, PITCH, 0, 32 * dt, lane),
-                                          acc, min(max(s_dsexp[pb][ct][2 + g] + kq, 0), 254),
-                                          s_ekb[2 + g]);
-                        _Float16* tile = a.dq_acc + ((size_t)(qb + 32 * ct) * Hq + h) * D + 32 * dt;
-                        const int row0 = 4 * g + (odd ? 1 : 0);
-                        const uint32_t lane_off = (uint32_t)(((size_t)row0 * dq_rs + (lane & 30)) * 2);
-                        if (nrows >= 32)
-                            dq_tile_atomics<false>(acc, tile, dq_rs, lane_off, dq_sel, row0, nrows);
-                        else
-                            dq_tile_atomics<true>(acc, tile, dq_rs, lane_off, dq_sel, row0, nrows);
+                            for (int i = 0; i < 2; ++i) {
+#pragma unroll
+                                for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+                                acc[i] = mfma_f8(a0, lds_tr_operand(s_kt, PITCH, 0, 32 * (dt0 + i), lane),
+                                                 acc[i], sa0, s_ekb[g]);
+                            }
+                            if (k0 + 64 < e) {
+                                const v8i a1 = lds_tr_operand(s_ds[pb] + 64 * SPITCH, SPITCH, 0, 32 * ct, lane);
+#pragma unroll
+                                for (int i = 0; i < 2; ++i)
+                                    acc[i] = mfma_f8(a1, lds_tr_operand(s_kt + 64 * PITCH, PITCH, 0,
+                                                                        32 * (dt0 + i), lane),
+                                                     acc[i], sa1, s_ekb[2 + g]);
+                            }
+                            _Float16* region = a.dq_acc + ((size_t)(qb + 32 * ct) * Hq + h) * D + 32 * dt0;
+                            if (nrows >= 32)
+                                dq_region_atomics<false>(acc[0], acc[1], region, dq_rs, lane, nrows);
+                            else
+                                dq_region_atomics<true>(acc[0], acc[1], region, dq_rs, lane, nrows);
+                        }
                     }
                 }
             }
-            stage(nxt, (j + 1) % 3);
             lds_barrier();
         }
 
@@ -453,7 +488,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(16))) uint8_t s_v[2][64 * PITCH];
     __shared__ int s_ek[2][64], s_ev[2][64];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5;
     const int Hq = a.Hq, Hkv = a.Hkv;
     const size_t T = (size_t)a.T;
     const int item = blockIdx.x / Hq, h = blockIdx.x % Hq;

@@ -220,6 +220,14 @@ __device__ __forceinline__ float wave_max_nonneg(float x)
     return __uint_as_float(wave_max_u32(__float_as_uint(x)));
 }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value: the compiler cannot prove threadIdx.x / 64 uniform by itself, and
+// everything derived from it would otherwise become per-lane branches.
+__device__ __forceinline__ int wave_id()
+{
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 __device__ __forceinline__ int doc_of(const int32_t* cu, int B, int t)
 {
     int lo = 0, hi = B - 1;

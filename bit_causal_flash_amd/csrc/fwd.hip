@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
     __shared__ int s_ek[2][64];
     __shared__ int s_ev[2][2];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5;
     const int Hq = a.Hq, Hkv = a.Hkv;
     const size_t T = (size_t)a.T;
     const int item = blockIdx.x / Hq, h = blockIdx.x % Hq;
