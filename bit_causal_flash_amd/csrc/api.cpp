@@ -180,8 +180,8 @@ flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_head
     st = check_head_dim(p->head_dim);
     if (st != FLAMIA_OK) return st;
     if (num_heads < 1) return FLAMIA_ERR_INVALID_ARG;
-    if (scale_mode == FLAMIA_SCALE_NVFP4_16) return FLAMIA_ERR_UNSUPPORTED;
-    if (scale_mode != FLAMIA_SCALE_TOKBLOCK32 && scale_mode != FLAMIA_SCALE_PER_TOKEN)
+    if (scale_mode != FLAMIA_SCALE_TOKBLOCK32 && scale_mode != FLAMIA_SCALE_PER_TOKEN &&
+        scale_mode != FLAMIA_SCALE_NVFP4_16)
         return FLAMIA_ERR_INVALID_ARG;
     if ((int64_t)(p->total_tokens + 31) / 32 * num_heads >= (int64_t)INT32_MAX * 64)
         return FLAMIA_ERR_UNSUPPORTED;
@@ -199,7 +199,9 @@ flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_head
     a.exps = exps;
     hipStream_t s = (hipStream_t)stream;
     if (record(p, true, s) != hipSuccess) return FLAMIA_ERR_HIP;
-    if (launch_quant(a, p->head_dim, false, s) != hipSuccess) return FLAMIA_ERR_HIP;
+    const hipError_t e = scale_mode == FLAMIA_SCALE_NVFP4_16 ? launch_nvfp4(a, p->head_dim, s)
+                                                             : launch_quant(a, p->head_dim, false, s);
+    if (e != hipSuccess) return FLAMIA_ERR_HIP;
     return hip_status(record(p, false, s));
 }
 

@@ -24,6 +24,8 @@ struct QuantArgs {
 };
 
 hipError_t launch_quant(const QuantArgs& a, int D, bool prep, hipStream_t stream);
+// E2M1 + E4M3-per-16 score view: codes [T][H][D/2], scales (in exps) [T][H][D/16]
+hipError_t launch_nvfp4(const QuantArgs& a, int D, hipStream_t stream);
 
 // Work list of (document, tile) items sorted by decreasing cost.
 struct WorklistArgs {

@@ -245,7 +245,86 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
     }
 }
 
+// E2M1 score view (FLAMIA review section 2: E2M1 values with an E4M3 scale
+// per 16 in-token features; jaehun.me section 3.1), without a tensor-level
+// scale.  One thread per group of 16 features of one (token, head): the
+// group scale is the smallest E4M3 value s with amax / s <= 6 (E2M1's largest
+// value, so nothing clips), s = 1 for a zero group; codes are the nearest
+// E2M1 values of x / s with ties to the even code, found by comparing |x|
+// with the lattice midpoints times s (exact FP32 products, no division).
+// Padding rows (t >= cu[B]) get zero codes and scale 1.
+__global__ __launch_bounds__(256) void nvfp4_kernel(QuantArgs a, int D)
+{
+    const size_t ng = (size_t)a.T * a.H * (D / 16);
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= ng) return;
+    const int t = (int)(i / ((size_t)a.H * (D / 16)));
+    const bool valid = t < a.cu[a.B];
+    float x[16];
+    if (valid) {
+        const v4i r0 = *(const v4i*)(a.x + 16 * i);
+        const v4i r1 = *(const v4i*)(a.x + 16 * i + 8);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[2 * k] = bf16_to_f32((uint16_t)(r0[k] & 0xffff));
+            x[2 * k + 1] = bf16_to_f32((uint16_t)((uint32_t)r0[k] >> 16));
+            x[8 + 2 * k] = bf16_to_f32((uint16_t)(r1[k] & 0xffff));
+            x[8 + 2 * k + 1] = bf16_to_f32((uint16_t)((uint32_t)r1[k] >> 16));
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) x[k] = 0.f;
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(x[k]));
+    // smallest E4M3 s with 6 s >= amax: start from the nearest code of
+    // amax / 6 and step (E4M3 codes 0..0x7E order like their values);
+    // 6 s is exact in FP32
+    int sc = 0x38;  // 1.0
+    if (amax > 0.f) {
+        sc = (int)(cvt2_fp8(fminf(amax * (1.f / 6.f), 448.f), 0.f) & 0x7f);
+        for (int it = 0; it < 2; ++it) {
+            const float sv = __builtin_amdgcn_cvt_f32_fp8(sc, 0);
+            if (6.f * sv < amax && sc < 0x7E) ++sc;
+        }
+        for (int it = 0; it < 2; ++it) {
+            if (sc <= 1) break;
+            const float pv = __builtin_amdgcn_cvt_f32_fp8(sc - 1, 0);
+            if (6.f * pv >= amax) --sc;
+        }
+    }
+    const float s = __builtin_amdgcn_cvt_f32_fp8(sc, 0);
+    // midpoints of {0, .5, 1, 1.5, 2, 3, 4, 6} times s; a tie goes to the
+    // even code, i.e. up from an odd code and down from an even one
+    const float m[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.f * s};
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const float ax = fabsf(x[k]);
+        int c = 0;
+#pragma unroll
+        for (int q = 0; q < 7; ++q) c += (ax > m[q] || (ax == m[q] && (q & 1))) ? 1 : 0;
+        const uint32_t code = (uint32_t)c | ((__float_as_uint(x[k]) >> 31) << 3);
+        if (k < 8) w0 |= code << (4 * k);
+        else w1 |= code << (4 * (k - 8));
+    }
+    v2i cw;
+    cw.x = (int)w0;
+    cw.y = (int)w1;
+    *(v2i*)(a.codes + 8 * i) = cw;
+    a.exps[i] = (uint8_t)sc;
+}
+
 }  // namespace
+
+hipError_t launch_nvfp4(const QuantArgs& a, int D, hipStream_t stream)
+{
+    const size_t ng = (size_t)a.T * a.H * (D / 16);
+    if (ng == 0) return hipSuccess;
+    hipLaunchKernelGGL(nvfp4_kernel, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, stream, a, D);
+    return hipGetLastError();
+}
 
 hipError_t launch_quant(const QuantArgs& a, int D, bool prep, hipStream_t stream)
 {

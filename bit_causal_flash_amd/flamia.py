@@ -198,6 +198,17 @@ def quantize(p, x, num_heads, scale_mode=FLAMIA_SCALE_TOKBLOCK32, stream=None):
     return codes, exps
 
 
+def quantize_nvfp4(p, x, num_heads, stream=None):
+    """x: bf16 [T][H][d] -> E2M1 score view (codes uint8 [T][H][d/2], E4M3
+    scales uint8 [T][H][d/16])."""
+    import torch
+    T, H, d = x.shape
+    codes = torch.empty((T, H, d // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((T, H, d // 16), dtype=torch.uint8, device=x.device)
+    flamia_quantize_tokblock(p, num_heads, FLAMIA_SCALE_NVFP4_16, x, codes, scales, stream)
+    return codes, scales
+
+
 def attn_fwd(p, q, k, v, stream=None):
     """q, k, v: (codes, exps) pairs.  Returns (o bf16 [T][Hq][d], lse [Hq][T])."""
     import torch

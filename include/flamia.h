@@ -72,8 +72,8 @@ enum {
     FLAMIA_SCALE_TOKBLOCK32 = 0, /* one exponent per document-local block of
                                     <= 32 tokens x full head dim */
     FLAMIA_SCALE_PER_TOKEN = 1,  /* one exponent per token x full head dim */
-    FLAMIA_SCALE_NVFP4_16 = 2    /* E2M1 + E4M3 per 16 features (not available
-                                    in this build) */
+    FLAMIA_SCALE_NVFP4_16 = 2    /* score view: E2M1 codes + an E4M3 scale per
+                                    16 in-token features */
 };
 
 /* Optional timing hook: hipEvent_t handles the library records on the call's
@@ -102,6 +102,14 @@ typedef struct {
 /*
  * Token-block quantizer (review section 3 "Why one shared exponent can serve
  * two reductions"; section 4 conservative exponent; jaehun.me section 3.1).
+ * With FLAMIA_SCALE_NVFP4_16 it instead writes the E2M1 score view of
+ * review section 2 / jaehun.me section 3.1 (no tensor-level scale): for each
+ * (token, head, group of 16 features), s = the smallest E4M3 value with
+ * amax / s <= 6 (s = 1 for a zero group), codes = nearest E2M1 value of x / s
+ * with ties to the even code (sign in bit 3);
+ *     codes [T][H][d / 2] (feature 2k in the low nibble of byte k),
+ *     exps  [T][H][d / 16] (the E4M3 scale bytes);
+ * padding rows get zero codes and scale 1.0 (0x38).
  * For each head and each document-local block of up to 32 consecutive tokens
  * (blocks start at every document start; the last may be partial), with amax
  * the block's largest |x| over all d features:

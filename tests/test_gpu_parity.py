@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_helpers import check_fwd, check_grad, dq_tiles, log, oracle_operands, run_gpu
+from tests.gpu_helpers import check_fwd, check_grad, dev, dq_tiles, host, log, oracle_operands, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -87,3 +87,28 @@ def test_quantizer_edge_values_bit_exact():
     g = run_gpu(w, backward=False)
     c, e = oracle.quantize(w.q, w.cu)
     assert np.array_equal(g["qc"], c) and np.array_equal(g["qe"], e)
+
+
+@pytest.mark.gpu
+def test_quantizer_nvfp4_bit_exact():
+    """E2M1 score view (E4M3 scale per 16 features): random groups, zero
+    groups, a group past the scale's range, bf16 subnormals, values on the
+    lattice midpoints (ties to the even code) and padding rows."""
+    from bit_causal_flash_amd import flamia as F
+    rng = np.random.default_rng(11)
+    T, H, d = 80, 3, 64
+    x = rng.standard_normal((T, H, d)).astype(np.float32)
+    x[0:4] = 0.0
+    x[5, 1, 3] = 3.0e38
+    x[6:9] *= np.float32(1e-39)
+    x[9, 0, :16] = np.array([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0,
+                             -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0, 0.0], np.float32)
+    x[10, 2, 16:32] = np.linspace(-7.0, 7.0, 16).astype(np.float32)
+    bits = workloads.f32_to_bf16_bits(x)
+    cu = np.array([0, 30, 71], np.int32)  # rows 71.. are padding
+    log("case nvfp4 T=%d H=%d d=%d" % (T, H, d))
+    p = F.make_problem(dev(cu), T, H, H, d, 0.0, F.FLAMIA_CAUSAL)
+    codes, scales = F.quantize_nvfp4(p, dev(bits.view(np.int16)), H)
+    rc, rs = oracle.quantize_nvfp4(bits, cu)
+    assert np.array_equal(host(codes), rc), "codes"
+    assert np.array_equal(host(scales), rs), "scales"
