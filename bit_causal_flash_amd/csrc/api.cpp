@@ -44,6 +44,22 @@ flamia_status check_head_dim(int32_t d)
     return FLAMIA_OK;
 }
 
+// The E2M1 score-view pointers are required with FLAMIA_FP4_SCORE and must
+// be NULL without it.
+flamia_status check_fp4_pointers(const flamia_problem* p, const void* q4, const void* q4s,
+                                 const void* k4, const void* k4s)
+{
+    if (p->flags & FLAMIA_FP4_SCORE)
+        return (q4 && q4s && k4 && k4s) ? FLAMIA_OK : FLAMIA_ERR_INVALID_ARG;
+    return (q4 || q4s || k4 || k4s) ? FLAMIA_ERR_INVALID_ARG : FLAMIA_OK;
+}
+
+int operand_mode(const flamia_problem* p)
+{
+    if (p->flags & FLAMIA_FP4_SCORE) return MODE_FP4;
+    return (p->flags & FLAMIA_EXACT) ? MODE_EXACT : MODE_BLOCK;
+}
+
 flamia_status check_attn(const flamia_problem* p, Dims* out)
 {
     flamia_status st = check_seq(p);
@@ -55,7 +71,6 @@ flamia_status check_attn(const flamia_problem* p, Dims* out)
     if (st != FLAMIA_OK) return st;
     if (p->flags & ~kKnownFlags) return FLAMIA_ERR_INVALID_ARG;
     if ((p->flags & FLAMIA_FP4_SCORE) && !(p->flags & FLAMIA_EXACT)) return FLAMIA_ERR_INVALID_ARG;
-    if (p->flags & (FLAMIA_EXACT | FLAMIA_FP4_SCORE)) return FLAMIA_ERR_UNSUPPORTED;
     if (std::isnan(p->softmax_scale) || std::isinf(p->softmax_scale)) return FLAMIA_ERR_INVALID_ARG;
     out->T = p->total_tokens;
     out->B = p->num_seqs;
@@ -223,7 +238,8 @@ flamia_status flamia_attn_fwd(const flamia_problem* p, const uint8_t* q_codes,
     Dims d;
     flamia_status st = check_attn(p, &d);
     if (st != FLAMIA_OK) return st;
-    if (q_fp4 || q_fp4_scales || k_fp4 || k_fp4_scales) return FLAMIA_ERR_INVALID_ARG;
+    st = check_fp4_pointers(p, q_fp4, q_fp4_scales, k_fp4, k_fp4_scales);
+    if (st != FLAMIA_OK) return st;
     if (d.T == 0) return FLAMIA_OK;
     if (!q_codes || !q_exps || !k_codes || !k_exps || !v_codes || !v_exps || !o || !lse)
         return FLAMIA_ERR_INVALID_ARG;
@@ -253,6 +269,11 @@ flamia_status flamia_attn_fwd(const flamia_problem* p, const uint8_t* q_codes,
     a.k_exps = k_exps;
     a.v_codes = v_codes;
     a.v_exps = v_exps;
+    a.mode = operand_mode(p);
+    a.q_fp4 = q_fp4;
+    a.q_fp4_scales = q_fp4_scales;
+    a.k_fp4 = k_fp4;
+    a.k_fp4_scales = k_fp4_scales;
     a.o = o;
     a.lse = lse;
     if (record(p, true, s) != hipSuccess) return FLAMIA_ERR_HIP;
@@ -292,7 +313,9 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     Dims d;
     flamia_status st = check_attn(p, &d);
     if (st != FLAMIA_OK) return st;
-    if (q_fp4 || q_fp4_scales || k_fp4 || k_fp4_scales) return FLAMIA_ERR_INVALID_ARG;
+    st = check_fp4_pointers(p, q_fp4, q_fp4_scales, k_fp4, k_fp4_scales);
+    if (st != FLAMIA_OK) return st;
+    if (p->flags & FLAMIA_EXACT) return FLAMIA_ERR_UNSUPPORTED;
     if (d.T == 0) return FLAMIA_OK;
     if (!q_codes || !q_exps || !k_codes || !k_exps || !v_codes || !v_exps || !o || !lse ||
         !dout || !dq || !dk || !dv)

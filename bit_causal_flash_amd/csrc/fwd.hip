@@ -31,32 +31,53 @@ namespace flamia {
 
 namespace {
 
-// One 64-key step of K and V codes (D / 64 16-byte chunks per thread of
-// each) and the raw exponents of key tid % 64 and of the V block of tid % 2.
-// Every load is unconditional, rows past the document end clamped to its last
-// row (staging replaces their exponents, and the masks zero their weights),
-// so that the only wait on the prefetch is where it is staged.
-template <int D>
+// One 64-key step of K and V, as staged for the forward: D / 64 16-byte
+// chunks per thread of the V codes and of the K codes (MODE_FP4: D / 8 bytes
+// of the row's E2M1 K codes and the D / 64 scale bytes they use), and the
+// raw exponents of key tid % 64 (K, and in the exact modes V) and of the V
+// block of tid % 2.  Every load is unconditional, rows past the document end
+// clamped to its last row (staging replaces their exponents, and the masks
+// zero their weights), so that the only wait on the prefetch is where it is
+// staged.
+template <int D, int MODE>
 struct KVTile {
     static constexpr int NC = D / 64;
     v4i k[NC], v[NC];
-    int ek, ev, kok, vok;
+    v4i k4;
+    uint32_t k4s;
+    int ek, ev, evk, kok, vok;
 };
 
-template <int D>
-__device__ __forceinline__ void load_kvtile(const AttnArgs& a, KVTile<D>& r, int hk, int kt0, int e,
-                                            int tid)
+template <int D, int MODE>
+__device__ __forceinline__ void load_kvtile(const AttnArgs& a, KVTile<D, MODE>& r, int hk, int kt0,
+                                            int e, int tid)
 {
     constexpr int CPR = D / 16;
     const int Hkv = a.Hkv;
     const size_t T = (size_t)a.T;
 #pragma unroll
-    for (int k = 0; k < KVTile<D>::NC; ++k) {
+    for (int k = 0; k < KVTile<D, MODE>::NC; ++k) {
         const int c = tid + 256 * k;
         const int row = c / CPR, col = 16 * (c % CPR);
         const int t = min(kt0 + row, e - 1);
-        r.k[k] = *(const v4i*)(a.k_codes + ((size_t)t * Hkv + hk) * D + col);
+        if constexpr (MODE != MODE_FP4)
+            r.k[k] = *(const v4i*)(a.k_codes + ((size_t)t * Hkv + hk) * D + col);
         r.v[k] = *(const v4i*)(a.v_codes + ((size_t)t * Hkv + hk) * D + col);
+    }
+    if constexpr (MODE == MODE_FP4) {
+        // thread -> key row tid / 4, features (tid % 4) D / 4 .. + D / 4 - 1
+        const int t = min(kt0 + (tid >> 2), e - 1);
+        const int part = tid & 3;
+        const uint8_t* src = a.k_fp4 + ((size_t)t * Hkv + hk) * (D / 2) + part * (D / 8);
+        const uint8_t* ssrc = a.k_fp4_scales + ((size_t)t * Hkv + hk) * (D / 16) + part * (D / 64);
+        if constexpr (D == 128) {
+            r.k4 = *(const v4i*)src;
+            r.k4s = (uint32_t)ssrc[0] | ((uint32_t)ssrc[1] << 8);
+        } else {
+            const v2i w = *(const v2i*)src;
+            r.k4 = v4i{w.x, w.y, 0, 0};
+            r.k4s = ssrc[0];
+        }
     }
     const int tk = kt0 + (tid & 63);
     const int tv = kt0 + 32 * (tid & 1);
@@ -64,16 +85,54 @@ __device__ __forceinline__ void load_kvtile(const AttnArgs& a, KVTile<D>& r, int
     r.vok = tv < e;
     r.ek = a.k_exps[(size_t)hk * T + min(tk, e - 1)];
     r.ev = a.v_exps[(size_t)hk * T + min(tv, e - 1)];
+    if constexpr (MODE != MODE_BLOCK) r.evk = a.v_exps[(size_t)hk * T + min(tk, e - 1)];
+}
+
+// Value of an E2M1 code (sign in bit 3): 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ float e2m1_value(uint32_t c)
+{
+    const uint32_t m = c & 7u;
+    const float mag = m < 2u ? 0.5f * (float)m
+                             : __uint_as_float((((m >> 1) + 126u) << 23) | ((m & 1u) << 22));
+    return (c & 8u) ? -mag : mag;
+}
+
+// Eight E2M1 codes (one per nibble, feature 2k in the low nibble of byte k)
+// times their E4M3 group scale, as FP16: exact, since the product has at most
+// six significant bits and lies in [2^-10, 2688].
+__device__ __forceinline__ h8 fp4x8_to_f16(uint32_t codes, float scale)
+{
+    h8 o;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] = (_Float16)(e2m1_value((codes >> (4 * k)) & 15u) * scale);
+    return o;
+}
+
+// Largest over each 32-lane half of the wave (unsigned), in every lane of it.
+__device__ __forceinline__ uint32_t half_wave_max_u32(uint32_t u)
+{
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x140, 0xF, 0xF, false));  // row_mirror
+    // v_permlane16_swap hands every lane, across its two results, the value
+    // of its own 16-lane row and of the neighbouring row in its half
+    const auto pr = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return max((uint32_t)pr[0], (uint32_t)pr[1]);
 }
 
 // Online-softmax update of one wave's 32 queries x 64 keys: the running
 // integer reference r, the rescale of O and l when it rises, and the
 // probability operand P^ (byte 16 t + v <-> key 32 t + 16 g + v) with its
 // rounded row sum.  Unless `full`, element (t, v) is kept only if
-// 32 t + v < lim.
-template <int NDT>
+// 32 t + v < lim.  With FOLD, the operand codes carry each key's V exponent
+// relative to its 32-key block, vf[32 t + v] = 2^(e_V(j) - max e_V): P^ is
+// rounded first (l sums the unshifted values), then shifted by that power of
+// two, which is exact while the shifted weight stays in E4M3's normal range.
+template <int NDT, bool FOLD>
 __device__ __forceinline__ void online_softmax(v16f (&sacc)[2], v16f (&oacc)[NDT], float& r,
-                                               float& l, v8i& pf, float c2, bool full, int lim)
+                                               float& l, v8i& pf, float c2, bool full, int lim,
+                                               const float* vf)
 {
     if (!full) {
 #pragma unroll
@@ -110,23 +169,37 @@ __device__ __forceinline__ void online_softmax(v16f (&sacc)[2], v16f (&oacc)[NDT
 #pragma unroll
             for (int k = 0; k < 4; ++k) p[k] = __builtin_amdgcn_exp2f(fmaf(sacc[t][4 * q + k], c2, off));
             const uint32_t w = cvt4_fp8(p[0], p[1], p[2], p[3]);
-            pf[4 * t + q] = (int)w;
             lsum += sum4_fp8(w);
+            if constexpr (FOLD) {
+                const v4i fv = *(const v4i*)(vf + 32 * t + 4 * q);
+                pf[4 * t + q] = (int)cvt4_fp8(p[0] * __int_as_float(fv.x), p[1] * __int_as_float(fv.y),
+                                              p[2] * __int_as_float(fv.z), p[3] * __int_as_float(fv.w));
+            } else {
+                pf[4 * t + q] = (int)w;
+            }
         }
     l += lsum * 0.00390625f;
 }
 
-template <int D>
+// Modes: MODE_BLOCK token-block operands; MODE_EXACT per-token exponents (the
+// V exponent folded into P^); MODE_FP4 the same with S from the E2M1 score
+// views of Q and K, expanded to exact FP16 and contracted by the FP16 MFMA.
+template <int D, int MODE>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
 {
-    constexpr int PITCH = D + 16;  // LDS row pitch (bytes): spreads rows over banks
-    constexpr int NKS = D / 64;    // k steps over the head dim
-    constexpr int NDT = D / 32;    // 32-wide head-dim tiles of O
-    constexpr int CPR = D / 16;    // 16-byte chunks per row
-    __shared__ __attribute__((aligned(16))) uint8_t s_k[2][64 * PITCH];
+    constexpr int PITCH = D + 16;      // LDS row pitch (bytes): spreads rows over banks
+    constexpr int PITCH16 = 2 * D + 16;
+    constexpr int NKS = D / 64;        // k steps over the head dim (E4M3 S)
+    constexpr int NKH = D / 16;        // k steps over the head dim (FP16 S)
+    constexpr int NDT = D / 32;        // 32-wide head-dim tiles of O
+    constexpr int CPR = D / 16;        // 16-byte chunks per row
+    constexpr bool FP4 = MODE == MODE_FP4;
+    constexpr bool FOLD = MODE != MODE_BLOCK;
+    __shared__ __attribute__((aligned(16))) uint8_t s_k[2][FP4 ? 64 * PITCH16 : 64 * PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t s_v[2][64 * PITCH];
     __shared__ int s_ek[2][64];
     __shared__ int s_ev[2][2];
+    __shared__ __attribute__((aligned(16))) float s_vf[2][FOLD ? 64 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5;
     const int Hq = a.Hq, Hkv = a.Hkv;
@@ -142,14 +215,28 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
     const bool qvalid = qi < e;
     const float c2 = a.c2;
 
-    // Q fragments: B operand of S^T = K Q^T (lane = query column, k = head dim)
-    v8i qf[NKS];
+    // Q fragments: B operand of S^T = K Q^T (lane = query column, k = head
+    // dim): E4M3 codes with the query's exponent, or the FP16 expansion of
+    // its E2M1 view (k = 16 per FP16 step: features 16 ks + 8 g .. + 7)
+    v8i qf[FP4 ? 1 : NKS];
+    h8 qh[FP4 ? NKH : 1];
+    int eq = 127;
+    if constexpr (FP4) {
+        const size_t row = (size_t)min(qi, e - 1) * Hq + h;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        if (qvalid) qf[ks] = row_operand(a.q_codes + ((size_t)qi * Hq + h) * D + 64 * ks, lane);
-        else qf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        for (int ks = 0; ks < NKH; ++ks) {
+            const uint32_t c = *(const uint32_t*)(a.q_fp4 + row * (D / 2) + 8 * ks + 4 * g);
+            const float sc = __builtin_amdgcn_cvt_f32_fp8((int)a.q_fp4_scales[row * (D / 16) + ks], 0);
+            qh[ks] = fp4x8_to_f16(c, sc);
+        }
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            if (qvalid) qf[ks] = row_operand(a.q_codes + ((size_t)qi * Hq + h) * D + 64 * ks, lane);
+            else qf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+        eq = qvalid ? (int)a.q_exps[(size_t)h * T + qi] : 127;
     }
-    const int eq = qvalid ? (int)a.q_exps[(size_t)h * T + qi] : 127;
 
     const int kend = a.causal ? min(q0 + 128, e) : e;
     const int nsteps = (kend - s + 63) / 64;
@@ -165,20 +252,38 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
 
     // every thread writes (the four waves write identical exponents), so
     // that every prefetched register is consumed on every path
-    auto stage = [&](const KVTile<D>& t, int buf) {
+    auto stage = [&](const KVTile<D, MODE>& t, int buf) {
 #pragma unroll
-        for (int k = 0; k < KVTile<D>::NC; ++k) {
+        for (int k = 0; k < KVTile<D, MODE>::NC; ++k) {
             const int c = tid + 256 * k;
             const int row = c / CPR, col = 16 * (c % CPR);
-            *(v4i*)(&s_k[buf][row * PITCH + col]) = t.k[k];
+            if constexpr (!FP4) *(v4i*)(&s_k[buf][row * PITCH + col]) = t.k[k];
             *(v4i*)(&s_v[buf][row * PITCH + col]) = t.v[k];
         }
+        if constexpr (FP4) {
+            // the row's features (tid % 4) D / 4 .. + D / 4 - 1 as FP16
+            uint8_t* dst = &s_k[buf][(tid >> 2) * PITCH16 + 2 * (tid & 3) * (D / 4)];
+#pragma unroll
+            for (int q = 0; q < D / 32; ++q) {
+                const float sc = __builtin_amdgcn_cvt_f32_fp8((int)((t.k4s >> (8 * (q / 2))) & 0xff), 0);
+                *(h8*)(dst + 16 * q) = fp4x8_to_f16((uint32_t)t.k4[q], sc);
+            }
+        }
         s_ek[buf][tid & 63] = t.kok ? t.ek : 127;
-        s_ev[buf][tid & 1] = t.vok ? t.ev : 127;
+        if constexpr (FOLD) {
+            // lane = key: the V block exponent is the largest over the
+            // block's valid keys, and the key's fold factor its offset
+            const uint32_t ek = t.kok ? (uint32_t)t.evk : 0u;
+            const uint32_t emax = half_wave_max_u32(ek);
+            s_ev[buf][(tid & 63) >> 5] = (int)emax;
+            s_vf[buf][tid & 63] = t.kok ? ldexpf(1.f, (int)ek - (int)emax) : 0.f;
+        } else {
+            s_ev[buf][tid & 1] = t.vok ? t.ev : 127;
+        }
     };
 
-    KVTile<D> nxt;
-    load_kvtile<D>(a, nxt, hk, s, e, tid);
+    KVTile<D, MODE> nxt;
+    load_kvtile<D, MODE>(a, nxt, hk, s, e, tid);
     stage(nxt, 0);
     // every load issued so far has landed (vmcnt(0)), so that inside the loop
     // only the prefetch of the next step is outstanding
@@ -189,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
         const int cur = st & 1;
         const int kt0 = s + 64 * st;
         // prefetch the next step (the last step reloads its own, unused)
-        load_kvtile<D>(a, nxt, hk, min(kt0 + 64, s + 64 * (nsteps - 1)), e, tid);
+        load_kvtile<D, MODE>(a, nxt, hk, min(kt0 + 64, s + 64 * (nsteps - 1)), e, tid);
         const uint8_t* sk = s_k[cur];
         const uint8_t* sv = s_v[cur];
 
@@ -199,13 +304,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int krow = perm_row(t, lane & 31);
-                const int ek = s_ek[cur][krow];
 #pragma unroll
                 for (int v = 0; v < 16; ++v) sacc[t][v] = 0.f;
+                if constexpr (FP4) {
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    sacc[t] = mfma_f8(row_operand(sk + krow * PITCH + 64 * ks, lane), qf[ks],
-                                      sacc[t], ek, eq);
+                    for (int ks = 0; ks < NKH; ++ks)
+                        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            *(const h8*)(sk + krow * PITCH16 + 2 * (16 * ks + 8 * g)), qh[ks], sacc[t],
+                            0, 0, 0);
+                } else {
+                    const int ek = s_ek[cur][krow];
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+                        sacc[t] = mfma_f8(row_operand(sk + krow * PITCH + 64 * ks, lane), qf[ks],
+                                          sacc[t], ek, eq);
+                }
             }
 
             // masking is needed only where the step runs past the document
@@ -214,7 +327,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
             v8i pf;
             const bool full = (kt0 + 64 <= e) && (!a.causal || kt0 + 63 <= qw);
             const int lim = min(e, a.causal ? qi + 1 : e) - kt0 - 16 * g;
-            online_softmax<NDT>(sacc, oacc, r, l, pf, c2, full, lim);
+            online_softmax<NDT, FOLD>(sacc, oacc, r, l, pf, c2, full, lim,
+                                      FOLD ? &s_vf[cur][16 * g] : nullptr);
 
             // O^T += V^T P^T: V^T read k-major from the token-major LDS tile
             const int sv_exp = s_ev[cur][g];
@@ -267,8 +381,17 @@ hipError_t launch_fwd(const AttnArgs& a, int D, int max_items, hipStream_t strea
 {
     if (max_items <= 0) return hipSuccess;
     const dim3 grid((unsigned)max_items * a.Hq);
-    if (D == 128) hipLaunchKernelGGL(fwd_kernel<128>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(fwd_kernel<64>, grid, dim3(256), 0, stream, a);
+#define FLAMIA_FWD(DD, MM) hipLaunchKernelGGL((fwd_kernel<DD, MM>), grid, dim3(256), 0, stream, a)
+    if (D == 128) {
+        if (a.mode == MODE_FP4) FLAMIA_FWD(128, MODE_FP4);
+        else if (a.mode == MODE_EXACT) FLAMIA_FWD(128, MODE_EXACT);
+        else FLAMIA_FWD(128, MODE_BLOCK);
+    } else {
+        if (a.mode == MODE_FP4) FLAMIA_FWD(64, MODE_FP4);
+        else if (a.mode == MODE_EXACT) FLAMIA_FWD(64, MODE_EXACT);
+        else FLAMIA_FWD(64, MODE_BLOCK);
+    }
+#undef FLAMIA_FWD
     return hipGetLastError();
 }
 

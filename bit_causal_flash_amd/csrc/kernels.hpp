@@ -41,8 +41,13 @@ struct WorklistArgs {
 
 hipError_t launch_worklist(const WorklistArgs& a, hipStream_t stream);
 
+// Operand modes of the attention kernels: token-block exponents; per-token
+// exponents; per-token exponents with S from the E2M1 score views.
+enum { MODE_BLOCK = 0, MODE_EXACT = 1, MODE_FP4 = 2 };
+
 struct AttnArgs {
     int T, B, Hq, Hkv, causal;
+    int mode;         // MODE_*
     float scale;      // softmax scale
     float c2;         // scale * log2(e)
     int scale_exp;    // f = floor(log2 scale)
@@ -51,6 +56,8 @@ struct AttnArgs {
     const int32_t* count;
     const int32_t* items;
     const uint8_t *q_codes, *q_exps, *k_codes, *k_exps, *v_codes, *v_exps;
+    // E2M1 score views (MODE_FP4): codes [T][H][D/2], E4M3 scales [T][H][D/16]
+    const uint8_t *q_fp4, *q_fp4_scales, *k_fp4, *k_fp4_scales;
     // forward
     uint16_t* o;
     float* lse;

@@ -209,19 +209,22 @@ def quantize_nvfp4(p, x, num_heads, stream=None):
     return codes, scales
 
 
-def attn_fwd(p, q, k, v, stream=None):
-    """q, k, v: (codes, exps) pairs.  Returns (o bf16 [T][Hq][d], lse [Hq][T])."""
+def attn_fwd(p, q, k, v, stream=None, fp4=None):
+    """q, k, v: (codes, exps) pairs; fp4: optional ((q codes, q scales),
+    (k codes, k scales)) E2M1 score views.  Returns (o bf16 [T][Hq][d],
+    lse [Hq][T])."""
     import torch
     dev = q[0].device
     T, Hq, d = q[0].shape
     o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
     ws = torch.empty(max(flamia_attn_fwd_workspace_size(p), 1), dtype=torch.uint8, device=dev)
-    flamia_attn_fwd(p, q[0], q[1], k[0], k[1], v[0], v[1], o, lse, ws, stream=stream)
+    f4 = None if fp4 is None else (fp4[0][0], fp4[0][1], fp4[1][0], fp4[1][1])
+    flamia_attn_fwd(p, q[0], q[1], k[0], k[1], v[0], v[1], o, lse, ws, fp4=f4, stream=stream)
     return o, lse
 
 
-def attn_bwd(p, q, k, v, o, lse, dout, stream=None, workspace=None):
+def attn_bwd(p, q, k, v, o, lse, dout, stream=None, workspace=None, fp4=None):
     """Returns (dq, dk, dv, workspace)."""
     import torch
     dev = q[0].device
@@ -233,6 +236,7 @@ def attn_bwd(p, q, k, v, o, lse, dout, stream=None, workspace=None):
     if workspace is None:
         workspace = torch.empty(max(flamia_attn_bwd_workspace_size(p), 1), dtype=torch.uint8,
                                 device=dev)
+    f4 = None if fp4 is None else (fp4[0][0], fp4[0][1], fp4[1][0], fp4[1][1])
     flamia_attn_bwd(p, q[0], q[1], k[0], k[1], v[0], v[1], o, lse, dout, dq, dk, dv, workspace,
-                    stream=stream)
+                    fp4=f4, stream=stream)
     return dq, dk, dv, workspace

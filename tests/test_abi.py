@@ -65,6 +65,10 @@ def test_invalid_arguments_rejected_before_launch():
     assert fwd(P(_problem()), *args12, None, ws, None) == F.FLAMIA_ERR_WORKSPACE
     bad_fp4 = [vp] * 6 + [vp, None, None, None] + [vp, vp]
     assert fwd(P(_problem()), *bad_fp4, vp, ws, None) == F.FLAMIA_ERR_INVALID_ARG
+    # the E2M1 score views are required with FP4_SCORE, which requires EXACT
+    fp4_flags = F.FLAMIA_CAUSAL | F.FLAMIA_EXACT | F.FLAMIA_FP4_SCORE
+    assert fwd(P(_problem(flags=fp4_flags)), *args12, vp, ws, None) == F.FLAMIA_ERR_INVALID_ARG
+    assert fwd(P(_problem(flags=fp4_flags)), *bad_fp4, vp, ws, None) == F.FLAMIA_ERR_INVALID_ARG
     assert fwd(P(_problem(T=0)), *([None] * 12), None, 0, None) == F.FLAMIA_OK
 
     wsb = F.flamia_attn_bwd_workspace_size(_problem())

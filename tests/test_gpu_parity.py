@@ -112,3 +112,41 @@ def test_quantizer_nvfp4_bit_exact():
     rc, rs = oracle.quantize_nvfp4(bits, cu)
     assert np.array_equal(host(codes), rc), "codes"
     assert np.array_equal(host(scales), rs), "scales"
+
+
+def _exact_case(name, lens, cap, Hq, Hkv, d, fp4, seed=5):
+    """Per-token operands (and the E2M1 score views) on the GPU and in the
+    oracle, for the exact-scale option."""
+    import torch
+    from bit_causal_flash_amd import flamia as F
+    w = workloads.make(name, seed, cap, lens, Hq, Hkv, d)
+    flags = F.FLAMIA_CAUSAL | F.FLAMIA_EXACT | (F.FLAMIA_FP4_SCORE if fp4 else 0)
+    p = F.make_problem(dev(w.cu.astype(np.int32)), w.T, Hq, Hkv, d, 0.0, flags)
+    x = {n: dev(getattr(w, n).view(np.int16)) for n in ("q", "k", "v", "do")}
+    q = F.quantize(p, x["q"], Hq, F.FLAMIA_SCALE_PER_TOKEN)
+    k = F.quantize(p, x["k"], Hkv, F.FLAMIA_SCALE_PER_TOKEN)
+    v = F.quantize(p, x["v"], Hkv, F.FLAMIA_SCALE_PER_TOKEN)
+    f4 = (F.quantize_nvfp4(p, x["q"], Hq), F.quantize_nvfp4(p, x["k"], Hkv)) if fp4 else None
+    o, lse = F.attn_fwd(p, q, k, v, fp4=f4)
+    torch.cuda.synchronize()
+    rq, rk, rv = (oracle.quantize(getattr(w, n), w.cu, block=1) for n in ("q", "k", "v"))
+    for tag, got, ref in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        assert np.array_equal(host(got[0]), ref[0]) and np.array_equal(host(got[1]), ref[1]), tag
+    r4 = None
+    if fp4:
+        r4 = (oracle.quantize_nvfp4(w.q, w.cu), oracle.quantize_nvfp4(w.k, w.cu))
+        for (gc, gs), (rc, rs) in zip(f4, r4):
+            assert np.array_equal(host(gc), rc) and np.array_equal(host(gs), rs)
+    ops = oracle.Operands.from_codes(rq, rk, rv, *(r4 or (None, None)))
+    return w, p, (q, k, v, f4, x), (o, lse), ops
+
+
+@pytest.mark.parametrize("fp4", [False, True], ids=["exact", "exact_fp4"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_exact_forward(fp4, d):
+    log("case exact forward fp4=%s d=%d" % (fp4, d))
+    w, p, _, (o, lse), ops = _exact_case("exact", [160, 97], 270, 4, 2, d, fp4)
+    O, L, ties = oracle.attn_fwd(w.cu, ops, causal=True, mode=oracle.MODE_TILED, kblock=64,
+                                 want_flags=True)
+    check_fwd(host(o).view(np.uint16).reshape(-1, d), host(lse).T.ravel(), O.reshape(-1, d),
+              L.T.ravel(), ties.transpose(1, 0, 2).reshape(-1, 2), tag="exact fp4=%s d=%d" % (fp4, d))
