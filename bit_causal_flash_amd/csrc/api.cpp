@@ -315,7 +315,10 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     if (st != FLAMIA_OK) return st;
     st = check_fp4_pointers(p, q_fp4, q_fp4_scales, k_fp4, k_fp4_scales);
     if (st != FLAMIA_OK) return st;
-    if (p->flags & FLAMIA_EXACT) return FLAMIA_ERR_UNSUPPORTED;
+    // the deterministic dQ pass uses block exponents only; the FP16 view of
+    // the Q tile does not fit the workgroup's LDS next to d = 128 tiles
+    if ((p->flags & FLAMIA_EXACT) && d.deterministic) return FLAMIA_ERR_UNSUPPORTED;
+    if ((p->flags & FLAMIA_FP4_SCORE) && d.d == 128) return FLAMIA_ERR_UNSUPPORTED;
     if (d.T == 0) return FLAMIA_OK;
     if (!q_codes || !q_exps || !k_codes || !k_exps || !v_codes || !v_exps || !o || !lse ||
         !dout || !dq || !dk || !dv)
@@ -331,7 +334,7 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     q.T = (int)d.T;
     q.B = (int)d.B;
     q.H = (int)d.Hq;
-    q.block = 32;
+    q.block = (p->flags & FLAMIA_EXACT) ? 1 : 32;
     q.cu = p->cu_seqlens;
     q.x = dout;
     q.codes = ws + L.do_codes;
@@ -385,6 +388,11 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
+    a.mode = operand_mode(p);
+    a.q_fp4 = q_fp4;
+    a.q_fp4_scales = q_fp4_scales;
+    a.k_fp4 = k_fp4;
+    a.k_fp4_scales = k_fp4_scales;
     if (record(p, true, s) != hipSuccess) return FLAMIA_ERR_HIP;
     e = launch_bwd(a, (int)d.d, w.max_items, !d.deterministic, s);
     if (e != hipSuccess) return FLAMIA_ERR_HIP;

@@ -47,12 +47,21 @@ struct QTile {
     v4i c[NC];
     int eq, edo, pre, ok;
     float lse, delta;
+    // E2M1 view of the Q rows (MODE_FP4): row tid / 4, D / 8 code bytes and
+    // D / 64 scale bytes from feature (tid % 4) D / 4
+    v2i q4;
+    uint32_t q4s;
 };
 
-template <int D, int NT>
+template <int D, int NT, int MODE>
 __device__ __forceinline__ void load_qtile(const AttnArgs& a, QTile<D, NT>& r, int h, int qb, int e,
                                            int tid)
 {
+    if constexpr (MODE == MODE_FP4) {
+        const size_t row = (size_t)min(qb + (tid >> 2), e - 1) * a.Hq + h;
+        r.q4 = *(const v2i*)(a.q_fp4 + row * (D / 2) + (tid & 3) * (D / 8));
+        r.q4s = a.q_fp4_scales[row * (D / 16) + (tid & 3) * (D / 64)];
+    }
     constexpr int CPR = D / 16;
     const int Hq = a.Hq;
     const size_t T = (size_t)a.T;
@@ -150,14 +159,28 @@ __device__ __forceinline__ void dq_region_atomics(const v16f& acc0, const v16f& 
 // instruction stream, and one barrier per tile suffices: Q / dO tiles are
 // triple-buffered (staging j + 1, scores j, gradients j - 1) and P^ / dS^
 // double-buffered.
-template <int D, bool WITH_DQ>
+//
+// Exact modes (per-token exponents; review section 4 and jaehun.me section
+// 3.2): an exponent that varies along an MFMA's contraction axis cannot ride
+// in its 32-wide block scale, so it is folded into the other operand, whose
+// FP32 values are scaled by 2^(e(token) - block maximum) just before their
+// E4M3 rounding: the dO exponent into P^ (dV), the Q exponent into dS^ (dK)
+// and the K exponent into the dQ copy of dS^, which carries one exponent per
+// (query row, 32-key block).  In the normal E4M3 range this equals shifting
+// the rounded codes, i.e. the unfolded products.  MODE_FP4 recomputes S from
+// the E2M1 score views through the FP16 MFMA, as the forward does.
+template <int D, bool WITH_DQ, int MODE>
 __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
 {
     constexpr int PITCH = D + 16;   // token-major code tiles
+    constexpr int PITCH16 = 2 * D + 16;
     constexpr int SPITCH = 64 + 16; // P^ / dS^ tiles, key-major: [128 keys][64 queries]
     constexpr int NKS = D / 64;
+    constexpr int NKH = D / 16;
     constexpr int NDT = D / 32;
     constexpr int CPR = D / 16;
+    constexpr bool EXACT = MODE != MODE_BLOCK;
+    constexpr bool FP4 = MODE == MODE_FP4;
     __shared__ __attribute__((aligned(16))) uint8_t s_kt[128 * PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t s_q[3][64 * PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t s_do[3][64 * PITCH];
@@ -168,6 +191,14 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(16))) float s_delta[3][64];
     __shared__ int s_dsexp[2][2][4];   // [buffer][query half][key group]
     __shared__ int s_ekb[4];
+    // exact modes: the dQ copy of dS^ and its per-row exponents, the Q / dO
+    // block maxima and fold factors; FP4: the FP16 expansion of the Q view
+    __shared__ __attribute__((aligned(16))) uint8_t s_dsr[EXACT ? 2 : 1][EXACT ? 128 * SPITCH : 16];
+    __shared__ int s_er[EXACT ? 2 : 1][EXACT ? 64 : 1][4];
+    __shared__ int s_eqb[3][2], s_egb[3][2];
+    __shared__ __attribute__((aligned(16))) float s_fq[EXACT ? 3 : 1][64];
+    __shared__ __attribute__((aligned(16))) float s_fg[EXACT ? 3 : 1][64];
+    __shared__ __attribute__((aligned(16))) uint8_t s_q16[FP4 ? 2 : 1][FP4 ? 64 * PITCH16 : 16];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5;
     const int kg = wave & 3;
@@ -194,7 +225,18 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
         if (t < e) kv = *(const v4i*)(a.k_codes + ((size_t)t * Hkv + hk) * D + col);
         *(v4i*)(s_kt + row * PITCH + col) = kv;
     }
-    if (tid < 4) s_ekb[tid] = (k0 + 32 * tid < e) ? (int)a.k_exps[(size_t)hk * T + k0 + 32 * tid] : 127;
+    // K block exponents of the dQ MFMA (lane = key of block kg); with
+    // per-token exponents the block maximum and this key's fold factor
+    const int ek = kvalid ? (int)a.k_exps[(size_t)hk * T + kj] : 127;
+    float fk = 1.f;
+    if constexpr (EXACT) {
+        const uint32_t ekb = half_wave_max_u32(kvalid ? (uint32_t)ek : 0u);
+        fk = kvalid ? ldexpf(1.f, ek - (int)ekb) : 0.f;
+        if (scorer && lane == 0) s_ekb[kg] = (int)ekb;
+    } else {
+        if (tid < 4)
+            s_ekb[tid] = (k0 + 32 * tid < e) ? (int)a.k_exps[(size_t)hk * T + k0 + 32 * tid] : 127;
+    }
 
     // iterations: q heads of the group (outer) x 64-query tiles that see the keys
     const int qt_lo = a.causal ? 2 * kt : 0;
@@ -209,7 +251,7 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
     // statistics), so that every prefetched register is consumed on every
     // path.
     using Tile = QTile<D, 256>;
-    auto stage = [&](const Tile& r, int buf) {
+    auto stage = [&](const Tile& r, int buf, int buf2) {
 #pragma unroll
         for (int k = 0; k < Tile::NC; ++k) {
             const int c = tid + 256 * k;
@@ -226,19 +268,35 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
         // the document end get -inf, so their P is exactly zero
         s_nlse[buf][row] = r.ok ? 8.f - r.lse * kLog2e : -INFINITY;
         s_delta[buf][row] = r.ok ? r.delta : 0.f;
+        if constexpr (EXACT) {
+            // lane = query row: block maxima of the Q and dO exponents over
+            // each 32-query half and the rows' fold factors
+            const uint32_t eqr = r.ok ? (uint32_t)r.eq : 0u, egr = r.ok ? (uint32_t)r.edo : 0u;
+            const uint32_t eqb = half_wave_max_u32(eqr), egb = half_wave_max_u32(egr);
+            s_eqb[buf][row >> 5] = (int)eqb;
+            s_egb[buf][row >> 5] = (int)egb;
+            s_fq[buf][row] = r.ok ? ldexpf(1.f, (int)eqr - (int)eqb) : 0.f;
+            s_fg[buf][row] = r.ok ? ldexpf(1.f, (int)egr - (int)egb) : 0.f;
+        }
+        if constexpr (FP4) {
+            // the Q row's features (tid % 4) D / 4 .. + D / 4 - 1 as FP16
+            uint8_t* dst = &s_q16[buf2][(tid >> 2) * PITCH16 + 2 * (tid & 3) * (D / 4)];
+#pragma unroll
+            for (int q = 0; q < D / 32; ++q) {
+                const float sc = __builtin_amdgcn_cvt_f32_fp8((int)((r.q4s >> (8 * (q / 2))) & 0xff), 0);
+                *(h8*)(dst + 16 * q) = fp4x8_to_f16((uint32_t)r.q4[q], sc);
+            }
+        }
     };
-    // prefetch of tile j + 1 (clamped: the last tiles reload the final one,
-    // into a buffer nobody reads) and its staging; unconditional, so the only
-    // wait on these loads is at staging
     Tile nxt;
     auto prefetch = [&](int j) {
         const int j1 = min(j + 1, niter - 1);
-        load_qtile<D, 256>(a, nxt, tile_head(j1), tile_base(j1), e, tid);
+        load_qtile<D, 256, MODE>(a, nxt, tile_head(j1), tile_base(j1), e, tid);
     };
 
     if (scorer) {
-        load_qtile<D, 256>(a, nxt, tile_head(0), tile_base(0), e, tid);
-        stage(nxt, 0);
+        load_qtile<D, 256, MODE>(a, nxt, tile_head(0), tile_base(0), e, tid);
+        stage(nxt, 0, 0);
     }
     // every load issued so far has landed (vmcnt(0)), so that inside the loop
     // only the prefetch of the next tile is outstanding
@@ -246,19 +304,30 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
     lds_barrier();
 
     if (scorer) {
-        // this wave's K and V rows: B operands of S = Q K^T and dP = dO V^T
-        v8i kf[NKS], vf[NKS];
+        // this wave's K and V rows: B operands of S = Q K^T (E4M3 codes, or
+        // the FP16 expansion of the E2M1 view) and dP = dO V^T
+        v8i kf[FP4 ? 1 : NKS], vf[NKS];
+        h8 kh[FP4 ? NKH : 1];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             if (kvalid) {
-                kf[ks] = row_operand(a.k_codes + ((size_t)kj * Hkv + hk) * D + 64 * ks, lane);
+                if constexpr (!FP4)
+                    kf[ks] = row_operand(a.k_codes + ((size_t)kj * Hkv + hk) * D + 64 * ks, lane);
                 vf[ks] = row_operand(a.v_codes + ((size_t)kj * Hkv + hk) * D + 64 * ks, lane);
             } else {
-                kf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                if constexpr (!FP4) kf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
                 vf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
             }
         }
-        const int ek = kvalid ? (int)a.k_exps[(size_t)hk * T + kj] : 127;
+        if constexpr (FP4) {
+            const size_t row = (size_t)min(kj, e - 1) * Hkv + hk;
+#pragma unroll
+            for (int ks = 0; ks < NKH; ++ks) {
+                const uint32_t c = *(const uint32_t*)(a.k_fp4 + row * (D / 2) + 8 * ks + 4 * g);
+                const float sc = __builtin_amdgcn_cvt_f32_fp8((int)a.k_fp4_scales[row * (D / 16) + ks], 0);
+                kh[ks] = fp4x8_to_f16(c, sc);
+            }
+        }
         const int ev = kvalid ? (int)a.v_exps[(size_t)hk * T + kj] : 127;
         __builtin_amdgcn_s_waitcnt(0x0F70);
 
@@ -270,7 +339,7 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                 const uint8_t* sq = s_q[c3];
                 const uint8_t* sg = s_do[c3];
                 // the two 32 x 32 blocks (queries 32 t .. + 31 of the tile):
-                // all eight S / dP MFMAs first, then the element-wise work
+                // all S / dP MFMAs first, then the element-wise work
                 bool active[2];
                 v16f sacc[2], pacc[2];
 #pragma unroll
@@ -280,28 +349,42 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                     for (int v = 0; v < 16; ++v) sacc[t][v] = pacc[t][v] = 0.f;
                     if (active[t]) {
                         const int qr = perm_row(t, lane & 31);
-                        const int eqr = s_eq[c3][qr], edr = s_edo[c3][qr];
+                        const int edr = s_edo[c3][qr];
+                        if constexpr (FP4) {
 #pragma unroll
-                        for (int ks = 0; ks < NKS; ++ks) {
-                            sacc[t] = mfma_f8(row_operand(sq + qr * PITCH + 64 * ks, lane), kf[ks],
-                                              sacc[t], eqr, ek);
+                            for (int ks = 0; ks < NKH; ++ks)
+                                sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                    *(const h8*)(s_q16[pb] + qr * PITCH16 + 2 * (16 * ks + 8 * g)), kh[ks],
+                                    sacc[t], 0, 0, 0);
+                        } else {
+                            const int eqr = s_eq[c3][qr];
+#pragma unroll
+                            for (int ks = 0; ks < NKS; ++ks)
+                                sacc[t] = mfma_f8(row_operand(sq + qr * PITCH + 64 * ks, lane), kf[ks],
+                                                  sacc[t], eqr, ek);
+                        }
+#pragma unroll
+                        for (int ks = 0; ks < NKS; ++ks)
                             pacc[t] = mfma_f8(row_operand(sg + qr * PITCH + 64 * ks, lane), vf[ks],
                                               pacc[t], edr, ev);
-                        }
                     }
                 }
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    v4i pf = {0, 0, 0, 0}, df = {0, 0, 0, 0};
+                    v4i pf = {0, 0, 0, 0}, df = {0, 0, 0, 0}, dfr = {0, 0, 0, 0};
                     int dse = 127;
+                    int er[16];
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) er[v] = 0;
                     if (active[t]) {
                         // Masking is needed only where some key is invalid or,
                         // causally, some query precedes some key; queries past
                         // the document end have 256 P = exp2(-inf) = 0 and
                         // D = 0.  Element v of lane group g is query
                         // qb + 32 t + 16 g + v.
-                        const float* nl = &s_nlse[c3][32 * t + 16 * g];
-                        const float* dl = &s_delta[c3][32 * t + 16 * g];
+                        const int q0 = 32 * t + 16 * g;
+                        const float* nl = &s_nlse[c3][q0];
+                        const float* dl = &s_delta[c3][q0];
                         const bool full = kw0 + 32 <= e && (!a.causal || qb + 32 * t >= kw0 + 31);
                         float amax;
                         if (full) {
@@ -313,23 +396,56 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                         // block exponent of dS = 2^-8 (256 dS); the scaling is exact
                         const int et = ceil_exp448(wave_max_nonneg(amax) * 0.00390625f);
                         dse = et + 127;
+                        if constexpr (EXACT) {
+                            // per-row exponents of the dQ copy: each query
+                            // row's largest |dS| over this block's 32 keys
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            pf[q] = (int)cvt4_fp8(sacc[t][4 * q], sacc[t][4 * q + 1],
-                                                  sacc[t][4 * q + 2], sacc[t][4 * q + 3]);
-                            df[q] = (int)cvt4_fp8(ldexpf(pacc[t][4 * q], -et - 8),
-                                                  ldexpf(pacc[t][4 * q + 1], -et - 8),
-                                                  ldexpf(pacc[t][4 * q + 2], -et - 8),
-                                                  ldexpf(pacc[t][4 * q + 3], -et - 8));
+                            for (int v = 0; v < 16; ++v)
+                                er[v] = ceil_exp448(__uint_as_float(half_wave_max_u32(
+                                                        __float_as_uint(fabsf(pacc[t][v])))) *
+                                                    0.00390625f);
+                            const float* fg = &s_fg[c3][q0];
+                            const float* fq = &s_fq[c3][q0];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                float pv[4], dv4[4], rv[4];
+#pragma unroll
+                                for (int k = 0; k < 4; ++k) {
+                                    const int v = 4 * q + k;
+                                    pv[k] = sacc[t][v] * fg[v];
+                                    dv4[k] = ldexpf(pacc[t][v] * fq[v], -et - 8);
+                                    rv[k] = ldexpf(pacc[t][v] * fk, -er[v] - 8);
+                                }
+                                pf[q] = (int)cvt4_fp8(pv[0], pv[1], pv[2], pv[3]);
+                                df[q] = (int)cvt4_fp8(dv4[0], dv4[1], dv4[2], dv4[3]);
+                                dfr[q] = (int)cvt4_fp8(rv[0], rv[1], rv[2], rv[3]);
+                            }
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                pf[q] = (int)cvt4_fp8(sacc[t][4 * q], sacc[t][4 * q + 1],
+                                                      sacc[t][4 * q + 2], sacc[t][4 * q + 3]);
+                                df[q] = (int)cvt4_fp8(ldexpf(pacc[t][4 * q], -et - 8),
+                                                      ldexpf(pacc[t][4 * q + 1], -et - 8),
+                                                      ldexpf(pacc[t][4 * q + 2], -et - 8),
+                                                      ldexpf(pacc[t][4 * q + 3], -et - 8));
+                            }
                         }
                     }
                     // key-major rows: 16 bytes at the block's queries and lane group
                     *(v4i*)(s_p[pb] + krow * SPITCH + 32 * t + 16 * g) = pf;
                     *(v4i*)(s_ds[pb] + krow * SPITCH + 32 * t + 16 * g) = df;
                     if (lane == 0) s_dsexp[pb][t][kg] = dse;
+                    if constexpr (EXACT) {
+                        *(v4i*)(s_dsr[pb] + krow * SPITCH + 32 * t + 16 * g) = dfr;
+                        if ((lane & 31) == 0) {
+#pragma unroll
+                            for (int v = 0; v < 16; ++v) s_er[pb][32 * t + 16 * g + v][kg] = er[v] + 127;
+                        }
+                    }
                 }
             }
-            stage(nxt, (j + 1) % 3);
+            stage(nxt, (j + 1) % 3, (j + 1) & 1);
             lds_barrier();
         }
     } else {
@@ -339,7 +455,6 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
         for (int i = 0; i < NDT; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) dk[i][v] = dv[i][v] = 0.f;
-
         const size_t dq_rs = (size_t)Hq * D;  // row stride of the dQ accumulator
 
         for (int j = 0; j <= niter; ++j) {
@@ -359,8 +474,8 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                     const v4i d1 = *(const v4i*)(s_ds[pb] + krow * SPITCH + 32 + 16 * g);
                     const v8i pfull = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
                     const v8i dfull = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-                    const int sdo = s_edo[c3][32 * g];
-                    const int sqe = s_eq[c3][32 * g];
+                    const int sdo = EXACT ? s_egb[c3][g] : s_edo[c3][32 * g];
+                    const int sqe = EXACT ? s_eqb[c3][g] : s_eq[c3][32 * g];
                     const int dsg = s_dsexp[pb][g][kg];
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
@@ -381,10 +496,14 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                         const int ct = kg / (NDT / 2), dt0 = 2 * (kg % (NDT / 2));
                         const int nrows = e - (qb + 32 * ct);
                         if (nrows > 0) {
-                            const int kq = s_kq[c3][32 * ct + (lane & 31)];
-                            const int sa0 = min(max(s_dsexp[pb][ct][g] + kq, 0), 254);
-                            const int sa1 = min(max(s_dsexp[pb][ct][2 + g] + kq, 0), 254);
-                            const v8i a0 = lds_tr_operand(s_ds[pb], SPITCH, 0, 32 * ct, lane);
+                            const int qrow = 32 * ct + (lane & 31);
+                            const int kq = s_kq[c3][qrow];
+                            const int e0 = EXACT ? s_er[pb][qrow][g] : s_dsexp[pb][ct][g];
+                            const int e1 = EXACT ? s_er[pb][qrow][2 + g] : s_dsexp[pb][ct][2 + g];
+                            const int sa0 = min(max(e0 + kq, 0), 254);
+                            const int sa1 = min(max(e1 + kq, 0), 254);
+                            const uint8_t* sdq = EXACT ? s_dsr[pb] : s_ds[pb];
+                            const v8i a0 = lds_tr_operand(sdq, SPITCH, 0, 32 * ct, lane);
                             v16f acc[2];
 #pragma unroll
                             for (int i = 0; i < 2; ++i) {
@@ -394,7 +513,7 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                                                  acc[i], sa0, s_ekb[g]);
                             }
                             if (k0 + 64 < e) {
-                                const v8i a1 = lds_tr_operand(s_ds[pb] + 64 * SPITCH, SPITCH, 0, 32 * ct, lane);
+                                const v8i a1 = lds_tr_operand(sdq + 64 * SPITCH, SPITCH, 0, 32 * ct, lane);
 #pragma unroll
                                 for (int i = 0; i < 2; ++i)
                                     acc[i] = mfma_f8(a1, lds_tr_operand(s_kt + 64 * PITCH, PITCH, 0,
@@ -665,13 +784,28 @@ hipError_t launch_bwd(const AttnArgs& a, int D, int max_items, bool with_dq, hip
 {
     if (max_items <= 0) return hipSuccess;
     const dim3 grid((unsigned)max_items * a.Hkv);
+#define FLAMIA_BWD(DD, WQ, MM) hipLaunchKernelGGL((bwd_kernel<DD, WQ, MM>), grid, dim3(512), 0, stream, a)
     if (D == 128) {
-        if (with_dq) hipLaunchKernelGGL((bwd_kernel<128, true>), grid, dim3(512), 0, stream, a);
-        else hipLaunchKernelGGL((bwd_kernel<128, false>), grid, dim3(512), 0, stream, a);
+        if (a.mode == MODE_EXACT) {
+            if (with_dq) FLAMIA_BWD(128, true, MODE_EXACT);
+            else FLAMIA_BWD(128, false, MODE_EXACT);
+        } else {
+            if (with_dq) FLAMIA_BWD(128, true, MODE_BLOCK);
+            else FLAMIA_BWD(128, false, MODE_BLOCK);
+        }
     } else {
-        if (with_dq) hipLaunchKernelGGL((bwd_kernel<64, true>), grid, dim3(512), 0, stream, a);
-        else hipLaunchKernelGGL((bwd_kernel<64, false>), grid, dim3(512), 0, stream, a);
+        if (a.mode == MODE_FP4) {
+            if (with_dq) FLAMIA_BWD(64, true, MODE_FP4);
+            else FLAMIA_BWD(64, false, MODE_FP4);
+        } else if (a.mode == MODE_EXACT) {
+            if (with_dq) FLAMIA_BWD(64, true, MODE_EXACT);
+            else FLAMIA_BWD(64, false, MODE_EXACT);
+        } else {
+            if (with_dq) FLAMIA_BWD(64, true, MODE_BLOCK);
+            else FLAMIA_BWD(64, false, MODE_BLOCK);
+        }
     }
+#undef FLAMIA_BWD
     return hipGetLastError();
 }
 

@@ -88,39 +88,6 @@ __device__ __forceinline__ void load_kvtile(const AttnArgs& a, KVTile<D, MODE>& 
     if constexpr (MODE != MODE_BLOCK) r.evk = a.v_exps[(size_t)hk * T + min(tk, e - 1)];
 }
 
-// Value of an E2M1 code (sign in bit 3): 0, 0.5, 1, 1.5, 2, 3, 4, 6.
-__device__ __forceinline__ float e2m1_value(uint32_t c)
-{
-    const uint32_t m = c & 7u;
-    const float mag = m < 2u ? 0.5f * (float)m
-                             : __uint_as_float((((m >> 1) + 126u) << 23) | ((m & 1u) << 22));
-    return (c & 8u) ? -mag : mag;
-}
-
-// Eight E2M1 codes (one per nibble, feature 2k in the low nibble of byte k)
-// times their E4M3 group scale, as FP16: exact, since the product has at most
-// six significant bits and lies in [2^-10, 2688].
-__device__ __forceinline__ h8 fp4x8_to_f16(uint32_t codes, float scale)
-{
-    h8 o;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) o[k] = (_Float16)(e2m1_value((codes >> (4 * k)) & 15u) * scale);
-    return o;
-}
-
-// Largest over each 32-lane half of the wave (unsigned), in every lane of it.
-__device__ __forceinline__ uint32_t half_wave_max_u32(uint32_t u)
-{
-    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, false));  // row_half_mirror
-    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x140, 0xF, 0xF, false));  // row_mirror
-    // v_permlane16_swap hands every lane, across its two results, the value
-    // of its own 16-lane row and of the neighbouring row in its half
-    const auto pr = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    return max((uint32_t)pr[0], (uint32_t)pr[1]);
-}
-
 // Online-softmax update of one wave's 32 queries x 64 keys: the running
 // integer reference r, the rescale of O and l when it rises, and the
 // probability operand P^ (byte 16 t + v <-> key 32 t + 16 g + v) with its

@@ -156,28 +156,36 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
     if constexpr (PREP) {
         // for every block starting in the window, the largest V and K block
         // exponents over the keys its rows may see (keys before the block's
-        // end, causal; the whole document otherwise): one wave-wide maximum
-        // per block, by the first wave
+        // end, causal; the whole document otherwise), by the first wave.  The
+        // blocks come in token order and their key ranges only grow within a
+        // document, so the lanes' partial maxima carry from block to block
+        // and each key block is read once per window.
         const int lane = tid & 63;
         if (tid < 64) {
             const int g = h * a.Hkv / H;
+            const int blk = a.block;
+            uint32_t pv = 0, pk = 0;
+            int cur_sd = -1, cur_nb = 0;
             for (int r0 = 0; r0 < 32; ++r0) {
                 if (s_bs[r0] != w0 + r0) continue;  // uniform across the workgroup
                 const int be = s_be[r0], de = s_de[r0];
-                const int blk = a.block;
                 int sd, ed;  // the block's document (its end is de)
                 doc_bounds(w0 + r0, s_cu, b0, B, cu, sd, ed);
                 (void)ed;
+                if (sd != cur_sd) {
+                    cur_sd = sd;
+                    cur_nb = 0;
+                    pv = pk = 0;
+                }
                 const int last = a.causal ? be : de;  // exclusive key end
                 const int nb = (last - sd + blk - 1) / blk;
-                uint32_t mv = 0, mk = 0;
-                for (int kb = lane; kb < nb; kb += 64) {
+                for (int kb = cur_nb + lane; kb < nb; kb += 64) {
                     const int jt = sd + kb * blk;
-                    mv = max(mv, (uint32_t)a.v_exps[(size_t)g * T + jt]);
-                    mk = max(mk, (uint32_t)a.k_exps[(size_t)g * T + jt]);
+                    pv = max(pv, (uint32_t)a.v_exps[(size_t)g * T + jt]);
+                    pk = max(pk, (uint32_t)a.k_exps[(size_t)g * T + jt]);
                 }
-                mv = wave_max_u32(mv);
-                mk = wave_max_u32(mk);
+                cur_nb = max(cur_nb, nb);
+                const uint32_t mv = wave_max_u32(pv), mk = wave_max_u32(pk);
                 if (lane == 0) s_pref[r0] = (int)mv + (int)mk - 254;
             }
         }

@@ -60,10 +60,14 @@ typedef enum {
 /* Problem flags. */
 enum {
     FLAMIA_CAUSAL = 1u << 0,        /* keys j <= i of the query's document */
-    FLAMIA_EXACT = 1u << 1,         /* per-token operand exponents + per-row dS
-                                       exponents (not available in this build) */
-    FLAMIA_FP4_SCORE = 1u << 2,     /* E2M1 score view; requires FLAMIA_EXACT
-                                       (not available in this build) */
+    FLAMIA_EXACT = 1u << 1,         /* exact-scale option: operands quantized
+                                       with FLAMIA_SCALE_PER_TOKEN, per-token dO,
+                                       per-(query row, 32-key block) dS
+                                       exponents for dQ; not with
+                                       FLAMIA_DETERMINISTIC in the backward */
+    FLAMIA_FP4_SCORE = 1u << 2,     /* scores from the E2M1 views of Q and K
+                                       (FLAMIA_SCALE_NVFP4_16); requires
+                                       FLAMIA_EXACT; backward: head_dim 64 */
     FLAMIA_DETERMINISTIC = 1u << 3  /* bitwise run-to-run repeatable backward */
 };
 
@@ -141,7 +145,15 @@ flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_head
  *   lse        float [Hq][T] (written)
  *   workspace  device scratch of at least flamia_attn_fwd_workspace_size(p)
  *              bytes; its contents are overwritten.
- * The fp4 pointers are reserved for FLAMIA_FP4_SCORE and must be NULL.
+ * With FLAMIA_EXACT the Q/K/V exponents are per token and enter the score
+ * and dP products through the matrix cores' per-row/per-column scales; the
+ * V exponent, which varies along the P^ V contraction, is folded into P^
+ * (its FP32 value times 2^(e_V(j) - max over the 32-key block) before the
+ * E4M3 rounding, equal to the unfolded product in E4M3's normal range); l
+ * still sums the unfolded P^.  With FLAMIA_FP4_SCORE s2 is computed from the
+ * E2M1 views (q_fp4 / k_fp4: codes uint8 [T][H][d/2], scales uint8
+ * [T][H][d/16], as FLAMIA_SCALE_NVFP4_16 writes them); the fp4 pointers must
+ * be NULL without the flag and non-NULL with it.
  */
 size_t flamia_attn_fwd_workspace_size(const flamia_problem* p);
 flamia_status flamia_attn_fwd(const flamia_problem* p, const uint8_t* q_codes,
@@ -172,6 +184,13 @@ flamia_status flamia_attn_fwd(const flamia_problem* p, const uint8_t* q_codes,
  *   workspace  at least flamia_attn_bwd_workspace_size(p) bytes; it holds the
  *              quantized dO, D, k_i, the FP16 dQ accumulator and work lists,
  *              at the offsets flamia_attn_bwd_workspace_layout reports.
+ * FLAMIA_EXACT (review section 4; jaehun.me section 3.2): dO is quantized per
+ * token; the dO, Q and K exponents, which vary along the contractions of
+ * dV, dK and dQ, are folded into P^, dS^ (dK copy) and dS^ (dQ copy) before
+ * their E4M3 rounding; the dQ copy of dS carries one exponent per (query
+ * row, 32-key block), from the row's largest |dS| over that block.  Returns
+ * FLAMIA_ERR_UNSUPPORTED with FLAMIA_DETERMINISTIC, and with
+ * FLAMIA_FP4_SCORE at head_dim 128.
  */
 size_t flamia_attn_bwd_workspace_size(const flamia_problem* p);
 flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,

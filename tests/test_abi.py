@@ -78,6 +78,14 @@ def test_invalid_arguments_rejected_before_launch():
     assert bwd(P(_problem(Hkv=0)), *args16, vp, wsb, None) == F.FLAMIA_ERR_INVALID_ARG
     missing = [vp] * 6 + [None] * 4 + [vp, vp, vp, None, vp, vp]
     assert bwd(P(_problem()), *missing, vp, wsb, None) == F.FLAMIA_ERR_INVALID_ARG
+    # the exact-scale backward has no deterministic dQ pass, and its E2M1
+    # score path covers head_dim 64 only
+    det_exact = F.FLAMIA_CAUSAL | F.FLAMIA_EXACT | F.FLAMIA_DETERMINISTIC
+    assert bwd(P(_problem(flags=det_exact)), *args16, vp, wsb, None) == F.FLAMIA_ERR_UNSUPPORTED
+    with4 = [vp] * 16
+    assert bwd(P(_problem(d=128, flags=fp4_flags)), *with4, vp,
+               F.flamia_attn_bwd_workspace_size(_problem(d=128, flags=fp4_flags)), None) == \
+        F.FLAMIA_ERR_UNSUPPORTED
 
 
 def test_workspace_layout_is_consistent():

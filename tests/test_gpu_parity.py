@@ -150,3 +150,43 @@ def test_exact_forward(fp4, d):
                                  want_flags=True)
     check_fwd(host(o).view(np.uint16).reshape(-1, d), host(lse).T.ravel(), O.reshape(-1, d),
               L.T.ravel(), ties.transpose(1, 0, 2).reshape(-1, 2), tag="exact fp4=%s d=%d" % (fp4, d))
+
+
+EXACT_BWD = [(64, False), (64, True), (128, False)]
+
+
+@pytest.mark.parametrize("d,fp4", EXACT_BWD, ids=["exact_d64", "exact_fp4_d64", "exact_d128"])
+def test_exact_backward(d, fp4):
+    """Exact-scale backward: per-token dO, folded exponents and per-(query
+    row, 32-key block) dS exponents for dQ, against the oracle's per-row dS
+    backward on the same per-token operands."""
+    import torch
+    from bit_causal_flash_amd import flamia as F
+    log("case exact backward fp4=%s d=%d" % (fp4, d))
+    Hq, Hkv = 4, 2
+    w, p, (q, k, v, f4, x), (o, lse), ops = _exact_case("exact_bwd", [230, 97, 40], 400, Hq, Hkv,
+                                                        d, fp4, seed=9)
+    dq, dk, dv, ws = F.attn_bwd(p, q, k, v, o, lse, x["do"].view(torch.bfloat16), fp4=f4)
+    torch.cuda.synchronize()
+    T = w.T
+    L = F.flamia_attn_bwd_workspace_layout(p)
+    wsn = host(ws)
+    O = host(o).view(np.uint16)
+    gc, ge, D, kpre = oracle.bwd_prep(w.cu, w.do, O, host(k[1]), host(v[1]), Hkv, block=1)
+    assert np.array_equal(wsn[L.do_codes:L.do_codes + T * Hq * d].reshape(T, Hq, d), gc)
+    assert np.array_equal(wsn[L.do_exps:L.do_exps + Hq * T].reshape(Hq, T), ge)
+    assert np.array_equal(wsn[L.dq_prescale:L.dq_prescale + Hq * T].view(np.int8).reshape(Hq, T)
+                          .astype(np.int32), kpre)
+    G = oracle.dequantize(gc, ge)
+    lse64 = host(lse).astype(np.float64)
+    dQ, tq, acc, aq = oracle.bwd_dq(w.cu, ops, G, D, lse64, per_row_ds=True, want_flags=True)
+    dK, dV, tk, tv, ak, av = oracle.bwd_dkdv(w.cu, ops, G, D, lse64, per_row_ds=True,
+                                             want_flags=True)
+    nt = np.repeat(dq_tiles(w.cu, T, True)[:, None], Hq, axis=1)
+    tag = "exact fp4=%s d=%d" % (fp4, d)
+    check_grad(host(dq).view(np.uint16), dQ, tag + " dQ", tq, acc=acc, ntiles=nt, absm=aq)
+    check_grad(host(dk).view(np.uint16), dK, tag + " dK", tk, absm=ak)
+    check_grad(host(dv).view(np.uint16), dV, tag + " dV", tv, absm=av)
+    n = int(w.cu[-1])
+    for t in (dq, dk, dv):
+        assert np.all(host(t)[n:] == 0)
