@@ -111,14 +111,19 @@ def cpu_baseline(w, flop_target=3e11):
     sub = workloads.Workload("sample", w.T, w.cu, nh, nkv, w.d, w.flags,
                              np.ascontiguousarray(w.q[:, :nh]), np.ascontiguousarray(w.k[:, :nkv]),
                              np.ascontiguousarray(w.v[:, :nkv]), np.ascontiguousarray(w.do[:, :nh]))
+    exact = bool(w.flags & workloads.FLAG_EXACT)
+    blk = 1 if exact else 32
     t0 = time.time()
-    q, k, v = (oracle.quantize(x, sub.cu) for x in (sub.q, sub.k, sub.v))
-    ops = oracle.Operands.from_codes(q, k, v)
+    q, k, v = (oracle.quantize(x, sub.cu, block=blk) for x in (sub.q, sub.k, sub.v))
+    views = (None, None)
+    if w.flags & workloads.FLAG_FP4_SCORE:
+        views = (oracle.quantize_nvfp4(sub.q, sub.cu), oracle.quantize_nvfp4(sub.k, sub.cu))
+    ops = oracle.Operands.from_codes(q, k, v, *views)
     O, L = oracle.attn_fwd(sub.cu, ops, mode=oracle.MODE_TILED, kblock=64)
-    gc, ge, D, _ = oracle.bwd_prep(sub.cu, sub.do, oracle.to_bf16(O), k[1], v[1], nkv)
+    gc, ge, D, _ = oracle.bwd_prep(sub.cu, sub.do, oracle.to_bf16(O), k[1], v[1], nkv, block=blk)
     Gd = oracle.dequantize(gc, ge)
-    oracle.bwd_dq(sub.cu, ops, Gd, D, L)
-    oracle.bwd_dkdv(sub.cu, ops, Gd, D, L)
+    oracle.bwd_dq(sub.cu, ops, Gd, D, L, per_row_ds=exact)
+    oracle.bwd_dkdv(sub.cu, ops, Gd, D, L, per_row_ds=exact)
     dt = time.time() - t0
     flop = 14.0 * w.d * nh * w.visible_pairs()
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
@@ -168,23 +173,36 @@ def main():
     dq = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
     dk = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
     dv = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev)
-    pq = F.make_problem(cu, T, Hq, Hkv, d, 0.0, F.FLAMIA_CAUSAL)
-    pf = F.make_problem(cu, T, Hq, Hkv, d, 0.0, F.FLAMIA_CAUSAL)
-    pb = F.make_problem(cu, T, Hq, Hkv, d, 0.0, F.FLAMIA_CAUSAL)
+    # the workload's options: the exact-scale path quantizes per token and,
+    # with the E2M1 score view, also writes the views of Q and K
+    exact = bool(w.flags & workloads.FLAG_EXACT)
+    fp4 = bool(w.flags & workloads.FLAG_FP4_SCORE)
+    flags = F.FLAMIA_CAUSAL | (F.FLAMIA_EXACT if exact else 0) | (F.FLAMIA_FP4_SCORE if fp4 else 0)
+    mode = F.FLAMIA_SCALE_PER_TOKEN if exact else F.FLAMIA_SCALE_TOKBLOCK32
+    pq = F.make_problem(cu, T, Hq, Hkv, d, 0.0, flags)
+    pf = F.make_problem(cu, T, Hq, Hkv, d, 0.0, flags)
+    pb = F.make_problem(cu, T, Hq, Hkv, d, 0.0, flags)
     wsf = torch.empty(F.flamia_attn_fwd_workspace_size(pf), **u8)
     wsb = torch.empty(F.flamia_attn_bwd_workspace_size(pb), **u8)
 
-    qargs = ((Hq, xq, qc, qe), (Hkv, xk, kc, ke), (Hkv, xv, vc, ve))
+    qargs = [(Hq, xq, qc, qe, mode), (Hkv, xk, kc, ke, mode), (Hkv, xv, vc, ve, mode)]
+    views = None
+    if fp4:
+        q4, k4 = (torch.empty((T, h, d // 2), **u8) for h in (Hq, Hkv))
+        q4s, k4s = (torch.empty((T, h, d // 16), **u8) for h in (Hq, Hkv))
+        qargs += [(Hq, xq, q4, q4s, F.FLAMIA_SCALE_NVFP4_16),
+                  (Hkv, xk, k4, k4s, F.FLAMIA_SCALE_NVFP4_16)]
+        views = (q4, q4s, k4, k4s)
 
     def quant():
-        for nh, x, c, e in qargs:
-            F.flamia_quantize_tokblock(pq, nh, 0, x, c, e)
+        for nh, x, c, e, m in qargs:
+            F.flamia_quantize_tokblock(pq, nh, m, x, c, e)
 
     def fwd():
-        F.flamia_attn_fwd(pf, qc, qe, kc, ke, vc, ve, o, lse, wsf)
+        F.flamia_attn_fwd(pf, qc, qe, kc, ke, vc, ve, o, lse, wsf, fp4=views)
 
     def bwd():
-        F.flamia_attn_bwd(pb, qc, qe, kc, ke, vc, ve, o, lse, xdo, dq, dk, dv, wsb)
+        F.flamia_attn_bwd(pb, qc, qe, kc, ke, vc, ve, o, lse, xdo, dq, dk, dv, wsb, fp4=views)
 
     def step():
         quant()
@@ -229,21 +247,23 @@ def main():
 
     # quantizer kernels alone: events recorded by the library around each
     # kernel, with a forward queued ahead so the GPU never waits on a launch
-    evq = [[(hip.create(), hip.create()) for _ in range(3)] for _ in range(K)]
+    evq = [[(hip.create(), hip.create()) for _ in qargs] for _ in range(K)]
     torch.cuda.synchronize()
     for i in range(K):
         fwd()
-        for j, (nh, x, c, e) in enumerate(qargs):
+        for j, (nh, x, c, e, m) in enumerate(qargs):
             F.set_events(pq, *evq[i][j])
-            F.flamia_quantize_tokblock(pq, nh, 0, x, c, e)
+            F.flamia_quantize_tokblock(pq, nh, m, x, c, e)
     torch.cuda.synchronize()
     F.set_events(pq, None, None)
     ms_qkern = sum(hip.elapsed_ms(a, b) for ev in evq for a, b in ev) / K
     ms_attn = timed(lambda: (fwd(), bwd()), K)
-    pdet = F.make_problem(cu, T, Hq, Hkv, d, 0.0, F.FLAMIA_CAUSAL | F.FLAMIA_DETERMINISTIC)
-    wsd = torch.empty(F.flamia_attn_bwd_workspace_size(pdet), **u8)
-    ms_bwd_det = timed(lambda: F.flamia_attn_bwd(pdet, qc, qe, kc, ke, vc, ve, o, lse, xdo, dq, dk,
-                                                 dv, wsd), K)
+    ms_bwd_det = None  # the exact-scale backward has no deterministic variant
+    if not exact:
+        pdet = F.make_problem(cu, T, Hq, Hkv, d, 0.0, F.FLAMIA_CAUSAL | F.FLAMIA_DETERMINISTIC)
+        wsd = torch.empty(F.flamia_attn_bwd_workspace_size(pdet), **u8)
+        ms_bwd_det = timed(lambda: F.flamia_attn_bwd(pdet, qc, qe, kc, ke, vc, ve, o, lse, xdo, dq,
+                                                     dk, dv, wsd), K)
 
     pairs = w.visible_pairs()
     flop = 14.0 * d * Hq * pairs
@@ -252,6 +272,8 @@ def main():
     value = flop / (ms_step * 1e-3) / 1e12
     bwd_tflops = flop_bwd / (ms_bwd * 1e-3) / 1e12
     qbytes = (T * (Hq + 2 * Hkv)) * (3 * d + 1)  # read bf16, write codes + exponent byte
+    if fp4:  # E2M1 views of Q and K: read bf16, write d / 2 code and d / 16 scale bytes
+        qbytes += T * (Hq + Hkv) * (2 * d + d // 2 + d // 16)
     out = {
         "metric": "causal packed attn fwd+bwd TFLOP/s at 1 MI355X; % of FP8 MFMA peak",
         "value": round(value, 2),
@@ -263,12 +285,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3",
+        "dtype": "fp8_e4m3+e2m1" if fp4 else "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": T, "documents": int(len(w.cu) - 1),
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "causal": True,
                    "visible_pairs": int(pairs), "seed": args.seed,
-                   "step": "quantize Q,K,V + attn fwd + attn bwd"},
+                   "scales": ("per-token operand exponents, per-(query row, 32-key block) dS "
+                              "exponents for dQ" if exact else
+                              "one exponent per 32 tokens x head dim, per 32x32 block for dS"),
+                   "score_view": "E2M1 + E4M3 per 16 features (FP16 MFMA)" if fp4 else None,
+                   "step": "quantize Q,K,V%s + attn fwd + attn bwd" %
+                           (" (+ E2M1 views of Q,K)" if fp4 else "")},
         "pct_fp8_peak": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
         "roofline": {"kernel": "bwd_kernel", "bound": "mfma", "achieved": round(bwd_tflops, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -280,7 +307,7 @@ def main():
             "bwd_kernel_tflops": round(bwd_tflops, 2),
             "attn_fwd_bwd_ms": round(ms_attn, 4),
             "attn_fwd_bwd_tflops": round(flop / (ms_attn * 1e-3) / 1e12, 2),
-            "bwd_call_deterministic_ms": round(ms_bwd_det, 4),
+            "bwd_call_deterministic_ms": None if ms_bwd_det is None else round(ms_bwd_det, 4),
             "quantize_qkv_call_ms": round(ms_quant, 4),
             "quantize_qkv_kernel_ms": round(ms_qkern, 4),
             "quantize_kernel_gbps": round(qbytes / (ms_qkern * 1e-3) / 1e9, 1),

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
     // exact modes: the dQ copy of dS^ and its per-row exponents, the Q / dO
     // block maxima and fold factors; FP4: the FP16 expansion of the Q view
     __shared__ __attribute__((aligned(16))) uint8_t s_dsr[EXACT ? 2 : 1][EXACT ? 128 * SPITCH : 16];
-    __shared__ int s_er[EXACT ? 2 : 1][EXACT ? 64 : 1][4];
+    __shared__ __attribute__((aligned(16))) int s_er[EXACT ? 2 : 1][4][EXACT ? 64 : 1];
     __shared__ int s_eqb[3][2], s_egb[3][2];
     __shared__ __attribute__((aligned(16))) float s_fq[EXACT ? 3 : 1][64];
     __shared__ __attribute__((aligned(16))) float s_fg[EXACT ? 3 : 1][64];
@@ -398,12 +398,24 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                         dse = et + 127;
                         if constexpr (EXACT) {
                             // per-row exponents of the dQ copy: each query
-                            // row's largest |dS| over this block's 32 keys
+                            // row's largest |dS| over this block's 32 keys,
+                            // one row per lane, then all 16 rows of the lane
+                            // group back from LDS (the same wave's write)
+                            uint32_t ab[16];
 #pragma unroll
-                            for (int v = 0; v < 16; ++v)
-                                er[v] = ceil_exp448(__uint_as_float(half_wave_max_u32(
-                                                        __float_as_uint(fabsf(pacc[t][v])))) *
-                                                    0.00390625f);
+                            for (int v = 0; v < 16; ++v) ab[v] = __float_as_uint(fabsf(pacc[t][v]));
+                            const int erl = ceil_exp448(
+                                __uint_as_float(row_max_transpose(ab, lane)) * 0.00390625f);
+                            int* erow = &s_er[pb][kg][32 * t + 16 * g];
+                            if ((lane & 16) == 0) erow[rev4(lane & 15)] = erl + 127;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const v4i e4 = *(const v4i*)(erow + 4 * q);
+                                er[4 * q] = e4.x - 127;
+                                er[4 * q + 1] = e4.y - 127;
+                                er[4 * q + 2] = e4.z - 127;
+                                er[4 * q + 3] = e4.w - 127;
+                            }
                             const float* fg = &s_fg[c3][q0];
                             const float* fq = &s_fq[c3][q0];
 #pragma unroll
@@ -438,10 +450,7 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                     if (lane == 0) s_dsexp[pb][t][kg] = dse;
                     if constexpr (EXACT) {
                         *(v4i*)(s_dsr[pb] + krow * SPITCH + 32 * t + 16 * g) = dfr;
-                        if ((lane & 31) == 0) {
-#pragma unroll
-                            for (int v = 0; v < 16; ++v) s_er[pb][32 * t + 16 * g + v][kg] = er[v] + 127;
-                        }
+                        if (!active[t] && (lane & 16) == 0) s_er[pb][kg][32 * t + 16 * g + (lane & 15)] = 127;
                     }
                 }
             }
@@ -498,8 +507,8 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                         if (nrows > 0) {
                             const int qrow = 32 * ct + (lane & 31);
                             const int kq = s_kq[c3][qrow];
-                            const int e0 = EXACT ? s_er[pb][qrow][g] : s_dsexp[pb][ct][g];
-                            const int e1 = EXACT ? s_er[pb][qrow][2 + g] : s_dsexp[pb][ct][2 + g];
+                            const int e0 = EXACT ? s_er[pb][g][qrow] : s_dsexp[pb][ct][g];
+                            const int e1 = EXACT ? s_er[pb][2 + g][qrow] : s_dsexp[pb][ct][2 + g];
                             const int sa0 = min(max(e0 + kq, 0), 254);
                             const int sa1 = min(max(e1 + kq, 0), 254);
                             const uint8_t* sdq = EXACT ? s_dsr[pb] : s_ds[pb];

@@ -261,6 +261,46 @@ __device__ __forceinline__ uint32_t half_wave_max_u32(uint32_t u)
     return max((uint32_t)pr[0], (uint32_t)pr[1]);
 }
 
+// Row maxima of a 32 x 32 block in the MFMA C layout (element v of lane c
+// of half g is row 16 g + v, column c): a transpose-reduce over the 32 lanes
+// of each half, halving the values a lane holds at every step (partners at
+// lane distance 1, 2, 4 and 8 inside a 16-lane row, each holding the same
+// rows and sending the half the lane keeps), then across the two rows of the
+// half.  Every lane returns the maximum over the 32 columns of row
+// 16 g + rev4(lane & 15) (its low four lane bits reversed); lanes l and
+// l ^ 16 return the same row.
+__device__ __forceinline__ uint32_t row_max_transpose(const uint32_t (&x)[16], int lane)
+{
+    const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4, b3 = lane & 8;
+    uint32_t y[8], z[4], w[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t send = b0 ? x[k] : x[k + 8], keep = b0 ? x[k + 8] : x[k];
+        y[k] = max(keep, (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false));
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t send = b1 ? y[k] : y[k + 4], keep = b1 ? y[k + 4] : y[k];
+        z[k] = max(keep, (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, false));
+    }
+    // row_ror:4 pairs lane i with lane i - 4 (mod 16): the same low two
+    // bits, the other bit 2
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t send = b2 ? z[k] : z[k + 2], keep = b2 ? z[k + 2] : z[k];
+        w[k] = max(keep, (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x124, 0xF, 0xF, false));
+    }
+    const uint32_t send = b3 ? w[0] : w[1], keep = b3 ? w[1] : w[0];
+    const uint32_t u = max(keep, (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x128, 0xF, 0xF, false));
+    const auto pr = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return max((uint32_t)pr[0], (uint32_t)pr[1]);
+}
+
+__device__ __forceinline__ int rev4(int i)
+{
+    return (int)(__builtin_bitreverse32((uint32_t)i) >> 28);
+}
+
 __device__ __forceinline__ int doc_of(const int32_t* cu, int B, int t)
 {
     int lo = 0, hi = B - 1;

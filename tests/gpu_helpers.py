@@ -56,6 +56,38 @@ def run_gpu(w, flags=None, scale=0.0, backward=True, scale_mode=0):
     return out
 
 
+def run_gpu_exact(w):
+    """The exact-scale path on the GPU: per-token quantizer, the E2M1 views of
+    Q and K when the workload asks for the score view, forward, backward."""
+    import torch
+    from bit_causal_flash_amd import flamia as F
+    fp4 = bool(w.flags & workloads.FLAG_FP4_SCORE)
+    flags = F.FLAMIA_CAUSAL | F.FLAMIA_EXACT | (F.FLAMIA_FP4_SCORE if fp4 else 0)
+    p = F.make_problem(dev(w.cu.astype(np.int32)), w.T, w.Hq, w.Hkv, w.d, 0.0, flags)
+    x = {n: dev(getattr(w, n).view(np.int16)) for n in ("q", "k", "v", "do")}
+    q = F.quantize(p, x["q"], w.Hq, F.FLAMIA_SCALE_PER_TOKEN)
+    k = F.quantize(p, x["k"], w.Hkv, F.FLAMIA_SCALE_PER_TOKEN)
+    v = F.quantize(p, x["v"], w.Hkv, F.FLAMIA_SCALE_PER_TOKEN)
+    f4 = (F.quantize_nvfp4(p, x["q"], w.Hq), F.quantize_nvfp4(p, x["k"], w.Hkv)) if fp4 else None
+    o, lse = F.attn_fwd(p, q, k, v, fp4=f4)
+    dq, dk, dv, ws = F.attn_bwd(p, q, k, v, o, lse, x["do"].view(torch.bfloat16), fp4=f4)
+    torch.cuda.synchronize()
+    L = F.flamia_attn_bwd_workspace_layout(p)
+    wsn = host(ws)
+    T, Hq, d = w.T, w.Hq, w.d
+    out = dict(qc=host(q[0]), qe=host(q[1]), kc=host(k[0]), ke=host(k[1]), vc=host(v[0]),
+               ve=host(v[1]), O=host(o).view(np.uint16), LSE=host(lse),
+               dQ=host(dq).view(np.uint16), dK=host(dk).view(np.uint16),
+               dV=host(dv).view(np.uint16),
+               gc=wsn[L.do_codes:L.do_codes + T * Hq * d].reshape(T, Hq, d),
+               ge=wsn[L.do_exps:L.do_exps + Hq * T].reshape(Hq, T),
+               D=wsn[L.delta:L.delta + 4 * Hq * T].view(np.float32).reshape(Hq, T),
+               kpre=wsn[L.dq_prescale:L.dq_prescale + Hq * T].view(np.int8).reshape(Hq, T))
+    if fp4:
+        out.update(q4=host(f4[0][0]), q4s=host(f4[0][1]), k4=host(f4[1][0]), k4s=host(f4[1][1]))
+    return out
+
+
 def oracle_operands(w, block=32):
     q = oracle.quantize(w.q, w.cu, block=block)
     k = oracle.quantize(w.k, w.cu, block=block)
