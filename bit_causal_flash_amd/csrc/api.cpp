@@ -66,7 +66,10 @@ flamia_status check_attn(const flamia_problem* p, Dims* out)
     if (st != FLAMIA_OK) return st;
     if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->num_q_heads % p->num_kv_heads != 0)
         return FLAMIA_ERR_INVALID_ARG;
-    if (p->num_q_heads > 65535) return FLAMIA_ERR_UNSUPPORTED;  // grid.y of the dO preparation
+    // the dO preparation launches a 1-D grid of (32-token window, head)
+    // workgroups of 256 threads
+    if ((int64_t)(p->total_tokens + 31) / 32 * p->num_q_heads >= ((int64_t)1 << 24))
+        return FLAMIA_ERR_UNSUPPORTED;
     st = check_head_dim(p->head_dim);
     if (st != FLAMIA_OK) return st;
     if (p->flags & ~kKnownFlags) return FLAMIA_ERR_INVALID_ARG;
@@ -198,9 +201,12 @@ flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_head
     if (scale_mode != FLAMIA_SCALE_TOKBLOCK32 && scale_mode != FLAMIA_SCALE_PER_TOKEN &&
         scale_mode != FLAMIA_SCALE_NVFP4_16)
         return FLAMIA_ERR_INVALID_ARG;
-    if ((int64_t)(p->total_tokens + 31) / 32 * num_heads >= (int64_t)INT32_MAX * 64)
+    // 1-D grid of (32-token window, head) workgroups of 256 threads; the
+    // E2M1 view launches one thread per 16 features
+    if ((int64_t)(p->total_tokens + 31) / 32 * num_heads >= ((int64_t)1 << 24))
         return FLAMIA_ERR_UNSUPPORTED;
-    if (num_heads > 65535) return FLAMIA_ERR_UNSUPPORTED;
+    if ((int64_t)p->total_tokens * num_heads * (p->head_dim / 16) >= ((int64_t)1 << 32) - 256)
+        return FLAMIA_ERR_UNSUPPORTED;
     if (p->total_tokens == 0) return FLAMIA_OK;
     if (x == nullptr || codes == nullptr || exps == nullptr) return FLAMIA_ERR_INVALID_ARG;
     QuantArgs a = {};

@@ -10,14 +10,18 @@
 // locality differ" (the dQ accumulator scale must come from the row's own dO
 // and the running maxima of the visible K and V magnitudes).
 //
-// Work decomposition: one workgroup per (32-token window, head).  It owns
-// every document-local block whose first token lies in the window, so it
-// touches at most 63 rows and every element is read exactly once; it also
-// writes the padding rows (t >= cu[B]) of its window.  The document lookup is
-// wave-uniform (scalar loads of cu_seqlens), block maxima meet in LDS through
-// integer atomics on the float bits, and the only barriers are the two around
-// them.  Many small workgroups hide the memory latency best: with 2, 4 heads
-// per workgroup the same kernel streamed 10 and 40 % slower on MI355X.
+// Work decomposition: one workgroup per (32-token window, head), heads
+// fastest in the launch order so that concurrently running workgroups cover
+// whole token rows (contiguous memory).  A workgroup owns every
+// document-local block whose first token lies in the window, so it touches
+// at most 63 rows and every element is read exactly once; it also writes the
+// padding rows (t >= cu[B]) of its window.  The document lookup is
+// wave-uniform (scalar loads of cu_seqlens, the documents overlapping the
+// window walked in order), the row loads issue right after it, and block
+// maxima meet in LDS through integer atomics on the float bits.  Inputs are
+// read and codes written with non-temporal hints (streamed once).  Measured
+// on MI355X: many small workgroups hide the latency best (a wave per window
+// without LDS, or several windows per wave, streamed slower).
 // The kernel is HBM-bound: 2 bytes read and 1 byte written per element (plus
 // 2 bytes of O read, 2 bytes of accumulator zeroing and 5 bytes per row for
 // the backward preparation).
@@ -54,25 +58,6 @@ __device__ __forceinline__ float group_sum(float x)
     return x;
 }
 
-// Start and end of the document holding token t (b0 <= its index), from the
-// staged starts s_cu[j] = cu[min(b0 + j, B)], j <= 65; a span crowded with
-// more than 64 document starts (empty documents included) falls back to a
-// search of cu_seqlens.
-__device__ __forceinline__ void doc_bounds(int t, const int* s_cu, int b0, int B,
-                                           const int32_t* cu, int& s, int& e)
-{
-    int j = 0;
-    while (j < 64 && b0 + j + 1 < B && s_cu[j + 1] <= t) ++j;
-    if (j == 64 && b0 + 65 < B && s_cu[65] <= t) {
-        const int b = doc_of(cu, B, t);
-        s = cu[b];
-        e = cu[b + 1];
-    } else {
-        s = s_cu[j];
-        e = s_cu[j + 1];
-    }
-}
-
 template <int D, bool PREP>
 __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
 {
@@ -82,18 +67,17 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
     const int tid = threadIdx.x;
     const int chunk = tid % TPR;
     const int rsub = tid / TPR;
-    const int w0 = 32 * blockIdx.x;       // window start
-    const int h = blockIdx.y;
+    const int h = blockIdx.x % a.H;         // heads fastest: concurrent workgroups
+    const int w0 = 32 * (blockIdx.x / a.H); // cover whole token rows
     const int H = a.H, T = a.T, B = a.B;
     const int32_t* __restrict__ cu = a.cu;
     const int ntok = cu[B];
 
-    __shared__ int s_bs[64], s_be[64], s_de[64];  // block start / end, document end (or -1)
-    __shared__ int s_cu[66];                       // document starts from the window's first doc
+    __shared__ int s_bs[64], s_be[64], s_ds[64], s_de[64];  // per row: owned block start / end, document start / end
     __shared__ uint32_t s_bmax[32];                // block amax bits, by block start - w0
     __shared__ int s_pref[32];                     // visible V + K exponent maxima (PREP)
 
-    // documents overlapping [w0, w0 + 64): b0 contains w0 (uniform search)
+    // b0: the document holding w0 (uniform binary search on cu_seqlens)
     int b0 = 0;
     if (w0 < ntok) {
         int lo = 0, hi = B - 1;
@@ -104,53 +88,73 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
         }
         b0 = lo;
     }
-    if (tid < 66) s_cu[tid] = cu[min(b0 + tid, B)];
-    if (tid < 32) s_bmax[tid] = 0u;
-    __syncthreads();
-    if (tid < 64) {
-        const int t = w0 + tid;
-        int bs = -1, be = -1, de = -1;
-        if (t < ntok && t < T) {
-            int s, e;
-            doc_bounds(t, s_cu, b0, B, cu, s, e);
-            const int blk = a.block;
-            const int start = s + blk * ((t - s) / blk);
-            if (start >= w0 && start < w0 + 32) {
-                bs = start;
-                be = min(start + blk, e);
-                de = e;
+    // this thread's rows w0 + p RPP + rsub: the block each belongs to, kept
+    // when the block starts in the window.  The documents overlapping the
+    // 64-row span are walked in order with uniform (scalar) loads, so the
+    // row loads issue without any LDS staging or barrier.
+    const int blk = a.block;
+    int bsr[NPASS], ber[NPASS], dsr[NPASS], der[NPASS];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) bsr[p] = ber[p] = dsr[p] = der[p] = -1;
+    if (w0 < ntok) {
+        int bb = b0, s = cu[b0], e = cu[b0 + 1];
+        while (true) {
+#pragma unroll
+            for (int p = 0; p < NPASS; ++p) {
+                const int t = w0 + p * RPP + rsub;
+                if (t >= s && t < e) {
+                    const int start = blk == 1 ? t : s + ((t - s) & ~31);
+                    if (start >= w0 && start < w0 + 32) {
+                        bsr[p] = start;
+                        ber[p] = min(start + blk, e);
+                        dsr[p] = s;
+                        der[p] = e;
+                    }
+                }
             }
+            if (e >= w0 + 64 || bb + 1 >= B) break;
+            ++bb;
+            s = e;
+            e = cu[bb + 1];
         }
-        s_bs[tid] = bs;
-        s_be[tid] = be;
-        s_de[tid] = de;
     }
-    __syncthreads();
 
-    // load the owned rows (and O for the preparation); block maxima
+    // load the owned rows (and O for the preparation)
     v4i raw[NPASS], oraw[PREP ? NPASS : 1];
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
-        const int r = p * RPP + rsub;
-        const int t = w0 + r;
+        const int t = w0 + p * RPP + rsub;
         raw[p] = v4i{0, 0, 0, 0};
         if (PREP) oraw[p] = v4i{0, 0, 0, 0};
-        if (s_bs[r] >= 0) {
+        if (bsr[p] >= 0) {
             const size_t off = ((size_t)t * H + h) * D + 8 * chunk;
-            raw[p] = *(const v4i*)(a.x + off);
-            if (PREP) oraw[p] = *(const v4i*)(a.o + off);
+            raw[p] = __builtin_nontemporal_load((const v4i*)(a.x + off));
+            if (PREP) oraw[p] = __builtin_nontemporal_load((const v4i*)(a.o + off));
         }
     }
+    // while they are in flight: clear the block maxima, publish the rows'
+    // blocks for the preparation's first wave
+    if (tid < 32) s_bmax[tid] = 0u;
+    if (PREP && chunk == 0) {
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int r = p * RPP + rsub;
+            s_bs[r] = bsr[p];
+            s_be[r] = ber[p];
+            s_ds[r] = dsr[p];
+            s_de[r] = der[p];
+        }
+    }
+    __syncthreads();
+    // block maxima
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
-        const int r = p * RPP + rsub;
         uint32_t m = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             m = max(m, max(((uint32_t)raw[p][k] << 16) & 0x7fff0000u, (uint32_t)raw[p][k] & 0x7fff0000u));
         m = group_max<TPR>(m);
-        const int bs = s_bs[r];
-        if (bs >= 0 && chunk == 0) atomicMax(&s_bmax[bs - w0], m);
+        if (bsr[p] >= 0 && chunk == 0) atomicMax(&s_bmax[bsr[p] - w0], m);
     }
 
     if constexpr (PREP) {
@@ -169,9 +173,7 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
             for (int r0 = 0; r0 < 32; ++r0) {
                 if (s_bs[r0] != w0 + r0) continue;  // uniform across the workgroup
                 const int be = s_be[r0], de = s_de[r0];
-                int sd, ed;  // the block's document (its end is de)
-                doc_bounds(w0 + r0, s_cu, b0, B, cu, sd, ed);
-                (void)ed;
+                const int sd = s_ds[r0];  // the block's document is [sd, de)
                 if (sd != cur_sd) {
                     cur_sd = sd;
                     cur_nb = 0;
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
         const int t = w0 + r;
         if (t >= T) continue;
         const size_t off = ((size_t)t * H + h) * D + 8 * chunk;
-        const int bs = s_bs[r];
+        const int bs = bsr[p];
         const bool mine = bs >= 0;
         const bool pad = (t >= ntok) && r < 32;
         if (!mine && !pad) continue;
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
         v2i cw;
         cw.x = (int)lo;
         cw.y = (int)hi;
-        *(v2i*)(a.codes + off) = cw;
+        __builtin_nontemporal_store(cw, (v2i*)(a.codes + off));
         if constexpr (PREP) {
             *(v4i*)(a.dq_acc + off) = v4i{0, 0, 0, 0};
             dot = group_sum<TPR>(dot);
@@ -337,7 +339,7 @@ hipError_t launch_nvfp4(const QuantArgs& a, int D, hipStream_t stream)
 hipError_t launch_quant(const QuantArgs& a, int D, bool prep, hipStream_t stream)
 {
     if (a.T == 0) return hipSuccess;
-    const dim3 grid((a.T + 31) / 32, a.H);
+    const dim3 grid((unsigned)(((a.T + 31) / 32) * a.H));
     if (D == 128) {
         if (prep) hipLaunchKernelGGL((quant_kernel<128, true>), grid, dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((quant_kernel<128, false>), grid, dim3(256), 0, stream, a);

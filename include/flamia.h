@@ -123,10 +123,14 @@ typedef struct {
  *     exps[h][t] = e + 127 on every token of the block.
  *   p          problem; only total_tokens, num_seqs and cu_seqlens are read
  *   num_heads  H >= 1 of this tensor (Hq for Q, Hkv for K and V)
- *   scale_mode FLAMIA_SCALE_TOKBLOCK32 or FLAMIA_SCALE_PER_TOKEN
+ *   scale_mode FLAMIA_SCALE_TOKBLOCK32, FLAMIA_SCALE_PER_TOKEN or
+ *              FLAMIA_SCALE_NVFP4_16
  *   x          bf16 [T][H][d] (device, read)
  *   codes      uint8 [T][H][d] (device, written)
  *   exps       uint8 [H][T] (device, written)
+ * Returns FLAMIA_ERR_UNSUPPORTED when ceil(T / 32) * H >= 2^24 (one
+ * 256-thread workgroup per 32-token window and head); the attention calls
+ * apply the same limit to Hq.
  */
 flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_heads,
                                        int32_t scale_mode, const uint16_t* x, uint8_t* codes,
