@@ -165,9 +165,45 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
         // document, so the lanes' partial maxima carry from block to block
         // and each key block is read once per window.
         const int lane = tid & 63;
-        if (tid < 64) {
+        if (tid < 64 && blk == 1 && a.causal) {
+            // per-token blocks, causal: row r sees its document's tokens up
+            // to itself, so a segmented inclusive prefix maximum over the
+            // window's rows (one lane each) gives every row at once, joined
+            // with the maximum over the keys that the document holding w0
+            // has before the window
             const int g = h * a.Hkv / H;
-            const int blk = a.block;
+            const int r = lane & 31;
+            const int t = w0 + r;
+            const bool own = lane < 32 && s_bs[r] == t;
+            const int seg = own ? s_ds[r] : t;  // the row's document start (itself when not owned)
+            uint32_t pv = own ? (uint32_t)a.v_exps[(size_t)g * T + t] : 0u;
+            uint32_t pk = own ? (uint32_t)a.k_exps[(size_t)g * T + t] : 0u;
+            const int sd0 = s_ds[0];  // meaningful when row 0 (t = w0) is owned
+            uint32_t bv = 0, bk = 0;
+            if (s_bs[0] == w0 && sd0 < w0) {  // uniform
+                for (int j = sd0 + lane; j < w0; j += 64) {
+                    bv = max(bv, (uint32_t)a.v_exps[(size_t)g * T + j]);
+                    bk = max(bk, (uint32_t)a.k_exps[(size_t)g * T + j]);
+                }
+                bv = wave_max_u32(bv);
+                bk = wave_max_u32(bk);
+            }
+#pragma unroll
+            for (int d = 1; d < 32; d <<= 1) {
+                const uint32_t ov = (uint32_t)__shfl_up((int)pv, d, 32);
+                const uint32_t ok = (uint32_t)__shfl_up((int)pk, d, 32);
+                if (r >= d && t - d >= seg) {
+                    pv = max(pv, ov);
+                    pk = max(pk, ok);
+                }
+            }
+            if (own && seg == sd0) {
+                pv = max(pv, bv);
+                pk = max(pk, bk);
+            }
+            if (own) s_pref[r] = (int)pv + (int)pk - 254;
+        } else if (tid < 64) {
+            const int g = h * a.Hkv / H;
             uint32_t pv = 0, pk = 0;
             int cur_sd = -1, cur_nb = 0;
             for (int r0 = 0; r0 < 32; ++r0) {
