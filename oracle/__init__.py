@@ -147,6 +147,51 @@ def quantize(x, cu, block: int = 32, rule: int = 0):
     return codes, exps
 
 
+def hadamard_matrix(d: int):
+    """Sylvester Hadamard matrix H_d (float64 [d][d]): entry (i, j) is
+    (-1)^popcount(i & j); H_d is symmetric and H_d H_d = d I."""
+    i = np.arange(d)
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i[:, None] & i[None, :])
+    return np.where(pc % 2 == 0, 1.0, -1.0)
+
+
+def hadamard_rotate(x):
+    """Rows of bf16 x [T][H][d] times H_d, by the FP32 fast Walsh-Hadamard
+    transform (stages h = 1, 2, ..., d/2) -> float32 [T][H][d]."""
+    x = _c(x, np.uint16)
+    T, H, d = x.shape
+    out = np.empty((T, H, d), dtype=np.float32)
+    _check(_load().orc_hadamard_rotate(T, H, d, _p(x), _p(out)))
+    return out
+
+
+def quantize_f32(x, cu, block: int = 32, rule: int = 0):
+    """The token-block quantizer over FP32 values [T][H][d]."""
+    x = _c(x, np.float32)
+    cu = _c(cu, np.int32)
+    T, H, d = x.shape
+    codes = np.empty((T, H, d), dtype=np.uint8)
+    exps = np.empty((H, T), dtype=np.uint8)
+    _check(_load().orc_quantize_f32(T, len(cu) - 1, _p(cu), H, d, _p(x), block, rule,
+                                    _p(codes), _p(exps)))
+    return codes, exps
+
+
+def quantize_rotated(x, cu, block: int = 32):
+    """Score-path operand with the Hadamard rotation: the rows of bf16 x
+    rotated (hadamard_rotate), then quantized by the token-block rule."""
+    return quantize_f32(hadamard_rotate(x), cu, block=block)
+
+
+def unrotate(g):
+    """Gradient with respect to a rotated operand (x_r = x H_d) taken back to
+    the original coordinates: dL/dx = dL/dx_r H_d, for every row of float64
+    g [T][H][d].  The rotated problem runs at softmax scale / d, since
+    q_r . k_r = d q . k."""
+    g = np.asarray(g, dtype=np.float64)
+    return g @ hadamard_matrix(g.shape[-1])
+
+
 def quantize_nvfp4(x, cu):
     """E2M1 + E4M3-per-16 score view.  -> (codes [T][H][d/2], scales
     [T][H][d/16])."""

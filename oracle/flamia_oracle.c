@@ -23,10 +23,13 @@
  *                                       quantization" (boost 256)
  *        S6  "Packed documents and GPU scheduling" (+inf LSE sentinel,
  *                                       masked keys outside the document)
+ *        S3  "Rotation, range, and the alternative", Algorithm 1 step 02
+ *                                       (Hadamard rotation of Q and K per token)
  *   [K]  jaehun.me review of arXiv 2611.03344, S1.2 (S, P, O and the five
  *        backward products), S2 (floor-rule group exponent), S3.1-S3.3
  *        (32x32 dS blocks, per-query-row dS exponent option, D from the
- *        quantized dO).
+ *        quantized dO), S3.4 (Hadamard rotation: dot products preserved,
+ *        no mixing across positions).
  *   [F]  richardcheam.github.io "efficient execution", "Attention without the
  *        score matrix" (blockwise online softmax), "Lower precision" (E4M3
  *        OCP max 448).
@@ -238,8 +241,10 @@ static int doc_of(int B, const int32_t* cu, int t)
  * block = 32 is the default policy, block = 1 the per-token exact option.
  * rule 0: conservative ceil exponent; rule 1: floor exponent (control only).
  * Padding rows: codes 0, exponent byte 127. */
-int orc_quantize(int T, int B, const int32_t* cu, int H, int d, const uint16_t* x, int block,
-                 int rule, uint8_t* codes, uint8_t* exps)
+/* The token-block rule over one tensor whose values are either bf16 bits (xb)
+ * or FP32 (xf, the rotated score operands). */
+static int quantize_impl(int T, int B, const int32_t* cu, int H, int d, const uint16_t* xb,
+                         const float* xf, int block, int rule, uint8_t* codes, uint8_t* exps)
 {
     if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
     if (H < 1 || d < 1 || block < 1) return ORC_EBADARG;
@@ -253,7 +258,8 @@ int orc_quantize(int T, int B, const int32_t* cu, int H, int d, const uint16_t* 
                 double amax = 0.0;
                 for (int t = s0; t < s1; ++t)
                     for (int c = 0; c < d; ++c) {
-                        double v = fabs(orc_bf16_to_f64(x[((size_t)t * H + h) * d + c]));
+                        size_t k = ((size_t)t * H + h) * d + c;
+                        double v = fabs(xb ? orc_bf16_to_f64(xb[k]) : (double)xf[k]);
                         if (v > amax) amax = v;
                     }
                 int e = rule == 0 ? orc_ceil_exponent(amax) : orc_floor_exponent(amax);
@@ -261,11 +267,56 @@ int orc_quantize(int T, int B, const int32_t* cu, int H, int d, const uint16_t* 
                     exps[(size_t)h * T + t] = (uint8_t)(e + 127);
                     for (int c = 0; c < d; ++c) {
                         size_t k = ((size_t)t * H + h) * d + c;
-                        codes[k] = orc_e4m3_encode(ldexp(orc_bf16_to_f64(x[k]), -e));
+                        double v = xb ? orc_bf16_to_f64(xb[k]) : (double)xf[k];
+                        codes[k] = orc_e4m3_encode(ldexp(v, -e));
                     }
                 }
             }
         }
+    }
+    return ORC_OK;
+}
+
+int orc_quantize(int T, int B, const int32_t* cu, int H, int d, const uint16_t* x, int block,
+                 int rule, uint8_t* codes, uint8_t* exps)
+{
+    return quantize_impl(T, B, cu, H, d, x, NULL, block, rule, codes, exps);
+}
+
+/* The same rule over FP32 values (the rotated Q and K of the score path). */
+int orc_quantize_f32(int T, int B, const int32_t* cu, int H, int d, const float* x, int block,
+                     int rule, uint8_t* codes, uint8_t* exps)
+{
+    return quantize_impl(T, B, cu, H, d, NULL, x, block, rule, codes, exps);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Hadamard rotation of the score operands ([R] S3 "Rotation, range, and the  */
+/* alternative", Algorithm 1 step 02; [K] S3.4 "Hadamard rotation").          */
+/* ------------------------------------------------------------------------- */
+
+/* Every row (token, head) of x, bf16 [T][H][d] with d a power of two, times
+ * the Sylvester Hadamard matrix H_d (entries (-1)^popcount(i & j), so that
+ * H_d H_d = d I; the 1/sqrt(d) normalisation is left to the softmax scale and
+ * the gradient un-rotation, where it is a power of two: q_r . k_r = d q . k).
+ * Computed as the fast Walsh-Hadamard transform in FP32: stages h = 1, 2, 4,
+ * ..., d/2 in that order, each replacing the pair (a, b) = (x[i], x[i + h]),
+ * i & h == 0, by (a + b, a - b).  FP32 because the rotated values decide the
+ * E4M3 codes, and the kernel forms them in FP32 in the same order. */
+int orc_hadamard_rotate(int T, int H, int d, const uint16_t* x, float* out)
+{
+    if (T < 0 || H < 1 || d < 1 || (d & (d - 1)) != 0) return ORC_EBADARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < (int64_t)T * H; ++r) {
+        float* y = out + (size_t)r * d;
+        for (int c = 0; c < d; ++c) y[c] = (float)orc_bf16_to_f64(x[(size_t)r * d + c]);
+        for (int hh = 1; hh < d; hh <<= 1)
+            for (int i = 0; i < d; ++i)
+                if ((i & hh) == 0) {
+                    float a = y[i], bb = y[i + hh];
+                    y[i] = a + bb;
+                    y[i + hh] = a - bb;
+                }
     }
     return ORC_OK;
 }
