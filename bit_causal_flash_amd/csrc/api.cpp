@@ -19,14 +19,14 @@ constexpr size_t kAlign = 256;
 constexpr int kFwdTile = 128;  // queries per forward work item
 constexpr int kBwdTile = 128;  // keys per backward work item
 constexpr uint32_t kKnownFlags =
-    FLAMIA_CAUSAL | FLAMIA_EXACT | FLAMIA_FP4_SCORE | FLAMIA_DETERMINISTIC;
+    FLAMIA_CAUSAL | FLAMIA_EXACT | FLAMIA_FP4_SCORE | FLAMIA_DETERMINISTIC | FLAMIA_HADAMARD;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Dims {
     int64_t T, B, Hq, Hkv, d;
     float scale;
-    bool causal, deterministic;
+    bool causal, deterministic, rotate;
 };
 
 flamia_status check_seq(const flamia_problem* p)
@@ -74,6 +74,7 @@ flamia_status check_attn(const flamia_problem* p, Dims* out)
     if (st != FLAMIA_OK) return st;
     if (p->flags & ~kKnownFlags) return FLAMIA_ERR_INVALID_ARG;
     if ((p->flags & FLAMIA_FP4_SCORE) && !(p->flags & FLAMIA_EXACT)) return FLAMIA_ERR_INVALID_ARG;
+    if ((p->flags & FLAMIA_HADAMARD) && (p->flags & FLAMIA_EXACT)) return FLAMIA_ERR_UNSUPPORTED;
     if (std::isnan(p->softmax_scale) || std::isinf(p->softmax_scale)) return FLAMIA_ERR_INVALID_ARG;
     out->T = p->total_tokens;
     out->B = p->num_seqs;
@@ -81,6 +82,10 @@ flamia_status check_attn(const flamia_problem* p, Dims* out)
     out->Hkv = p->num_kv_heads;
     out->d = p->head_dim;
     out->scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+    // rotated Q and K: q_r . k_r = d q . k (unnormalised Sylvester matrix), so
+    // every use of the scale takes scale / d (exact: d is a power of two)
+    if (p->flags & FLAMIA_HADAMARD) out->scale /= (float)p->head_dim;
+    out->rotate = (p->flags & FLAMIA_HADAMARD) != 0;
     out->causal = (p->flags & FLAMIA_CAUSAL) != 0;
     out->deterministic = (p->flags & FLAMIA_DETERMINISTIC) != 0;
     // grid limits: items x heads must fit a 1-D launch
@@ -198,9 +203,12 @@ flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_head
     st = check_head_dim(p->head_dim);
     if (st != FLAMIA_OK) return st;
     if (num_heads < 1) return FLAMIA_ERR_INVALID_ARG;
+    const bool rotate = (scale_mode & FLAMIA_SCALE_ROTATE) != 0;
+    scale_mode &= ~(int32_t)FLAMIA_SCALE_ROTATE;
     if (scale_mode != FLAMIA_SCALE_TOKBLOCK32 && scale_mode != FLAMIA_SCALE_PER_TOKEN &&
         scale_mode != FLAMIA_SCALE_NVFP4_16)
         return FLAMIA_ERR_INVALID_ARG;
+    if (rotate && scale_mode == FLAMIA_SCALE_NVFP4_16) return FLAMIA_ERR_INVALID_ARG;
     // 1-D grid of (32-token window, head) workgroups of 256 threads; the
     // E2M1 view launches one thread per 16 features
     if ((int64_t)(p->total_tokens + 31) / 32 * num_heads >= ((int64_t)1 << 24))
@@ -214,6 +222,7 @@ flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_head
     a.B = p->num_seqs;
     a.H = num_heads;
     a.block = scale_mode == FLAMIA_SCALE_PER_TOKEN ? 1 : 32;
+    a.rotate = rotate ? 1 : 0;
     a.cu = p->cu_seqlens;
     a.x = x;
     a.codes = codes;
@@ -276,6 +285,7 @@ flamia_status flamia_attn_fwd(const flamia_problem* p, const uint8_t* q_codes,
     a.v_codes = v_codes;
     a.v_exps = v_exps;
     a.mode = operand_mode(p);
+    a.rotate = d.rotate ? 1 : 0;
     a.q_fp4 = q_fp4;
     a.q_fp4_scales = q_fp4_scales;
     a.k_fp4 = k_fp4;
@@ -323,7 +333,7 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     if (st != FLAMIA_OK) return st;
     // the deterministic dQ pass uses block exponents only; the FP16 view of
     // the Q tile does not fit the workgroup's LDS next to d = 128 tiles
-    if ((p->flags & FLAMIA_EXACT) && d.deterministic) return FLAMIA_ERR_UNSUPPORTED;
+    if ((p->flags & (FLAMIA_EXACT | FLAMIA_HADAMARD)) && d.deterministic) return FLAMIA_ERR_UNSUPPORTED;
     if ((p->flags & FLAMIA_FP4_SCORE) && d.d == 128) return FLAMIA_ERR_UNSUPPORTED;
     if (d.T == 0) return FLAMIA_OK;
     if (!q_codes || !q_exps || !k_codes || !k_exps || !v_codes || !v_exps || !o || !lse ||
@@ -395,6 +405,7 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     a.dk = dk;
     a.dv = dv;
     a.mode = operand_mode(p);
+    a.rotate = d.rotate ? 1 : 0;
     a.q_fp4 = q_fp4;
     a.q_fp4_scales = q_fp4_scales;
     a.k_fp4 = k_fp4;

@@ -541,6 +541,9 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
             lds_barrier();
         }
 
+        // rotated Q and K: dK = dK_r H (the Sylvester matrix, unnormalised;
+        // the softmax scale already carries the 1 / d)
+        if (a.rotate) fwht_cols<NDT>(dk, lane);
         if (kvalid) {
             uint16_t* krp = a.dk + ((size_t)kj * Hkv + hk) * D;
             uint16_t* vrp = a.dv + ((size_t)kj * Hkv + hk) * D;
@@ -768,11 +771,16 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(AttnArgs a)
         if constexpr (FROM_ACC) {
             const float f = ldexpf(a.scale_res, -(int)a.prescale[(size_t)h * T + t]);
             const h8 raw = *(const h8*)(a.dq_acc + row * D + 8 * c);
+            float y[8] = {(float)raw.s0 * f, (float)raw.s1 * f, (float)raw.s2 * f, (float)raw.s3 * f,
+                          (float)raw.s4 * f, (float)raw.s5 * f, (float)raw.s6 * f, (float)raw.s7 * f};
+            // rotated Q and K: dQ = dQ_r H (a row is D / 8 consecutive lanes:
+            // the stride keeps every lane on the same chunk c)
+            if (a.rotate) fwht_row<D>(y, threadIdx.x & 63);
             v4i out;
-            out.x = (int)pack_bf16x2((float)raw.s0 * f, (float)raw.s1 * f);
-            out.y = (int)pack_bf16x2((float)raw.s2 * f, (float)raw.s3 * f);
-            out.z = (int)pack_bf16x2((float)raw.s4 * f, (float)raw.s5 * f);
-            out.w = (int)pack_bf16x2((float)raw.s6 * f, (float)raw.s7 * f);
+            out.x = (int)pack_bf16x2(y[0], y[1]);
+            out.y = (int)pack_bf16x2(y[2], y[3]);
+            out.z = (int)pack_bf16x2(y[4], y[5]);
+            out.w = (int)pack_bf16x2(y[6], y[7]);
             *(v4i*)(a.dq + row * D + 8 * c) = out;
         } else if (t >= ntok) {
             *(v4i*)(a.dq + row * D + 8 * c) = v4i{0, 0, 0, 0};

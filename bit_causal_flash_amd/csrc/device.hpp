@@ -296,6 +296,96 @@ __device__ __forceinline__ uint32_t row_max_transpose(const uint32_t (&x)[16], i
     return max((uint32_t)pr[0], (uint32_t)pr[1]);
 }
 
+// Walsh-Hadamard transform (Sylvester matrix, unnormalised) of a row of D
+// features held by D / 8 consecutive lanes, lane l holding features
+// 8 (l % (D / 8)) .. + 7 in y[0..7]: the butterflies (a, b) -> (a + b, a - b)
+// on feature pairs (i, i + h), i & h == 0, for h = 1, 2, ..., D / 2 in that
+// order (FLAMIA review section 3 "Rotation, range, and the alternative").
+// h = 1, 2, 4 pair values inside a lane; h = 8, 16, 32, 64 pair lanes whose
+// index differs in bit 0, 1, 2, 3: DPP quad permutations for bits 0 and 1, a
+// swizzle for bit 2 and a rotation by 8 inside the 16-lane row for bit 3.
+// The lower element of a pair takes own + partner, the upper one
+// partner - own, so each result is one FP32 addition of the same operands.
+template <int D>
+__device__ __forceinline__ void fwht_row(float (&y)[8], int lane)
+{
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if ((i & h) == 0) {
+                const float p = y[i], q = y[i + h];
+                y[i] = p + q;
+                y[i + h] = p - q;
+            }
+    constexpr int NS = D == 128 ? 4 : 3;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const bool hi = (lane >> s) & 1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int u = __float_as_int(y[i]);
+            int w;
+            if (s == 0) w = __builtin_amdgcn_mov_dpp(u, 0xB1, 0xF, 0xF, false);        // lane ^ 1
+            else if (s == 1) w = __builtin_amdgcn_mov_dpp(u, 0x4E, 0xF, 0xF, false);   // lane ^ 2
+            else if (s == 2) w = __builtin_amdgcn_ds_swizzle(u, 0x101F);               // lane ^ 4
+            else w = __builtin_amdgcn_mov_dpp(u, 0x128, 0xF, 0xF, false);              // lane ^ 8
+            const float t = __int_as_float(w);
+            y[i] = hi ? t - y[i] : y[i] + t;
+        }
+    }
+}
+
+// The same transform along the head dim of MFMA accumulators holding a
+// transposed D-column block: acc[dt][v] of lane l is column 32 dt + 8 (v / 4)
+// + 4 (l / 32) + v % 4 (lane = the other index).  Feature bits 0, 1, 3, 4
+// are bits of v, bit 2 the lane half (exchanged with v_permlane32_swap),
+// bits 5 and 6 the tile index dt.
+template <int NDT>
+__device__ __forceinline__ void fwht_cols(v16f (&acc)[NDT], int lane)
+{
+    const bool upper = lane >= 32;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int vb = 1; vb <= 2; vb <<= 1)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                if ((v & vb) == 0) {
+                    const float p = acc[dt][v], q = acc[dt][v + vb];
+                    acc[dt][v] = p + q;
+                    acc[dt][v + vb] = p - q;
+                }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[dt][v]),
+                                                            __float_as_uint(acc[dt][v]), false, false);
+            const float t = __uint_as_float(upper ? sw[0] : sw[1]);
+            acc[dt][v] = upper ? t - acc[dt][v] : acc[dt][v] + t;
+        }
+#pragma unroll
+        for (int vb = 4; vb <= 8; vb <<= 1)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                if ((v & vb) == 0) {
+                    const float p = acc[dt][v], q = acc[dt][v + vb];
+                    acc[dt][v] = p + q;
+                    acc[dt][v + vb] = p - q;
+                }
+    }
+#pragma unroll
+    for (int hb = 1; hb < NDT; hb <<= 1)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            if ((dt & hb) == 0)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float p = acc[dt][v], q = acc[dt + hb][v];
+                    acc[dt][v] = p + q;
+                    acc[dt + hb][v] = p - q;
+                }
+}
+
 __device__ __forceinline__ int rev4(int i)
 {
     return (int)(__builtin_bitreverse32((uint32_t)i) >> 28);

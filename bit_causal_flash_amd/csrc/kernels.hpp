@@ -9,6 +9,7 @@ namespace flamia {
 
 struct QuantArgs {
     int T, B, H, block;
+    int rotate;          // Hadamard-rotate every row before quantizing (score operands)
     const int32_t* cu;
     const uint16_t* x;   // bf16 [T][H][D]
     uint8_t* codes;      // [T][H][D]
@@ -48,6 +49,7 @@ enum { MODE_BLOCK = 0, MODE_EXACT = 1, MODE_FP4 = 2 };
 struct AttnArgs {
     int T, B, Hq, Hkv, causal;
     int mode;         // MODE_*
+    int rotate;       // Q and K rotated (Hadamard): dQ and dK are rotated back
     float scale;      // softmax scale
     float c2;         // scale * log2(e)
     int scale_exp;    // f = floor(log2 scale)

@@ -58,7 +58,11 @@ __device__ __forceinline__ float group_sum(float x)
     return x;
 }
 
-template <int D, bool PREP>
+// ROT: Q and K of the score path are rotated first, each row times the
+// Sylvester Hadamard matrix (FLAMIA review section 3 "Rotation, range, and
+// the alternative"; jaehun.me section 3.4), in FP32 by the fast transform;
+// the block maxima and codes then come from the rotated values.
+template <int D, bool PREP, bool ROT>
 __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
 {
     constexpr int TPR = D / 8;            // threads per row: 16 bytes of bf16 each
@@ -146,13 +150,32 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
         }
     }
     __syncthreads();
+    // rotated rows (a row is spread over TPR consecutive lanes, 8 features
+    // each; rows that are not owned are zero and stay zero)
+    float yr[ROT ? NPASS : 1][8];
+    if constexpr (ROT) {
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                yr[p][2 * k] = bf16_to_f32((uint16_t)(raw[p][k] & 0xffff));
+                yr[p][2 * k + 1] = bf16_to_f32((uint16_t)((uint32_t)raw[p][k] >> 16));
+            }
+            fwht_row<D>(yr[p], tid & 63);
+        }
+    }
     // block maxima
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
         uint32_t m = 0;
+        if constexpr (ROT) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            m = max(m, max(((uint32_t)raw[p][k] << 16) & 0x7fff0000u, (uint32_t)raw[p][k] & 0x7fff0000u));
+            for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(yr[p][k]) & 0x7fffffffu);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                m = max(m, max(((uint32_t)raw[p][k] << 16) & 0x7fff0000u, (uint32_t)raw[p][k] & 0x7fff0000u));
+        }
         m = group_max<TPR>(m);
         if (bsr[p] >= 0 && chunk == 0) atomicMax(&s_bmax[bsr[p] - w0], m);
     }
@@ -248,10 +271,15 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
         if (mine) {
             e = ceil_exp448(__uint_as_float(s_bmax[bs - w0]));
             float y[8];
+            if constexpr (ROT) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                y[2 * k] = ldexpf(bf16_to_f32((uint16_t)(raw[p][k] & 0xffff)), -e);
-                y[2 * k + 1] = ldexpf(bf16_to_f32((uint16_t)((uint32_t)raw[p][k] >> 16)), -e);
+                for (int k = 0; k < 8; ++k) y[k] = ldexpf(yr[p][k], -e);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    y[2 * k] = ldexpf(bf16_to_f32((uint16_t)(raw[p][k] & 0xffff)), -e);
+                    y[2 * k + 1] = ldexpf(bf16_to_f32((uint16_t)((uint32_t)raw[p][k] >> 16)), -e);
+                }
             }
             lo = cvt4_fp8(y[0], y[1], y[2], y[3]);
             hi = cvt4_fp8(y[4], y[5], y[6], y[7]);
@@ -377,11 +405,13 @@ hipError_t launch_quant(const QuantArgs& a, int D, bool prep, hipStream_t stream
     if (a.T == 0) return hipSuccess;
     const dim3 grid((unsigned)(((a.T + 31) / 32) * a.H));
     if (D == 128) {
-        if (prep) hipLaunchKernelGGL((quant_kernel<128, true>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((quant_kernel<128, false>), grid, dim3(256), 0, stream, a);
+        if (prep) hipLaunchKernelGGL((quant_kernel<128, true, false>), grid, dim3(256), 0, stream, a);
+        else if (a.rotate) hipLaunchKernelGGL((quant_kernel<128, false, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((quant_kernel<128, false, false>), grid, dim3(256), 0, stream, a);
     } else {
-        if (prep) hipLaunchKernelGGL((quant_kernel<64, true>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((quant_kernel<64, false>), grid, dim3(256), 0, stream, a);
+        if (prep) hipLaunchKernelGGL((quant_kernel<64, true, false>), grid, dim3(256), 0, stream, a);
+        else if (a.rotate) hipLaunchKernelGGL((quant_kernel<64, false, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((quant_kernel<64, false, false>), grid, dim3(256), 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -23,10 +23,12 @@ FLAMIA_CAUSAL = 1 << 0
 FLAMIA_EXACT = 1 << 1
 FLAMIA_FP4_SCORE = 1 << 2
 FLAMIA_DETERMINISTIC = 1 << 3
+FLAMIA_HADAMARD = 1 << 4
 
 FLAMIA_SCALE_TOKBLOCK32 = 0
 FLAMIA_SCALE_PER_TOKEN = 1
 FLAMIA_SCALE_NVFP4_16 = 2
+FLAMIA_SCALE_ROTATE = 0x100
 
 EXPORTED = [
     "flamia_quantize_tokblock",

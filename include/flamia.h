@@ -68,7 +68,11 @@ enum {
     FLAMIA_FP4_SCORE = 1u << 2,     /* scores from the E2M1 views of Q and K
                                        (FLAMIA_SCALE_NVFP4_16); requires
                                        FLAMIA_EXACT; backward: head_dim 64 */
-    FLAMIA_DETERMINISTIC = 1u << 3  /* bitwise run-to-run repeatable backward */
+    FLAMIA_DETERMINISTIC = 1u << 3, /* bitwise run-to-run repeatable backward */
+    FLAMIA_HADAMARD = 1u << 4       /* Q and K codes come from the rotated rows
+                                       (FLAMIA_SCALE_ROTATE); not with
+                                       FLAMIA_EXACT, nor with
+                                       FLAMIA_DETERMINISTIC in the backward */
 };
 
 /* Quantizer scale policies. */
@@ -76,8 +80,10 @@ enum {
     FLAMIA_SCALE_TOKBLOCK32 = 0, /* one exponent per document-local block of
                                     <= 32 tokens x full head dim */
     FLAMIA_SCALE_PER_TOKEN = 1,  /* one exponent per token x full head dim */
-    FLAMIA_SCALE_NVFP4_16 = 2    /* score view: E2M1 codes + an E4M3 scale per
+    FLAMIA_SCALE_NVFP4_16 = 2,   /* score view: E2M1 codes + an E4M3 scale per
                                     16 in-token features */
+    FLAMIA_SCALE_ROTATE = 0x100  /* OR-ed into TOKBLOCK32 or PER_TOKEN: rotate
+                                    every row by the Hadamard matrix first */
 };
 
 /* Optional timing hook: hipEvent_t handles the library records on the call's
@@ -124,7 +130,16 @@ typedef struct {
  *   p          problem; only total_tokens, num_seqs and cu_seqlens are read
  *   num_heads  H >= 1 of this tensor (Hq for Q, Hkv for K and V)
  *   scale_mode FLAMIA_SCALE_TOKBLOCK32, FLAMIA_SCALE_PER_TOKEN or
- *              FLAMIA_SCALE_NVFP4_16
+ *              FLAMIA_SCALE_NVFP4_16; the first two may be OR-ed with
+ *              FLAMIA_SCALE_ROTATE (review section 3 "Rotation, range, and
+ *              the alternative", Algorithm 1 step 02; jaehun.me section 3.4):
+ *              every row x (d features) is first replaced by x H_d, H_d the
+ *              Sylvester Hadamard matrix (entries (-1)^popcount(i & j),
+ *              H_d H_d = d I), computed in FP32 by the fast Walsh-Hadamard
+ *              transform (butterflies (a, b) -> (a + b, a - b) for pair
+ *              distances 1, 2, ..., d / 2 in that order); the block maxima and
+ *              codes are those of the rotated values.  For Q and K of a
+ *              FLAMIA_HADAMARD problem.
  *   x          bf16 [T][H][d] (device, read)
  *   codes      uint8 [T][H][d] (device, written)
  *   exps       uint8 [H][T] (device, written)
@@ -158,6 +173,10 @@ flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_head
  * E2M1 views (q_fp4 / k_fp4: codes uint8 [T][H][d/2], scales uint8
  * [T][H][d/16], as FLAMIA_SCALE_NVFP4_16 writes them); the fp4 pointers must
  * be NULL without the flag and non-NULL with it.
+ * With FLAMIA_HADAMARD the Q and K codes must be those of the rotated rows
+ * (FLAMIA_SCALE_ROTATE): since q H . k H = d q . k, the softmax scale is
+ * divided by d, and O and LSE are those of the unrotated problem up to
+ * rounding.
  */
 size_t flamia_attn_fwd_workspace_size(const flamia_problem* p);
 flamia_status flamia_attn_fwd(const flamia_problem* p, const uint8_t* q_codes,
@@ -188,6 +207,9 @@ flamia_status flamia_attn_fwd(const flamia_problem* p, const uint8_t* q_codes,
  *   workspace  at least flamia_attn_bwd_workspace_size(p) bytes; it holds the
  *              quantized dO, D, k_i, the FP16 dQ accumulator and work lists,
  *              at the offsets flamia_attn_bwd_workspace_layout reports.
+ * FLAMIA_HADAMARD: Q and K codes of the rotated rows; the gradient products
+ * use them at softmax scale / d, and dQ, dK are taken back to the original
+ * coordinates (times H_d) before they are written.
  * FLAMIA_EXACT (review section 4; jaehun.me section 3.2): dO is quantized per
  * token; the dO, Q and K exponents, which vary along the contractions of
  * dV, dK and dQ, are folded into P^, dS^ (dK copy) and dS^ (dQ copy) before

@@ -82,6 +82,18 @@ def test_invalid_arguments_rejected_before_launch():
     # score path covers head_dim 64 only
     det_exact = F.FLAMIA_CAUSAL | F.FLAMIA_EXACT | F.FLAMIA_DETERMINISTIC
     assert bwd(P(_problem(flags=det_exact)), *args16, vp, wsb, None) == F.FLAMIA_ERR_UNSUPPORTED
+    # the Hadamard option: not with the exact-scale option, and no
+    # deterministic backward; the rotation bit only with the E4M3 policies
+    had = F.FLAMIA_CAUSAL | F.FLAMIA_HADAMARD
+    assert fwd(P(_problem(flags=had | F.FLAMIA_EXACT)), *args12, vp, ws, None) == \
+        F.FLAMIA_ERR_UNSUPPORTED
+    assert bwd(P(_problem(flags=had | F.FLAMIA_DETERMINISTIC)), *args16, vp, wsb, None) == \
+        F.FLAMIA_ERR_UNSUPPORTED
+    q = lib.flamia_quantize_tokblock
+    assert q(P(_problem()), 1, F.FLAMIA_SCALE_NVFP4_16 | F.FLAMIA_SCALE_ROTATE, vp, vp, vp, None) == \
+        F.FLAMIA_ERR_INVALID_ARG
+    assert q(P(_problem()), 1, 5 | F.FLAMIA_SCALE_ROTATE, vp, vp, vp, None) == F.FLAMIA_ERR_INVALID_ARG
+    assert q(P(_problem(T=0)), 1, F.FLAMIA_SCALE_ROTATE, None, None, None, None) == F.FLAMIA_OK
     with4 = [vp] * 16
     assert bwd(P(_problem(d=128, flags=fp4_flags)), *with4, vp,
                F.flamia_attn_bwd_workspace_size(_problem(d=128, flags=fp4_flags)), None) == \
