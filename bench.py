@@ -97,7 +97,7 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes": mib << 20, "copies": 3}), flush=True)
 
 
-def cpu_baseline(w, flop_target=3e11):
+def cpu_baseline(w, flop_target=3e11, hadamard=False):
     """The FP64 oracle on a bounded sample of the same workload: the first q
     heads (whole kv groups), every document, quantize + forward + backward,
     sized to about `flop_target` algorithmic FLOPs (10-30 s on a host)."""
@@ -114,16 +114,24 @@ def cpu_baseline(w, flop_target=3e11):
     exact = bool(w.flags & workloads.FLAG_EXACT)
     blk = 1 if exact else 32
     t0 = time.time()
-    q, k, v = (oracle.quantize(x, sub.cu, block=blk) for x in (sub.q, sub.k, sub.v))
+    if hadamard:
+        q, k = (oracle.quantize_rotated(x, sub.cu, block=blk) for x in (sub.q, sub.k))
+        v = oracle.quantize(sub.v, sub.cu, block=blk)
+    else:
+        q, k, v = (oracle.quantize(x, sub.cu, block=blk) for x in (sub.q, sub.k, sub.v))
+    scale = oracle.default_scale(w.d) / (w.d if hadamard else 1)
     views = (None, None)
     if w.flags & workloads.FLAG_FP4_SCORE:
         views = (oracle.quantize_nvfp4(sub.q, sub.cu), oracle.quantize_nvfp4(sub.k, sub.cu))
     ops = oracle.Operands.from_codes(q, k, v, *views)
-    O, L = oracle.attn_fwd(sub.cu, ops, mode=oracle.MODE_TILED, kblock=64)
-    gc, ge, D, _ = oracle.bwd_prep(sub.cu, sub.do, oracle.to_bf16(O), k[1], v[1], nkv, block=blk)
+    O, L = oracle.attn_fwd(sub.cu, ops, scale=scale, mode=oracle.MODE_TILED, kblock=64)
+    gc, ge, D, _ = oracle.bwd_prep(sub.cu, sub.do, oracle.to_bf16(O), k[1], v[1], nkv, scale=scale,
+                                   block=blk)
     Gd = oracle.dequantize(gc, ge)
-    oracle.bwd_dq(sub.cu, ops, Gd, D, L, per_row_ds=exact)
-    oracle.bwd_dkdv(sub.cu, ops, Gd, D, L, per_row_ds=exact)
+    dq = oracle.bwd_dq(sub.cu, ops, Gd, D, L, scale=scale, per_row_ds=exact)
+    dk, _ = oracle.bwd_dkdv(sub.cu, ops, Gd, D, L, scale=scale, per_row_ds=exact)
+    if hadamard:
+        oracle.unrotate(dq), oracle.unrotate(dk)
     dt = time.time() - t0
     flop = 14.0 * w.d * nh * w.visible_pairs()
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
@@ -139,6 +147,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="packed_mha", choices=sorted(workloads.NAMED))
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--hadamard", action="store_true",
+                    help="rotate Q and K by the Hadamard matrix (FLAMIA_HADAMARD)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB (traffic counter reference)")
@@ -178,14 +188,16 @@ def main():
     exact = bool(w.flags & workloads.FLAG_EXACT)
     fp4 = bool(w.flags & workloads.FLAG_FP4_SCORE)
     flags = F.FLAMIA_CAUSAL | (F.FLAMIA_EXACT if exact else 0) | (F.FLAMIA_FP4_SCORE if fp4 else 0)
+    flags |= F.FLAMIA_HADAMARD if args.hadamard else 0
     mode = F.FLAMIA_SCALE_PER_TOKEN if exact else F.FLAMIA_SCALE_TOKBLOCK32
+    qk_mode = mode | (F.FLAMIA_SCALE_ROTATE if args.hadamard else 0)
     pq = F.make_problem(cu, T, Hq, Hkv, d, 0.0, flags)
     pf = F.make_problem(cu, T, Hq, Hkv, d, 0.0, flags)
     pb = F.make_problem(cu, T, Hq, Hkv, d, 0.0, flags)
     wsf = torch.empty(F.flamia_attn_fwd_workspace_size(pf), **u8)
     wsb = torch.empty(F.flamia_attn_bwd_workspace_size(pb), **u8)
 
-    qargs = [(Hq, xq, qc, qe, mode), (Hkv, xk, kc, ke, mode), (Hkv, xv, vc, ve, mode)]
+    qargs = [(Hq, xq, qc, qe, qk_mode), (Hkv, xk, kc, ke, qk_mode), (Hkv, xv, vc, ve, mode)]
     views = None
     if fp4:
         q4, k4 = (torch.empty((T, h, d // 2), **u8) for h in (Hq, Hkv))
@@ -258,8 +270,8 @@ def main():
     F.set_events(pq, None, None)
     ms_qkern = sum(hip.elapsed_ms(a, b) for ev in evq for a, b in ev) / K
     ms_attn = timed(lambda: (fwd(), bwd()), K)
-    ms_bwd_det = None  # the exact-scale backward has no deterministic variant
-    if not exact:
+    ms_bwd_det = None  # the exact-scale and rotated backwards have no deterministic variant
+    if not exact and not args.hadamard:
         pdet = F.make_problem(cu, T, Hq, Hkv, d, 0.0, F.FLAMIA_CAUSAL | F.FLAMIA_DETERMINISTIC)
         wsd = torch.empty(F.flamia_attn_bwd_workspace_size(pdet), **u8)
         ms_bwd_det = timed(lambda: F.flamia_attn_bwd(pdet, qc, qe, kc, ke, vc, ve, o, lse, xdo, dq,
@@ -294,6 +306,7 @@ def main():
                               "exponents for dQ" if exact else
                               "one exponent per 32 tokens x head dim, per 32x32 block for dS"),
                    "score_view": "E2M1 + E4M3 per 16 features (FP16 MFMA)" if fp4 else None,
+                   "rotation": "Hadamard on Q, K (scale / d; dQ, dK rotated back)" if args.hadamard else None,
                    "step": "quantize Q,K,V%s + attn fwd + attn bwd" %
                            (" (+ E2M1 views of Q,K)" if fp4 else "")},
         "pct_fp8_peak": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
@@ -314,10 +327,11 @@ def main():
             "quantize_kernel_frac_hbm_peak": round(qbytes / (ms_qkern * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         },
     }
-    out["roofline"]["traffic"] = measured_traffic(w.name)
+    # counters were taken without the rotation epilogue
+    out["roofline"]["traffic"] = None if args.hadamard else measured_traffic(w.name)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, hadamard=args.hadamard)
     print(json.dumps(out), flush=True)
 
 

@@ -321,7 +321,8 @@ __device__ __forceinline__ void fwht_row(float (&y)[8], int lane)
     constexpr int NS = D == 128 ? 4 : 3;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        const bool hi = (lane >> s) & 1;
+        // fma(y, -1, t) = t - y and fma(y, 1, t) = y + t, each rounded once
+        const float sgn = ((lane >> s) & 1) ? -1.f : 1.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int u = __float_as_int(y[i]);
@@ -330,8 +331,7 @@ __device__ __forceinline__ void fwht_row(float (&y)[8], int lane)
             else if (s == 1) w = __builtin_amdgcn_mov_dpp(u, 0x4E, 0xF, 0xF, false);   // lane ^ 2
             else if (s == 2) w = __builtin_amdgcn_ds_swizzle(u, 0x101F);               // lane ^ 4
             else w = __builtin_amdgcn_mov_dpp(u, 0x128, 0xF, 0xF, false);              // lane ^ 8
-            const float t = __int_as_float(w);
-            y[i] = hi ? t - y[i] : y[i] + t;
+            y[i] = fmaf(y[i], sgn, __int_as_float(w));
         }
     }
 }

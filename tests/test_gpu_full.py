@@ -134,3 +134,69 @@ def test_exact_option_full_size_sampled():
         kmask[t0:t0 + 32, hk] = True
     check_grad(g["dK"], dK, w.name + " dK", tk, rows=kmask, absm=ak)
     check_grad(g["dV"], dV, w.name + " dV", tv, rows=kmask, absm=av)
+
+
+@pytest.mark.timeout(600)
+def test_hadamard_full_size_sampled():
+    """The packed MHA workload with the Hadamard option at full size, in the
+    benchmark's launch configuration: rotated codes and exponents in full,
+    forward rows and backward blocks sampled against the oracle on the same
+    rotated codes at scale / d, gradients rotated back."""
+    import torch
+    from bit_causal_flash_amd import flamia as F
+    from tests.gpu_helpers import dev, host
+    w = workloads.NAMED["packed_mha"](0)
+    log("workload %s with the Hadamard rotation" % w.name)
+    d, Hq, Hkv, T = w.d, w.Hq, w.Hkv, w.T
+    p = F.make_problem(dev(w.cu.astype(np.int32)), T, Hq, Hkv, d, 0.0, F.FLAMIA_CAUSAL | F.FLAMIA_HADAMARD)
+    x = {n: dev(getattr(w, n).view(np.int16)) for n in ("q", "k", "v", "do")}
+    rot = F.FLAMIA_SCALE_TOKBLOCK32 | F.FLAMIA_SCALE_ROTATE
+    q, k, v = F.quantize(p, x["q"], Hq, rot), F.quantize(p, x["k"], Hkv, rot), F.quantize(p, x["v"], Hkv)
+    o, lse = F.attn_fwd(p, q, k, v)
+    dq, dk, dv, ws = F.attn_bwd(p, q, k, v, o, lse, x["do"].view(torch.bfloat16))
+    torch.cuda.synchronize()
+    log("gpu done")
+    rq, rk, rv = oracle.quantize_rotated(w.q, w.cu), oracle.quantize_rotated(w.k, w.cu), oracle.quantize(w.v, w.cu)
+    for tag, got, ref in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        assert np.array_equal(host(got[0]), ref[0]) and np.array_equal(host(got[1]), ref[1]), tag
+    log("codes bit-exact")
+    s = oracle.default_scale(d) / d
+    ops = oracle.Operands.from_codes(rq, rk, rv)
+    rng = np.random.default_rng(4)
+    toks = _sample_tokens(w.cu, rng, per_doc=6)
+    heads = list(rng.choice(Hq, 5, replace=False))
+    rows = np.array([(h, t) for h in heads for t in toks], dtype=np.int32)
+    O, L, ties = oracle.attn_fwd(w.cu, ops, scale=s, rows=rows, mode=oracle.MODE_TILED, kblock=64,
+                                 want_flags=True)
+    Og, Lg = host(o).view(np.uint16), host(lse)
+    mask = np.zeros((T, Hq), dtype=bool)
+    mask[rows[:, 1], rows[:, 0]] = True
+    check_fwd(Og[mask], Lg.T[mask], O[mask], L.T[mask], ties.transpose(1, 0, 2)[mask], tag="hadamard")
+    log("forward ok")
+    gc, ge, D, kpre = oracle.bwd_prep(w.cu, w.do, Og, rk[1], rv[1], Hkv, scale=s)
+    G = oracle.dequantize(gc, ge)
+    lse64 = Lg.astype(np.float64)
+    qstarts = oracle.doc_blocks(w.cu, toks)
+    qblocks = np.array([(h, t0) for h in heads for t0 in qstarts], dtype=np.int32)
+    dQr, tq, acc, aq = oracle.bwd_dq(w.cu, ops, G, D, lse64, scale=s, qblocks=qblocks, want_flags=True)
+    nt = np.repeat(dq_tiles(w.cu, T, True)[:, None], Hq, axis=1)
+    qmask = np.zeros((T, Hq), dtype=bool)
+    for h, t0 in qblocks:
+        b = int(np.searchsorted(w.cu, t0, side="right") - 1)
+        qmask[t0:min(t0 + 32, int(w.cu[b + 1])), h] = True
+    # rows are rotated back whole, so the sampled blocks' rows are exact;
+    # per-row allowances grow by at most d under the rotation
+    check_grad(host(dq).view(np.uint16), oracle.unrotate(dQr), "hadamard dQ", d * tq, rows=qmask,
+               acc=d * acc, ntiles=nt, absm=d * aq)
+    kheads = sorted(set(h * Hkv // Hq for h in heads))[:3]
+    kstarts = qstarts[:: max(1, len(qstarts) // 10)]
+    kblocks = np.array([(hk, t0) for hk in kheads for t0 in kstarts], dtype=np.int32)
+    dKr, dV, tk, tv, ak, av = oracle.bwd_dkdv(w.cu, ops, G, D, lse64, scale=s, kblocks=kblocks,
+                                              want_flags=True)
+    kmask = np.zeros((T, Hkv), dtype=bool)
+    for hk, t0 in kblocks:
+        b = int(np.searchsorted(w.cu, t0, side="right") - 1)
+        kmask[t0:min(t0 + 32, int(w.cu[b + 1])), hk] = True
+    check_grad(host(dk).view(np.uint16), oracle.unrotate(dKr), "hadamard dK", d * tk, rows=kmask,
+               absm=d * ak)
+    check_grad(host(dv).view(np.uint16), dV, "hadamard dV", tv, rows=kmask, absm=av)
