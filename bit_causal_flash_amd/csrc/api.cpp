@@ -204,11 +204,12 @@ flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_head
     if (st != FLAMIA_OK) return st;
     if (num_heads < 1) return FLAMIA_ERR_INVALID_ARG;
     const bool rotate = (scale_mode & FLAMIA_SCALE_ROTATE) != 0;
-    scale_mode &= ~(int32_t)FLAMIA_SCALE_ROTATE;
+    const bool floor_rule = (scale_mode & FLAMIA_SCALE_FLOOR_CONTROL) != 0;
+    scale_mode &= ~(int32_t)(FLAMIA_SCALE_ROTATE | FLAMIA_SCALE_FLOOR_CONTROL);
     if (scale_mode != FLAMIA_SCALE_TOKBLOCK32 && scale_mode != FLAMIA_SCALE_PER_TOKEN &&
         scale_mode != FLAMIA_SCALE_NVFP4_16)
         return FLAMIA_ERR_INVALID_ARG;
-    if (rotate && scale_mode == FLAMIA_SCALE_NVFP4_16) return FLAMIA_ERR_INVALID_ARG;
+    if ((rotate || floor_rule) && scale_mode == FLAMIA_SCALE_NVFP4_16) return FLAMIA_ERR_INVALID_ARG;
     // 1-D grid of (32-token window, head) workgroups of 256 threads; the
     // E2M1 view launches one thread per 16 features
     if ((int64_t)(p->total_tokens + 31) / 32 * num_heads >= ((int64_t)1 << 24))
@@ -223,6 +224,7 @@ flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_head
     a.H = num_heads;
     a.block = scale_mode == FLAMIA_SCALE_PER_TOKEN ? 1 : 32;
     a.rotate = rotate ? 1 : 0;
+    a.floor_rule = floor_rule ? 1 : 0;
     a.cu = p->cu_seqlens;
     a.x = x;
     a.codes = codes;

@@ -10,6 +10,7 @@ namespace flamia {
 struct QuantArgs {
     int T, B, H, block;
     int rotate;          // Hadamard-rotate every row before quantizing (score operands)
+    int floor_rule;      // floor exponent rule (negative control for the causality tests)
     const int32_t* cu;
     const uint16_t* x;   // bf16 [T][H][D]
     uint8_t* codes;      // [T][H][D]

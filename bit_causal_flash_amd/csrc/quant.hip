@@ -58,6 +58,21 @@ __device__ __forceinline__ float group_sum(float x)
     return x;
 }
 
+// The floor rule of the reference MX conversion (jaehun.me section 2):
+// e = floor(log2 amax) - 8, clamped to [-127, 127], 0 for amax == 0.  It can
+// push amax / 2^e past 448 (the codes then saturate), so a later token of the
+// same block can change an earlier token's value: a negative control for the
+// causality tests, never the method's rule.
+__device__ __forceinline__ int floor_exp_e4m3(float amax)
+{
+    const uint32_t u = __float_as_uint(amax) & 0x7fffffffu;
+    if (u == 0) return 0;
+    const uint32_t bexp = u >> 23;
+    const int E = bexp != 0 ? (int)bexp - 127 : -126 - ((int)__clz(u) - 8);
+    const int e = E - 8;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
 // ROT: Q and K of the score path are rotated first, each row times the
 // Sylvester Hadamard matrix (FLAMIA review section 3 "Rotation, range, and
 // the alternative"; jaehun.me section 3.4), in FP32 by the fast transform;
@@ -269,7 +284,8 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
         int e = 0;
         float dot = 0.f;
         if (mine) {
-            e = ceil_exp448(__uint_as_float(s_bmax[bs - w0]));
+            e = a.floor_rule ? floor_exp_e4m3(__uint_as_float(s_bmax[bs - w0]))
+                             : ceil_exp448(__uint_as_float(s_bmax[bs - w0]));
             float y[8];
             if constexpr (ROT) {
 #pragma unroll
@@ -280,6 +296,10 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
                     y[2 * k] = ldexpf(bf16_to_f32((uint16_t)(raw[p][k] & 0xffff)), -e);
                     y[2 * k + 1] = ldexpf(bf16_to_f32((uint16_t)((uint32_t)raw[p][k] >> 16)), -e);
                 }
+            }
+            if (a.floor_rule) {  // saturate what the floor rule pushes past 448
+#pragma unroll
+                for (int k = 0; k < 8; ++k) y[k] = fminf(fmaxf(y[k], -448.f), 448.f);
             }
             lo = cvt4_fp8(y[0], y[1], y[2], y[3]);
             hi = cvt4_fp8(y[4], y[5], y[6], y[7]);

@@ -29,6 +29,7 @@ FLAMIA_SCALE_TOKBLOCK32 = 0
 FLAMIA_SCALE_PER_TOKEN = 1
 FLAMIA_SCALE_NVFP4_16 = 2
 FLAMIA_SCALE_ROTATE = 0x100
+FLAMIA_SCALE_FLOOR_CONTROL = 0x200
 
 EXPORTED = [
     "flamia_quantize_tokblock",

@@ -82,8 +82,15 @@ enum {
     FLAMIA_SCALE_PER_TOKEN = 1,  /* one exponent per token x full head dim */
     FLAMIA_SCALE_NVFP4_16 = 2,   /* score view: E2M1 codes + an E4M3 scale per
                                     16 in-token features */
-    FLAMIA_SCALE_ROTATE = 0x100  /* OR-ed into TOKBLOCK32 or PER_TOKEN: rotate
+    FLAMIA_SCALE_ROTATE = 0x100, /* OR-ed into TOKBLOCK32 or PER_TOKEN: rotate
                                     every row by the Hadamard matrix first */
+    FLAMIA_SCALE_FLOOR_CONTROL = 0x200 /* OR-ed into TOKBLOCK32 or PER_TOKEN:
+                                    the reference floor exponent rule
+                                    e = floor(log2 amax) - 8 with saturation
+                                    at 448 (jaehun.me section 2), which can
+                                    leak a later token of a block into an
+                                    earlier one's value.  A negative control
+                                    for causality tests only. */
 };
 
 /* Optional timing hook: hipEvent_t handles the library records on the call's

@@ -94,6 +94,8 @@ def test_invalid_arguments_rejected_before_launch():
         F.FLAMIA_ERR_INVALID_ARG
     assert q(P(_problem()), 1, 5 | F.FLAMIA_SCALE_ROTATE, vp, vp, vp, None) == F.FLAMIA_ERR_INVALID_ARG
     assert q(P(_problem(T=0)), 1, F.FLAMIA_SCALE_ROTATE, None, None, None, None) == F.FLAMIA_OK
+    assert q(P(_problem()), 1, F.FLAMIA_SCALE_NVFP4_16 | F.FLAMIA_SCALE_FLOOR_CONTROL, vp, vp, vp,
+             None) == F.FLAMIA_ERR_INVALID_ARG
     with4 = [vp] * 16
     assert bwd(P(_problem(d=128, flags=fp4_flags)), *with4, vp,
                F.flamia_attn_bwd_workspace_size(_problem(d=128, flags=fp4_flags)), None) == \

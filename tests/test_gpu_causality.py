@@ -91,3 +91,110 @@ def test_other_document_negative_control():
     for k in ("O", "dQ", "dK", "dV"):
         assert np.array_equal(a[k][:77], b[k][:77]), k
     assert np.array_equal(a["LSE"][:, :77], b["LSE"][:, :77])
+
+
+FLOOR = 0x200  # FLAMIA_SCALE_FLOOR_CONTROL
+
+
+@pytest.mark.parametrize("per_token", [False, True])
+def test_floor_rule_control_codes_bit_exact(per_token):
+    """The test-only floor rule (jaehun.me section 2) on the GPU, including
+    block maxima that it clips, against the oracle's rule 1."""
+    import torch
+    from bit_causal_flash_amd import flamia as F
+    from tests.gpu_helpers import dev, host
+    rng = np.random.default_rng(13)
+    T, H, d = 200, 2, 64
+    x = rng.standard_normal((T, H, d)).astype(np.float32)
+    x[5, 0, 3] = 15.0      # mantissa 1.875: clipped by the floor rule
+    x[77, 1, 9] = -30.0
+    x[100:104] *= np.float32(1e-30)
+    bits = workloads.f32_to_bf16_bits(x)
+    cu = np.array([0, 45, 190], np.int32)
+    log("case floor rule per_token=%s" % per_token)
+    p = F.make_problem(dev(cu), T, H, H, d, 0.0, F.FLAMIA_CAUSAL)
+    mode = (F.FLAMIA_SCALE_PER_TOKEN if per_token else 0) | FLOOR
+    codes, exps = F.quantize(p, dev(bits.view(np.int16)), H, mode)
+    torch.cuda.synchronize()
+    rc, re = oracle.quantize(bits, cu, block=1 if per_token else 32, rule=1)
+    assert np.array_equal(host(codes), rc) and np.array_equal(host(exps), re)
+
+
+def _value_leak(rule_mode):
+    # one document, d = 64; V of token 3 holds 480 and token 20 of the same
+    # block is raised to 900; all other values are integers in [1, 16]
+    T, d = 32, 64
+    rng = np.random.default_rng(6)
+    q = np.zeros((T, 1, d), np.float32)
+    k = np.zeros((T, 1, d), np.float32)
+    v = rng.integers(1, 17, (T, 1, d)).astype(np.float32)
+    v[3, 0, 0] = 480.0
+    do = np.ones((T, 1, d), np.float32)
+    cu = np.array([0, T], dtype=np.int32)
+    v2 = v.copy()
+    v2[20, 0, 0] = 900.0
+    out = []
+    for vv in (v, v2):
+        w = workloads.Workload("leak", T, cu, 1, 1, d, workloads.FLAG_CAUSAL,
+                               workloads.f32_to_bf16_bits(q), workloads.f32_to_bf16_bits(k),
+                               workloads.f32_to_bf16_bits(vv), workloads.f32_to_bf16_bits(do))
+        out.append(run_gpu(w, flags=DET, scale_mode=rule_mode))
+    return out
+
+
+def test_floor_rule_positive_control_leaks_and_ceil_rule_does_not():
+    """Token 20 of a block moves query 5's output under the floor rule (its
+    value 480 is clipped to 448 before and exact after), never under the
+    method's conservative rule."""
+    a, b = _value_leak(FLOOR)
+    assert not np.array_equal(a["O"][5], b["O"][5])
+    a, b = _value_leak(0)
+    assert np.array_equal(a["O"][:20], b["O"][:20])
+    assert np.array_equal(a["LSE"][:, :20], b["LSE"][:, :20])
+    assert np.array_equal(a["dQ"][:20], b["dQ"][:20])
+
+
+def _rel_change(a, b, rows):
+    a = oracle.bf16_to_float(a[rows]).reshape(len(range(*rows.indices(a.shape[0]))), -1)
+    b = oracle.bf16_to_float(b[rows]).reshape(a.shape)
+    den = np.maximum(np.abs(a).max(axis=1), 1e-30)
+    return float((np.abs(a - b).max(axis=1) / den).max())
+
+
+def test_leak_probe_table5():
+    """A Table-5-style probe (review section 9, "Separate numerical closeness,
+    invariance, and training quality"): a later token of a block is raised so
+    that the block's maximum, and with it the scale, changes; report the
+    largest relative change of the outputs and dQ rows of every earlier
+    query.  The block's earlier maximum (15 = 1.875 * 2^3) is clipped by the
+    floor rule at the old scale and exact at the new one.  Method rule: earlier
+    blocks bit-identical, earlier rows of the same block unchanged up to the
+    subnormal lattice shift; floor rule (control): a visible change; the
+    exact option (per-token scales): every earlier row bit-identical."""
+    lens, cap = [300, 190], 500
+    res = {}
+    for tag, mode in (("ceil", 0), ("floor", FLOOR), ("exact", 1)):
+        flags = (1 | 2) if tag == "exact" else DET  # the exact option: per-token scales
+        runs = []
+        for perturb in (False, True):
+            w = _make(lens, cap, Hq=2, Hkv=2, d=128)
+            for name in ("k", "v"):
+                f = workloads.bf16_bits_to_f32(getattr(w, name)).copy()
+                f[70, :, 0] = 15.0
+                if perturb:
+                    f[84, :, 0] = 31.0
+                setattr(w, name, workloads.f32_to_bf16_bits(f))
+            runs.append(run_gpu(w, flags=flags, scale_mode=mode))
+        a, b = runs
+        res[tag] = {"O earlier blocks": _rel_change(a["O"], b["O"], slice(0, 64)),
+                    "O same block": _rel_change(a["O"], b["O"], slice(70, 84))}
+        if tag != "exact":  # its dQ is accumulated by atomics: not run-to-run exact
+            res[tag].update({"dQ earlier blocks": _rel_change(a["dQ"], b["dQ"], slice(0, 64)),
+                             "dQ same block": _rel_change(a["dQ"], b["dQ"], slice(70, 84))})
+        log("leak probe, %s rule: %s" % (tag, res[tag]))
+    assert res["ceil"]["O earlier blocks"] == 0.0 and res["ceil"]["dQ earlier blocks"] == 0.0
+    assert res["floor"]["O earlier blocks"] == 0.0
+    assert res["floor"]["O same block"] > 1e-3
+    assert res["ceil"]["O same block"] <= 1e-2 * res["floor"]["O same block"]
+    # per-token scales: no earlier output depends on a later token at all
+    assert res["exact"]["O earlier blocks"] == 0.0 and res["exact"]["O same block"] == 0.0
