@@ -297,8 +297,7 @@ flamia_status flamia_attn_fwd(const flamia_problem* p, const uint8_t* q_codes,
     if (record(p, true, s) != hipSuccess) return FLAMIA_ERR_HIP;
     e = launch_fwd(a, (int)d.d, w.max_items, s);
     if (e != hipSuccess) return FLAMIA_ERR_HIP;
-    if (record(p, false, s) != hipSuccess) return FLAMIA_ERR_HIP;
-    return hip_status(launch_fwd_padding(a, (int)d.d, s));
+    return hip_status(record(p, false, s));
 }
 
 size_t flamia_attn_bwd_workspace_size(const flamia_problem* p)

@@ -151,9 +151,32 @@ __device__ __forceinline__ void online_softmax(v16f (&sacc)[2], v16f (&oacc)[NDT
 // Modes: MODE_BLOCK token-block operands; MODE_EXACT per-token exponents (the
 // V exponent folded into P^); MODE_FP4 the same with S from the E2M1 score
 // views of Q and K, expanded to exact FP16 and contracted by the FP16 MFMA.
+// Rows after the last document (t >= cu[B]): O = 0, LSE = +inf, written by
+// kFwdPadWgs extra workgroups of the forward launch.
+constexpr int kFwdPadWgs = 64;
+
+template <int D>
+__device__ void fwd_padding(const AttnArgs& a, int wg)
+{
+    const int ntok = a.cu[a.B];
+    const size_t T = (size_t)a.T;
+    const size_t first = (size_t)ntok * a.Hq * (D / 8);
+    const size_t nchunks = T * a.Hq * (D / 8);
+    for (size_t i = first + (size_t)wg * 256 + threadIdx.x; i < nchunks; i += (size_t)kFwdPadWgs * 256) {
+        const size_t row = i / (D / 8);
+        const int t = (int)(row / a.Hq), h = (int)(row % a.Hq);
+        *(v4i*)(a.o + row * D + 8 * (i % (D / 8))) = v4i{0, 0, 0, 0};
+        if (i % (D / 8) == 0) a.lse[(size_t)h * T + t] = INFINITY;
+    }
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
 {
+    if ((int)blockIdx.x >= a.work_wgs) {
+        fwd_padding<D>(a, (int)blockIdx.x - a.work_wgs);
+        return;
+    }
     constexpr int PITCH = D + 16;      // LDS row pitch (bytes): spreads rows over banks
     constexpr int PITCH16 = 2 * D + 16;
     constexpr int NKS = D / 64;        // k steps over the head dim (E4M3 S)
@@ -325,30 +348,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
     }
 }
 
-// Rows after the last document: O = 0, LSE = +inf.
-template <int D>
-__global__ __launch_bounds__(256) void fwd_padding_kernel(AttnArgs a)
-{
-    const int ntok = a.cu[a.B];
-    const size_t T = (size_t)a.T;
-    const size_t nchunks = (size_t)a.T * a.Hq * (D / 8);
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < nchunks;
-         i += (size_t)gridDim.x * 256) {
-        const size_t row = i / (D / 8);
-        const int t = (int)(row / a.Hq), h = (int)(row % a.Hq);
-        if (t < ntok) continue;
-        *(v4i*)(a.o + row * D + 8 * (i % (D / 8))) = v4i{0, 0, 0, 0};
-        if (i % (D / 8) == 0) a.lse[(size_t)h * T + t] = INFINITY;
-    }
-}
-
 }  // namespace
 
 hipError_t launch_fwd(const AttnArgs& a, int D, int max_items, hipStream_t stream)
 {
     if (max_items <= 0) return hipSuccess;
-    const dim3 grid((unsigned)max_items * a.Hq);
-#define FLAMIA_FWD(DD, MM) hipLaunchKernelGGL((fwd_kernel<DD, MM>), grid, dim3(256), 0, stream, a)
+    AttnArgs args = a;
+    args.work_wgs = max_items * a.Hq;
+    const dim3 grid((unsigned)(args.work_wgs + kFwdPadWgs));
+#define FLAMIA_FWD(DD, MM) hipLaunchKernelGGL((fwd_kernel<DD, MM>), grid, dim3(256), 0, stream, args)
     if (D == 128) {
         if (a.mode == MODE_FP4) FLAMIA_FWD(128, MODE_FP4);
         else if (a.mode == MODE_EXACT) FLAMIA_FWD(128, MODE_EXACT);
@@ -359,16 +367,6 @@ hipError_t launch_fwd(const AttnArgs& a, int D, int max_items, hipStream_t strea
         else FLAMIA_FWD(64, MODE_BLOCK);
     }
 #undef FLAMIA_FWD
-    return hipGetLastError();
-}
-
-hipError_t launch_fwd_padding(const AttnArgs& a, int D, hipStream_t stream)
-{
-    if (a.T == 0) return hipSuccess;
-    const size_t nchunks = (size_t)a.T * a.Hq * (D / 8);
-    const unsigned blocks = (unsigned)min((size_t)4096, (nchunks + 255) / 256);
-    if (D == 128) hipLaunchKernelGGL(fwd_padding_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(fwd_padding_kernel<64>, dim3(blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -51,6 +51,7 @@ struct AttnArgs {
     int T, B, Hq, Hkv, causal;
     int mode;         // MODE_*
     int rotate;       // Q and K rotated (Hadamard): dQ and dK are rotated back
+    int work_wgs;     // forward: workgroups of attention work (the rest write padding rows)
     float scale;      // softmax scale
     float c2;         // scale * log2(e)
     int scale_exp;    // f = floor(log2 scale)
@@ -74,7 +75,6 @@ struct AttnArgs {
 };
 
 hipError_t launch_fwd(const AttnArgs& a, int D, int max_items, hipStream_t stream);
-hipError_t launch_fwd_padding(const AttnArgs& a, int D, hipStream_t stream);
 hipError_t launch_bwd(const AttnArgs& a, int D, int max_items, bool with_dq, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnArgs& a, int D, int max_items, hipStream_t stream);
 hipError_t launch_bwd_finalize(const AttnArgs& a, int D, bool dq_from_acc, hipStream_t stream);

@@ -58,11 +58,21 @@ __device__ __forceinline__ int item_cost(const WorklistArgs& a, int n, int m)
     return a.causal ? (min(a.tile * (m + 1), n) + 63) / 64 : steps64;
 }
 
+// Sizes up to which the document offsets, the histogram and the bucket
+// cursors live in LDS (48 KB), so that the phases meet through LDS instead
+// of device memory; larger problems use the workspace arrays.
+constexpr int kLdsEntries = 4096;
+
+template <bool LDS>
 __global__ __launch_bounds__(kThreads) void worklist_kernel(WorklistArgs a)
 {
     __shared__ int s_tmp[kThreads / 64 + 1];
+    __shared__ int s_arr[LDS ? 3 : 1][LDS ? kLdsEntries : 1];
     const int tid = threadIdx.x;
     const int32_t* cu = a.cu;
+    int* doc_off = LDS ? s_arr[0] : a.doc_off;
+    int* hist = LDS ? s_arr[1] : a.hist;
+    int* cursor = LDS ? s_arr[2] : a.cursor;
 
     // 1. items per document, exclusive scan -> doc_off
     int carry = 0;
@@ -75,12 +85,12 @@ __global__ __launch_bounds__(kThreads) void worklist_kernel(WorklistArgs a)
         }
         int total;
         int pre = block_exclusive_scan(c, s_tmp, &total);
-        if (b < a.B) a.doc_off[b] = carry + pre;
+        if (b < a.B) doc_off[b] = carry + pre;
         carry += total;
     }
-    if (tid == 0) a.doc_off[a.B] = carry;
+    if (tid == 0) doc_off[a.B] = carry;
     const int nitems = min(carry, a.max_items);
-    for (int c = tid; c <= a.max_cost; c += kThreads) a.hist[c] = 0;
+    for (int c = tid; c <= a.max_cost; c += kThreads) hist[c] = 0;
     __syncthreads();
     __threadfence_block();
 
@@ -89,12 +99,12 @@ __global__ __launch_bounds__(kThreads) void worklist_kernel(WorklistArgs a)
         int lo = 0, hi = a.B - 1;
         while (lo < hi) {
             int mid = (lo + hi + 1) >> 1;
-            if (a.doc_off[mid] <= i) lo = mid;
+            if (doc_off[mid] <= i) lo = mid;
             else hi = mid - 1;
         }
         const int n = cu[lo + 1] - cu[lo];
-        const int cost = min(item_cost(a, n, i - a.doc_off[lo]), a.max_cost);
-        atomicAdd(&a.hist[cost], 1);
+        const int cost = min(item_cost(a, n, i - doc_off[lo]), a.max_cost);
+        atomicAdd(&hist[cost], 1);
     }
     __syncthreads();
     __threadfence_block();
@@ -103,10 +113,10 @@ __global__ __launch_bounds__(kThreads) void worklist_kernel(WorklistArgs a)
     carry = 0;
     for (int base = 0; base <= a.max_cost; base += kThreads) {
         const int c = a.max_cost - (base + tid);  // descending cost
-        const int v = c >= 0 ? a.hist[c] : 0;
+        const int v = c >= 0 ? hist[c] : 0;
         int total;
         int pre = block_exclusive_scan(v, s_tmp, &total);
-        if (c >= 0) a.cursor[c] = carry + pre;
+        if (c >= 0) cursor[c] = carry + pre;
         carry += total;
     }
     __syncthreads();
@@ -117,13 +127,13 @@ __global__ __launch_bounds__(kThreads) void worklist_kernel(WorklistArgs a)
         int lo = 0, hi = a.B - 1;
         while (lo < hi) {
             int mid = (lo + hi + 1) >> 1;
-            if (a.doc_off[mid] <= i) lo = mid;
+            if (doc_off[mid] <= i) lo = mid;
             else hi = mid - 1;
         }
-        const int m = i - a.doc_off[lo];
+        const int m = i - doc_off[lo];
         const int n = cu[lo + 1] - cu[lo];
         const int cost = min(item_cost(a, n, m), a.max_cost);
-        const int pos = atomicAdd(&a.cursor[cost], 1);
+        const int pos = atomicAdd(&cursor[cost], 1);
         a.items[2 * pos] = lo;
         a.items[2 * pos + 1] = m;
     }
@@ -134,7 +144,10 @@ __global__ __launch_bounds__(kThreads) void worklist_kernel(WorklistArgs a)
 
 hipError_t launch_worklist(const WorklistArgs& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(kThreads), 0, stream, a);
+    if (a.B + 1 <= kLdsEntries && a.max_cost + 1 <= kLdsEntries)
+        hipLaunchKernelGGL(worklist_kernel<true>, dim3(1), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(worklist_kernel<false>, dim3(1), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
