@@ -124,12 +124,13 @@ def cpu_baseline(w, flop_target=3e11, hadamard=False):
     if w.flags & workloads.FLAG_FP4_SCORE:
         views = (oracle.quantize_nvfp4(sub.q, sub.cu), oracle.quantize_nvfp4(sub.k, sub.cu))
     ops = oracle.Operands.from_codes(q, k, v, *views)
-    O, L = oracle.attn_fwd(sub.cu, ops, scale=scale, mode=oracle.MODE_TILED, kblock=64)
+    c = w.causal
+    O, L = oracle.attn_fwd(sub.cu, ops, scale=scale, causal=c, mode=oracle.MODE_TILED, kblock=64)
     gc, ge, D, _ = oracle.bwd_prep(sub.cu, sub.do, oracle.to_bf16(O), k[1], v[1], nkv, scale=scale,
-                                   block=blk)
+                                   causal=c, block=blk)
     Gd = oracle.dequantize(gc, ge)
-    dq = oracle.bwd_dq(sub.cu, ops, Gd, D, L, scale=scale, per_row_ds=exact)
-    dk, _ = oracle.bwd_dkdv(sub.cu, ops, Gd, D, L, scale=scale, per_row_ds=exact)
+    dq = oracle.bwd_dq(sub.cu, ops, Gd, D, L, scale=scale, causal=c, per_row_ds=exact)
+    dk, _ = oracle.bwd_dkdv(sub.cu, ops, Gd, D, L, scale=scale, causal=c, per_row_ds=exact)
     if hadamard:
         oracle.unrotate(dq), oracle.unrotate(dk)
     dt = time.time() - t0
@@ -147,6 +148,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="packed_mha", choices=sorted(workloads.NAMED))
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--noncausal", action="store_true",
+                    help="the same workload without the causal mask (pairs counted as n^2)")
     ap.add_argument("--hadamard", action="store_true",
                     help="rotate Q and K by the Hadamard matrix (FLAMIA_HADAMARD)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -166,6 +169,8 @@ def main():
     F.load()
     dev = torch.device("cuda:0")
     w = workloads.NAMED[args.workload](args.seed)
+    if args.noncausal:
+        w.flags &= ~workloads.FLAG_CAUSAL
     log("workload %s: T=%d docs=%d Hq=%d Hkv=%d d=%d" % (w.name, w.T, len(w.cu) - 1, w.Hq, w.Hkv,
                                                          w.d))
     T, Hq, Hkv, d = w.T, w.Hq, w.Hkv, w.d
@@ -187,7 +192,8 @@ def main():
     # with the E2M1 score view, also writes the views of Q and K
     exact = bool(w.flags & workloads.FLAG_EXACT)
     fp4 = bool(w.flags & workloads.FLAG_FP4_SCORE)
-    flags = F.FLAMIA_CAUSAL | (F.FLAMIA_EXACT if exact else 0) | (F.FLAMIA_FP4_SCORE if fp4 else 0)
+    flags = (F.FLAMIA_CAUSAL if w.causal else 0) | (F.FLAMIA_EXACT if exact else 0) | \
+        (F.FLAMIA_FP4_SCORE if fp4 else 0)
     flags |= F.FLAMIA_HADAMARD if args.hadamard else 0
     mode = F.FLAMIA_SCALE_PER_TOKEN if exact else F.FLAMIA_SCALE_TOKBLOCK32
     qk_mode = mode | (F.FLAMIA_SCALE_ROTATE if args.hadamard else 0)
@@ -272,7 +278,8 @@ def main():
     ms_attn = timed(lambda: (fwd(), bwd()), K)
     ms_bwd_det = None  # the exact-scale and rotated backwards have no deterministic variant
     if not exact and not args.hadamard:
-        pdet = F.make_problem(cu, T, Hq, Hkv, d, 0.0, F.FLAMIA_CAUSAL | F.FLAMIA_DETERMINISTIC)
+        pdet = F.make_problem(cu, T, Hq, Hkv, d, 0.0,
+                              (F.FLAMIA_CAUSAL if w.causal else 0) | F.FLAMIA_DETERMINISTIC)
         wsd = torch.empty(F.flamia_attn_bwd_workspace_size(pdet), **u8)
         ms_bwd_det = timed(lambda: F.flamia_attn_bwd(pdet, qc, qe, kc, ke, vc, ve, o, lse, xdo, dq,
                                                      dk, dv, wsd), K)
@@ -300,7 +307,7 @@ def main():
         "dtype": "fp8_e4m3+e2m1" if fp4 else "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": T, "documents": int(len(w.cu) - 1),
-                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "causal": True,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "causal": bool(w.causal),
                    "visible_pairs": int(pairs), "seed": args.seed,
                    "scales": ("per-token operand exponents, per-(query row, 32-key block) dS "
                               "exponents for dQ" if exact else

@@ -200,3 +200,52 @@ def test_hadamard_full_size_sampled():
     check_grad(host(dk).view(np.uint16), oracle.unrotate(dKr), "hadamard dK", d * tk, rows=kmask,
                absm=d * ak)
     check_grad(host(dv).view(np.uint16), dV, "hadamard dV", tv, rows=kmask, absm=av)
+
+
+@pytest.mark.timeout(600)
+def test_noncausal_full_size_sampled():
+    """The packed MHA workload without the causal mask (the non-causal
+    variant of the same kernels), at full size: codes in full, forward rows
+    and backward blocks sampled against the oracle."""
+    w = workloads.NAMED["packed_mha"](0)
+    w.flags &= ~workloads.FLAG_CAUSAL
+    log("workload %s, non-causal" % w.name)
+    g = run_gpu(w)
+    q, k, v = oracle_operands(w)
+    for tag, (c, e) in (("q", q), ("k", k), ("v", v)):
+        assert np.array_equal(g[tag + "c"], c) and np.array_equal(g[tag + "e"], e), tag
+    rng = np.random.default_rng(8)
+    toks = _sample_tokens(w.cu, rng, per_doc=5)
+    heads = list(rng.choice(w.Hq, 5, replace=False))
+    rows = np.array([(h, t) for h in heads for t in toks], dtype=np.int32)
+    ops = oracle.Operands.from_codes(q, k, v)
+    O, L, ties = oracle.attn_fwd(w.cu, ops, causal=False, rows=rows, mode=oracle.MODE_TILED, kblock=64,
+                                 want_flags=True)
+    mask = np.zeros((w.T, w.Hq), dtype=bool)
+    mask[rows[:, 1], rows[:, 0]] = True
+    check_fwd(g["O"][mask], g["LSE"].T[mask], O[mask], L.T[mask], ties.transpose(1, 0, 2)[mask],
+              tag="non-causal")
+    gc, ge, D, kpre = oracle.bwd_prep(w.cu, w.do, g["O"], k[1], v[1], w.Hkv, causal=False)
+    assert np.array_equal(g["gc"], gc) and np.array_equal(g["kpre"].astype(np.int32), kpre)
+    G = oracle.dequantize(gc, ge)
+    lse = g["LSE"].astype(np.float64)
+    qstarts = oracle.doc_blocks(w.cu, toks)
+    qblocks = np.array([(h, t0) for h in heads for t0 in qstarts[::2]], dtype=np.int32)
+    dQ, tq, acc, aq = oracle.bwd_dq(w.cu, ops, G, D, lse, causal=False, qblocks=qblocks, want_flags=True)
+    nt = np.repeat(dq_tiles(w.cu, w.T, False)[:, None], w.Hq, axis=1)
+    qmask = np.zeros((w.T, w.Hq), dtype=bool)
+    for h, t0 in qblocks:
+        b = int(np.searchsorted(w.cu, t0, side="right") - 1)
+        qmask[t0:min(t0 + 32, int(w.cu[b + 1])), h] = True
+    check_grad(g["dQ"], dQ, "non-causal dQ", tq, rows=qmask, acc=acc, ntiles=nt, absm=aq)
+    kheads = sorted(set(h * w.Hkv // w.Hq for h in heads))[:3]
+    kstarts = qstarts[:: max(1, len(qstarts) // 8)]
+    kblocks = np.array([(hk, t0) for hk in kheads for t0 in kstarts], dtype=np.int32)
+    dK, dV, tk, tv, ak, av = oracle.bwd_dkdv(w.cu, ops, G, D, lse, causal=False, kblocks=kblocks,
+                                             want_flags=True)
+    kmask = np.zeros((w.T, w.Hkv), dtype=bool)
+    for hk, t0 in kblocks:
+        b = int(np.searchsorted(w.cu, t0, side="right") - 1)
+        kmask[t0:min(t0 + 32, int(w.cu[b + 1])), hk] = True
+    check_grad(g["dK"], dK, "non-causal dK", tk, rows=kmask, absm=ak)
+    check_grad(g["dV"], dV, "non-causal dV", tv, rows=kmask, absm=av)
