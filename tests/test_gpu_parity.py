@@ -17,6 +17,10 @@ SMALL = [
     ("gqa_d128", [190, 333], 560, 4, 2, 128, True),
     ("gqa_d64_tail", [45, 250, 97], 400, 6, 2, 64, True),
     ("noncausal_d128", [150, 80, 33], 300, 2, 1, 128, False),
+    # empty documents at the start, in the middle and at the end, a 1-token
+    # document and padding rows
+    ("empty_docs_d64", [0, 50, 0, 0, 33, 1, 0], 100, 2, 1, 64, True),
+    ("empty_docs_noncausal_d128", [0, 70, 0, 40, 0], 128, 2, 2, 128, False),
 ]
 
 
@@ -156,7 +160,7 @@ EXACT_BWD = [(64, False), (64, True), (128, False)]
 
 
 @pytest.mark.parametrize("d,fp4", EXACT_BWD, ids=["exact_d64", "exact_fp4_d64", "exact_d128"])
-def test_exact_backward(d, fp4):
+def test_exact_backward(d, fp4, lens=(230, 97, 40), cap=400):
     """Exact-scale backward: per-token dO, folded exponents and per-(query
     row, 32-key block) dS exponents for dQ, against the oracle's per-row dS
     backward on the same per-token operands."""
@@ -164,7 +168,7 @@ def test_exact_backward(d, fp4):
     from bit_causal_flash_amd import flamia as F
     log("case exact backward fp4=%s d=%d" % (fp4, d))
     Hq, Hkv = 4, 2
-    w, p, (q, k, v, f4, x), (o, lse), ops = _exact_case("exact_bwd", [230, 97, 40], 400, Hq, Hkv,
+    w, p, (q, k, v, f4, x), (o, lse), ops = _exact_case("exact_bwd", list(lens), cap, Hq, Hkv,
                                                         d, fp4, seed=9)
     dq, dk, dv, ws = F.attn_bwd(p, q, k, v, o, lse, x["do"].view(torch.bfloat16), fp4=f4)
     torch.cuda.synchronize()
@@ -190,3 +194,9 @@ def test_exact_backward(d, fp4):
     n = int(w.cu[-1])
     for t in (dq, dk, dv):
         assert np.all(host(t)[n:] == 0)
+
+
+def test_exact_backward_empty_documents():
+    """The exact-scale path (E2M1 score view) with empty documents between and
+    after the others."""
+    test_exact_backward(64, True, lens=(0, 61, 0, 140, 0), cap=220)
