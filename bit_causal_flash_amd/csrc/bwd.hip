@@ -15,18 +15,20 @@
 //        added into an FP16 accumulator with packed atomics; the finalize
 //        kernel divides the prescale back out and writes bf16.
 //
-// Tiling: a workgroup (4 waves) owns a document-local 128-key tile of one kv
-// head (wave w: 32 keys, one token block) and loops over the q heads of its
-// group and the 64-query tiles that can see its keys; dK and dV accumulate
-// in registers across all of them (GQA head reduction without atomics).  S and
-// dP are computed with the query rows permuted so the accumulators already
-// hold P^ and dS^ in the k layout of the dV / dK MFMAs.  Q, dO and K are
-// staged token-major in LDS and read k-major with ds_read_b64_tr_b8 where the
-// contraction runs over tokens: one copy of every code tensor serves both
-// orientations.  dS^ goes through LDS once, key-major, and is read
-// transposed for dQ.  The next Q/dO tile is fetched into registers while the
-// current one is processed (double-buffered LDS), and barriers order LDS
-// traffic only, so the FP16 dQ atomics never stall the workgroup.
+// Tiling: a workgroup owns a document-local 128-key tile of one kv head and
+// loops over the q heads of its group and the 64-query tiles that can see its
+// keys.  Its 8 waves have two roles (see bwd_kernel): score waves (S, dP, P,
+// dS for one 32-key token block each) and gradient waves (dV, dK for the same
+// keys, accumulated in registers across the whole loop, i.e. the GQA head
+// reduction without atomics, and the tile's dQ).  S and dP are computed with
+// the query rows permuted so the accumulators already hold P^ and dS^ in the
+// k layout of the dV / dK MFMAs.  Q, dO and K are staged token-major in LDS
+// and read k-major with ds_read_b64_tr_b8 where the contraction runs over
+// tokens: one copy of every code tensor serves both orientations.  dS^ goes
+// through LDS once, key-major, and is read transposed for dQ.  Barriers order
+// LDS traffic only.  The dQ partials (one per query tile and 128-key tile)
+// are added with packed FP16 atomics, whose throughput, not the MFMAs, bounds
+// the kernel on long documents.
 #include "device.hpp"
 #include "kernels.hpp"
 

@@ -172,13 +172,6 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Value of the neighbouring lane (lane ^ 1), through DPP.
-__device__ __forceinline__ float swap_adjacent(float x)
-{
-    // quad_perm [1, 0, 3, 2]
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
-}
-
 // Combining a value with the one of lane i ^ 32.  v_permlane32_swap
 // exchanges the upper half of its first operand with the lower half of its
 // second; with both operands x, each lane receives, across the two results,
@@ -389,17 +382,6 @@ __device__ __forceinline__ void fwht_cols(v16f (&acc)[NDT], int lane)
 __device__ __forceinline__ int rev4(int i)
 {
     return (int)(__builtin_bitreverse32((uint32_t)i) >> 28);
-}
-
-__device__ __forceinline__ int doc_of(const int32_t* cu, int B, int t)
-{
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (cu[mid] <= t) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
 }
 
 }  // namespace flamia

@@ -23,7 +23,8 @@
 // leaves registers.  V is read k-major straight from its token-major LDS tile
 // with ds_read_b64_tr_b8, so no transposed copy of V exists anywhere.  The
 // next step's K/V tile is fetched into registers while the current one is
-// processed (double-buffered LDS, one LDS-only barrier per step).
+// processed (double-buffered LDS, one LDS-only barrier per step).  A few
+// extra workgroups of the same launch write the rows after the last document.
 #include "device.hpp"
 #include "kernels.hpp"
 
