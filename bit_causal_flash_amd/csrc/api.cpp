@@ -225,6 +225,9 @@ flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_head
     a.block = scale_mode == FLAMIA_SCALE_PER_TOKEN ? 1 : 32;
     a.rotate = rotate ? 1 : 0;
     a.floor_rule = floor_rule ? 1 : 0;
+    a.ntensors = 1;
+    a.Htot = num_heads;
+    a.ten[0] = QuantTensor{x, codes, exps, num_heads, rotate ? 1 : 0};
     a.cu = p->cu_seqlens;
     a.x = x;
     a.codes = codes;
@@ -234,6 +237,44 @@ flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_head
     const hipError_t e = scale_mode == FLAMIA_SCALE_NVFP4_16 ? launch_nvfp4(a, p->head_dim, s)
                                                              : launch_quant(a, p->head_dim, false, s);
     if (e != hipSuccess) return FLAMIA_ERR_HIP;
+    return hip_status(record(p, false, s));
+}
+
+flamia_status flamia_quantize_qkv(const flamia_problem* p, int32_t scale_mode, const uint16_t* q,
+                                  const uint16_t* k, const uint16_t* v, uint8_t* q_codes,
+                                  uint8_t* q_exps, uint8_t* k_codes, uint8_t* k_exps,
+                                  uint8_t* v_codes, uint8_t* v_exps, void* stream)
+{
+    flamia_status st = check_seq(p);
+    if (st != FLAMIA_OK) return st;
+    st = check_head_dim(p->head_dim);
+    if (st != FLAMIA_OK) return st;
+    const int Hq = p->num_q_heads, Hkv = p->num_kv_heads;
+    if (Hq < 1 || Hkv < 1) return FLAMIA_ERR_INVALID_ARG;
+    const bool rotate = (scale_mode & FLAMIA_SCALE_ROTATE) != 0;
+    const bool floor_rule = (scale_mode & FLAMIA_SCALE_FLOOR_CONTROL) != 0;
+    scale_mode &= ~(int32_t)(FLAMIA_SCALE_ROTATE | FLAMIA_SCALE_FLOOR_CONTROL);
+    if (scale_mode != FLAMIA_SCALE_TOKBLOCK32 && scale_mode != FLAMIA_SCALE_PER_TOKEN)
+        return FLAMIA_ERR_INVALID_ARG;
+    const int64_t Htot = (int64_t)Hq + 2 * (int64_t)Hkv;
+    if ((int64_t)(p->total_tokens + 31) / 32 * Htot >= ((int64_t)1 << 24)) return FLAMIA_ERR_UNSUPPORTED;
+    if (p->total_tokens == 0) return FLAMIA_OK;
+    if (!q || !k || !v || !q_codes || !q_exps || !k_codes || !k_exps || !v_codes || !v_exps)
+        return FLAMIA_ERR_INVALID_ARG;
+    QuantArgs a = {};
+    a.T = p->total_tokens;
+    a.B = p->num_seqs;
+    a.block = scale_mode == FLAMIA_SCALE_PER_TOKEN ? 1 : 32;
+    a.floor_rule = floor_rule ? 1 : 0;
+    a.cu = p->cu_seqlens;
+    a.ntensors = 3;
+    a.Htot = (int)Htot;
+    a.ten[0] = QuantTensor{q, q_codes, q_exps, Hq, rotate ? 1 : 0};
+    a.ten[1] = QuantTensor{k, k_codes, k_exps, Hkv, rotate ? 1 : 0};
+    a.ten[2] = QuantTensor{v, v_codes, v_exps, Hkv, 0};
+    hipStream_t s = (hipStream_t)stream;
+    if (record(p, true, s) != hipSuccess) return FLAMIA_ERR_HIP;
+    if (launch_quant(a, p->head_dim, false, s) != hipSuccess) return FLAMIA_ERR_HIP;
     return hip_status(record(p, false, s));
 }
 
@@ -356,6 +397,9 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     q.x = dout;
     q.codes = ws + L.do_codes;
     q.exps = ws + L.do_exps;
+    q.ntensors = 1;
+    q.Htot = q.H;
+    q.ten[0] = QuantTensor{dout, q.codes, q.exps, q.H, 0};
     q.Hkv = (int)d.Hkv;
     q.causal = d.causal ? 1 : 0;
     q.prescale_c = prescale_c(d);

@@ -7,8 +7,21 @@
 
 namespace flamia {
 
+// One tensor of a quantizer launch.
+struct QuantTensor {
+    const uint16_t* x;   // bf16 [T][H][D]
+    uint8_t* codes;      // [T][H][D]
+    uint8_t* exps;       // [H][T]
+    int H;
+    int rotate;          // Hadamard-rotate every row first (score operands)
+};
+
 struct QuantArgs {
     int T, B, H, block;
+    // the token-block kernel: up to three tensors (Q, K, V) in one launch,
+    // heads of all of them fastest; ten[0] alone for one tensor or dO
+    int ntensors, Htot;
+    QuantTensor ten[3];
     int rotate;          // Hadamard-rotate every row before quantizing (score operands)
     int floor_rule;      // floor exponent rule (negative control for the causality tests)
     const int32_t* cu;

@@ -86,9 +86,22 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
     const int tid = threadIdx.x;
     const int chunk = tid % TPR;
     const int rsub = tid / TPR;
-    const int h = blockIdx.x % a.H;         // heads fastest: concurrent workgroups
-    const int w0 = 32 * (blockIdx.x / a.H); // cover whole token rows
-    const int H = a.H, T = a.T, B = a.B;
+    // heads (of every tensor of the launch) fastest: concurrent workgroups
+    // cover whole token rows
+    int h = (int)(blockIdx.x % a.Htot);
+    const int w0 = 32 * (int)(blockIdx.x / a.Htot);
+    int ti = 0;
+    if (h >= a.ten[0].H) {
+        h -= a.ten[0].H;
+        ti = 1;
+        if (h >= a.ten[1].H) {
+            h -= a.ten[1].H;
+            ti = 2;
+        }
+    }
+    const QuantTensor tt = a.ten[ti];
+    const bool rot = ROT && tt.rotate;
+    const int H = tt.H, T = a.T, B = a.B;
     const int32_t* __restrict__ cu = a.cu;
     const int ntok = cu[B];
 
@@ -147,7 +160,7 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
         if (PREP) oraw[p] = v4i{0, 0, 0, 0};
         if (bsr[p] >= 0) {
             const size_t off = ((size_t)t * H + h) * D + 8 * chunk;
-            raw[p] = __builtin_nontemporal_load((const v4i*)(a.x + off));
+            raw[p] = __builtin_nontemporal_load((const v4i*)(tt.x + off));
             if (PREP) oraw[p] = __builtin_nontemporal_load((const v4i*)(a.o + off));
         }
     }
@@ -168,24 +181,24 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
     // rotated rows (a row is spread over TPR consecutive lanes, 8 features
     // each; rows that are not owned are zero and stay zero)
     float yr[ROT ? NPASS : 1][8];
-    if constexpr (ROT) {
+    if (rot) {
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                yr[p][2 * k] = bf16_to_f32((uint16_t)(raw[p][k] & 0xffff));
-                yr[p][2 * k + 1] = bf16_to_f32((uint16_t)((uint32_t)raw[p][k] >> 16));
+                yr[ROT ? p : 0][2 * k] = bf16_to_f32((uint16_t)(raw[p][k] & 0xffff));
+                yr[ROT ? p : 0][2 * k + 1] = bf16_to_f32((uint16_t)((uint32_t)raw[p][k] >> 16));
             }
-            fwht_row<D>(yr[p], tid & 63);
+            fwht_row<D>(yr[ROT ? p : 0], tid & 63);
         }
     }
     // block maxima
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
         uint32_t m = 0;
-        if constexpr (ROT) {
+        if (rot) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(yr[p][k]) & 0x7fffffffu);
+            for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(yr[ROT ? p : 0][k]) & 0x7fffffffu);
         } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
@@ -287,9 +300,9 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
             e = a.floor_rule ? floor_exp_e4m3(__uint_as_float(s_bmax[bs - w0]))
                              : ceil_exp448(__uint_as_float(s_bmax[bs - w0]));
             float y[8];
-            if constexpr (ROT) {
+            if (rot) {
 #pragma unroll
-                for (int k = 0; k < 8; ++k) y[k] = ldexpf(yr[p][k], -e);
+                for (int k = 0; k < 8; ++k) y[k] = ldexpf(yr[ROT ? p : 0][k], -e);
             } else {
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
@@ -319,7 +332,7 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
         v2i cw;
         cw.x = (int)lo;
         cw.y = (int)hi;
-        __builtin_nontemporal_store(cw, (v2i*)(a.codes + off));
+        __builtin_nontemporal_store(cw, (v2i*)(tt.codes + off));
         if constexpr (PREP) {
             *(v4i*)(a.dq_acc + off) = v4i{0, 0, 0, 0};
             dot = group_sum<TPR>(dot);
@@ -335,7 +348,7 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
                 a.prescale[(size_t)h * T + t] = (int8_t)k;
             }
         }
-        if (chunk == 0) a.exps[(size_t)h * T + t] = (uint8_t)(e + 127);
+        if (chunk == 0) tt.exps[(size_t)h * T + t] = (uint8_t)(e + 127);
     }
 }
 
@@ -423,14 +436,16 @@ hipError_t launch_nvfp4(const QuantArgs& a, int D, hipStream_t stream)
 hipError_t launch_quant(const QuantArgs& a, int D, bool prep, hipStream_t stream)
 {
     if (a.T == 0) return hipSuccess;
-    const dim3 grid((unsigned)(((a.T + 31) / 32) * a.H));
+    const dim3 grid((unsigned)(((a.T + 31) / 32) * a.Htot));
+    bool rotate = false;
+    for (int i = 0; i < a.ntensors; ++i) rotate = rotate || a.ten[i].rotate;
     if (D == 128) {
         if (prep) hipLaunchKernelGGL((quant_kernel<128, true, false>), grid, dim3(256), 0, stream, a);
-        else if (a.rotate) hipLaunchKernelGGL((quant_kernel<128, false, true>), grid, dim3(256), 0, stream, a);
+        else if (rotate) hipLaunchKernelGGL((quant_kernel<128, false, true>), grid, dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((quant_kernel<128, false, false>), grid, dim3(256), 0, stream, a);
     } else {
         if (prep) hipLaunchKernelGGL((quant_kernel<64, true, false>), grid, dim3(256), 0, stream, a);
-        else if (a.rotate) hipLaunchKernelGGL((quant_kernel<64, false, true>), grid, dim3(256), 0, stream, a);
+        else if (rotate) hipLaunchKernelGGL((quant_kernel<64, false, true>), grid, dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((quant_kernel<64, false, false>), grid, dim3(256), 0, stream, a);
     }
     return hipGetLastError();

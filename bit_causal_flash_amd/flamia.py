@@ -33,6 +33,7 @@ FLAMIA_SCALE_FLOOR_CONTROL = 0x200
 
 EXPORTED = [
     "flamia_quantize_tokblock",
+    "flamia_quantize_qkv",
     "flamia_attn_fwd_workspace_size",
     "flamia_attn_fwd",
     "flamia_attn_bwd_workspace_size",
@@ -86,6 +87,8 @@ def load():
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.flamia_quantize_tokblock.restype = ctypes.c_int
     lib.flamia_quantize_tokblock.argtypes = [P, i32, i32, vp, vp, vp, vp]
+    lib.flamia_quantize_qkv.restype = ctypes.c_int
+    lib.flamia_quantize_qkv.argtypes = [P, i32] + [vp] * 10
     lib.flamia_attn_fwd_workspace_size.restype = sz
     lib.flamia_attn_fwd_workspace_size.argtypes = [P]
     lib.flamia_attn_fwd.restype = ctypes.c_int
@@ -153,6 +156,14 @@ def flamia_quantize_tokblock(p, num_heads, scale_mode, x, codes, exps, stream=No
                                            _ptr(x), _ptr(codes), _ptr(exps), _stream(stream)))
 
 
+def flamia_quantize_qkv(p, scale_mode, q, k, v, q_codes, q_exps, k_codes, k_exps, v_codes, v_exps,
+                        stream=None):
+    _check("flamia_quantize_qkv",
+           load().flamia_quantize_qkv(ctypes.byref(p), int(scale_mode), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(q_codes), _ptr(q_exps), _ptr(k_codes), _ptr(k_exps),
+                                      _ptr(v_codes), _ptr(v_exps), _stream(stream)))
+
+
 def flamia_attn_fwd_workspace_size(p) -> int:
     return int(load().flamia_attn_fwd_workspace_size(ctypes.byref(p)))
 
@@ -199,6 +210,19 @@ def quantize(p, x, num_heads, scale_mode=FLAMIA_SCALE_TOKBLOCK32, stream=None):
     exps = torch.empty((H, T), dtype=torch.uint8, device=x.device)
     flamia_quantize_tokblock(p, num_heads, scale_mode, x, codes, exps, stream)
     return codes, exps
+
+
+def quantize_qkv(p, q, k, v, scale_mode=FLAMIA_SCALE_TOKBLOCK32, stream=None):
+    """Q, K, V in one launch -> ((q codes, q exps), (k ...), (v ...))."""
+    import torch
+    out = []
+    for x in (q, k, v):
+        T, H, d = x.shape
+        out.append((torch.empty((T, H, d), dtype=torch.uint8, device=x.device),
+                    torch.empty((H, T), dtype=torch.uint8, device=x.device)))
+    flamia_quantize_qkv(p, scale_mode, q, k, v, out[0][0], out[0][1], out[1][0], out[1][1],
+                        out[2][0], out[2][1], stream)
+    return tuple(out)
 
 
 def quantize_nvfp4(p, x, num_heads, stream=None):

@@ -159,6 +159,23 @@ flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_head
                                        uint8_t* exps, void* stream);
 
 /*
+ * Q, K and V of one problem in a single launch: the same results as
+ * flamia_quantize_tokblock on each (num_heads = num_q_heads for Q,
+ * num_kv_heads for K and V), with FLAMIA_SCALE_ROTATE in scale_mode
+ * applying to Q and K only and FLAMIA_SCALE_FLOOR_CONTROL to all three.
+ *   scale_mode FLAMIA_SCALE_TOKBLOCK32 or FLAMIA_SCALE_PER_TOKEN, optionally
+ *              OR-ed with FLAMIA_SCALE_ROTATE / FLAMIA_SCALE_FLOOR_CONTROL
+ *   q, k, v    bf16 [T][Hq][d], [T][Hkv][d], [T][Hkv][d] (device, read)
+ *   *_codes    uint8 like their inputs; *_exps uint8 [H][T] (device, written)
+ * Returns FLAMIA_ERR_INVALID_ARG for NULL pointers (T > 0) or another scale
+ * mode, FLAMIA_ERR_UNSUPPORTED when ceil(T / 32) * (Hq + 2 Hkv) >= 2^24.
+ */
+flamia_status flamia_quantize_qkv(const flamia_problem* p, int32_t scale_mode, const uint16_t* q,
+                                  const uint16_t* k, const uint16_t* v, uint8_t* q_codes,
+                                  uint8_t* q_exps, uint8_t* k_codes, uint8_t* k_exps,
+                                  uint8_t* v_codes, uint8_t* v_exps, void* stream);
+
+/*
  * Forward (review section 2 online softmax, section 3 separable score
  * scaling, section 5 Algorithm 1 steps 04-08 and the range budget):
  *   s2_ij = softmax_scale * log2(e) * Q^_i . K^_j over visible keys, with the

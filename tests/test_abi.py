@@ -96,6 +96,12 @@ def test_invalid_arguments_rejected_before_launch():
     assert q(P(_problem(T=0)), 1, F.FLAMIA_SCALE_ROTATE, None, None, None, None) == F.FLAMIA_OK
     assert q(P(_problem()), 1, F.FLAMIA_SCALE_NVFP4_16 | F.FLAMIA_SCALE_FLOOR_CONTROL, vp, vp, vp,
              None) == F.FLAMIA_ERR_INVALID_ARG
+    qkv = lib.flamia_quantize_qkv
+    nine = [vp] * 9  # q, k, v, then codes and exponents of each
+    assert qkv(P(_problem()), F.FLAMIA_SCALE_NVFP4_16, *nine, None) == F.FLAMIA_ERR_INVALID_ARG
+    assert qkv(P(_problem()), 0, *([vp] * 8), None, None) == F.FLAMIA_ERR_INVALID_ARG
+    assert qkv(P(_problem(d=96)), 0, *nine, None) == F.FLAMIA_ERR_UNSUPPORTED
+    assert qkv(P(_problem(T=0)), 0, *([None] * 9), None) == F.FLAMIA_OK
     with4 = [vp] * 16
     assert bwd(P(_problem(d=128, flags=fp4_flags)), *with4, vp,
                F.flamia_attn_bwd_workspace_size(_problem(d=128, flags=fp4_flags)), None) == \

@@ -200,3 +200,27 @@ def test_exact_backward_empty_documents():
     """The exact-scale path (E2M1 score view) with empty documents between and
     after the others."""
     test_exact_backward(64, True, lens=(0, 61, 0, 140, 0), cap=220)
+
+
+@pytest.mark.parametrize("mode", ["tokblock", "per_token", "rotated"])
+def test_fused_qkv_quantizer_bit_exact(mode):
+    """Q, K, V in one launch: the same codes and exponents as the oracle (and
+    so as three separate calls), with GQA head counts and padding rows."""
+    import torch
+    from bit_causal_flash_amd import flamia as F
+    log("case fused qkv quantizer %s" % mode)
+    w = workloads.make("qkv", 3, 420, [150, 7, 200, 0, 33], 6, 2, 128)
+    scale_mode = {"tokblock": F.FLAMIA_SCALE_TOKBLOCK32, "per_token": F.FLAMIA_SCALE_PER_TOKEN,
+                  "rotated": F.FLAMIA_SCALE_TOKBLOCK32 | F.FLAMIA_SCALE_ROTATE}[mode]
+    p = F.make_problem(dev(w.cu.astype(np.int32)), w.T, w.Hq, w.Hkv, w.d, 0.0, F.FLAMIA_CAUSAL)
+    x = [dev(getattr(w, n).view(np.int16)) for n in ("q", "k", "v")]
+    got = F.quantize_qkv(p, *x, scale_mode=scale_mode)
+    torch.cuda.synchronize()
+    blk = 1 if mode == "per_token" else 32
+    for i, n in enumerate(("q", "k", "v")):
+        if mode == "rotated" and n != "v":
+            rc, re = oracle.quantize_rotated(getattr(w, n), w.cu, block=blk)
+        else:
+            rc, re = oracle.quantize(getattr(w, n), w.cu, block=blk)
+        assert np.array_equal(host(got[i][0]), rc), n + " codes"
+        assert np.array_equal(host(got[i][1]), re), n + " exponents"
