@@ -76,7 +76,9 @@ __device__ __forceinline__ uint32_t cvt2_fp8(float x, float y)
 // Four floats -> four E4M3 codes packed little-endian.
 __device__ __forceinline__ uint32_t cvt4_fp8(float a, float b, float c, float d)
 {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    // the low half's instruction keeps the destination's upper half, which the
+    // second one overwrites: any value serves, a's bits need no extra move
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
 }

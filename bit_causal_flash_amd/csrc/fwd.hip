@@ -90,17 +90,28 @@ __device__ __forceinline__ void load_kvtile(const AttnArgs& a, KVTile<D, MODE>& 
 }
 
 // Online-softmax update of one wave's 32 queries x 64 keys: the running
-// integer reference r, the rescale of O and l when it rises, and the
-// probability operand P^ (byte 16 t + v <-> key 32 t + 16 g + v) with its
-// rounded row sum.  Unless `full`, element (t, v) is kept only if
-// 32 t + v < lim.  With FOLD, the operand codes carry each key's V exponent
-// relative to its 32-key block, vf[32 t + v] = 2^(e_V(j) - max e_V): P^ is
-// rounded first (l sums the unshifted values), then shifted by that power of
-// two, which is exact while the shifted weight stays in E4M3's normal range.
+// integer reference r, and the probability operand P^ (byte 16 t + v <->
+// key 32 t + 16 g + v) with its rounded row sum.  Unless `full`, element
+// (t, v) is kept only if 32 t + v < lim.  With FOLD, the operand codes carry
+// each key's V exponent relative to its 32-key block, vf[32 t + v] =
+// 2^(e_V(j) - max e_V): P^ is rounded first (l sums the unshifted values),
+// then shifted by that power of two, which is exact while the shifted weight
+// stays in E4M3's normal range.
+//
+// The method rescales O and l by 2^(r_old - r_new) whenever r rises.  Here
+// the accumulators instead stay in units of a per-query base R (the first
+// finite reference): a step's P^ enters the O MFMA with the block scale
+// 2^(r - R - 8) and its row sum is added to l with the same factor, so O and
+// l hold exactly 2^(r - R) times the rescaled sums (a power of two commutes
+// with every FP32 rounding), and the rescale is applied once, at the end.
+// Only when r - R exceeds 32 are the accumulators rescaled and R moved up,
+// which keeps them far from the FP32 range limit.  Returns the E8M0 code of
+// the step's P^ scale.  (l stays a VALU sum: the MFMA's internal
+// accumulation is not the exact FP32 sum of the rounded weights.)
 template <int NDT, bool FOLD>
-__device__ __forceinline__ void online_softmax(v16f (&sacc)[2], v16f (&oacc)[NDT], float& r,
-                                               float& l, v8i& pf, float c2, bool full, int lim,
-                                               const float* vf)
+__device__ __forceinline__ int online_softmax(v16f (&sacc)[2], v16f (&oacc)[NDT], float& r,
+                                              float& base, float& l, v8i& pf, float c2, bool full,
+                                              int lim, const float* vf)
 {
     if (!full) {
 #pragma unroll
@@ -117,17 +128,22 @@ __device__ __forceinline__ void online_softmax(v16f (&sacc)[2], v16f (&oacc)[NDT
     // the other half of the keys sits in the lane 32 away
     mloc = max_xor32(mloc);
     const float rn = fmaxf(r, ceilf(mloc * c2));
-    if (__any(rn > r)) {
-        float alpha = 1.f;
-        if (rn > r) alpha = (r == -INFINITY) ? 0.f : ldexpf(1.f, (int)fmaxf(r - rn, -200.f));
+    r = rn;
+    // nothing has been accumulated before the first finite reference
+    if (base == -INFINITY) base = rn;
+    if (__any(rn - base > 32.f)) {
+        const bool mv = rn - base > 32.f;
+        const float alpha = mv ? ldexpf(1.f, (int)fmaxf(base - rn, -200.f)) : 1.f;
+        if (mv) base = rn;
         l *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
     }
-    r = rn;
-    const float off = (r == -INFINITY) ? 0.f : 8.f - r;
+    const bool fin = rn != -INFINITY;
+    const float off = fin ? 8.f - rn : 0.f;
+    const int rel = fin ? (int)(rn - base) : 0;
     float lsum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -146,7 +162,10 @@ __device__ __forceinline__ void online_softmax(v16f (&sacc)[2], v16f (&oacc)[NDT
                 pf[4 * t + q] = (int)w;
             }
         }
-    l += lsum * 0.00390625f;
+    // the row sum is exact in FP32 (multiples of 2^-9 below 2^14), and so is
+    // its product with the power of two
+    l = fmaf(lsum, ldexpf(1.f, rel - 8), l);
+    return kScaleMinus8 + rel;
 }
 
 // Modes: MODE_BLOCK token-block operands; MODE_EXACT per-token exponents (the
@@ -238,8 +257,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
-    float r = -INFINITY;  // integer base-2 row reference
-    float l = 0.f;        // sum of rounded weights
+    float r = -INFINITY;     // integer base-2 row reference
+    float base = -INFINITY;  // reference the accumulators are kept in
+    float l = 0.f;           // sum of rounded weights
 
     // every thread writes (the four waves write identical exponents), so
     // that every prefetched register is consumed on every path
@@ -318,15 +338,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
             v8i pf;
             const bool full = (kt0 + 64 <= e) && (!a.causal || kt0 + 63 <= qw);
             const int lim = min(e, a.causal ? qi + 1 : e) - kt0 - 16 * g;
-            online_softmax<NDT, FOLD>(sacc, oacc, r, l, pf, c2, full, lim,
-                                      FOLD ? &s_vf[cur][16 * g] : nullptr);
+            const int sp = online_softmax<NDT, FOLD>(sacc, oacc, r, base, l, pf, c2, full, lim,
+                                                     FOLD ? &s_vf[cur][16 * g] : nullptr);
 
             // O^T += V^T P^T: V^T read k-major from the token-major LDS tile
             const int sv_exp = s_ev[cur][g];
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
                 oacc[dt] = mfma_f8(lds_tr_operand(sv, PITCH, 0, 32 * dt, lane), pf, oacc[dt],
-                                   sv_exp, kScaleMinus8);
+                                   sv_exp, sp);
         }
         stage(nxt, cur ^ 1);
         lds_barrier();
@@ -334,7 +354,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
 
     l = sum_xor32(l);
     if (qvalid) {
+        // O / l needs no rescale (both carry 2^(r - base)); the LSE takes the
+        // rescaled sum
         const float inv = 1.f / l;
+        l = ldexpf(l, (int)(base - r));
         uint16_t* orow = a.o + ((size_t)qi * Hq + h) * D;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
