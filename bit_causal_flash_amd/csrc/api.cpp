@@ -19,7 +19,8 @@ constexpr size_t kAlign = 256;
 constexpr int kFwdTile = 128;  // queries per forward work item
 constexpr int kBwdTile = 128;  // keys per backward work item
 constexpr uint32_t kKnownFlags =
-    FLAMIA_CAUSAL | FLAMIA_EXACT | FLAMIA_FP4_SCORE | FLAMIA_DETERMINISTIC | FLAMIA_HADAMARD;
+    FLAMIA_CAUSAL | FLAMIA_EXACT | FLAMIA_FP4_SCORE | FLAMIA_DETERMINISTIC | FLAMIA_HADAMARD |
+    FLAMIA_DQ_PRESCALE_SEQUENCE;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -373,9 +374,11 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     if (st != FLAMIA_OK) return st;
     st = check_fp4_pointers(p, q_fp4, q_fp4_scales, k_fp4, k_fp4_scales);
     if (st != FLAMIA_OK) return st;
-    // the deterministic dQ pass uses block exponents only; the FP16 view of
-    // the Q tile does not fit the workgroup's LDS next to d = 128 tiles
-    if ((p->flags & (FLAMIA_EXACT | FLAMIA_HADAMARD)) && d.deterministic) return FLAMIA_ERR_UNSUPPORTED;
+    // the deterministic dQ pass uses block exponents only and accumulates in
+    // FP32 (no prescale); the FP16 view of the Q tile does not fit the
+    // workgroup's LDS next to d = 128 tiles
+    if ((p->flags & (FLAMIA_EXACT | FLAMIA_HADAMARD | FLAMIA_DQ_PRESCALE_SEQUENCE)) && d.deterministic)
+        return FLAMIA_ERR_UNSUPPORTED;
     if ((p->flags & FLAMIA_FP4_SCORE) && d.d == 128) return FLAMIA_ERR_UNSUPPORTED;
     if (d.T == 0) return FLAMIA_OK;
     if (!q_codes || !q_exps || !k_codes || !k_exps || !v_codes || !v_exps || !o || !lse ||
@@ -411,6 +414,10 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     q.dq_acc = (_Float16*)(ws + L.dq_accum);
     hipError_t e = launch_quant(q, (int)d.d, true, s);
     if (e != hipSuccess) return FLAMIA_ERR_HIP;
+    if (p->flags & FLAMIA_DQ_PRESCALE_SEQUENCE) {
+        e = launch_seq_prescale(q, s);
+        if (e != hipSuccess) return FLAMIA_ERR_HIP;
+    }
 
     const WorklistLayout wl = worklist_layout(d, kBwdTile, wl_base[0]);
     WorklistArgs w = make_worklist_args(d, p, kBwdTile, true, ws, wl);

@@ -39,6 +39,9 @@ struct QuantArgs {
 };
 
 hipError_t launch_quant(const QuantArgs& a, int D, bool prep, hipStream_t stream);
+// Sequence-wide dQ prescale (negative control): overwrites a.prescale after
+// the backward preparation, from a.exps (dO), a.k_exps and a.v_exps
+hipError_t launch_seq_prescale(const QuantArgs& a, hipStream_t stream);
 // E2M1 + E4M3-per-16 score view: codes [T][H][D/2], scales (in exps) [T][H][D/16]
 hipError_t launch_nvfp4(const QuantArgs& a, int D, hipStream_t stream);
 

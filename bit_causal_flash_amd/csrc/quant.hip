@@ -423,7 +423,49 @@ __global__ __launch_bounds__(256) void nvfp4_kernel(QuantArgs a, int D)
     a.exps[i] = (uint8_t)sc;
 }
 
+// Sequence-wide dQ prescale, a test-only negative control (FLAMIA review
+// section 4 "Forward locality and backward locality differ"; jaehun.me
+// section 3.3): the size estimate from the largest dO, V and K exponents
+// over every token of every document, so that a later outlier moves the FP16
+// rounding of every earlier row.  One exponent per q head,
+// 14 - C - (max e_dO + max e_V + max e_K) clamped to [-60, 60], written over
+// the per-row exponents of the backward preparation; 0 on padding rows.
+// One workgroup per q head.
+__global__ __launch_bounds__(256) void seq_prescale_kernel(QuantArgs a)
+{
+    __shared__ int s_m[3][256];
+    const int h = blockIdx.x, g = h * a.Hkv / a.H, tid = threadIdx.x;
+    const int ntok = a.cu[a.B];
+    const size_t T = (size_t)a.T;
+    int mg = 0, mv = 0, mk = 0;  // biased exponent bytes: 0 is below every real one
+    for (int t = tid; t < ntok; t += 256) {
+        mg = max(mg, (int)a.exps[(size_t)h * T + t]);
+        mv = max(mv, (int)a.v_exps[(size_t)g * T + t]);
+        mk = max(mk, (int)a.k_exps[(size_t)g * T + t]);
+    }
+    s_m[0][tid] = mg;
+    s_m[1][tid] = mv;
+    s_m[2][tid] = mk;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w)
+#pragma unroll
+            for (int i = 0; i < 3; ++i) s_m[i][tid] = max(s_m[i][tid], s_m[i][tid + w]);
+        __syncthreads();
+    }
+    int k = 14 - a.prescale_c - (s_m[0][0] + s_m[1][0] + s_m[2][0] - 3 * 127);
+    k = k < -60 ? -60 : (k > 60 ? 60 : k);
+    for (int t = tid; t < a.T; t += 256) a.prescale[(size_t)h * T + t] = (int8_t)(t < ntok ? k : 0);
+}
+
 }  // namespace
+
+hipError_t launch_seq_prescale(const QuantArgs& a, hipStream_t stream)
+{
+    if (a.T == 0 || a.H == 0) return hipSuccess;
+    hipLaunchKernelGGL(seq_prescale_kernel, dim3((unsigned)a.H), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_nvfp4(const QuantArgs& a, int D, hipStream_t stream)
 {

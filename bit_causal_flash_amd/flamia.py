@@ -24,6 +24,7 @@ FLAMIA_EXACT = 1 << 1
 FLAMIA_FP4_SCORE = 1 << 2
 FLAMIA_DETERMINISTIC = 1 << 3
 FLAMIA_HADAMARD = 1 << 4
+FLAMIA_DQ_PRESCALE_SEQUENCE = 1 << 5  # test-only negative control (backward)
 
 FLAMIA_SCALE_TOKBLOCK32 = 0
 FLAMIA_SCALE_PER_TOKEN = 1

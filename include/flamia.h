@@ -69,10 +69,16 @@ enum {
                                        (FLAMIA_SCALE_NVFP4_16); requires
                                        FLAMIA_EXACT; backward: head_dim 64 */
     FLAMIA_DETERMINISTIC = 1u << 3, /* bitwise run-to-run repeatable backward */
-    FLAMIA_HADAMARD = 1u << 4       /* Q and K codes come from the rotated rows
+    FLAMIA_HADAMARD = 1u << 4,      /* Q and K codes come from the rotated rows
                                        (FLAMIA_SCALE_ROTATE); not with
                                        FLAMIA_EXACT, nor with
                                        FLAMIA_DETERMINISTIC in the backward */
+    FLAMIA_DQ_PRESCALE_SEQUENCE = 1u << 5 /* test-only negative control, backward
+                                       only: the dQ prescale from sequence-wide
+                                       maxima instead of each row's visible
+                                       keys (a later outlier then moves the
+                                       FP16 rounding of earlier rows); not with
+                                       FLAMIA_DETERMINISTIC */
 };
 
 /* Quantizer scale policies. */
@@ -234,6 +240,13 @@ flamia_status flamia_attn_fwd(const flamia_problem* p, const uint8_t* q_codes,
  * FLAMIA_HADAMARD: Q and K codes of the rotated rows; the gradient products
  * use them at softmax scale / d, and dQ, dK are taken back to the original
  * coordinates (times H_d) before they are written.
+ * FLAMIA_DQ_PRESCALE_SEQUENCE (test-only negative control; review section 4
+ * "Forward locality and backward locality differ", jaehun.me section 3.3):
+ * every row of q head h takes k = 14 - C - (max e_dO + max e_V + max e_K),
+ * the maxima over all tokens of all documents (h for dO, its kv head for V
+ * and K), clamped to [-60, 60]; padding rows 0.  Only the FP16 rounding of dQ
+ * changes.  Returns FLAMIA_ERR_UNSUPPORTED with FLAMIA_DETERMINISTIC, whose
+ * FP32 dQ has no prescale.
  * FLAMIA_EXACT (review section 4; jaehun.me section 3.2): dO is quantized per
  * token; the dO, Q and K exponents, which vary along the contractions of
  * dV, dK and dQ, are folded into P^, dS^ (dK copy) and dS^ (dQ copy) before

@@ -58,6 +58,8 @@ def _load():
         _lib.orc_ceil_exponent.argtypes = [ctypes.c_double]
         _lib.orc_floor_exponent.restype = ctypes.c_int
         _lib.orc_floor_exponent.argtypes = [ctypes.c_double]
+        _lib.orc_f16_round.restype = ctypes.c_double
+        _lib.orc_f16_round.argtypes = [ctypes.c_double]
     return _lib
 
 
@@ -104,6 +106,11 @@ def ceil_exponent(amax: float) -> int:
 
 def floor_exponent(amax: float) -> int:
     return int(_load().orc_floor_exponent(float(amax)))
+
+
+def f16_round(x: float) -> float:
+    """Nearest IEEE binary16 value (ties to even), as a float."""
+    return _load().orc_f16_round(float(x))
 
 
 def to_bf16(x) -> np.ndarray:
@@ -317,6 +324,21 @@ def bwd_prep(cu, dO, O, k_exps, v_exps, Hkv, scale=None, causal=True, block=32):
     return gc, ge, D, kpre
 
 
+def bwd_prescale_seq(cu, do_exps, k_exps, v_exps, Hkv, d, scale=None):
+    """The sequence-wide dQ prescale exponents (test-only negative control):
+    int32 [Hq][T] from the sequence-wide maxima of the dO, V and K
+    exponents."""
+    cu = _c(cu, np.int32)
+    do_exps = _c(do_exps, np.uint8)
+    Hq, T = do_exps.shape
+    scale = default_scale(d) if scale is None else scale
+    kpre = np.empty((Hq, T), dtype=np.int32)
+    _check(_load().orc_bwd_prescale_seq(T, len(cu) - 1, _p(cu), Hq, Hkv, d, ctypes.c_double(scale),
+                                        _p(do_exps), _p(_c(k_exps, np.uint8)),
+                                        _p(_c(v_exps, np.uint8)), _p(kpre)))
+    return kpre
+
+
 def doc_blocks(cu, tokens=None):
     """First tokens of the document-local 32-token blocks (all, or those
     holding the given tokens)."""
@@ -342,10 +364,14 @@ def _pairs(heads, starts):
 
 
 def bwd_dq(cu, ops: Operands, G, D, LSE, scale=None, causal=True, mode=MODE_ROUNDED,
-           per_row_ds=False, qblocks=None, want_flags=False):
+           per_row_ds=False, qblocks=None, want_flags=False, kpre=None):
     """dQ (float64 [T][Hq][d]) for the listed (q head, block start) pairs
     (default: every block of every head).  G: dequantized dO; D: [Hq][T];
-    LSE: [Hq][T] natural log as saved by a forward."""
+    LSE: [Hq][T] natural log as saved by a forward.  With kpre (int32
+    [Hq][T] prescale exponents) returns (dQ, dQ16): dQ16 is the same
+    gradient through the FP16 accumulation model (per 128-key tile partials
+    boosted by 2^(kpre + f), rounded to FP16, summed in FP16 in tile
+    order)."""
     cu = _c(cu, np.int32)
     T, Hq, Hkv, d = ops.T, ops.Hq, ops.Hkv, ops.d
     scale = default_scale(d) if scale is None else scale
@@ -356,11 +382,16 @@ def bwd_dq(cu, ops: Operands, G, D, LSE, scale=None, causal=True, mode=MODE_ROUN
     tie = np.zeros((T, Hq), dtype=np.float64)
     acc = np.zeros((T, Hq), dtype=np.float64)
     absm = np.zeros((T, Hq), dtype=np.float64)
+    kp = _c(kpre, np.int32) if kpre is not None else None
+    dq16 = np.zeros((T, Hq, d), dtype=np.float64) if kpre is not None else None
     _check(_load().orc_bwd_dq(
         T, len(cu) - 1, _p(cu), Hq, Hkv, d, ctypes.c_double(scale), int(bool(causal)),
         *ops.ptrs(), _p(_c(G, np.float64)), _p(_c(D, np.float64)), _p(_c(LSE, np.float64)),
         mode, int(bool(per_row_ds)), ctypes.c_int64(qblocks.shape[0]), _p(qblocks), _p(dQ),
-        _p(tie), _p(acc), _p(absm)))
+        _p(tie), _p(acc), _p(absm), _p(kp) if kp is not None else None,
+        _p(dq16) if dq16 is not None else None))
+    if kpre is not None:
+        return (dQ, dq16, tie, acc, absm) if want_flags else (dQ, dq16)
     return (dQ, tie, acc, absm) if want_flags else dQ
 
 

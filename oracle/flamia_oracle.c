@@ -117,6 +117,30 @@ uint8_t orc_e4m3_encode(double y)
     return (uint8_t)(sign | mag);
 }
 
+/* IEEE binary16 rounding of a double (the dQ accumulator's format, [R] S4
+ * "Forward locality and backward locality differ": a five-bit exponent):
+ * nearest value with ties to the even significand; normals carry 10
+ * fraction bits from 2^-14 up, subnormals are multiples of 2^-24, and
+ * magnitudes from 65520 (half way between the largest finite value 65504 and
+ * the next power of two) on round to infinity.  The sign is kept. */
+double orc_f16_round(double x)
+{
+    double a = fabs(x);
+    double r;
+    if (isnan(x)) return x;
+    if (a >= 65520.0) {
+        r = INFINITY;
+    } else if (a < ldexp(1.0, -14)) {
+        r = ldexp(rne_nonneg(ldexp(a, 24)), -24);
+    } else {
+        int E;
+        frexp(a, &E);
+        E -= 1; /* a in [2^E, 2^(E+1)) */
+        r = ldexp(rne_nonneg(ldexp(a, 10 - E)), E - 10);
+    }
+    return signbit(x) ? -r : r;
+}
+
 double orc_e4m3_decode(uint8_t c)
 {
     int E = (c >> 3) & 15, M = c & 7;
@@ -736,6 +760,41 @@ int orc_bwd_prep(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double
     return ORC_OK;
 }
 
+/* Sequence-wide dQ prescale (test-only negative control; [R] S4 "Forward
+ * locality and backward locality differ" and [K] S3.3: the size estimate
+ * taken from sequence-wide maxima of the dO, V and K magnitudes, which lets
+ * a later token change the FP16 rounding of every earlier row).  Reading:
+ * the same bound as the causal rule with every maximum taken over all tokens
+ * of all documents (head h for dO, its kv head for V and K):
+ *     kpre = 14 - C - (max e_dO + max e_V + max e_K),
+ * clamped to [-60, 60], for every row of every document; 0 for padding rows.
+ * do_exps: [Hq][T] (the dO exponents orc_bwd_prep returns). */
+int orc_bwd_prescale_seq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale,
+                         const uint8_t* do_exps, const uint8_t* ke, const uint8_t* ve,
+                         int32_t* kpre)
+{
+    if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
+    if (Hkv < 1 || Hq % Hkv != 0) return ORC_EBADARG;
+    int C = (int)ceil(log2(4.0 * scale * d * 448.0 * 448.0 * 448.0));
+    int ntok = cu[B];
+    for (int h = 0; h < Hq; ++h) {
+        int g = h * Hkv / Hq;
+        int mg = -1000, mv = -1000, mk = -1000;
+        for (int t = 0; t < ntok; ++t) {
+            int eg = (int)do_exps[(size_t)h * T + t] - 127;
+            int ev = (int)ve[(size_t)g * T + t] - 127, ek = (int)ke[(size_t)g * T + t] - 127;
+            mg = eg > mg ? eg : mg;
+            mv = ev > mv ? ev : mv;
+            mk = ek > mk ? ek : mk;
+        }
+        int k = 14 - C - (mg + mv + mk);
+        if (k < -60) k = -60;
+        if (k > 60) k = 60;
+        for (int t = 0; t < T; ++t) kpre[(size_t)h * T + t] = t < ntok ? k : 0;
+    }
+    return ORC_OK;
+}
+
 typedef struct {
     const orc_attn* a;
     const double* G;   /* dequantized dO, [T][Hq][d] */
@@ -883,19 +942,23 @@ int orc_bwd_dq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double s
                const double* Q, const double* K, const double* V, const double* Qs,
                const double* Ks, const double* G, const double* D, const double* LSE, int mode,
                int per_row_ds, int64_t n, const int32_t* qblocks, double* dQ, double* tie,
-               double* acc_mag, double* abs_mag)
+               double* acc_mag, double* abs_mag, const int32_t* kpre, double* dq16)
 {
     if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
     if (Hkv < 1 || Hq % Hkv != 0) return ORC_EBADARG;
     if (check_blocks(B, cu, n, qblocks, Hq) != ORC_OK) return ORC_EBADARG;
     orc_attn a = {T, B, Hq, Hkv, d, causal, cu, scale, Q, K, V, Qs, Ks};
     orc_bwd w = {&a, G, D, LSE, mode, per_row_ds};
+    int fexp;
+    frexp(scale, &fexp);
+    fexp -= 1; /* 2^fexp <= scale < 2^(fexp + 1) */
 #pragma omp parallel
     {
         double* buf = (double*)malloc(sizeof(double) * 6 * 1024);
         double* stp = (double*)malloc(sizeof(double) * 3 * 1024);
         double* part = (double*)malloc(sizeof(double) * 32 * d);
         double* absp = (double*)malloc(sizeof(double) * 32 * d);
+        double* acc16 = (double*)malloc(sizeof(double) * 32 * d);
 #pragma omp for schedule(dynamic)
         for (int64_t k = 0; k < n; ++k) {
             int h = qblocks[2 * k], q0 = qblocks[2 * k + 1];
@@ -904,7 +967,7 @@ int orc_bwd_dq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double s
             int kend = causal ? q1 : cu[b + 1];
             double *P = buf, *dP = buf + 1024, *dS = buf + 2048, *Pq = buf + 3072,
                    *dSk = buf + 4096, *dSq = buf + 5120;
-            for (int x = 0; x < 32 * d; ++x) part[x] = absp[x] = 0.0;
+            for (int x = 0; x < 32 * d; ++x) part[x] = absp[x] = acc16[x] = 0.0;
             for (int k0 = cu[b]; k0 < kend; k0 += 32) {
                 int k1 = k0 + 32 < cu[b + 1] ? k0 + 32 : cu[b + 1];
                 bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq, stp);
@@ -927,7 +990,7 @@ int orc_bwd_dq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double s
                             ab += fabs(t);
                         }
                         out[c] += scale * acc;
-                        part[(i - q0) * d + c] += scale * acc;
+                        part[(i - q0) * d + c] += acc;
                         absp[(i - q0) * d + c] += scale * ab;
                     }
                 }
@@ -938,24 +1001,41 @@ int orc_bwd_dq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double s
                         abs_mag[(size_t)i * Hq + h] = m;
                     }
                 /* per 128-key tile (document-relative): add the tile partial's
-                   largest magnitude to the row's accumulation magnitude */
-                if (acc_mag && (((k0 - cu[b]) / 32) % 4 == 3 || k0 + 32 >= kend)) {
+                   largest magnitude to the row's accumulation magnitude.
+                   With kpre, the FP16 accumulation model: the unscaled
+                   partial dS^ K^ of the tile times 2^(kpre_i + f), where
+                   2^f <= scale < 2^(f + 1), rounded to FP16 and added into
+                   an FP16 accumulator (rounded again) in key-tile order; the
+                   result is the accumulator times scale / 2^(kpre_i + f) */
+                if ((acc_mag || kpre) && (((k0 - cu[b]) / 32) % 4 == 3 || k0 + 32 >= kend)) {
                     for (int i = q0; i < q1; ++i) {
                         double m = 0.0;
+                        int kp = kpre ? kpre[(size_t)h * T + i] + fexp : 0;
                         for (int c = 0; c < d; ++c) {
-                            double v = fabs(part[(i - q0) * d + c]);
+                            double* pc = &part[(i - q0) * d + c];
+                            double v = scale * fabs(*pc);
                             m = v > m ? v : m;
-                            part[(i - q0) * d + c] = 0.0;
+                            if (kpre) {
+                                double* ac = &acc16[(i - q0) * d + c];
+                                *ac = orc_f16_round(*ac + orc_f16_round(ldexp(*pc, kp)));
+                            }
+                            *pc = 0.0;
                         }
-                        acc_mag[(size_t)i * Hq + h] += m;
+                        if (acc_mag) acc_mag[(size_t)i * Hq + h] += m;
                     }
                 }
+                if (kpre && dq16 && k0 + 32 >= kend)
+                    for (int i = q0; i < q1; ++i)
+                        for (int c = 0; c < d; ++c)
+                            dq16[((size_t)i * Hq + h) * d + c] =
+                                scale * ldexp(acc16[(i - q0) * d + c], -(kpre[(size_t)h * T + i] + fexp));
             }
         }
         free(buf);
         free(stp);
         free(part);
         free(absp);
+        free(acc16);
     }
     return ORC_OK;
 }

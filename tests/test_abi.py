@@ -89,6 +89,12 @@ def test_invalid_arguments_rejected_before_launch():
         F.FLAMIA_ERR_UNSUPPORTED
     assert bwd(P(_problem(flags=had | F.FLAMIA_DETERMINISTIC)), *args16, vp, wsb, None) == \
         F.FLAMIA_ERR_UNSUPPORTED
+    # the sequence-wide prescale control has no deterministic backward (FP32
+    # dQ, no prescale); bit 5 is a known flag, bit 7 is not
+    seqc = F.FLAMIA_CAUSAL | F.FLAMIA_DQ_PRESCALE_SEQUENCE
+    assert bwd(P(_problem(flags=seqc | F.FLAMIA_DETERMINISTIC)), *args16, vp, wsb, None) == \
+        F.FLAMIA_ERR_UNSUPPORTED
+    assert F.flamia_attn_bwd_workspace_size(_problem(flags=seqc)) == wsb
     q = lib.flamia_quantize_tokblock
     assert q(P(_problem()), 1, F.FLAMIA_SCALE_NVFP4_16 | F.FLAMIA_SCALE_ROTATE, vp, vp, vp, None) == \
         F.FLAMIA_ERR_INVALID_ARG

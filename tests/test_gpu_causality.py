@@ -11,11 +11,12 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_helpers import check_grad, log, oracle_operands, run_gpu
+from tests.gpu_helpers import check_grad, dq_tiles, log, oracle_operands, run_gpu
 
 pytestmark = pytest.mark.gpu
 
 DET = 1 | 8  # causal | deterministic
+SEQC = 1 | 32  # causal | sequence-wide dQ prescale (negative control)
 
 
 def _perturb(x, rows, factor):
@@ -198,3 +199,40 @@ def test_leak_probe_table5():
     assert res["ceil"]["O same block"] <= 1e-2 * res["floor"]["O same block"]
     # per-token scales: no earlier output depends on a later token at all
     assert res["exact"]["O earlier blocks"] == 0.0 and res["exact"]["O same block"] == 0.0
+
+
+def test_sequence_prescale_control():
+    """The sequence-wide dQ prescale, a test-only negative control (review
+    section 4 "Forward locality and backward locality differ"; jaehun.me
+    section 3.3).  Its exponents are bit-exact against the oracle's rule.  A
+    V outlier in the last block of a later document lowers them for every
+    earlier row, while the method's per-row exponents of those rows stay put.
+    dQ under the control keeps parity: only its FP16 rounding moves.  (The
+    size of that move is measured on the oracle's FP16 accumulation model:
+    on the GPU it is as small as the run-to-run spread of the atomic order.)"""
+    lens, cap = [130, 90], 240
+    first = 130 + 64  # the perturbed token's block
+    runs = {}
+    for perturb in (False, True):
+        w = _make(lens, cap, Hq=2, Hkv=1, d=64, seed=54)
+        if perturb:
+            w.v = _perturb(w.v, slice(200, 201), 4096.0)
+        q, k, v = oracle_operands(w)
+        ctl = run_gpu(w, flags=SEQC)
+        met = run_gpu(w, flags=1)
+        gc, ge, D, kc = oracle.bwd_prep(w.cu, w.do, ctl["O"], k[1], v[1], w.Hkv)
+        ks = oracle.bwd_prescale_seq(w.cu, ge, k[1], v[1], w.Hkv, w.d)
+        assert np.array_equal(ctl["kpre"].astype(np.int32), ks)
+        assert np.array_equal(met["kpre"].astype(np.int32), kc)
+        runs[perturb] = dict(w=w, ctl=ctl, met=met, ops=oracle.Operands.from_codes(q, k, v),
+                             G=oracle.dequantize(gc, ge), D=D)
+    a, b = runs[False], runs[True]
+    assert np.array_equal(a["met"]["kpre"][:, :first], b["met"]["kpre"][:, :first])
+    assert np.all(b["ctl"]["kpre"][:, :first] < a["ctl"]["kpre"][:, :first])
+    log("sequence-wide prescale: earlier rows' exponent %d -> %d; per-row rule unchanged"
+        % (int(a["ctl"]["kpre"][0, 0]), int(b["ctl"]["kpre"][0, 0])))
+    w = b["w"]
+    dQ, tq, acc, aq = oracle.bwd_dq(w.cu, b["ops"], b["G"], b["D"],
+                                    b["ctl"]["LSE"].astype(np.float64), want_flags=True)
+    nt = np.repeat(dq_tiles(w.cu, w.T, True)[:, None], w.Hq, axis=1)
+    check_grad(b["ctl"]["dQ"], dQ, "dQ, sequence-wide prescale", tq, acc=acc, ntiles=nt, absm=aq)
