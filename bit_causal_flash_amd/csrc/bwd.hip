@@ -174,7 +174,7 @@ __device__ __forceinline__ void dq_region_atomics(const v16f& acc0, const v16f& 
 template <int D, bool WITH_DQ, int MODE>
 __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
 {
-    constexpr int PITCH = D + 16;   // token-major code tiles
+    using CT = CodeTile<D>;         // token-major code tiles (swizzled rows at D = 128)
     constexpr int PITCH16 = 2 * D + 16;
     constexpr int SPITCH = 64 + 16; // P^ / dS^ tiles, key-major: [128 keys][64 queries]
     constexpr int NKS = D / 64;
@@ -183,9 +183,9 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
     constexpr int CPR = D / 16;
     constexpr bool EXACT = MODE != MODE_BLOCK;
     constexpr bool FP4 = MODE == MODE_FP4;
-    __shared__ __attribute__((aligned(16))) uint8_t s_kt[128 * PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t s_q[3][64 * PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t s_do[3][64 * PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_kt[128 * CT::PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[3][64 * CT::PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_do[3][64 * CT::PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t s_p[2][128 * SPITCH];
     __shared__ __attribute__((aligned(16))) uint8_t s_ds[2][128 * SPITCH];
     __shared__ int s_eq[3][64], s_edo[3][64], s_kq[3][64];
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
         const int t = k0 + row;
         v4i kv = {0, 0, 0, 0};
         if (t < e) kv = *(const v4i*)(a.k_codes + ((size_t)t * Hkv + hk) * D + col);
-        *(v4i*)(s_kt + row * PITCH + col) = kv;
+        *(v4i*)(s_kt + CT::off(row, col)) = kv;
     }
     // K block exponents of the dQ MFMA (lane = key of block kg); with
     // per-token exponents the block maximum and this key's fold factor
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
             const bool isq = c < 4 * D;
             const int cc = isq ? c : c - 4 * D;
             const int row = cc / CPR, col = 16 * (cc % CPR);
-            *(v4i*)((isq ? s_q[buf] : s_do[buf]) + row * PITCH + col) = r.c[k];
+            *(v4i*)((isq ? s_q[buf] : s_do[buf]) + CT::off(row, col)) = r.c[k];
         }
         const int row = tid & 63;
         s_eq[buf][row] = r.ok ? r.eq : 127;
@@ -362,12 +362,12 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                             const int eqr = s_eq[c3][qr];
 #pragma unroll
                             for (int ks = 0; ks < NKS; ++ks)
-                                sacc[t] = mfma_f8(row_operand(sq + qr * PITCH + 64 * ks, lane), kf[ks],
+                                sacc[t] = mfma_f8(tile_row_operand<D>(sq, qr, 64 * ks, lane), kf[ks],
                                                   sacc[t], eqr, ek);
                         }
 #pragma unroll
                         for (int ks = 0; ks < NKS; ++ks)
-                            pacc[t] = mfma_f8(row_operand(sg + qr * PITCH + 64 * ks, lane), vf[ks],
+                            pacc[t] = mfma_f8(tile_row_operand<D>(sg, qr, 64 * ks, lane), vf[ks],
                                               pacc[t], edr, ev);
                     }
                 }
@@ -490,9 +490,9 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                     const int dsg = s_dsexp[pb][g][kg];
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
-                        dv[dt] = mfma_f8(lds_tr_operand(sg, PITCH, 0, 32 * dt, lane), pfull, dv[dt],
+                        dv[dt] = mfma_f8(tile_tr_operand<D>(sg, 0, 32 * dt, lane), pfull, dv[dt],
                                          sdo, kScaleMinus8);
-                        dk[dt] = mfma_f8(lds_tr_operand(sq, PITCH, 0, 32 * dt, lane), dfull, dk[dt],
+                        dk[dt] = mfma_f8(tile_tr_operand<D>(sq, 0, 32 * dt, lane), dfull, dk[dt],
                                          sqe, dsg);
                     }
                 }
@@ -520,14 +520,14 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                             for (int i = 0; i < 2; ++i) {
 #pragma unroll
                                 for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
-                                acc[i] = mfma_f8(a0, lds_tr_operand(s_kt, PITCH, 0, 32 * (dt0 + i), lane),
+                                acc[i] = mfma_f8(a0, tile_tr_operand<D>(s_kt, 0, 32 * (dt0 + i), lane),
                                                  acc[i], sa0, s_ekb[g]);
                             }
                             if (k0 + 64 < e) {
                                 const v8i a1 = lds_tr_operand(sdq + 64 * SPITCH, SPITCH, 0, 32 * ct, lane);
 #pragma unroll
                                 for (int i = 0; i < 2; ++i)
-                                    acc[i] = mfma_f8(a1, lds_tr_operand(s_kt + 64 * PITCH, PITCH, 0,
+                                    acc[i] = mfma_f8(a1, tile_tr_operand<D>(s_kt, 64,
                                                                         32 * (dt0 + i), lane),
                                                      acc[i], sa1, s_ekb[2 + g]);
                             }

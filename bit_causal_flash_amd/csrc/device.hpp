@@ -156,6 +156,70 @@ __device__ __forceinline__ v8i row_operand(const uint8_t* row, int lane)
     return o;
 }
 
+// Token-major E4M3 code tiles in LDS (K, V, Q, dO: one row per token, D
+// bytes).  D = 128: rows of exactly 128 bytes whose 16-byte chunks are
+// permuted by XOR with tile_swizzle(row).  On gfx950's 64 four-byte banks
+// this leaves no bank conflict in the three patterns the kernels use: eight
+// lanes per row (staging stores), 16-byte operand reads of the permuted rows
+// of perm_row, and ds_read_b64_tr_b8 over eight consecutive rows (without
+// it, a 144-byte pitch conflicts 2-way on the transposed reads and on the
+// stores).  D = 64: rows padded to 80 bytes, not permuted.
+__device__ __forceinline__ int tile_swizzle(int row) { return (row & 6) | ((row >> 4) & 1); }
+
+template <int D>
+struct CodeTile {
+    static constexpr bool SWZ = D == 128;
+    static constexpr int PITCH = SWZ ? 128 : D + 16;
+    // byte offset of column `col` (a multiple of 8) of row `row`
+    __device__ static __forceinline__ int off(int row, int col)
+    {
+        if constexpr (SWZ) return row * 128 + ((((col >> 4) ^ tile_swizzle(row)) << 4) | (col & 15));
+        else return row * PITCH + col;
+    }
+};
+
+// row_operand of row `row` of a code tile, from byte column col0.
+template <int D>
+__device__ __forceinline__ v8i tile_row_operand(const uint8_t* tile, int row, int col0, int lane)
+{
+    using CT = CodeTile<D>;
+    const int g = lane >> 5;
+    v4i a = *(const v4i*)(tile + CT::off(row, col0 + 16 * g));
+    v4i b = *(const v4i*)(tile + CT::off(row, col0 + 32 + 16 * g));
+    v8i o;
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    return o;
+}
+
+// lds_tr_operand over a code tile; row0 is a multiple of 32.  The four
+// reads of a lane fall on rows row0 + r + 16 g + {0, 8, 32, 40} (r < 8), whose
+// swizzle is the same, (r & 6) | g, so one address serves all four.
+template <int D>
+__device__ __forceinline__ v8i tile_tr_operand(const uint8_t* tile, int row0, int col0, int lane)
+{
+    using CT = CodeTile<D>;
+    if constexpr (!CT::SWZ) {
+        return lds_tr_operand(tile, CT::PITCH, row0, col0, lane);
+    } else {
+        const int grp = lane >> 4;
+        const int l16 = lane & 15;
+        const int g = grp >> 1;
+        const int col = col0 + 16 * (grp & 1) + 8 * (l16 & 1);
+        const int r = l16 >> 1;
+        const int sw = (r & 6) | g;
+        const uint8_t* base = tile + (row0 + r) * 128 + ((((col >> 4) ^ sw) << 4) | (col & 15));
+        v2i a = lds_read_tr8(base + (16 * g) * 128);
+        v2i b = lds_read_tr8(base + (16 * g + 8) * 128);
+        v2i c = lds_read_tr8(base + (32 + 16 * g) * 128);
+        v2i d = lds_read_tr8(base + (40 + 16 * g) * 128);
+        v8i o;
+        o[0] = a.x; o[1] = a.y; o[2] = b.x; o[3] = b.y;
+        o[4] = c.x; o[5] = c.y; o[6] = d.x; o[7] = d.y;
+        return o;
+    }
+}
+
 // Token of the 64-token step held by accumulator row `rho` of tile t when
 // the rows are permuted so that, in the accumulator, lane group g holds the
 // tokens whose positions match the k layout above: VGPR v of tile t in lane

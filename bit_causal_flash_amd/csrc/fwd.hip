@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
         fwd_padding<D>(a, (int)blockIdx.x - a.work_wgs);
         return;
     }
-    constexpr int PITCH = D + 16;      // LDS row pitch (bytes): spreads rows over banks
+    using CT = CodeTile<D>;            // K and V code tiles (swizzled rows at D = 128)
     constexpr int PITCH16 = 2 * D + 16;
     constexpr int NKS = D / 64;        // k steps over the head dim (E4M3 S)
     constexpr int NKH = D / 16;        // k steps over the head dim (FP16 S)
@@ -205,8 +205,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
     constexpr int CPR = D / 16;        // 16-byte chunks per row
     constexpr bool FP4 = MODE == MODE_FP4;
     constexpr bool FOLD = MODE != MODE_BLOCK;
-    __shared__ __attribute__((aligned(16))) uint8_t s_k[2][FP4 ? 64 * PITCH16 : 64 * PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t s_v[2][64 * PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_k[2][FP4 ? 64 * PITCH16 : 64 * CT::PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_v[2][64 * CT::PITCH];
     __shared__ int s_ek[2][64];
     __shared__ int s_ev[2][2];
     __shared__ __attribute__((aligned(16))) float s_vf[2][FOLD ? 64 : 1];
@@ -268,8 +268,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
         for (int k = 0; k < KVTile<D, MODE>::NC; ++k) {
             const int c = tid + 256 * k;
             const int row = c / CPR, col = 16 * (c % CPR);
-            if constexpr (!FP4) *(v4i*)(&s_k[buf][row * PITCH + col]) = t.k[k];
-            *(v4i*)(&s_v[buf][row * PITCH + col]) = t.v[k];
+            if constexpr (!FP4) *(v4i*)(&s_k[buf][CT::off(row, col)]) = t.k[k];
+            *(v4i*)(&s_v[buf][CT::off(row, col)]) = t.v[k];
         }
         if constexpr (FP4) {
             // the row's features (tid % 4) D / 4 .. + D / 4 - 1 as FP16
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
                     const int ek = s_ek[cur][krow];
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
-                        sacc[t] = mfma_f8(row_operand(sk + krow * PITCH + 64 * ks, lane), qf[ks],
+                        sacc[t] = mfma_f8(tile_row_operand<D>(sk, krow, 64 * ks, lane), qf[ks],
                                           sacc[t], ek, eq);
                 }
             }
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
             const int sv_exp = s_ev[cur][g];
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
-                oacc[dt] = mfma_f8(lds_tr_operand(sv, PITCH, 0, 32 * dt, lane), pf, oacc[dt],
+                oacc[dt] = mfma_f8(tile_tr_operand<D>(sv, 0, 32 * dt, lane), pf, oacc[dt],
                                    sv_exp, sp);
         }
         stage(nxt, cur ^ 1);
