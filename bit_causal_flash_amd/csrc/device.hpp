@@ -164,6 +164,8 @@ __device__ __forceinline__ v8i row_operand(const uint8_t* row, int lane)
 // of perm_row, and ds_read_b64_tr_b8 over eight consecutive rows (without
 // it, a 144-byte pitch conflicts 2-way on the transposed reads and on the
 // stores).  D = 64: rows padded to 80 bytes, not permuted.
+typedef __attribute__((address_space(3))) void lds_void;  // LDS pointer of direct loads
+
 __device__ __forceinline__ int tile_swizzle(int row) { return (row & 6) | ((row >> 4) & 1); }
 
 template <int D>

@@ -32,14 +32,16 @@ namespace flamia {
 
 namespace {
 
-// One 64-key step of K and V, as staged for the forward: D / 64 16-byte
-// chunks per thread of the V codes and of the K codes (MODE_FP4: D / 8 bytes
-// of the row's E2M1 K codes and the D / 64 scale bytes they use), and the
-// raw exponents of key tid % 64 (K, and in the exact modes V) and of the V
-// block of tid % 2.  Every load is unconditional, rows past the document end
-// clamped to its last row (staging replaces their exponents, and the masks
-// zero their weights), so that the only wait on the prefetch is where it is
-// staged.
+// One 64-key step of K and V, as staged for the forward through registers:
+// D / 64 16-byte chunks per thread of the V codes and of the K codes
+// (MODE_FP4: D / 8 bytes of the row's E2M1 K codes and the D / 64 scale bytes
+// they use), and the raw exponents of key tid % 64 (K, and in the exact modes
+// V) and of the V block of tid % 2.  At D = 128 the E4M3 codes bypass the
+// registers (direct global -> LDS loads, see fwd_kernel) and only the rest
+// comes through here.  Every load is unconditional, rows past the document
+// end clamped to its last row (staging replaces their exponents, and the
+// masks zero their weights), so that the only wait on the prefetch is where
+// it is staged.
 template <int D, int MODE>
 struct KVTile {
     static constexpr int NC = D / 64;
@@ -56,14 +58,16 @@ __device__ __forceinline__ void load_kvtile(const AttnArgs& a, KVTile<D, MODE>& 
     constexpr int CPR = D / 16;
     const int Hkv = a.Hkv;
     const size_t T = (size_t)a.T;
+    if constexpr (D != 128) {
 #pragma unroll
-    for (int k = 0; k < KVTile<D, MODE>::NC; ++k) {
-        const int c = tid + 256 * k;
-        const int row = c / CPR, col = 16 * (c % CPR);
-        const int t = min(kt0 + row, e - 1);
-        if constexpr (MODE != MODE_FP4)
-            r.k[k] = *(const v4i*)(a.k_codes + ((size_t)t * Hkv + hk) * D + col);
-        r.v[k] = *(const v4i*)(a.v_codes + ((size_t)t * Hkv + hk) * D + col);
+        for (int k = 0; k < KVTile<D, MODE>::NC; ++k) {
+            const int c = tid + 256 * k;
+            const int row = c / CPR, col = 16 * (c % CPR);
+            const int t = min(kt0 + row, e - 1);
+            if constexpr (MODE != MODE_FP4)
+                r.k[k] = *(const v4i*)(a.k_codes + ((size_t)t * Hkv + hk) * D + col);
+            r.v[k] = *(const v4i*)(a.v_codes + ((size_t)t * Hkv + hk) * D + col);
+        }
     }
     if constexpr (MODE == MODE_FP4) {
         // thread -> key row tid / 4, features (tid % 4) D / 4 .. + D / 4 - 1
@@ -261,15 +265,38 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
     float base = -INFINITY;  // reference the accumulators are kept in
     float l = 0.f;           // sum of rounded weights
 
+    // D = 128: the E4M3 code tiles go from global memory straight into the
+    // swizzled LDS layout.  Wave w fills rows 16 w .. 16 w + 15 of each tile
+    // with two loads of 1 KB (eight rows), lane L of a load writing LDS bytes
+    // 16 L .. 16 L + 15 of its block: row + L / 8, physical chunk L % 8, so it
+    // fetches the logical chunk (L % 8) ^ tile_swizzle(row).
+    constexpr bool DMA = CT::SWZ;
+    auto dma = [&](int kt0, int buf) {
+        if constexpr (DMA) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int rb = 16 * wave + 8 * i;
+                const int row = rb + (lane >> 3);
+                const int c = (lane & 7) ^ tile_swizzle(row);
+                const size_t src = ((size_t)min(kt0 + row, e - 1) * Hkv + hk) * D + 16 * c;
+                if constexpr (!FP4)
+                    __builtin_amdgcn_global_load_lds(a.k_codes + src, (lds_void*)&s_k[buf][rb * 128], 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(a.v_codes + src, (lds_void*)&s_v[buf][rb * 128], 16, 0, 0);
+            }
+        }
+    };
+
     // every thread writes (the four waves write identical exponents), so
     // that every prefetched register is consumed on every path
     auto stage = [&](const KVTile<D, MODE>& t, int buf) {
+        if constexpr (!DMA) {
 #pragma unroll
-        for (int k = 0; k < KVTile<D, MODE>::NC; ++k) {
-            const int c = tid + 256 * k;
-            const int row = c / CPR, col = 16 * (c % CPR);
-            if constexpr (!FP4) *(v4i*)(&s_k[buf][CT::off(row, col)]) = t.k[k];
-            *(v4i*)(&s_v[buf][CT::off(row, col)]) = t.v[k];
+            for (int k = 0; k < KVTile<D, MODE>::NC; ++k) {
+                const int c = tid + 256 * k;
+                const int row = c / CPR, col = 16 * (c % CPR);
+                if constexpr (!FP4) *(v4i*)(&s_k[buf][CT::off(row, col)]) = t.k[k];
+                *(v4i*)(&s_v[buf][CT::off(row, col)]) = t.v[k];
+            }
         }
         if constexpr (FP4) {
             // the row's features (tid % 4) D / 4 .. + D / 4 - 1 as FP16
@@ -295,6 +322,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
 
     KVTile<D, MODE> nxt;
     load_kvtile<D, MODE>(a, nxt, hk, s, e, tid);
+    dma(s, 0);
     stage(nxt, 0);
     // every load issued so far has landed (vmcnt(0)), so that inside the loop
     // only the prefetch of the next step is outstanding
@@ -305,7 +333,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
         const int cur = st & 1;
         const int kt0 = s + 64 * st;
         // prefetch the next step (the last step reloads its own, unused)
-        load_kvtile<D, MODE>(a, nxt, hk, min(kt0 + 64, s + 64 * (nsteps - 1)), e, tid);
+        const int kn0 = min(kt0 + 64, s + 64 * (nsteps - 1));
+        load_kvtile<D, MODE>(a, nxt, hk, kn0, e, tid);
+        dma(kn0, cur ^ 1);
         const uint8_t* sk = s_k[cur];
         const uint8_t* sv = s_v[cur];
 
@@ -349,6 +379,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
                                    sv_exp, sp);
         }
         stage(nxt, cur ^ 1);
+        // the direct loads count in vmcnt: they have landed once it is zero
+        if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0x0F70);
         lds_barrier();
     }
 
