@@ -172,11 +172,12 @@ int prescale_c(const Dims& d)
 
 flamia_status hip_status(hipError_t e) { return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP; }
 
-hipError_t record(const flamia_problem* p, bool start, hipStream_t s)
+// The caller's timing events, if any, for the launch of the call's main
+// kernel (stamped from its dispatch, see AttnArgs).
+void set_events(const flamia_problem* p, hipEvent_t& start, hipEvent_t& stop)
 {
-    if (p->events == nullptr) return hipSuccess;
-    void* ev = start ? p->events->attn_start : p->events->attn_stop;
-    return ev ? hipEventRecord((hipEvent_t)ev, s) : hipSuccess;
+    start = p->events ? (hipEvent_t)p->events->attn_start : nullptr;
+    stop = p->events ? (hipEvent_t)p->events->attn_stop : nullptr;
 }
 
 }  // namespace
@@ -234,11 +235,10 @@ flamia_status flamia_quantize_tokblock(const flamia_problem* p, int32_t num_head
     a.codes = codes;
     a.exps = exps;
     hipStream_t s = (hipStream_t)stream;
-    if (record(p, true, s) != hipSuccess) return FLAMIA_ERR_HIP;
+    set_events(p, a.ev_start, a.ev_stop);
     const hipError_t e = scale_mode == FLAMIA_SCALE_NVFP4_16 ? launch_nvfp4(a, p->head_dim, s)
                                                              : launch_quant(a, p->head_dim, false, s);
-    if (e != hipSuccess) return FLAMIA_ERR_HIP;
-    return hip_status(record(p, false, s));
+    return hip_status(e);
 }
 
 flamia_status flamia_quantize_qkv(const flamia_problem* p, int32_t scale_mode, const uint16_t* q,
@@ -274,9 +274,8 @@ flamia_status flamia_quantize_qkv(const flamia_problem* p, int32_t scale_mode, c
     a.ten[1] = QuantTensor{k, k_codes, k_exps, Hkv, rotate ? 1 : 0};
     a.ten[2] = QuantTensor{v, v_codes, v_exps, Hkv, 0};
     hipStream_t s = (hipStream_t)stream;
-    if (record(p, true, s) != hipSuccess) return FLAMIA_ERR_HIP;
-    if (launch_quant(a, p->head_dim, false, s) != hipSuccess) return FLAMIA_ERR_HIP;
-    return hip_status(record(p, false, s));
+    set_events(p, a.ev_start, a.ev_stop);
+    return hip_status(launch_quant(a, p->head_dim, false, s));
 }
 
 size_t flamia_attn_fwd_workspace_size(const flamia_problem* p)
@@ -336,10 +335,8 @@ flamia_status flamia_attn_fwd(const flamia_problem* p, const uint8_t* q_codes,
     a.k_fp4_scales = k_fp4_scales;
     a.o = o;
     a.lse = lse;
-    if (record(p, true, s) != hipSuccess) return FLAMIA_ERR_HIP;
-    e = launch_fwd(a, (int)d.d, w.max_items, s);
-    if (e != hipSuccess) return FLAMIA_ERR_HIP;
-    return hip_status(record(p, false, s));
+    set_events(p, a.ev_start, a.ev_stop);
+    return hip_status(launch_fwd(a, (int)d.d, w.max_items, s));
 }
 
 size_t flamia_attn_bwd_workspace_size(const flamia_problem* p)
@@ -462,10 +459,10 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     a.q_fp4_scales = q_fp4_scales;
     a.k_fp4 = k_fp4;
     a.k_fp4_scales = k_fp4_scales;
-    if (record(p, true, s) != hipSuccess) return FLAMIA_ERR_HIP;
+    set_events(p, a.ev_start, a.ev_stop);
     e = launch_bwd(a, (int)d.d, w.max_items, !d.deterministic, s);
     if (e != hipSuccess) return FLAMIA_ERR_HIP;
-    if (record(p, false, s) != hipSuccess) return FLAMIA_ERR_HIP;
+    a.ev_start = a.ev_stop = nullptr;
     if (d.deterministic) {
         // dQ by query-major blocks in FP32 registers, written directly
         const WorklistLayout wq = worklist_layout(d, kFwdTile, wl_base[1]);

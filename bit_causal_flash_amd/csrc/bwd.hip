@@ -803,7 +803,8 @@ hipError_t launch_bwd(const AttnArgs& a, int D, int max_items, bool with_dq, hip
 {
     if (max_items <= 0) return hipSuccess;
     const dim3 grid((unsigned)max_items * a.Hkv);
-#define FLAMIA_BWD(DD, WQ, MM) hipLaunchKernelGGL((bwd_kernel<DD, WQ, MM>), grid, dim3(512), 0, stream, a)
+#define FLAMIA_BWD(DD, WQ, MM) \
+    hipExtLaunchKernelGGL((bwd_kernel<DD, WQ, MM>), grid, dim3(512), 0, stream, a.ev_start, a.ev_stop, 0, a)
     if (D == 128) {
         if (a.mode == MODE_EXACT) {
             if (with_dq) FLAMIA_BWD(128, true, MODE_EXACT);

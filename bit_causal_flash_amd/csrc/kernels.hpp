@@ -2,6 +2,7 @@
 // the public interface is include/flamia.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,6 +37,8 @@ struct QuantArgs {
     float* delta;             // [H][T]
     int8_t* prescale;         // [H][T]
     _Float16* dq_acc;         // [T][H][D]
+    // optional: stamped with the start / end of the launch's kernel
+    hipEvent_t ev_start, ev_stop;
 };
 
 hipError_t launch_quant(const QuantArgs& a, int D, bool prep, hipStream_t stream);
@@ -88,6 +91,10 @@ struct AttnArgs {
     const int8_t* prescale;
     _Float16* dq_acc;
     uint16_t *dq, *dk, *dv;
+    // optional: stamped with the start / end of the forward kernel or of the
+    // backward main kernel (hipExtLaunchKernel: no extra packets in the
+    // stream, unlike hipEventRecord around the launch)
+    hipEvent_t ev_start, ev_stop;
 };
 
 hipError_t launch_fwd(const AttnArgs& a, int D, int max_items, hipStream_t stream);

@@ -471,7 +471,8 @@ hipError_t launch_nvfp4(const QuantArgs& a, int D, hipStream_t stream)
 {
     const size_t ng = (size_t)a.T * a.H * (D / 16);
     if (ng == 0) return hipSuccess;
-    hipLaunchKernelGGL(nvfp4_kernel, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, stream, a, D);
+    hipExtLaunchKernelGGL(nvfp4_kernel, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, stream, a.ev_start,
+                          a.ev_stop, 0, a, D);
     return hipGetLastError();
 }
 
@@ -482,13 +483,13 @@ hipError_t launch_quant(const QuantArgs& a, int D, bool prep, hipStream_t stream
     bool rotate = false;
     for (int i = 0; i < a.ntensors; ++i) rotate = rotate || a.ten[i].rotate;
     if (D == 128) {
-        if (prep) hipLaunchKernelGGL((quant_kernel<128, true, false>), grid, dim3(256), 0, stream, a);
-        else if (rotate) hipLaunchKernelGGL((quant_kernel<128, false, true>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((quant_kernel<128, false, false>), grid, dim3(256), 0, stream, a);
+        if (prep) hipExtLaunchKernelGGL((quant_kernel<128, true, false>), grid, dim3(256), 0, stream, a.ev_start, a.ev_stop, 0, a);
+        else if (rotate) hipExtLaunchKernelGGL((quant_kernel<128, false, true>), grid, dim3(256), 0, stream, a.ev_start, a.ev_stop, 0, a);
+        else hipExtLaunchKernelGGL((quant_kernel<128, false, false>), grid, dim3(256), 0, stream, a.ev_start, a.ev_stop, 0, a);
     } else {
-        if (prep) hipLaunchKernelGGL((quant_kernel<64, true, false>), grid, dim3(256), 0, stream, a);
-        else if (rotate) hipLaunchKernelGGL((quant_kernel<64, false, true>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((quant_kernel<64, false, false>), grid, dim3(256), 0, stream, a);
+        if (prep) hipExtLaunchKernelGGL((quant_kernel<64, true, false>), grid, dim3(256), 0, stream, a.ev_start, a.ev_stop, 0, a);
+        else if (rotate) hipExtLaunchKernelGGL((quant_kernel<64, false, true>), grid, dim3(256), 0, stream, a.ev_start, a.ev_stop, 0, a);
+        else hipExtLaunchKernelGGL((quant_kernel<64, false, false>), grid, dim3(256), 0, stream, a.ev_start, a.ev_stop, 0, a);
     }
     return hipGetLastError();
 }
