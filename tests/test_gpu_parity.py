@@ -33,7 +33,36 @@ def _workload(name, lens, cap, Hq, Hkv, d, causal, seed=0):
 def test_small_forward_backward(case):
     name, lens, cap, Hq, Hkv, d, causal = case
     log("case %s" % name)
-    w = _workload(*case)
+    _check_case(_workload(*case), name)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rising_scores_take_the_rescale_path(d):
+    """Scores that climb by about 50 (base-2 logits) along each document: the
+    forward keeps O and l in units of each query's first reference and moves
+    that base (with a rescale) once the reference has risen more than 32 above
+    it, which the later queries here do.  Parity as in the small cases."""
+    lens, cap, Hq, Hkv = [256, 200], 480, 2, 1
+    w = workloads.make("rising_d%d" % d, 7, cap, lens, Hq, Hkv, d)
+    rng = np.random.default_rng(8)
+    q = 1.0 + 0.05 * rng.standard_normal((cap, Hq, d))
+    k = 0.05 * rng.standard_normal((cap, Hkv, d)) + 1.0
+    alpha = np.zeros(cap)
+    for s, e in zip(w.cu[:-1], w.cu[1:]):
+        # q . k reaches d alpha: base-2 logits up to about 50
+        alpha[s:e] = np.linspace(0.0, 50.0 / (d ** 0.5 * 1.4426950408889634), e - s)
+    k *= alpha[:, None, None]
+    w.q = workloads.f32_to_bf16_bits(q.astype(np.float32))
+    w.k = workloads.f32_to_bf16_bits(k.astype(np.float32))
+    # the last query of the first document: its integer reference (the ceiling
+    # of its largest logit) rises by more than 32 after the first 64-key step
+    s2 = (q[255, 0] @ k[:256, 0].T) / d ** 0.5 * 1.4426950408889634
+    assert np.ceil(s2.max()) - np.ceil(s2[:64].max()) > 33
+    _check_case(w, "rising_d%d" % d)
+
+
+def _check_case(w, name):
+    Hq, Hkv, d, causal = w.Hq, w.Hkv, w.d, w.causal
     g = run_gpu(w)
     # quantizer: bit-exact
     q, k, v = oracle_operands(w)
