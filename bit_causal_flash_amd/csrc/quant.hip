@@ -178,37 +178,9 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
         }
     }
     __syncthreads();
-    // rotated rows (a row is spread over TPR consecutive lanes, 8 features
-    // each; rows that are not owned are zero and stay zero)
-    float yr[ROT ? NPASS : 1][8];
-    if (rot) {
-#pragma unroll
-        for (int p = 0; p < NPASS; ++p) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                yr[ROT ? p : 0][2 * k] = bf16_to_f32((uint16_t)(raw[p][k] & 0xffff));
-                yr[ROT ? p : 0][2 * k + 1] = bf16_to_f32((uint16_t)((uint32_t)raw[p][k] >> 16));
-            }
-            fwht_row<D>(yr[ROT ? p : 0], tid & 63);
-        }
-    }
-    // block maxima
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-        uint32_t m = 0;
-        if (rot) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(yr[ROT ? p : 0][k]) & 0x7fffffffu);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                m = max(m, max(((uint32_t)raw[p][k] << 16) & 0x7fff0000u, (uint32_t)raw[p][k] & 0x7fff0000u));
-        }
-        m = group_max<TPR>(m);
-        if (bsr[p] >= 0 && chunk == 0) atomicMax(&s_bmax[bsr[p] - w0], m);
-    }
-
     if constexpr (PREP) {
+        // (issued before the block maxima, so that these small loads overlap
+        // the row loads instead of following them)
         // for every block starting in the window, the largest V and K block
         // exponents over the keys its rows may see (keys before the block's
         // end, causal; the whole document otherwise), by the first wave.  The
@@ -279,6 +251,36 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a)
             }
         }
     }
+    // rotated rows (a row is spread over TPR consecutive lanes, 8 features
+    // each; rows that are not owned are zero and stay zero)
+    float yr[ROT ? NPASS : 1][8];
+    if (rot) {
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                yr[ROT ? p : 0][2 * k] = bf16_to_f32((uint16_t)(raw[p][k] & 0xffff));
+                yr[ROT ? p : 0][2 * k + 1] = bf16_to_f32((uint16_t)((uint32_t)raw[p][k] >> 16));
+            }
+            fwht_row<D>(yr[ROT ? p : 0], tid & 63);
+        }
+    }
+    // block maxima
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+        uint32_t m = 0;
+        if (rot) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(yr[ROT ? p : 0][k]) & 0x7fffffffu);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                m = max(m, max(((uint32_t)raw[p][k] << 16) & 0x7fff0000u, (uint32_t)raw[p][k] & 0x7fff0000u));
+        }
+        m = group_max<TPR>(m);
+        if (bsr[p] >= 0 && chunk == 0) atomicMax(&s_bmax[bsr[p] - w0], m);
+    }
+
     __syncthreads();
 
     // codes (and, for the backward preparation, D, the prescale exponent and
