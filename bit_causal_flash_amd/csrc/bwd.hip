@@ -344,6 +344,22 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                 // all S / dP MFMAs first, then the element-wise work
                 bool active[2];
                 v16f sacc[2], pacc[2];
+                // the rows' statistics (8 - LSE log2 e and D) into registers
+                // ahead of the MFMAs, so their LDS latency overlaps them (not
+                // with the FP16 score path, whose registers are spoken for)
+                float nlv[2][16], dlv[2][16];
+#pragma unroll
+                for (int t = 0; t < (FP4 ? 0 : 2); ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float4 x = *(const float4*)&s_nlse[c3][32 * t + 16 * g + 4 * i];
+                        const float4 y = *(const float4*)&s_delta[c3][32 * t + 16 * g + 4 * i];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            nlv[t][4 * i + k] = k == 0 ? x.x : k == 1 ? x.y : k == 2 ? x.z : x.w;
+                            dlv[t][4 * i + k] = k == 0 ? y.x : k == 1 ? y.y : k == 2 ? y.z : y.w;
+                        }
+                    }
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     active[t] = wave_keys && (!a.causal || qb + 32 * t + 31 >= kw0);
@@ -385,8 +401,8 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                         // D = 0.  Element v of lane group g is query
                         // qb + 32 t + 16 g + v.
                         const int q0 = 32 * t + 16 * g;
-                        const float* nl = &s_nlse[c3][q0];
-                        const float* dl = &s_delta[c3][q0];
+                        const float* nl = FP4 ? &s_nlse[c3][q0] : nlv[t];
+                        const float* dl = FP4 ? &s_delta[c3][q0] : dlv[t];
                         const bool full = kw0 + 32 <= e && (!a.causal || qb + 32 * t >= kw0 + 31);
                         float amax;
                         if (full) {
