@@ -253,3 +253,28 @@ def test_fused_qkv_quantizer_bit_exact(mode):
             rc, re = oracle.quantize(getattr(w, n), w.cu, block=blk)
         assert np.array_equal(host(got[i][0]), rc), n + " codes"
         assert np.array_equal(host(got[i][1]), re), n + " exponents"
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+def test_all_documents_empty(causal):
+    """Every row is padding: three zero-length documents over 64 rows of
+    random data.  Codes 0 and exponent bytes 127 (as the oracle's quantizer
+    gives), O = 0, LSE = +inf, the backward preparation's outputs as the
+    oracle's, and zero gradients."""
+    w = workloads.make("all_empty", 0, 64, [0, 0, 0], 2, 1, 64,
+                       flags=workloads.FLAG_CAUSAL if causal else 0)
+    log("all documents empty, causal=%d" % causal)
+    g = run_gpu(w)
+    q, k, v = oracle_operands(w)
+    for tag, (c, e) in (("q", q), ("k", k), ("v", v)):
+        assert np.all(c == 0) and np.all(e == 127)
+        assert np.array_equal(g[tag + "c"], c), tag + " codes"
+        assert np.array_equal(g[tag + "e"], e), tag + " exps"
+    assert np.all(g["O"] == 0)
+    assert np.all(np.isinf(g["LSE"])) and np.all(g["LSE"] > 0)
+    gc, ge, D, kpre = oracle.bwd_prep(w.cu, w.do, g["O"], k[1], v[1], w.Hkv, causal=causal)
+    assert np.array_equal(g["gc"], gc) and np.array_equal(g["ge"], ge)
+    assert np.array_equal(g["kpre"].astype(np.int32), kpre)
+    assert np.array_equal(g["D"], D.astype(np.float32))
+    for t in ("dQ", "dK", "dV"):
+        assert np.all(g[t] == 0), t
