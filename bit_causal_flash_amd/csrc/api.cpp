@@ -437,6 +437,7 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     }
     a.cu = p->cu_seqlens;
     a.count = w.count;
+    a.tickets = w.count + 1;
     a.items = w.items;
     a.q_codes = q_codes;
     a.q_exps = q_exps;

@@ -29,6 +29,8 @@
 // LDS traffic only.  The dQ partials (one per query tile and 128-key tile)
 // are added with packed FP16 atomics, whose throughput, not the MFMAs, bounds
 // the kernel on long documents.
+#include <algorithm>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -202,384 +204,405 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(16))) float s_fg[EXACT ? 3 : 1][64];
     __shared__ __attribute__((aligned(16))) uint8_t s_q16[FP4 ? 2 : 1][FP4 ? 64 * PITCH16 : 16];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5;
-    const int kg = wave & 3;
-    const bool scorer = wave < 4;
     const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
     const size_t T = (size_t)a.T;
-    const int item = blockIdx.x / Hkv, hk = blockIdx.x % Hkv;
-    if (item >= *a.count) return;
-    const int b = a.items[2 * item], kt = a.items[2 * item + 1];
-    const int s = a.cu[b], e = a.cu[b + 1];
-    const int k0 = s + 128 * kt;
-    const int kw0 = k0 + 32 * kg;
-    const int kj = kw0 + (lane & 31);
-    const bool kvalid = kj < e;
-    const bool wave_keys = kw0 < e;
-    const float c2 = a.c2;
-    const int krow = 32 * kg + (lane & 31);  // this lane's key in the key-major tiles
+    // Persistent: one workgroup per CU slot takes (item, kv head) tickets in
+    // cost order from an atomic counter (zeroed with the work list), the
+    // next ticket fetched while the current one runs, so no workgroup
+    // dispatch and no ticket latency sits between items.
+    __shared__ int s_ticket[2];
+    int* const next_ticket = a.tickets;
+    const int ntickets = *a.count * Hkv;
+    if (threadIdx.x == 0) s_ticket[0] = atomicAdd(next_ticket, 1);
+    __syncthreads();
+    for (int slot = 0;; slot ^= 1) {
+        const int ticket = __builtin_amdgcn_readfirstlane(s_ticket[slot]);
+        if (ticket >= ntickets) break;  // uniform: every thread read the slot after a barrier
+        // the thread index is re-read per item (opaque to the compiler), so
+        // lane-dependent offsets are recomputed per item instead of being
+        // held in registers across the whole loop
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, wave = wave_id(), g = lane >> 5;
+        const int kg = wave & 3;
+        const bool scorer = wave < 4;
+        if (tid == 0) s_ticket[slot ^ 1] = atomicAdd(next_ticket, 1);
+        const int item = ticket / Hkv, hk = ticket % Hkv;
+        const int b = a.items[2 * item], kt = a.items[2 * item + 1];
+        const int s = a.cu[b], e = a.cu[b + 1];
+        const int k0 = s + 128 * kt;
+        const int kw0 = k0 + 32 * kg;
+        const int kj = kw0 + (lane & 31);
+        const bool kvalid = kj < e;
+        const bool wave_keys = kw0 < e;
+        const float c2 = a.c2;
+        const int krow = 32 * kg + (lane & 31);  // this lane's key in the key-major tiles
 
-    // the workgroup's K tile, token-major, for the dQ MFMA (k = keys)
-    for (int c = tid; c < 128 * CPR; c += 512) {
-        const int row = c / CPR, col = 16 * (c % CPR);
-        const int t = k0 + row;
-        v4i kv = {0, 0, 0, 0};
-        if (t < e) kv = *(const v4i*)(a.k_codes + ((size_t)t * Hkv + hk) * D + col);
-        *(v4i*)(s_kt + CT::off(row, col)) = kv;
-    }
-    // K block exponents of the dQ MFMA (lane = key of block kg); with
-    // per-token exponents the block maximum and this key's fold factor
-    const int ek = kvalid ? (int)a.k_exps[(size_t)hk * T + kj] : 127;
-    float fk = 1.f;
-    if constexpr (EXACT) {
-        const uint32_t ekb = half_wave_max_u32(kvalid ? (uint32_t)ek : 0u);
-        fk = kvalid ? ldexpf(1.f, ek - (int)ekb) : 0.f;
-        if (scorer && lane == 0) s_ekb[kg] = (int)ekb;
-    } else {
-        if (tid < 4)
-            s_ekb[tid] = (k0 + 32 * tid < e) ? (int)a.k_exps[(size_t)hk * T + k0 + 32 * tid] : 127;
-    }
-
-    // iterations: q heads of the group (outer) x 64-query tiles that see the keys
-    const int qt_lo = a.causal ? 2 * kt : 0;
-    const int nqt = (e - s + 63) / 64 - qt_lo;
-    const int niter = G * nqt;
-    auto tile_head = [&](int j) { return hk * G + j / nqt; };
-    auto tile_base = [&](int j) { return s + 64 * (qt_lo + j % nqt); };
-
-    // The score waves (threads 0-255) fetch and stage the query tiles, so
-    // the gradient waves' dQ atomics never sit ahead of a load they must wait
-    // for.  Every staging thread writes (the waves write identical
-    // statistics), so that every prefetched register is consumed on every
-    // path.
-    using Tile = QTile<D, 256>;
-    auto stage = [&](const Tile& r, int buf, int buf2) {
-#pragma unroll
-        for (int k = 0; k < Tile::NC; ++k) {
-            const int c = tid + 256 * k;
-            const bool isq = c < 4 * D;
-            const int cc = isq ? c : c - 4 * D;
-            const int row = cc / CPR, col = 16 * (cc % CPR);
-            *(v4i*)((isq ? s_q[buf] : s_do[buf]) + CT::off(row, col)) = r.c[k];
+        // the workgroup's K tile, token-major, for the dQ MFMA (k = keys)
+        for (int c = tid; c < 128 * CPR; c += 512) {
+            const int row = c / CPR, col = 16 * (c % CPR);
+            const int t = k0 + row;
+            v4i kv = {0, 0, 0, 0};
+            if (t < e) kv = *(const v4i*)(a.k_codes + ((size_t)t * Hkv + hk) * D + col);
+            *(v4i*)(s_kt + CT::off(row, col)) = kv;
         }
-        const int row = tid & 63;
-        s_eq[buf][row] = r.ok ? r.eq : 127;
-        s_edo[buf][row] = r.ok ? r.edo : 127;
-        s_kq[buf][row] = r.ok ? r.pre + a.scale_exp : 0;
-        // 8 - LSE log2 e: exp2 of the score term then yields 256 P; rows past
-        // the document end get -inf, so their P is exactly zero
-        s_nlse[buf][row] = r.ok ? 8.f - r.lse * kLog2e : -INFINITY;
-        s_delta[buf][row] = r.ok ? r.delta : 0.f;
+        // K block exponents of the dQ MFMA (lane = key of block kg); with
+        // per-token exponents the block maximum and this key's fold factor
+        const int ek = kvalid ? (int)a.k_exps[(size_t)hk * T + kj] : 127;
+        float fk = 1.f;
         if constexpr (EXACT) {
-            // lane = query row: block maxima of the Q and dO exponents over
-            // each 32-query half and the rows' fold factors
-            const uint32_t eqr = r.ok ? (uint32_t)r.eq : 0u, egr = r.ok ? (uint32_t)r.edo : 0u;
-            const uint32_t eqb = half_wave_max_u32(eqr), egb = half_wave_max_u32(egr);
-            s_eqb[buf][row >> 5] = (int)eqb;
-            s_egb[buf][row >> 5] = (int)egb;
-            s_fq[buf][row] = r.ok ? ldexpf(1.f, (int)eqr - (int)eqb) : 0.f;
-            s_fg[buf][row] = r.ok ? ldexpf(1.f, (int)egr - (int)egb) : 0.f;
+            const uint32_t ekb = half_wave_max_u32(kvalid ? (uint32_t)ek : 0u);
+            fk = kvalid ? ldexpf(1.f, ek - (int)ekb) : 0.f;
+            if (scorer && lane == 0) s_ekb[kg] = (int)ekb;
+        } else {
+            if (tid < 4)
+                s_ekb[tid] = (k0 + 32 * tid < e) ? (int)a.k_exps[(size_t)hk * T + k0 + 32 * tid] : 127;
         }
-        if constexpr (FP4) {
-            // the Q row's features (tid % 4) D / 4 .. + D / 4 - 1 as FP16
-            uint8_t* dst = &s_q16[buf2][(tid >> 2) * PITCH16 + 2 * (tid & 3) * (D / 4)];
-#pragma unroll
-            for (int q = 0; q < D / 32; ++q) {
-                const float sc = __builtin_amdgcn_cvt_f32_fp8((int)((r.q4s >> (8 * (q / 2))) & 0xff), 0);
-                *(h8*)(dst + 16 * q) = fp4x8_to_f16((uint32_t)r.q4[q], sc);
-            }
-        }
-    };
-    Tile nxt;
-    auto prefetch = [&](int j) {
-        const int j1 = min(j + 1, niter - 1);
-        load_qtile<D, 256, MODE>(a, nxt, tile_head(j1), tile_base(j1), e, tid);
-    };
 
-    if (scorer) {
-        load_qtile<D, 256, MODE>(a, nxt, tile_head(0), tile_base(0), e, tid);
-        stage(nxt, 0, 0);
-    }
-    // every load issued so far has landed (vmcnt(0)), so that inside the loop
-    // only the prefetch of the next tile is outstanding
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    lds_barrier();
+        // iterations: q heads of the group (outer) x 64-query tiles that see the keys
+        const int qt_lo = a.causal ? 2 * kt : 0;
+        const int nqt = (e - s + 63) / 64 - qt_lo;
+        const int niter = G * nqt;
+        auto tile_head = [&](int j) { return hk * G + j / nqt; };
+        auto tile_base = [&](int j) { return s + 64 * (qt_lo + j % nqt); };
 
-    if (scorer) {
-        // this wave's K and V rows: B operands of S = Q K^T (E4M3 codes, or
-        // the FP16 expansion of the E2M1 view) and dP = dO V^T
-        v8i kf[FP4 ? 1 : NKS], vf[NKS];
-        h8 kh[FP4 ? NKH : 1];
+        // The score waves (threads 0-255) fetch and stage the query tiles, so
+        // the gradient waves' dQ atomics never sit ahead of a load they must wait
+        // for.  Every staging thread writes (the waves write identical
+        // statistics), so that every prefetched register is consumed on every
+        // path.
+        using Tile = QTile<D, 256>;
+        auto stage = [&](const Tile& r, int buf, int buf2) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            if (kvalid) {
-                if constexpr (!FP4)
-                    kf[ks] = row_operand(a.k_codes + ((size_t)kj * Hkv + hk) * D + 64 * ks, lane);
-                vf[ks] = row_operand(a.v_codes + ((size_t)kj * Hkv + hk) * D + 64 * ks, lane);
-            } else {
-                if constexpr (!FP4) kf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-                vf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            for (int k = 0; k < Tile::NC; ++k) {
+                const int c = tid + 256 * k;
+                const bool isq = c < 4 * D;
+                const int cc = isq ? c : c - 4 * D;
+                const int row = cc / CPR, col = 16 * (cc % CPR);
+                *(v4i*)((isq ? s_q[buf] : s_do[buf]) + CT::off(row, col)) = r.c[k];
             }
-        }
-        if constexpr (FP4) {
-            const size_t row = (size_t)min(kj, e - 1) * Hkv + hk;
+            const int row = tid & 63;
+            s_eq[buf][row] = r.ok ? r.eq : 127;
+            s_edo[buf][row] = r.ok ? r.edo : 127;
+            s_kq[buf][row] = r.ok ? r.pre + a.scale_exp : 0;
+            // 8 - LSE log2 e: exp2 of the score term then yields 256 P; rows past
+            // the document end get -inf, so their P is exactly zero
+            s_nlse[buf][row] = r.ok ? 8.f - r.lse * kLog2e : -INFINITY;
+            s_delta[buf][row] = r.ok ? r.delta : 0.f;
+            if constexpr (EXACT) {
+                // lane = query row: block maxima of the Q and dO exponents over
+                // each 32-query half and the rows' fold factors
+                const uint32_t eqr = r.ok ? (uint32_t)r.eq : 0u, egr = r.ok ? (uint32_t)r.edo : 0u;
+                const uint32_t eqb = half_wave_max_u32(eqr), egb = half_wave_max_u32(egr);
+                s_eqb[buf][row >> 5] = (int)eqb;
+                s_egb[buf][row >> 5] = (int)egb;
+                s_fq[buf][row] = r.ok ? ldexpf(1.f, (int)eqr - (int)eqb) : 0.f;
+                s_fg[buf][row] = r.ok ? ldexpf(1.f, (int)egr - (int)egb) : 0.f;
+            }
+            if constexpr (FP4) {
+                // the Q row's features (tid % 4) D / 4 .. + D / 4 - 1 as FP16
+                uint8_t* dst = &s_q16[buf2][(tid >> 2) * PITCH16 + 2 * (tid & 3) * (D / 4)];
 #pragma unroll
-            for (int ks = 0; ks < NKH; ++ks) {
-                const uint32_t c = *(const uint32_t*)(a.k_fp4 + row * (D / 2) + 8 * ks + 4 * g);
-                const float sc = __builtin_amdgcn_cvt_f32_fp8((int)a.k_fp4_scales[row * (D / 16) + ks], 0);
-                kh[ks] = fp4x8_to_f16(c, sc);
+                for (int q = 0; q < D / 32; ++q) {
+                    const float sc = __builtin_amdgcn_cvt_f32_fp8((int)((r.q4s >> (8 * (q / 2))) & 0xff), 0);
+                    *(h8*)(dst + 16 * q) = fp4x8_to_f16((uint32_t)r.q4[q], sc);
+                }
             }
+        };
+        Tile nxt;
+        auto prefetch = [&](int j) {
+            const int j1 = min(j + 1, niter - 1);
+            load_qtile<D, 256, MODE>(a, nxt, tile_head(j1), tile_base(j1), e, tid);
+        };
+
+        if (scorer) {
+            load_qtile<D, 256, MODE>(a, nxt, tile_head(0), tile_base(0), e, tid);
+            stage(nxt, 0, 0);
         }
-        const int ev = kvalid ? (int)a.v_exps[(size_t)hk * T + kj] : 127;
+        // every load issued so far has landed (vmcnt(0)), so that inside the loop
+        // only the prefetch of the next tile is outstanding
         __builtin_amdgcn_s_waitcnt(0x0F70);
+        lds_barrier();
 
-        for (int j = 0; j <= niter; ++j) {
-            prefetch(j);
-            if (j < niter) {
-                const int c3 = j % 3, pb = j & 1;
-                const int qb = tile_base(j);
-                const uint8_t* sq = s_q[c3];
-                const uint8_t* sg = s_do[c3];
-                // the two 32 x 32 blocks (queries 32 t .. + 31 of the tile):
-                // all S / dP MFMAs first, then the element-wise work
-                bool active[2];
-                v16f sacc[2], pacc[2];
-                // the rows' statistics (8 - LSE log2 e and D) into registers
-                // ahead of the MFMAs, so their LDS latency overlaps them (not
-                // with the FP16 score path, whose registers are spoken for)
-                float nlv[2][16], dlv[2][16];
+        if (scorer) {
+            // this wave's K and V rows: B operands of S = Q K^T (E4M3 codes, or
+            // the FP16 expansion of the E2M1 view) and dP = dO V^T
+            v8i kf[FP4 ? 1 : NKS], vf[NKS];
+            h8 kh[FP4 ? NKH : 1];
 #pragma unroll
-                for (int t = 0; t < (FP4 ? 0 : 2); ++t)
+            for (int ks = 0; ks < NKS; ++ks) {
+                if (kvalid) {
+                    if constexpr (!FP4)
+                        kf[ks] = row_operand(a.k_codes + ((size_t)kj * Hkv + hk) * D + 64 * ks, lane);
+                    vf[ks] = row_operand(a.v_codes + ((size_t)kj * Hkv + hk) * D + 64 * ks, lane);
+                } else {
+                    if constexpr (!FP4) kf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                    vf[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                }
+            }
+            if constexpr (FP4) {
+                const size_t row = (size_t)min(kj, e - 1) * Hkv + hk;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float4 x = *(const float4*)&s_nlse[c3][32 * t + 16 * g + 4 * i];
-                        const float4 y = *(const float4*)&s_delta[c3][32 * t + 16 * g + 4 * i];
+                for (int ks = 0; ks < NKH; ++ks) {
+                    const uint32_t c = *(const uint32_t*)(a.k_fp4 + row * (D / 2) + 8 * ks + 4 * g);
+                    const float sc = __builtin_amdgcn_cvt_f32_fp8((int)a.k_fp4_scales[row * (D / 16) + ks], 0);
+                    kh[ks] = fp4x8_to_f16(c, sc);
+                }
+            }
+            const int ev = kvalid ? (int)a.v_exps[(size_t)hk * T + kj] : 127;
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+
+            for (int j = 0; j <= niter; ++j) {
+                prefetch(j);
+                if (j < niter) {
+                    const int c3 = j % 3, pb = j & 1;
+                    const int qb = tile_base(j);
+                    const uint8_t* sq = s_q[c3];
+                    const uint8_t* sg = s_do[c3];
+                    // the two 32 x 32 blocks (queries 32 t .. + 31 of the tile):
+                    // all S / dP MFMAs first, then the element-wise work
+                    bool active[2];
+                    v16f sacc[2], pacc[2];
+                    // the rows' statistics (8 - LSE log2 e and D) into registers
+                    // ahead of the MFMAs, so their LDS latency overlaps them (not
+                    // with the FP16 score path, whose registers are spoken for)
+                    float nlv[2][16], dlv[2][16];
 #pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            nlv[t][4 * i + k] = k == 0 ? x.x : k == 1 ? x.y : k == 2 ? x.z : x.w;
-                            dlv[t][4 * i + k] = k == 0 ? y.x : k == 1 ? y.y : k == 2 ? y.z : y.w;
+                    for (int t = 0; t < (FP4 ? 0 : 2); ++t)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float4 x = *(const float4*)&s_nlse[c3][32 * t + 16 * g + 4 * i];
+                            const float4 y = *(const float4*)&s_delta[c3][32 * t + 16 * g + 4 * i];
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) {
+                                nlv[t][4 * i + k] = k == 0 ? x.x : k == 1 ? x.y : k == 2 ? x.z : x.w;
+                                dlv[t][4 * i + k] = k == 0 ? y.x : k == 1 ? y.y : k == 2 ? y.z : y.w;
+                            }
                         }
-                    }
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    active[t] = wave_keys && (!a.causal || qb + 32 * t + 31 >= kw0);
+                    for (int t = 0; t < 2; ++t) {
+                        active[t] = wave_keys && (!a.causal || qb + 32 * t + 31 >= kw0);
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) sacc[t][v] = pacc[t][v] = 0.f;
-                    if (active[t]) {
-                        const int qr = perm_row(t, lane & 31);
-                        const int edr = s_edo[c3][qr];
-                        if constexpr (FP4) {
+                        for (int v = 0; v < 16; ++v) sacc[t][v] = pacc[t][v] = 0.f;
+                        if (active[t]) {
+                            const int qr = perm_row(t, lane & 31);
+                            const int edr = s_edo[c3][qr];
+                            if constexpr (FP4) {
 #pragma unroll
-                            for (int ks = 0; ks < NKH; ++ks)
-                                sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                    *(const h8*)(s_q16[pb] + qr * PITCH16 + 2 * (16 * ks + 8 * g)), kh[ks],
-                                    sacc[t], 0, 0, 0);
-                        } else {
-                            const int eqr = s_eq[c3][qr];
+                                for (int ks = 0; ks < NKH; ++ks)
+                                    sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                        *(const h8*)(s_q16[pb] + qr * PITCH16 + 2 * (16 * ks + 8 * g)), kh[ks],
+                                        sacc[t], 0, 0, 0);
+                            } else {
+                                const int eqr = s_eq[c3][qr];
+#pragma unroll
+                                for (int ks = 0; ks < NKS; ++ks)
+                                    sacc[t] = mfma_f8(tile_row_operand<D>(sq, qr, 64 * ks, lane), kf[ks],
+                                                      sacc[t], eqr, ek);
+                            }
 #pragma unroll
                             for (int ks = 0; ks < NKS; ++ks)
-                                sacc[t] = mfma_f8(tile_row_operand<D>(sq, qr, 64 * ks, lane), kf[ks],
-                                                  sacc[t], eqr, ek);
+                                pacc[t] = mfma_f8(tile_row_operand<D>(sg, qr, 64 * ks, lane), vf[ks],
+                                                  pacc[t], edr, ev);
                         }
-#pragma unroll
-                        for (int ks = 0; ks < NKS; ++ks)
-                            pacc[t] = mfma_f8(tile_row_operand<D>(sg, qr, 64 * ks, lane), vf[ks],
-                                              pacc[t], edr, ev);
                     }
-                }
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    v4i pf = {0, 0, 0, 0}, df = {0, 0, 0, 0}, dfr = {0, 0, 0, 0};
-                    int dse = 127;
-                    int er[16];
+                    for (int t = 0; t < 2; ++t) {
+                        v4i pf = {0, 0, 0, 0}, df = {0, 0, 0, 0}, dfr = {0, 0, 0, 0};
+                        int dse = 127;
+                        int er[16];
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) er[v] = 0;
-                    if (active[t]) {
-                        // Masking is needed only where some key is invalid or,
-                        // causally, some query precedes some key; queries past
-                        // the document end have 256 P = exp2(-inf) = 0 and
-                        // D = 0.  Element v of lane group g is query
-                        // qb + 32 t + 16 g + v.
-                        const int q0 = 32 * t + 16 * g;
-                        const float* nl = FP4 ? &s_nlse[c3][q0] : nlv[t];
-                        const float* dl = FP4 ? &s_delta[c3][q0] : dlv[t];
-                        const bool full = kw0 + 32 <= e && (!a.causal || qb + 32 * t >= kw0 + 31);
-                        float amax;
-                        if (full) {
-                            amax = softmax_grad<false>(sacc[t], pacc[t], nl, dl, c2, 0);
-                        } else {
-                            const int lim = a.causal ? kj - qb - 32 * t - 16 * g : (kvalid ? -1 : 16);
-                            amax = softmax_grad<true>(sacc[t], pacc[t], nl, dl, c2, lim);
-                        }
-                        // block exponent of dS = 2^-8 (256 dS); the scaling is exact
-                        const int et = ceil_exp448(wave_max_nonneg(amax) * 0.00390625f);
-                        dse = et + 127;
-                        if constexpr (EXACT) {
-                            // per-row exponents of the dQ copy: each query
-                            // row's largest |dS| over this block's 32 keys,
-                            // one row per lane, then all 16 rows of the lane
-                            // group back from LDS (the same wave's write)
-                            uint32_t ab[16];
-#pragma unroll
-                            for (int v = 0; v < 16; ++v) ab[v] = __float_as_uint(fabsf(pacc[t][v]));
-                            const int erl = ceil_exp448(
-                                __uint_as_float(row_max_transpose(ab, lane)) * 0.00390625f);
-                            int* erow = &s_er[pb][kg][32 * t + 16 * g];
-                            if ((lane & 16) == 0) erow[rev4(lane & 15)] = erl + 127;
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                const v4i e4 = *(const v4i*)(erow + 4 * q);
-                                er[4 * q] = e4.x - 127;
-                                er[4 * q + 1] = e4.y - 127;
-                                er[4 * q + 2] = e4.z - 127;
-                                er[4 * q + 3] = e4.w - 127;
+                        for (int v = 0; v < 16; ++v) er[v] = 0;
+                        if (active[t]) {
+                            // Masking is needed only where some key is invalid or,
+                            // causally, some query precedes some key; queries past
+                            // the document end have 256 P = exp2(-inf) = 0 and
+                            // D = 0.  Element v of lane group g is query
+                            // qb + 32 t + 16 g + v.
+                            const int q0 = 32 * t + 16 * g;
+                            const float* nl = FP4 ? &s_nlse[c3][q0] : nlv[t];
+                            const float* dl = FP4 ? &s_delta[c3][q0] : dlv[t];
+                            const bool full = kw0 + 32 <= e && (!a.causal || qb + 32 * t >= kw0 + 31);
+                            float amax;
+                            if (full) {
+                                amax = softmax_grad<false>(sacc[t], pacc[t], nl, dl, c2, 0);
+                            } else {
+                                const int lim = a.causal ? kj - qb - 32 * t - 16 * g : (kvalid ? -1 : 16);
+                                amax = softmax_grad<true>(sacc[t], pacc[t], nl, dl, c2, lim);
                             }
-                            const float* fg = &s_fg[c3][q0];
-                            const float* fq = &s_fq[c3][q0];
+                            // block exponent of dS = 2^-8 (256 dS); the scaling is exact
+                            const int et = ceil_exp448(wave_max_nonneg(amax) * 0.00390625f);
+                            dse = et + 127;
+                            if constexpr (EXACT) {
+                                // per-row exponents of the dQ copy: each query
+                                // row's largest |dS| over this block's 32 keys,
+                                // one row per lane, then all 16 rows of the lane
+                                // group back from LDS (the same wave's write)
+                                uint32_t ab[16];
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                float pv[4], dv4[4], rv[4];
+                                for (int v = 0; v < 16; ++v) ab[v] = __float_as_uint(fabsf(pacc[t][v]));
+                                const int erl = ceil_exp448(
+                                    __uint_as_float(row_max_transpose(ab, lane)) * 0.00390625f);
+                                int* erow = &s_er[pb][kg][32 * t + 16 * g];
+                                if ((lane & 16) == 0) erow[rev4(lane & 15)] = erl + 127;
 #pragma unroll
-                                for (int k = 0; k < 4; ++k) {
-                                    const int v = 4 * q + k;
-                                    pv[k] = sacc[t][v] * fg[v];
-                                    dv4[k] = ldexpf(pacc[t][v] * fq[v], -et - 8);
-                                    rv[k] = ldexpf(pacc[t][v] * fk, -er[v] - 8);
+                                for (int q = 0; q < 4; ++q) {
+                                    const v4i e4 = *(const v4i*)(erow + 4 * q);
+                                    er[4 * q] = e4.x - 127;
+                                    er[4 * q + 1] = e4.y - 127;
+                                    er[4 * q + 2] = e4.z - 127;
+                                    er[4 * q + 3] = e4.w - 127;
                                 }
-                                pf[q] = (int)cvt4_fp8(pv[0], pv[1], pv[2], pv[3]);
-                                df[q] = (int)cvt4_fp8(dv4[0], dv4[1], dv4[2], dv4[3]);
-                                dfr[q] = (int)cvt4_fp8(rv[0], rv[1], rv[2], rv[3]);
-                            }
-                        } else {
+                                const float* fg = &s_fg[c3][q0];
+                                const float* fq = &s_fq[c3][q0];
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                pf[q] = (int)cvt4_fp8(sacc[t][4 * q], sacc[t][4 * q + 1],
-                                                      sacc[t][4 * q + 2], sacc[t][4 * q + 3]);
-                                df[q] = (int)cvt4_fp8(ldexpf(pacc[t][4 * q], -et - 8),
-                                                      ldexpf(pacc[t][4 * q + 1], -et - 8),
-                                                      ldexpf(pacc[t][4 * q + 2], -et - 8),
-                                                      ldexpf(pacc[t][4 * q + 3], -et - 8));
+                                for (int q = 0; q < 4; ++q) {
+                                    float pv[4], dv4[4], rv[4];
+#pragma unroll
+                                    for (int k = 0; k < 4; ++k) {
+                                        const int v = 4 * q + k;
+                                        pv[k] = sacc[t][v] * fg[v];
+                                        dv4[k] = ldexpf(pacc[t][v] * fq[v], -et - 8);
+                                        rv[k] = ldexpf(pacc[t][v] * fk, -er[v] - 8);
+                                    }
+                                    pf[q] = (int)cvt4_fp8(pv[0], pv[1], pv[2], pv[3]);
+                                    df[q] = (int)cvt4_fp8(dv4[0], dv4[1], dv4[2], dv4[3]);
+                                    dfr[q] = (int)cvt4_fp8(rv[0], rv[1], rv[2], rv[3]);
+                                }
+                            } else {
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) {
+                                    pf[q] = (int)cvt4_fp8(sacc[t][4 * q], sacc[t][4 * q + 1],
+                                                          sacc[t][4 * q + 2], sacc[t][4 * q + 3]);
+                                    df[q] = (int)cvt4_fp8(ldexpf(pacc[t][4 * q], -et - 8),
+                                                          ldexpf(pacc[t][4 * q + 1], -et - 8),
+                                                          ldexpf(pacc[t][4 * q + 2], -et - 8),
+                                                          ldexpf(pacc[t][4 * q + 3], -et - 8));
+                                }
                             }
                         }
-                    }
-                    // key-major rows: 16 bytes at the block's queries and lane group
-                    *(v4i*)(s_p[pb] + krow * SPITCH + 32 * t + 16 * g) = pf;
-                    *(v4i*)(s_ds[pb] + krow * SPITCH + 32 * t + 16 * g) = df;
-                    if (lane == 0) s_dsexp[pb][t][kg] = dse;
-                    if constexpr (EXACT) {
-                        *(v4i*)(s_dsr[pb] + krow * SPITCH + 32 * t + 16 * g) = dfr;
-                        if (!active[t] && (lane & 16) == 0) s_er[pb][kg][32 * t + 16 * g + (lane & 15)] = 127;
-                    }
-                }
-            }
-            stage(nxt, (j + 1) % 3, (j + 1) & 1);
-            lds_barrier();
-        }
-    } else {
-        // dK^T, dV^T of the wave's keys over the whole head dim
-        v16f dk[NDT], dv[NDT];
-#pragma unroll
-        for (int i = 0; i < NDT; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) dk[i][v] = dv[i][v] = 0.f;
-        const size_t dq_rs = (size_t)Hq * D;  // row stride of the dQ accumulator
-
-        for (int j = 0; j <= niter; ++j) {
-            if (j >= 1) {
-                const int jp = j - 1;
-                const int c3 = jp % 3, pb = jp & 1;
-                const int qb = tile_base(jp), h = tile_head(jp);
-                const uint8_t* sq = s_q[c3];
-                const uint8_t* sg = s_do[c3];
-                // dV^T += dO^T P^ and dK^T += Q^T dS^ over the tile's 64
-                // queries (k); the B operands are the key's P^ / dS^ rows in
-                // the k layout (bytes 0-15 query half 0, 16-31 half 1)
-                if (wave_keys && (!a.causal || qb + 63 >= kw0)) {
-                    const v4i p0 = *(const v4i*)(s_p[pb] + krow * SPITCH + 16 * g);
-                    const v4i p1 = *(const v4i*)(s_p[pb] + krow * SPITCH + 32 + 16 * g);
-                    const v4i d0 = *(const v4i*)(s_ds[pb] + krow * SPITCH + 16 * g);
-                    const v4i d1 = *(const v4i*)(s_ds[pb] + krow * SPITCH + 32 + 16 * g);
-                    const v8i pfull = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-                    const v8i dfull = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-                    const int sdo = EXACT ? s_egb[c3][g] : s_edo[c3][32 * g];
-                    const int sqe = EXACT ? s_eqb[c3][g] : s_eq[c3][32 * g];
-                    const int dsg = s_dsexp[pb][g][kg];
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) {
-                        dv[dt] = mfma_f8(tile_tr_operand<D>(sg, 0, 32 * dt, lane), pfull, dv[dt],
-                                         sdo, kScaleMinus8);
-                        dk[dt] = mfma_f8(tile_tr_operand<D>(sq, 0, 32 * dt, lane), dfull, dk[dt],
-                                         sqe, dsg);
-                    }
-                }
-
-                if constexpr (WITH_DQ) {
-                    // dQ = dS^ K^ over the tile's 128 keys: wave kg computes the
-                    // 32 x 64 region (query half ct, head-dim tiles dt0, dt0 + 1).
-                    // The row's prescale 2^(k_i + f) (2^f <= softmax scale <
-                    // 2^(f + 1)) rides in the A operand's block scale; the
-                    // finalize applies the remaining scale 2^-(k_i + f).
-                    if (kg < NDT) {
-                        const int ct = kg / (NDT / 2), dt0 = 2 * (kg % (NDT / 2));
-                        const int nrows = e - (qb + 32 * ct);
-                        if (nrows > 0) {
-                            const int qrow = 32 * ct + (lane & 31);
-                            const int kq = s_kq[c3][qrow];
-                            const int e0 = EXACT ? s_er[pb][g][qrow] : s_dsexp[pb][ct][g];
-                            const int e1 = EXACT ? s_er[pb][2 + g][qrow] : s_dsexp[pb][ct][2 + g];
-                            const int sa0 = min(max(e0 + kq, 0), 254);
-                            const int sa1 = min(max(e1 + kq, 0), 254);
-                            const uint8_t* sdq = EXACT ? s_dsr[pb] : s_ds[pb];
-                            const v8i a0 = lds_tr_operand(sdq, SPITCH, 0, 32 * ct, lane);
-                            v16f acc[2];
-#pragma unroll
-                            for (int i = 0; i < 2; ++i) {
-#pragma unroll
-                                for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
-                                acc[i] = mfma_f8(a0, tile_tr_operand<D>(s_kt, 0, 32 * (dt0 + i), lane),
-                                                 acc[i], sa0, s_ekb[g]);
-                            }
-                            if (k0 + 64 < e) {
-                                const v8i a1 = lds_tr_operand(sdq + 64 * SPITCH, SPITCH, 0, 32 * ct, lane);
-#pragma unroll
-                                for (int i = 0; i < 2; ++i)
-                                    acc[i] = mfma_f8(a1, tile_tr_operand<D>(s_kt, 64,
-                                                                        32 * (dt0 + i), lane),
-                                                     acc[i], sa1, s_ekb[2 + g]);
-                            }
-                            _Float16* region = a.dq_acc + ((size_t)(qb + 32 * ct) * Hq + h) * D + 32 * dt0;
-                            if (nrows >= 32)
-                                dq_region_atomics<false>(acc[0], acc[1], region, dq_rs, lane, nrows);
-                            else
-                                dq_region_atomics<true>(acc[0], acc[1], region, dq_rs, lane, nrows);
+                        // key-major rows: 16 bytes at the block's queries and lane group
+                        *(v4i*)(s_p[pb] + krow * SPITCH + 32 * t + 16 * g) = pf;
+                        *(v4i*)(s_ds[pb] + krow * SPITCH + 32 * t + 16 * g) = df;
+                        if (lane == 0) s_dsexp[pb][t][kg] = dse;
+                        if constexpr (EXACT) {
+                            *(v4i*)(s_dsr[pb] + krow * SPITCH + 32 * t + 16 * g) = dfr;
+                            if (!active[t] && (lane & 16) == 0) s_er[pb][kg][32 * t + 16 * g + (lane & 15)] = 127;
                         }
                     }
                 }
+                stage(nxt, (j + 1) % 3, (j + 1) & 1);
+                lds_barrier();
             }
-            lds_barrier();
-        }
+        } else {
+            // dK^T, dV^T of the wave's keys over the whole head dim
+            v16f dk[NDT], dv[NDT];
+#pragma unroll
+            for (int i = 0; i < NDT; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) dk[i][v] = dv[i][v] = 0.f;
+            const size_t dq_rs = (size_t)Hq * D;  // row stride of the dQ accumulator
 
-        // rotated Q and K: dK = dK_r H (the Sylvester matrix, unnormalised;
-        // the softmax scale already carries the 1 / d)
-        if (a.rotate) fwht_cols<NDT>(dk, lane);
-        if (kvalid) {
-            uint16_t* krp = a.dk + ((size_t)kj * Hkv + hk) * D;
-            uint16_t* vrp = a.dv + ((size_t)kj * Hkv + hk) * D;
-            const float sc = a.scale;
+            for (int j = 0; j <= niter; ++j) {
+                if (j >= 1) {
+                    const int jp = j - 1;
+                    const int c3 = jp % 3, pb = jp & 1;
+                    const int qb = tile_base(jp), h = tile_head(jp);
+                    const uint8_t* sq = s_q[c3];
+                    const uint8_t* sg = s_do[c3];
+                    // dV^T += dO^T P^ and dK^T += Q^T dS^ over the tile's 64
+                    // queries (k); the B operands are the key's P^ / dS^ rows in
+                    // the k layout (bytes 0-15 query half 0, 16-31 half 1)
+                    if (wave_keys && (!a.causal || qb + 63 >= kw0)) {
+                        const v4i p0 = *(const v4i*)(s_p[pb] + krow * SPITCH + 16 * g);
+                        const v4i p1 = *(const v4i*)(s_p[pb] + krow * SPITCH + 32 + 16 * g);
+                        const v4i d0 = *(const v4i*)(s_ds[pb] + krow * SPITCH + 16 * g);
+                        const v4i d1 = *(const v4i*)(s_ds[pb] + krow * SPITCH + 32 + 16 * g);
+                        const v8i pfull = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+                        const v8i dfull = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                        const int sdo = EXACT ? s_egb[c3][g] : s_edo[c3][32 * g];
+                        const int sqe = EXACT ? s_eqb[c3][g] : s_eq[c3][32 * g];
+                        const int dsg = s_dsexp[pb][g][kg];
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
+                        for (int dt = 0; dt < NDT; ++dt) {
+                            dv[dt] = mfma_f8(tile_tr_operand<D>(sg, 0, 32 * dt, lane), pfull, dv[dt],
+                                             sdo, kScaleMinus8);
+                            dk[dt] = mfma_f8(tile_tr_operand<D>(sq, 0, 32 * dt, lane), dfull, dk[dt],
+                                             sqe, dsg);
+                        }
+                    }
+
+                    if constexpr (WITH_DQ) {
+                        // dQ = dS^ K^ over the tile's 128 keys: wave kg computes the
+                        // 32 x 64 region (query half ct, head-dim tiles dt0, dt0 + 1).
+                        // The row's prescale 2^(k_i + f) (2^f <= softmax scale <
+                        // 2^(f + 1)) rides in the A operand's block scale; the
+                        // finalize applies the remaining scale 2^-(k_i + f).
+                        if (kg < NDT) {
+                            const int ct = kg / (NDT / 2), dt0 = 2 * (kg % (NDT / 2));
+                            const int nrows = e - (qb + 32 * ct);
+                            if (nrows > 0) {
+                                const int qrow = 32 * ct + (lane & 31);
+                                const int kq = s_kq[c3][qrow];
+                                const int e0 = EXACT ? s_er[pb][g][qrow] : s_dsexp[pb][ct][g];
+                                const int e1 = EXACT ? s_er[pb][2 + g][qrow] : s_dsexp[pb][ct][2 + g];
+                                const int sa0 = min(max(e0 + kq, 0), 254);
+                                const int sa1 = min(max(e1 + kq, 0), 254);
+                                const uint8_t* sdq = EXACT ? s_dsr[pb] : s_ds[pb];
+                                const v8i a0 = lds_tr_operand(sdq, SPITCH, 0, 32 * ct, lane);
+                                v16f acc[2];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    v2i wk, wv;
-                    wk.x = (int)pack_bf16x2(dk[dt][4 * q] * sc, dk[dt][4 * q + 1] * sc);
-                    wk.y = (int)pack_bf16x2(dk[dt][4 * q + 2] * sc, dk[dt][4 * q + 3] * sc);
-                    wv.x = (int)pack_bf16x2(dv[dt][4 * q], dv[dt][4 * q + 1]);
-                    wv.y = (int)pack_bf16x2(dv[dt][4 * q + 2], dv[dt][4 * q + 3]);
-                    *(v2i*)(krp + 32 * dt + 8 * q + 4 * g) = wk;
-                    *(v2i*)(vrp + 32 * dt + 8 * q + 4 * g) = wv;
+                                for (int i = 0; i < 2; ++i) {
+#pragma unroll
+                                    for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+                                    acc[i] = mfma_f8(a0, tile_tr_operand<D>(s_kt, 0, 32 * (dt0 + i), lane),
+                                                     acc[i], sa0, s_ekb[g]);
+                                }
+                                if (k0 + 64 < e) {
+                                    const v8i a1 = lds_tr_operand(sdq + 64 * SPITCH, SPITCH, 0, 32 * ct, lane);
+#pragma unroll
+                                    for (int i = 0; i < 2; ++i)
+                                        acc[i] = mfma_f8(a1, tile_tr_operand<D>(s_kt, 64,
+                                                                            32 * (dt0 + i), lane),
+                                                         acc[i], sa1, s_ekb[2 + g]);
+                                }
+                                _Float16* region = a.dq_acc + ((size_t)(qb + 32 * ct) * Hq + h) * D + 32 * dt0;
+                                if (nrows >= 32)
+                                    dq_region_atomics<false>(acc[0], acc[1], region, dq_rs, lane, nrows);
+                                else
+                                    dq_region_atomics<true>(acc[0], acc[1], region, dq_rs, lane, nrows);
+                            }
+                        }
+                    }
                 }
+                lds_barrier();
+            }
+
+            // rotated Q and K: dK = dK_r H (the Sylvester matrix, unnormalised;
+            // the softmax scale already carries the 1 / d)
+            if (a.rotate) fwht_cols<NDT>(dk, lane);
+            if (kvalid) {
+                uint16_t* krp = a.dk + ((size_t)kj * Hkv + hk) * D;
+                uint16_t* vrp = a.dv + ((size_t)kj * Hkv + hk) * D;
+                const float sc = a.scale;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        v2i wk, wv;
+                        wk.x = (int)pack_bf16x2(dk[dt][4 * q] * sc, dk[dt][4 * q + 1] * sc);
+                        wk.y = (int)pack_bf16x2(dk[dt][4 * q + 2] * sc, dk[dt][4 * q + 3] * sc);
+                        wv.x = (int)pack_bf16x2(dv[dt][4 * q], dv[dt][4 * q + 1]);
+                        wv.y = (int)pack_bf16x2(dv[dt][4 * q + 2], dv[dt][4 * q + 3]);
+                        *(v2i*)(krp + 32 * dt + 8 * q + 4 * g) = wk;
+                        *(v2i*)(vrp + 32 * dt + 8 * q + 4 * g) = wv;
+                    }
+            }
         }
-    }
+        // item boundary: every wave is done with this item's LDS before the next
+        // item's first writes, and the next ticket is visible
+        __syncthreads();
+    }  // tickets
 }
 
 // Query-major dQ for the deterministic backward: a workgroup (4 waves x 32
@@ -818,7 +841,13 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(AttnArgs a)
 hipError_t launch_bwd(const AttnArgs& a, int D, int max_items, bool with_dq, hipStream_t stream)
 {
     if (max_items <= 0) return hipSuccess;
-    const dim3 grid((unsigned)max_items * a.Hkv);
+    // persistent grid: as many workgroups as the device holds at once (one per
+    // CU at this kernel's register and LDS use), never more than the tickets
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+        return hipErrorInvalidDevice;
+    const dim3 grid((unsigned)std::min<int64_t>((int64_t)max_items * a.Hkv, ncu));
 #define FLAMIA_BWD(DD, WQ, MM) \
     hipExtLaunchKernelGGL((bwd_kernel<DD, WQ, MM>), grid, dim3(512), 0, stream, a.ev_start, a.ev_stop, 0, a)
     if (D == 128) {

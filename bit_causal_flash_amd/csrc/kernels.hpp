@@ -78,6 +78,7 @@ struct AttnArgs {
     const int32_t* cu;
     const int32_t* count;
     const int32_t* items;
+    int32_t* tickets;   // backward: the persistent grid's ticket counter (count + 1, zeroed with the list)
     const uint8_t *q_codes, *q_exps, *k_codes, *k_exps, *v_codes, *v_exps;
     // E2M1 score views (MODE_FP4): codes [T][H][D/2], E4M3 scales [T][H][D/16]
     const uint8_t *q_fp4, *q_fp4_scales, *k_fp4, *k_fp4_scales;

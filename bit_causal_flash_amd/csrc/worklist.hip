@@ -137,7 +137,11 @@ __global__ __launch_bounds__(kThreads) void worklist_kernel(WorklistArgs a)
         a.items[2 * pos] = lo;
         a.items[2 * pos + 1] = m;
     }
-    if (tid == 0) *a.count = nitems;
+    // count[1]: the ticket counter of the persistent backward, taken from 0
+    if (tid == 0) {
+        a.count[0] = nitems;
+        a.count[1] = 0;
+    }
 }
 
 }  // namespace
