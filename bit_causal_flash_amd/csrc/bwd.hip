@@ -663,7 +663,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), g = lane >> 5;
     const int Hq = a.Hq, Hkv = a.Hkv;
     const size_t T = (size_t)a.T;
-    const int item = blockIdx.x / Hq, h = blockIdx.x % Hq;
+    // kv heads first within an item: the q heads sharing a kv head run on one
+    // XCD (workgroup i runs on XCD i % 8) and share its L2 copy of K/V
+    const int item = blockIdx.x / Hq, rr = blockIdx.x % Hq;
+    const int h = (rr % Hkv) * (Hq / Hkv) + rr / Hkv;
     if (item >= *a.count) return;
     const int b = a.items[2 * item], m = a.items[2 * item + 1];
     const int s = a.cu[b], e = a.cu[b + 1];
