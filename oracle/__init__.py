@@ -60,6 +60,8 @@ def _load():
         _lib.orc_floor_exponent.argtypes = [ctypes.c_double]
         _lib.orc_f16_round.restype = ctypes.c_double
         _lib.orc_f16_round.argtypes = [ctypes.c_double]
+        _lib.orc_bwd_dq_ranges.restype = ctypes.c_int64
+        _lib.orc_bwd_dkdv_ranges.restype = ctypes.c_int64
     return _lib
 
 
@@ -281,7 +283,7 @@ class Operands:
 
 
 def attn_fwd(cu, ops: Operands, scale=None, causal=True, mode=MODE_ROUNDED, kblock=32,
-             rows=None, want_rescale=False, want_flags=False):
+             rows=None, want_rescale=False):
     """Forward.  rows: None (all) or int array [n][2] of (q head, token).
     Returns (O float64 [T][Hq][d], LSE float64 [Hq][T][, n_rescale])."""
     cu = _c(cu, np.int32)
@@ -290,19 +292,83 @@ def attn_fwd(cu, ops: Operands, scale=None, causal=True, mode=MODE_ROUNDED, kblo
     O = np.zeros((T, Hq, d), dtype=np.float64)
     LSE = np.zeros((Hq, T), dtype=np.float64)
     nres = np.zeros((Hq, T), dtype=np.int32) if want_rescale else None
-    ties = np.zeros((Hq, T, 2), dtype=np.float64) if want_flags else None
     r = None if rows is None else _c(rows, np.int32).reshape(-1, 2)
     n = 0 if r is None else r.shape[0]
     _check(_load().orc_attn_fwd(
         T, len(cu) - 1, _p(cu), Hq, Hkv, d, ctypes.c_double(scale), int(bool(causal)),
-        *ops.ptrs(), mode, kblock, ctypes.c_int64(n), _p(r), _p(O), _p(LSE), _p(nres),
-        _p(ties)))
-    out = (O, LSE)
-    if want_rescale:
-        out += (nres,)
-    if want_flags:
-        out += (ties,)
-    return out
+        *ops.ptrs(), mode, kblock, ctypes.c_int64(n), _p(r), _p(O), _p(LSE), _p(nres)))
+    return (O, LSE, nres) if want_rescale else (O, LSE)
+
+
+# --------------------------------------------------------------------------
+# evaluation-noise bookkeeping (for comparisons with an FP32 implementation;
+# not part of the method's arithmetic)
+# --------------------------------------------------------------------------
+
+def fwd_ties(cu, ops: Operands, noise, scale=None, causal=True, mode=MODE_TILED, kblock=64,
+             rows=None):
+    """Per row (float64 [Hq][T][2]): bounds on how far different roundings of
+    weights lying within `noise` (fraction of each score's sum of absolute
+    terms) of an E4M3 midpoint can move O (any element) and l (relative)."""
+    cu = _c(cu, np.int32)
+    T, Hq, Hkv, d = ops.T, ops.Hq, ops.Hkv, ops.d
+    scale = default_scale(d) if scale is None else scale
+    ties = np.zeros((Hq, T, 2), dtype=np.float64)
+    r = None if rows is None else _c(rows, np.int32).reshape(-1, 2)
+    n = 0 if r is None else r.shape[0]
+    _check(_load().orc_fwd_ties(
+        T, len(cu) - 1, _p(cu), Hq, Hkv, d, ctypes.c_double(scale), int(bool(causal)),
+        *ops.ptrs(), mode, kblock, ctypes.c_double(noise), ctypes.c_int64(n), _p(r), _p(ties)))
+    return ties
+
+
+def dq_ranges(cu, ops: Operands, G, D, LSE, h, q0, noise, scale=None, causal=True,
+              per_row_ds=False):
+    """Near-midpoint elements of the dQ product's dS^ for the 32 rows of the
+    block at q0 (head h): arrays (i, j, lo, hi), lo / hi the lowest / highest
+    dS^ an evaluation within `noise` could give, minus the oracle's choice."""
+    cu = _c(cu, np.int32)
+    G, D, LSE = (_c(x, np.float64) for x in (G, D, LSE))
+    T, Hq, Hkv, d = ops.T, ops.Hq, ops.Hkv, ops.d
+    scale = default_scale(d) if scale is None else scale
+    args = [T, len(cu) - 1, _p(cu), Hq, Hkv, d, ctypes.c_double(scale), int(bool(causal)),
+            *ops.ptrs(), _p(G), _p(D), _p(LSE), int(bool(per_row_ds)), ctypes.c_double(noise),
+            int(h), int(q0)]
+    cap = 4096
+    while True:
+        oi, oj = np.zeros(cap, np.int32), np.zeros(cap, np.int32)
+        lo, hi = np.zeros(cap), np.zeros(cap)
+        n = _load().orc_bwd_dq_ranges(*args, ctypes.c_int64(cap), _p(oi), _p(oj), _p(lo), _p(hi))
+        if n < 0:
+            raise OracleError("oracle returned %d" % n)
+        if n <= cap:
+            return oi[:n], oj[:n], lo[:n], hi[:n]
+        cap = int(n)
+
+
+def dkdv_ranges(cu, ops: Operands, G, D, LSE, g, k0, which, noise, scale=None, causal=True,
+                per_row_ds=False):
+    """Near-midpoint elements of the 32 keys of the block at k0 (kv head g):
+    which 0 the P^ of dV, 1 the dS^ of dK; arrays (h, i, j, lo, hi) as in
+    dq_ranges."""
+    cu = _c(cu, np.int32)
+    G, D, LSE = (_c(x, np.float64) for x in (G, D, LSE))
+    T, Hq, Hkv, d = ops.T, ops.Hq, ops.Hkv, ops.d
+    scale = default_scale(d) if scale is None else scale
+    args = [T, len(cu) - 1, _p(cu), Hq, Hkv, d, ctypes.c_double(scale), int(bool(causal)),
+            *ops.ptrs(), _p(G), _p(D), _p(LSE), int(bool(per_row_ds)), ctypes.c_double(noise),
+            int(g), int(k0), int(which)]
+    cap = 4096
+    while True:
+        oh, oi, oj = (np.zeros(cap, np.int32) for _ in range(3))
+        lo, hi = np.zeros(cap), np.zeros(cap)
+        n = _load().orc_bwd_dkdv_ranges(*args, ctypes.c_int64(cap), _p(oh), _p(oi), _p(oj),
+                                        _p(lo), _p(hi))
+        if n < 0:
+            raise OracleError("oracle returned %d" % n)
+        if n <= cap:
+            return oh[:n], oi[:n], oj[:n], lo[:n], hi[:n]
+        cap = int(n)
 
 
 def bwd_prep(cu, dO, O, k_exps, v_exps, Hkv, scale=None, causal=True, block=32):
@@ -364,13 +430,13 @@ def _pairs(heads, starts):
 
 
 def bwd_dq(cu, ops: Operands, G, D, LSE, scale=None, causal=True, mode=MODE_ROUNDED,
-           per_row_ds=False, qblocks=None, want_flags=False, kpre=None):
+           per_row_ds=False, qblocks=None, kpre=None):
     """dQ (float64 [T][Hq][d]) for the listed (q head, block start) pairs
     (default: every block of every head).  G: dequantized dO; D: [Hq][T];
     LSE: [Hq][T] natural log as saved by a forward.  With kpre (int32
     [Hq][T] prescale exponents) returns (dQ, dQ16): dQ16 is the same
-    gradient through the FP16 accumulation model (per 128-key tile partials
-    boosted by 2^(kpre + f), rounded to FP16, summed in FP16 in tile
+    gradient through the method's FP16 accumulation (per 128-key tile
+    partials boosted by 2^(kpre + f), rounded to FP16, summed in FP16 in tile
     order)."""
     cu = _c(cu, np.int32)
     T, Hq, Hkv, d = ops.T, ops.Hq, ops.Hkv, ops.d
@@ -379,24 +445,18 @@ def bwd_dq(cu, ops: Operands, G, D, LSE, scale=None, causal=True, mode=MODE_ROUN
         qblocks = _pairs(range(Hq), doc_blocks(cu))
     qblocks = _c(qblocks, np.int32).reshape(-1, 2)
     dQ = np.zeros((T, Hq, d), dtype=np.float64)
-    tie = np.zeros((T, Hq), dtype=np.float64)
-    acc = np.zeros((T, Hq), dtype=np.float64)
-    absm = np.zeros((T, Hq), dtype=np.float64)
     kp = _c(kpre, np.int32) if kpre is not None else None
     dq16 = np.zeros((T, Hq, d), dtype=np.float64) if kpre is not None else None
     _check(_load().orc_bwd_dq(
         T, len(cu) - 1, _p(cu), Hq, Hkv, d, ctypes.c_double(scale), int(bool(causal)),
         *ops.ptrs(), _p(_c(G, np.float64)), _p(_c(D, np.float64)), _p(_c(LSE, np.float64)),
         mode, int(bool(per_row_ds)), ctypes.c_int64(qblocks.shape[0]), _p(qblocks), _p(dQ),
-        _p(tie), _p(acc), _p(absm), _p(kp) if kp is not None else None,
-        _p(dq16) if dq16 is not None else None))
-    if kpre is not None:
-        return (dQ, dq16, tie, acc, absm) if want_flags else (dQ, dq16)
-    return (dQ, tie, acc, absm) if want_flags else dQ
+        _p(kp), _p(dq16)))
+    return (dQ, dq16) if kpre is not None else dQ
 
 
 def bwd_dkdv(cu, ops: Operands, G, D, LSE, scale=None, causal=True, mode=MODE_ROUNDED,
-             per_row_ds=False, kblocks=None, want_flags=False):
+             per_row_ds=False, kblocks=None):
     """dK, dV (float64 [T][Hkv][d]) for the listed (kv head, block start)
     pairs (default: every block of every kv head)."""
     cu = _c(cu, np.int32)
@@ -407,33 +467,25 @@ def bwd_dkdv(cu, ops: Operands, G, D, LSE, scale=None, causal=True, mode=MODE_RO
     kblocks = _c(kblocks, np.int32).reshape(-1, 2)
     dK = np.zeros((T, Hkv, d), dtype=np.float64)
     dV = np.zeros((T, Hkv, d), dtype=np.float64)
-    tie_k = np.zeros((T, Hkv), dtype=np.float64)
-    tie_v = np.zeros((T, Hkv), dtype=np.float64)
-    abs_k = np.zeros((T, Hkv), dtype=np.float64)
-    abs_v = np.zeros((T, Hkv), dtype=np.float64)
     _check(_load().orc_bwd_dkdv(
         T, len(cu) - 1, _p(cu), Hq, Hkv, d, ctypes.c_double(scale), int(bool(causal)),
         *ops.ptrs(), _p(_c(G, np.float64)), _p(_c(D, np.float64)), _p(_c(LSE, np.float64)),
         mode, int(bool(per_row_ds)), ctypes.c_int64(kblocks.shape[0]), _p(kblocks), _p(dK),
-        _p(dV), _p(tie_k), _p(tie_v), _p(abs_k), _p(abs_v)))
-    return (dK, dV, tie_k, tie_v, abs_k, abs_v) if want_flags else (dK, dV)
+        _p(dV)))
+    return dK, dV
 
 
 def bwd_block(cu, ops: Operands, G, D, LSE, h, q0, k0, scale=None, causal=True,
               mode=MODE_ROUNDED, per_row_ds=False):
     """One document-local 32x32 block of the recomputed backward.  Returns a
-    dict of [32][32] float64 arrays: P, dP, dS, Pq, dSk, dSq, and the flip
-    steps stepP, stepSk, stepSq (nonzero where a GPU's FP32 evaluation may
-    round P^ or dS^ to the neighbouring E4M3 value)."""
+    dict of [32][32] float64 arrays: P, dP, dS, Pq, dSk, dSq."""
     cu = _c(cu, np.int32)
     T, Hq, Hkv, d = ops.T, ops.Hq, ops.Hkv, ops.d
     scale = default_scale(d) if scale is None else scale
     out = {k: np.zeros((32, 32), dtype=np.float64) for k in ("P", "dP", "dS", "Pq", "dSk", "dSq")}
-    steps = np.zeros((3, 32, 32), dtype=np.float64)
     _check(_load().orc_bwd_block(
         T, len(cu) - 1, _p(cu), Hq, Hkv, d, ctypes.c_double(scale), int(bool(causal)),
         *ops.ptrs(), _p(_c(G, np.float64)), _p(_c(D, np.float64)), _p(_c(LSE, np.float64)),
         mode, int(bool(per_row_ds)), int(h), int(q0), int(k0),
-        *[_p(out[k]) for k in ("P", "dP", "dS", "Pq", "dSk", "dSq")], _p(steps)))
-    out["stepP"], out["stepSk"], out["stepSq"] = steps[0], steps[1], steps[2]
+        *[_p(out[k]) for k in ("P", "dP", "dS", "Pq", "dSk", "dSq")]))
     return out

@@ -38,28 +38,19 @@
  * extraction) are listed in the repository's design notes; the ones that
  * change arithmetic are restated next to the code that implements them.
  *
- * Rounding-tie flags: the GPU evaluates P and dS in FP32 and this oracle in
- * FP64, so an element lying within FP32 evaluation noise of an E4M3 rounding
- * midpoint (or a dS block whose max lies that close to an exponent
- * threshold) can legitimately round either way; a row with few contributors
- * then moves by one E4M3 step of one term.  The forward and backward routines
- * report, per output row, a bound on how far such flips could move it (the
- * sum over near-tie elements of their step times the magnitude of the
- * companion operand row), so that comparisons can allow exactly that and
- * report it instead of silently excluding rows.  The evaluation noise assumed
- * is 2^-11 of the sum of the absolute terms of each dot product (the GPU's
- * FP8 matrix cores round inside each instruction at about that level).  The
- * gradient routines also report, per row, the largest sum of absolute terms
- * of the gradient product itself, which bounds that rounding in the output.  orc_bwd_dq also reports,
- * per row, the sum over the 128-key tiles of the largest partial-sum
- * magnitude: dQ partials are accumulated in FP16 on the GPU, and that sum
- * bounds the accumulation error.
+ * Comparisons with an FP32 implementation: a GPU evaluates scores and dP in
+ * its own precision, so an element of P^ or dS^ lying that close to an E4M3
+ * rounding midpoint may round either way, and both are results of the
+ * method.  The last section of this file ("Evaluation-noise bookkeeping")
+ * says which elements, and to what, for an evaluation error the caller
+ * states; it recomputes what it needs and is kept apart from the arithmetic
+ * above it, which never depends on the device.
  *
  * Parity pins: every function here is pinned by tests under tests/ that check
  * it against values the pages print, closed forms, invariants or brute force.
  * The dQ prescale exponent (orc_bwd_prep, kpre) has no printed value on the
- * pages: it is pinned only by its defining inequality ("parity unpinned"
- * against the pages).
+ * pages (its formula is lost): it is pinned by its bound on every partial sum
+ * and, from both sides, by a worst-case input that reaches the bound.
  */
 #include <math.h>
 #include <omp.h>
@@ -458,31 +449,13 @@ static inline const double* row(const double* X, int H, int d, int t, int h)
  * view (the E2M1 route) the score uses it ([R] S2: the mixed route
  * reconstructs scores from the selected Q/K format and re-quantizes Q and K
  * in E4M3 for the gradient products). */
-static double score_abs(const orc_attn* a, int h, int i, int j, double* sabs)
+static double score(const orc_attn* a, int h, int i, int j)
 {
     const double* q = row(a->Qs ? a->Qs : a->Q, a->Hq, a->d, i, h);
     const double* k = row(a->Ks ? a->Ks : a->K, a->Hkv, a->d, j, kv_head(a, h));
-    double acc = 0.0, ab = 0.0;
-    for (int c = 0; c < a->d; ++c) {
-        acc += q[c] * k[c];
-        ab += fabs(q[c] * k[c]);
-    }
-    if (sabs) *sabs = a->scale * ab;
+    double acc = 0.0;
+    for (int c = 0; c < a->d; ++c) acc += q[c] * k[c];
     return a->scale * acc;
-}
-
-/* Evaluation noise assumed for a GPU dot product of E4M3 codes: 2^-11 of the
- * sum of the absolute values of its terms.  (gfx950's FP8 matrix cores keep
- * about 12 bits below the largest product inside one instruction: measured
- * deviations from FP64 reach 2^-12.6 of that sum.) */
-#define ORC_FP32_NOISE 4.8828125e-04
-
-/* Size of the jump between the E4M3 values y - tol and y + tol round to (0
- * when both round alike), in code units. */
-static double tie_step(double y, double tol)
-{
-    return fabs(orc_e4m3_decode(orc_e4m3_encode(y + tol)) -
-                orc_e4m3_decode(orc_e4m3_encode(y - tol)));
 }
 
 /* Visible keys of query i in document b: [s_b, i] when causal, else the whole
@@ -491,6 +464,9 @@ static inline int key_end(const orc_attn* a, int b, int i)
 {
     return a->causal ? i + 1 : a->cu[b + 1];
 }
+
+/* E4M3 value nearest to y (the rounding of orc_e4m3_encode, decoded). */
+static double e4m3_round(double y) { return orc_e4m3_decode(orc_e4m3_encode(y)); }
 
 /* ------------------------------------------------------------------------- */
 /* Forward                                                                    */
@@ -518,60 +494,39 @@ static inline int key_end(const orc_attn* a, int b, int i)
  *      the max grows; O = acc / l; LSE = m + ln l.
  * Rows outside every document get O = 0 and LSE = +inf ([R] S6). */
 static void fwd_row(const orc_attn* a, int mode, int kblock, int h, int i, double* O, double* LSE,
-                    int32_t* n_rescale, double* tie, double* s_buf, double* a_buf)
+                    int32_t* n_rescale, double* s_buf)
 {
     int d = a->d, g = kv_head(a, h);
     int b = doc_of(a->B, a->cu, i);
     for (int c = 0; c < d; ++c) O[c] = 0.0;
     if (n_rescale) *n_rescale = 0;
-    if (tie) tie[0] = tie[1] = 0.0;
     if (b < 0) {
         *LSE = INFINITY;
         return;
     }
     int j0 = a->cu[b], j1 = key_end(a, b, i);
-    for (int j = j0; j < j1; ++j) s_buf[j - j0] = score_abs(a, h, i, j, &a_buf[j - j0]);
+    for (int j = j0; j < j1; ++j) s_buf[j - j0] = score(a, h, i, j);
 
     if (mode == 0 || mode == 1) {
         double mx = -INFINITY;
-        for (int j = j0; j < j1; ++j) {
-            double s2 = s_buf[j - j0] * M_LOG2E;
-            if (s2 > mx) mx = s2;
-        }
+        for (int j = j0; j < j1; ++j)
+            if (s_buf[j - j0] * M_LOG2E > mx) mx = s_buf[j - j0] * M_LOG2E;
         double r = ceil(mx);
         double l = 0.0;
-        double tie_w = 0.0, tie_wv = 0.0; /* sum of flip steps, and times |V_j| */
         for (int j = j0; j < j1; ++j) {
             double p = exp2(s_buf[j - j0] * M_LOG2E - r);
-            double ph = orc_e4m3_decode(orc_e4m3_encode(256.0 * p)) / 256.0;
-            double tol = 256.0 * p * (ORC_FP32_NOISE * a_buf[j - j0] + ldexp(1.0, -20));
-            double step = tie_step(256.0 * p, tol) / 256.0;
-            if (step > 0.0) {
-                const double* vj = row(a->V, a->Hkv, d, j, g);
-                double vm = 0.0;
-                for (int c = 0; c < d; ++c) vm = fabs(vj[c]) > vm ? fabs(vj[c]) : vm;
-                tie_w += step;
-                tie_wv += step * vm;
-            }
+            double ph = e4m3_round(256.0 * p) / 256.0;
             l += (mode == 0) ? ph : p;
             const double* v = row(a->V, a->Hkv, d, j, g);
             for (int c = 0; c < d; ++c) O[c] += ph * v[c];
         }
         for (int c = 0; c < d; ++c) O[c] /= l;
         *LSE = (r + log2(l)) * M_LN2;
-        if (tie) {
-            /* a flip of weight j by step changes O by step (V_j - O) / l and l
-               by step: bounds on |dO| and on the relative change of l */
-            double om = 0.0;
-            for (int c = 0; c < d; ++c) om = fabs(O[c]) > om ? fabs(O[c]) : om;
-            tie[0] = (tie_wv + tie_w * om) / l;
-            tie[1] = tie_w / l;
-        }
         return;
     }
 
     if (mode == 3) {
-        double r = -INFINITY, l = 0.0, tie_w = 0.0, tie_wv = 0.0;
+        double r = -INFINITY, l = 0.0;
         for (int k0 = j0; k0 < j1; k0 += kblock) {
             int k1 = k0 + kblock < j1 ? k0 + kblock : j1;
             double mb = -INFINITY;
@@ -581,36 +536,19 @@ static void fwd_row(const orc_attn* a, int mode, int kblock, int h, int i, doubl
             if (r != -INFINITY && r_new > r) {
                 double alpha = exp2(r - r_new);
                 l *= alpha;
-                tie_w *= alpha;
-                tie_wv *= alpha;
                 for (int c = 0; c < d; ++c) O[c] *= alpha;
                 if (n_rescale) ++*n_rescale;
             }
             r = r_new;
             for (int j = k0; j < k1; ++j) {
-                double p = exp2(s_buf[j - j0] * M_LOG2E - r);
-                double ph = orc_e4m3_decode(orc_e4m3_encode(256.0 * p)) / 256.0;
-                double tol = 256.0 * p * (ORC_FP32_NOISE * a_buf[j - j0] + ldexp(1.0, -20));
-                double step = tie_step(256.0 * p, tol) / 256.0;
-                const double* vj = row(a->V, a->Hkv, d, j, g);
-                if (step > 0.0) {
-                    double vm = 0.0;
-                    for (int c = 0; c < d; ++c) vm = fabs(vj[c]) > vm ? fabs(vj[c]) : vm;
-                    tie_w += step;
-                    tie_wv += step * vm;
-                }
+                double ph = e4m3_round(256.0 * exp2(s_buf[j - j0] * M_LOG2E - r)) / 256.0;
+                const double* v = row(a->V, a->Hkv, d, j, g);
                 l += ph;
-                for (int c = 0; c < d; ++c) O[c] += ph * vj[c];
+                for (int c = 0; c < d; ++c) O[c] += ph * v[c];
             }
         }
         for (int c = 0; c < d; ++c) O[c] /= l;
         *LSE = (r + log2(l)) * M_LN2;
-        if (tie) {
-            double om = 0.0;
-            for (int c = 0; c < d; ++c) om = fabs(O[c]) > om ? fabs(O[c]) : om;
-            tie[0] = (tie_wv + tie_w * om) / l;
-            tie[1] = tie_w / l;
-        }
         return;
     }
 
@@ -642,34 +580,37 @@ static void fwd_row(const orc_attn* a, int mode, int kblock, int h, int i, doubl
     if (n_rescale) *n_rescale = nres;
 }
 
+static int check_attn_args(int T, int B, const int32_t* cu, int Hq, int Hkv, int d)
+{
+    if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d < 1) return ORC_EBADARG;
+    return ORC_OK;
+}
+
 /* Q, K, V: dequantized operands; Qs, Ks: optional score view (else NULL).
  * rows: n_rows pairs (h, t); NULL means every (h, t).  O: [T][Hq][d],
  * LSE: [Hq][T], n_rescale: [Hq][T] or NULL.  Unlisted rows are untouched. */
 int orc_attn_fwd(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale,
                  int causal, const double* Q, const double* K, const double* V, const double* Qs,
                  const double* Ks, int mode, int kblock, int64_t n_rows, const int32_t* rows,
-                 double* O, double* LSE, int32_t* n_rescale, double* ties)
+                 double* O, double* LSE, int32_t* n_rescale)
 {
-    if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
-    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d < 1 || kblock < 1 || mode < 0 || mode > 3)
-        return ORC_EBADARG;
+    if (check_attn_args(T, B, cu, Hq, Hkv, d) != ORC_OK) return ORC_EBADARG;
+    if (kblock < 1 || mode < 0 || mode > 3) return ORC_EBADARG;
     orc_attn a = {T, B, Hq, Hkv, d, causal, cu, scale, Q, K, V, Qs, Ks};
     int64_t n = rows ? n_rows : (int64_t)Hq * T;
     int Tn = T > 0 ? T : 1;
 #pragma omp parallel
     {
         double* s_buf = (double*)malloc(sizeof(double) * Tn);
-        double* a_buf = (double*)malloc(sizeof(double) * Tn);
 #pragma omp for schedule(dynamic, 4)
         for (int64_t k = 0; k < n; ++k) {
             int h = rows ? rows[2 * k] : (int)(k / Tn);
             int t = rows ? rows[2 * k + 1] : (int)(k % Tn);
             fwd_row(&a, mode, kblock, h, t, O + ((size_t)t * Hq + h) * d, LSE + (size_t)h * T + t,
-                    n_rescale ? n_rescale + (size_t)h * T + t : NULL,
-                    ties ? ties + 2 * ((size_t)h * T + t) : NULL, s_buf, a_buf);
+                    n_rescale ? n_rescale + (size_t)h * T + t : NULL, s_buf);
         }
         free(s_buf);
-        free(a_buf);
     }
     return ORC_OK;
 }
@@ -684,18 +625,20 @@ int orc_attn_fwd(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double
  *   - dO (bf16 [T][Hq][d]) is quantized with the operand rule (block 32 or the
  *     per-token option);
  *   - D_i = dO^_i . O_i with the dequantized dO and the saved bf16 O;
- *   - kpre_i, the power-of-two prescale exponent of row i's FP16 dQ partials.
- *     It must depend only on what row i may see ([R] S4 "Forward locality and
- *     backward locality differ": the row's own dO and running maxima of the
- *     visible key and value magnitudes).  Reading: with e_dO the row's dO
- *     exponent and maxV, maxK the largest V and K exponents over the visible
- *     keys, every partial sum of dQ_i is bounded by
+ *   - kpre_i, the power-of-two prescale exponent of row i's FP16 dQ partials,
+ *     the stylised boost 2^floor(log2(target / estimate)) of [R] S4 with
+ *     target 2^14 and an estimate built only from what row i may see ([R] S4
+ *     "Forward locality and backward locality differ": the row's own dO and
+ *     running maxima of the visible key and value magnitudes).  Reading: with
+ *     e_dO the row's dO exponent and maxV, maxK the largest V and K exponents
+ *     over the visible keys, every partial sum of dQ_i is bounded by
  *         2 * scale * d * 448^3 * 2^(e_dO + maxV + maxK),
- *     so with C = ceil(log2(4 * scale * d * 448^3)) (a factor 2 of margin)
- *     kpre_i = 14 - C - (e_dO + maxV + maxK) keeps boosted partials below
- *     2^14, inside FP16's finite range.  Clamped to [-60, 60]; 0 for padding
- *     rows and rows whose quantized dO is all zero.  (Parity unpinned against
- *     the pages: their formula is lost; pinned by the inequality only.) */
+ *     and the estimate is twice that (a factor 2 of margin), so
+ *         kpre_i = 14 - C - (e_dO + maxV + maxK),
+ *         C = ceil(log2(4 * scale * d * 448^3)).
+ *     Clamped to [-60, 60]; 0 for padding rows and rows whose quantized dO is
+ *     all zero.  The pages' own formula is lost; the rule is pinned by its
+ *     bound and by a worst-case input that reaches it. */
 int orc_bwd_prep(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale,
                  int causal, int block, const uint16_t* dO, const uint16_t* O, const uint8_t* ke,
                  const uint8_t* ve, uint8_t* do_codes, uint8_t* do_exps, double* D, int32_t* kpre)
@@ -818,17 +761,11 @@ typedef struct {
  *       block (the per-query-row option, [R] S4, [K] S3.2), used for dQ.
  * Entries with j > i (causal) and entries outside the block are zero. */
 static void bwd_block(const orc_bwd* w, int h, int q0, int q1, int k0, int k1, double* P,
-                      double* dP, double* dS, double* Pq, double* dSk, double* dSq, double* stp)
+                      double* dP, double* dS, double* Pq, double* dSk, double* dSq)
 {
-    /* stp: [3][1024] flip steps of P^ (P units), dS^ on the 32x32 grid and
-       dS^ of the dQ product (dS units); 0 where the rounding is settled */
     const orc_attn* a = w->a;
     int T = a->T, d = a->d, g = kv_head(a, h);
-    double tolv[1024];
-    for (int k = 0; k < 1024; ++k) {
-        P[k] = dP[k] = dS[k] = Pq[k] = dSk[k] = dSq[k] = tolv[k] = 0.0;
-        stp[k] = stp[1024 + k] = stp[2048 + k] = 0.0;
-    }
+    for (int k = 0; k < 1024; ++k) P[k] = dP[k] = dS[k] = Pq[k] = dSk[k] = dSq[k] = 0.0;
     double amax = 0.0;
     for (int i = q0; i < q1; ++i) {
         const double* gi = row(w->G, a->Hq, d, i, h);
@@ -836,69 +773,28 @@ static void bwd_block(const orc_bwd* w, int h, int q0, int q1, int k0, int k1, d
             if (a->causal && j > i) continue;
             int e = (i - q0) * 32 + (j - k0);
             const double* vj = row(a->V, a->Hkv, d, j, g);
-            double sabs;
-            P[e] = exp(score_abs(a, h, i, j, &sabs) - w->LSE[(size_t)h * T + i]);
-            double acc = 0.0, pabs = 0.0;
-            for (int c = 0; c < d; ++c) {
-                acc += gi[c] * vj[c];
-                pabs += fabs(gi[c] * vj[c]);
-            }
+            P[e] = exp(score(a, h, i, j) - w->LSE[(size_t)h * T + i]);
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c) acc += gi[c] * vj[c];
             dP[e] = acc;
             dS[e] = P[e] * (dP[e] - w->D[(size_t)h * T + i]);
             if (fabs(dS[e]) > amax) amax = fabs(dS[e]);
-            Pq[e] = w->mode == 0 ? orc_e4m3_decode(orc_e4m3_encode(256.0 * P[e])) / 256.0 : P[e];
-            /* FP32 evaluation noise of P (through the score) and of dP - D,
-               which can cancel */
-            double ds_rel = ORC_FP32_NOISE * sabs + ldexp(1.0, -20);
-            tolv[e] = fabs(dS[e]) * ds_rel + P[e] * ORC_FP32_NOISE * 2.0 * (pabs + fabs(dP[e]));
-            if (w->mode == 0) stp[e] = tie_step(256.0 * P[e], 256.0 * P[e] * ds_rel) / 256.0;
+            Pq[e] = w->mode == 0 ? e4m3_round(256.0 * P[e]) / 256.0 : P[e];
         }
     }
     int eb = orc_ceil_exponent(amax);
-    if (w->mode == 0) {
-        double tmax = 0.0;
-        for (int k = 0; k < 1024; ++k) tmax = tolv[k] > tmax ? tolv[k] : tmax;
-        int e_hi = orc_ceil_exponent(amax + tmax);
-        int block_shift = orc_ceil_exponent(amax - tmax) != e_hi;
-        for (int i = q0; i < q1; ++i)
-            for (int j = k0; j < k1; ++j) {
-                int e = (i - q0) * 32 + (j - k0);
-                if (a->causal && j > i) continue;
-                double st = ldexp(tie_step(ldexp(dS[e], -eb), ldexp(tolv[e], -eb)), eb);
-                /* an exponent shift moves values below the coarser normal
-                   range by up to one subnormal step of the larger scale */
-                if (block_shift && fabs(dS[e]) < ldexp(1.0, e_hi - 6)) st += ldexp(1.0, e_hi - 9);
-                stp[1024 + e] = st;
-                stp[2048 + e] = st;
-            }
-    }
     for (int i = q0; i < q1; ++i) {
         int base = (i - q0) * 32;
         double ramax = 0.0;
         for (int j = k0; j < k1; ++j)
             if (fabs(dS[base + j - k0]) > ramax) ramax = fabs(dS[base + j - k0]);
         int er = orc_ceil_exponent(ramax);
-        if (w->mode == 0 && w->per_row_ds) {
-            double rt = 0.0;
-            for (int j = k0; j < k1; ++j) rt = tolv[base + j - k0] > rt ? tolv[base + j - k0] : rt;
-            int r_hi = orc_ceil_exponent(ramax + rt);
-            int shift = orc_ceil_exponent(ramax - rt) != r_hi;
-            for (int j = k0; j < k1; ++j) {
-                int e = base + (j - k0);
-                if (a->causal && j > i) continue;
-                double st = ldexp(tie_step(ldexp(dS[e], -er), ldexp(tolv[e], -er)), er);
-                if (shift && fabs(dS[e]) < ldexp(1.0, r_hi - 6)) st += ldexp(1.0, r_hi - 9);
-                stp[2048 + e] = st;
-            }
-        }
         for (int j = k0; j < k1; ++j) {
             int e = base + (j - k0);
             if (a->causal && j > i) continue;
             if (w->mode == 0) {
-                dSk[e] = ldexp(orc_e4m3_decode(orc_e4m3_encode(ldexp(dS[e], -eb))), eb);
-                dSq[e] = w->per_row_ds
-                             ? ldexp(orc_e4m3_decode(orc_e4m3_encode(ldexp(dS[e], -er))), er)
-                             : dSk[e];
+                dSk[e] = ldexp(e4m3_round(ldexp(dS[e], -eb)), eb);
+                dSq[e] = w->per_row_ds ? ldexp(e4m3_round(ldexp(dS[e], -er)), er) : dSk[e];
             } else {
                 dSk[e] = dSq[e] = dS[e];
             }
@@ -921,31 +817,37 @@ int orc_bwd_block(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, doubl
                   int causal, const double* Q, const double* K, const double* V,
                   const double* Qs, const double* Ks, const double* G, const double* D,
                   const double* LSE, int mode, int per_row_ds, int h, int q0, int k0, double* P,
-                  double* dP, double* dS, double* Pq, double* dSk, double* dSq, double* stp)
+                  double* dP, double* dS, double* Pq, double* dSk, double* dSq)
 {
-    if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
+    if (check_attn_args(T, B, cu, Hq, Hkv, d) != ORC_OK) return ORC_EBADARG;
     int b = doc_of(B, cu, q0);
-    if (b < 0 || doc_of(B, cu, k0) != b || (q0 - cu[b]) % 32 || (k0 - cu[b]) % 32)
+    if (b < 0 || doc_of(B, cu, k0) != b || (q0 - cu[b]) % 32 || (k0 - cu[b]) % 32 || h < 0 ||
+        h >= Hq)
         return ORC_EBADARG;
     orc_attn a = {T, B, Hq, Hkv, d, causal, cu, scale, Q, K, V, Qs, Ks};
     orc_bwd w = {&a, G, D, LSE, mode, per_row_ds};
     int q1 = q0 + 32 < cu[b + 1] ? q0 + 32 : cu[b + 1];
     int k1 = k0 + 32 < cu[b + 1] ? k0 + 32 : cu[b + 1];
-    bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq, stp);
+    bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq);
     return ORC_OK;
 }
 
 /* dQ_i = scale * sum_j dS^_ij K^_j for every query of the listed
  * document-local 32-query blocks.  qblocks: n pairs (q head, t0), t0 the
- * first token of a block.  dQ: [T][Hq][d], accumulated into. */
+ * first token of a block.  dQ: [T][Hq][d], accumulated into.
+ * With kpre (int32 [Hq][T]) and dq16, also the method's FP16 accumulation of
+ * dQ ([R] S4 and [K] S3.3: FP16 partials with a power-of-two row prescale):
+ * per document-relative 128-key tile the partial sum_j dS^_ij K^_j times
+ * 2^(kpre_i + f), where 2^f <= scale < 2^(f + 1), is rounded to FP16 and
+ * added into an FP16 accumulator (rounded again), tiles in key order; dq16 =
+ * accumulator * scale / 2^(kpre_i + f). */
 int orc_bwd_dq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale, int causal,
                const double* Q, const double* K, const double* V, const double* Qs,
                const double* Ks, const double* G, const double* D, const double* LSE, int mode,
-               int per_row_ds, int64_t n, const int32_t* qblocks, double* dQ, double* tie,
-               double* acc_mag, double* abs_mag, const int32_t* kpre, double* dq16)
+               int per_row_ds, int64_t n, const int32_t* qblocks, double* dQ,
+               const int32_t* kpre, double* dq16)
 {
-    if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
-    if (Hkv < 1 || Hq % Hkv != 0) return ORC_EBADARG;
+    if (check_attn_args(T, B, cu, Hq, Hkv, d) != ORC_OK) return ORC_EBADARG;
     if (check_blocks(B, cu, n, qblocks, Hq) != ORC_OK) return ORC_EBADARG;
     orc_attn a = {T, B, Hq, Hkv, d, causal, cu, scale, Q, K, V, Qs, Ks};
     orc_bwd w = {&a, G, D, LSE, mode, per_row_ds};
@@ -955,9 +857,7 @@ int orc_bwd_dq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double s
 #pragma omp parallel
     {
         double* buf = (double*)malloc(sizeof(double) * 6 * 1024);
-        double* stp = (double*)malloc(sizeof(double) * 3 * 1024);
         double* part = (double*)malloc(sizeof(double) * 32 * d);
-        double* absp = (double*)malloc(sizeof(double) * 32 * d);
         double* acc16 = (double*)malloc(sizeof(double) * 32 * d);
 #pragma omp for schedule(dynamic)
         for (int64_t k = 0; k < n; ++k) {
@@ -967,74 +867,41 @@ int orc_bwd_dq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double s
             int kend = causal ? q1 : cu[b + 1];
             double *P = buf, *dP = buf + 1024, *dS = buf + 2048, *Pq = buf + 3072,
                    *dSk = buf + 4096, *dSq = buf + 5120;
-            for (int x = 0; x < 32 * d; ++x) part[x] = absp[x] = acc16[x] = 0.0;
+            for (int x = 0; x < 32 * d; ++x) part[x] = acc16[x] = 0.0;
             for (int k0 = cu[b]; k0 < kend; k0 += 32) {
                 int k1 = k0 + 32 < cu[b + 1] ? k0 + 32 : cu[b + 1];
-                bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq, stp);
+                bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq);
                 for (int i = q0; i < q1; ++i) {
                     double* out = dQ + ((size_t)i * Hq + h) * d;
-                    if (tie)
-                        for (int j = k0; j < k1; ++j) {
-                            double st = stp[2048 + (i - q0) * 32 + (j - k0)];
-                            if (st == 0.0) continue;
-                            double km = 0.0;
-                            for (int c = 0; c < d; ++c)
-                                km = fabs(row(K, Hkv, d, j, g)[c]) > km ? fabs(row(K, Hkv, d, j, g)[c]) : km;
-                            tie[(size_t)i * Hq + h] += scale * st * km;
-                        }
                     for (int c = 0; c < d; ++c) {
-                        double acc = 0.0, ab = 0.0;
-                        for (int j = k0; j < k1; ++j) {
-                            double t = dSq[(i - q0) * 32 + (j - k0)] * row(K, Hkv, d, j, g)[c];
-                            acc += t;
-                            ab += fabs(t);
-                        }
+                        double acc = 0.0;
+                        for (int j = k0; j < k1; ++j)
+                            acc += dSq[(i - q0) * 32 + (j - k0)] * row(K, Hkv, d, j, g)[c];
                         out[c] += scale * acc;
                         part[(i - q0) * d + c] += acc;
-                        absp[(i - q0) * d + c] += scale * ab;
                     }
                 }
-                if (abs_mag && k0 + 32 >= kend)
+                /* the FP16 model: one partial per 128-key tile */
+                if (kpre && dq16 && (((k0 - cu[b]) / 32) % 4 == 3 || k0 + 32 >= kend)) {
                     for (int i = q0; i < q1; ++i) {
-                        double m = 0.0;
-                        for (int c = 0; c < d; ++c) m = absp[(i - q0) * d + c] > m ? absp[(i - q0) * d + c] : m;
-                        abs_mag[(size_t)i * Hq + h] = m;
-                    }
-                /* per 128-key tile (document-relative): add the tile partial's
-                   largest magnitude to the row's accumulation magnitude.
-                   With kpre, the FP16 accumulation model: the unscaled
-                   partial dS^ K^ of the tile times 2^(kpre_i + f), where
-                   2^f <= scale < 2^(f + 1), rounded to FP16 and added into
-                   an FP16 accumulator (rounded again) in key-tile order; the
-                   result is the accumulator times scale / 2^(kpre_i + f) */
-                if ((acc_mag || kpre) && (((k0 - cu[b]) / 32) % 4 == 3 || k0 + 32 >= kend)) {
-                    for (int i = q0; i < q1; ++i) {
-                        double m = 0.0;
-                        int kp = kpre ? kpre[(size_t)h * T + i] + fexp : 0;
+                        int kp = kpre[(size_t)h * T + i] + fexp;
                         for (int c = 0; c < d; ++c) {
                             double* pc = &part[(i - q0) * d + c];
-                            double v = scale * fabs(*pc);
-                            m = v > m ? v : m;
-                            if (kpre) {
-                                double* ac = &acc16[(i - q0) * d + c];
-                                *ac = orc_f16_round(*ac + orc_f16_round(ldexp(*pc, kp)));
-                            }
+                            double* ac = &acc16[(i - q0) * d + c];
+                            *ac = orc_f16_round(*ac + orc_f16_round(ldexp(*pc, kp)));
                             *pc = 0.0;
                         }
-                        if (acc_mag) acc_mag[(size_t)i * Hq + h] += m;
                     }
                 }
-                if (kpre && dq16 && k0 + 32 >= kend)
-                    for (int i = q0; i < q1; ++i)
-                        for (int c = 0; c < d; ++c)
-                            dq16[((size_t)i * Hq + h) * d + c] =
-                                scale * ldexp(acc16[(i - q0) * d + c], -(kpre[(size_t)h * T + i] + fexp));
             }
+            if (kpre && dq16)
+                for (int i = q0; i < q1; ++i)
+                    for (int c = 0; c < d; ++c)
+                        dq16[((size_t)i * Hq + h) * d + c] =
+                            scale * ldexp(acc16[(i - q0) * d + c], -(kpre[(size_t)h * T + i] + fexp));
         }
         free(buf);
-        free(stp);
         free(part);
-        free(absp);
         free(acc16);
     }
     return ORC_OK;
@@ -1048,11 +915,9 @@ int orc_bwd_dq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double s
 int orc_bwd_dkdv(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale,
                  int causal, const double* Q, const double* K, const double* V, const double* Qs,
                  const double* Ks, const double* G, const double* D, const double* LSE, int mode,
-                 int per_row_ds, int64_t n, const int32_t* kblocks, double* dK, double* dV,
-                 double* tie_k, double* tie_v, double* abs_k, double* abs_v)
+                 int per_row_ds, int64_t n, const int32_t* kblocks, double* dK, double* dV)
 {
-    if (orc_check_seqlens(T, B, cu) != ORC_OK) return ORC_EBADSEQ;
-    if (Hkv < 1 || Hq % Hkv != 0) return ORC_EBADARG;
+    if (check_attn_args(T, B, cu, Hq, Hkv, d) != ORC_OK) return ORC_EBADARG;
     if (check_blocks(B, cu, n, kblocks, Hkv) != ORC_OK) return ORC_EBADARG;
     orc_attn a = {T, B, Hq, Hkv, d, causal, cu, scale, Q, K, V, Qs, Ks};
     orc_bwd w = {&a, G, D, LSE, mode, per_row_ds};
@@ -1060,72 +925,387 @@ int orc_bwd_dkdv(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double
 #pragma omp parallel
     {
         double* buf = (double*)malloc(sizeof(double) * 6 * 1024);
-        double* stp = (double*)malloc(sizeof(double) * 3 * 1024);
-        double* ak_sum = (double*)malloc(sizeof(double) * 32 * d);
-        double* av_sum = (double*)malloc(sizeof(double) * 32 * d);
 #pragma omp for schedule(dynamic)
         for (int64_t k = 0; k < n; ++k) {
             int g = kblocks[2 * k], k0 = kblocks[2 * k + 1];
             int b = doc_of(B, cu, k0);
             int k1 = k0 + 32 < cu[b + 1] ? k0 + 32 : cu[b + 1];
-            for (int x = 0; x < 32 * d; ++x) ak_sum[x] = av_sum[x] = 0.0;
             double *P = buf, *dP = buf + 1024, *dS = buf + 2048, *Pq = buf + 3072,
                    *dSk = buf + 4096, *dSq = buf + 5120;
             for (int h = g * Gr; h < (g + 1) * Gr; ++h) {
                 int qstart = causal ? k0 : cu[b];
                 for (int q0 = qstart; q0 < cu[b + 1]; q0 += 32) {
                     int q1 = q0 + 32 < cu[b + 1] ? q0 + 32 : cu[b + 1];
-                    bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq, stp);
+                    bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq);
                     for (int j = k0; j < k1; ++j) {
                         double* ov = dV + ((size_t)j * Hkv + g) * d;
-                        if (tie_k && tie_v)
-                            for (int i = q0; i < q1; ++i) {
-                                int e = (i - q0) * 32 + (j - k0);
-                                if (stp[e] == 0.0 && stp[1024 + e] == 0.0) continue;
-                                double qm = 0.0, gm = 0.0;
-                                for (int c = 0; c < d; ++c) {
-                                    double qv = fabs(row(Q, Hq, d, i, h)[c]), gv = fabs(row(G, Hq, d, i, h)[c]);
-                                    qm = qv > qm ? qv : qm;
-                                    gm = gv > gm ? gv : gm;
-                                }
-                                tie_v[(size_t)j * Hkv + g] += stp[e] * gm;
-                                tie_k[(size_t)j * Hkv + g] += scale * stp[1024 + e] * qm;
-                            }
                         double* ok = dK + ((size_t)j * Hkv + g) * d;
                         for (int c = 0; c < d; ++c) {
-                            double av = 0.0, ak = 0.0, bv = 0.0, bk = 0.0;
+                            double av = 0.0, ak = 0.0;
                             for (int i = q0; i < q1; ++i) {
                                 int e = (i - q0) * 32 + (j - k0);
-                                double tv = Pq[e] * row(G, Hq, d, i, h)[c];
-                                double tk = dSk[e] * row(Q, Hq, d, i, h)[c];
-                                av += tv;
-                                ak += tk;
-                                bv += fabs(tv);
-                                bk += fabs(tk);
+                                av += Pq[e] * row(G, Hq, d, i, h)[c];
+                                ak += dSk[e] * row(Q, Hq, d, i, h)[c];
                             }
                             ov[c] += av;
                             ok[c] += scale * ak;
-                            av_sum[(j - k0) * d + c] += bv;
-                            ak_sum[(j - k0) * d + c] += scale * bk;
                         }
                     }
                 }
             }
-            if (abs_k && abs_v)
+        }
+        free(buf);
+    }
+    return ORC_OK;
+}
+
+/* ========================================================================= */
+/* Evaluation-noise bookkeeping (test support; not part of the method)        */
+/* ========================================================================= */
+/* A GPU forms each score and each dP as a sum of E4M3 products in its own
+ * order and precision, and P, dS in FP32, so a value can land on the other
+ * side of an E4M3 rounding midpoint than the FP64 value above; both roundings
+ * are results of the method ([R] S8 "What the experiments establish" compares
+ * against references within tolerances for this reason).  The routines below
+ * take the evaluation error as an argument, `noise`: the largest deviation of
+ * a dot product, as a fraction of the sum of the absolute values of its
+ * terms (the caller states the figure for its hardware).  For the forward
+ * they bound how far such flips can move a row; for the backward they list,
+ * per element, the range of E4M3 results that any evaluation within that
+ * error could produce.  They recompute what they need from the definitions
+ * above and feed nothing back into them. */
+
+/* scale * sum_c |Q_ic K_jc| over the score's terms (its evaluation scale). */
+static double score_terms(const orc_attn* a, int h, int i, int j)
+{
+    const double* q = row(a->Qs ? a->Qs : a->Q, a->Hq, a->d, i, h);
+    const double* k = row(a->Ks ? a->Ks : a->K, a->Hkv, a->d, j, kv_head(a, h));
+    double ab = 0.0;
+    for (int c = 0; c < a->d; ++c) ab += fabs(q[c] * k[c]);
+    return a->scale * ab;
+}
+
+/* Relative error of a weight or probability whose score may be off by
+ * noise * (score terms): exp of that deviation is 1 + (deviation) to first
+ * order; 2^-20 more covers the FP32 exponential itself. */
+static double weight_rel_tol(double noise, double sterms) { return noise * sterms + ldexp(1.0, -20); }
+
+/* E4M3 results of all values within tol of y: [lo, hi] (rounding is
+ * monotone, so the ends suffice). */
+static void e4m3_range(double y, double tol, double* lo, double* hi)
+{
+    *lo = e4m3_round(y - tol);
+    *hi = e4m3_round(y + tol);
+}
+
+/* Forward: for each listed row (mode 0, 1 or 3 of fwd_row), ties[0] bounds
+ * the change of any element of O and ties[1] the relative change of l that
+ * different roundings of near-midpoint weights could cause: with step_j the
+ * spread of the possible P^_j (in units of the final reference) and l the
+ * row's normaliser, a change of P^_j by step_j moves O by step_j (V_j - O) / l
+ * and l by step_j, so ties[0] = sum_j step_j (max|V_j| + max|O|) / l and
+ * ties[1] = sum_j step_j / l.  Rows outside every document get 0. */
+int orc_fwd_ties(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale,
+                 int causal, const double* Q, const double* K, const double* V, const double* Qs,
+                 const double* Ks, int mode, int kblock, double noise, int64_t n_rows,
+                 const int32_t* rows, double* ties)
+{
+    if (check_attn_args(T, B, cu, Hq, Hkv, d) != ORC_OK) return ORC_EBADARG;
+    if (kblock < 1 || !(mode == 0 || mode == 1 || mode == 3)) return ORC_EBADARG;
+    orc_attn a = {T, B, Hq, Hkv, d, causal, cu, scale, Q, K, V, Qs, Ks};
+    int64_t n = rows ? n_rows : (int64_t)Hq * T;
+    int Tn = T > 0 ? T : 1;
+#pragma omp parallel
+    {
+        double* s_buf = (double*)malloc(sizeof(double) * Tn);
+        double* r_buf = (double*)malloc(sizeof(double) * Tn);
+        double* O = (double*)malloc(sizeof(double) * d);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t k = 0; k < n; ++k) {
+            int h = rows ? rows[2 * k] : (int)(k / Tn);
+            int i = rows ? rows[2 * k + 1] : (int)(k % Tn);
+            double* out = ties + 2 * ((size_t)h * T + i);
+            out[0] = out[1] = 0.0;
+            int b = doc_of(B, cu, i);
+            if (b < 0) continue;
+            double LSE;
+            fwd_row(&a, mode, kblock, h, i, O, &LSE, NULL, s_buf);
+            int j0 = cu[b], j1 = key_end(&a, b, i), g = kv_head(&a, h);
+            /* the reference each weight was rounded against */
+            double r = -INFINITY;
+            for (int k0 = j0; k0 < j1; k0 += (mode == 3 ? kblock : j1 - j0)) {
+                int k1 = (mode == 3 && k0 + kblock < j1) ? k0 + kblock : j1;
                 for (int j = k0; j < k1; ++j) {
-                    double mk = 0.0, mv = 0.0;
-                    for (int c = 0; c < d; ++c) {
-                        mk = ak_sum[(j - k0) * d + c] > mk ? ak_sum[(j - k0) * d + c] : mk;
-                        mv = av_sum[(j - k0) * d + c] > mv ? av_sum[(j - k0) * d + c] : mv;
+                    double c = ceil(s_buf[j - j0] * M_LOG2E);
+                    r = c > r ? c : r;
+                }
+                for (int j = k0; j < k1; ++j) r_buf[j - j0] = r;
+            }
+            double l = exp2(LSE * M_LOG2E - r); /* in units of the final reference */
+            double om = 0.0, sw = 0.0, swv = 0.0;
+            for (int c = 0; c < d; ++c) om = fabs(O[c]) > om ? fabs(O[c]) : om;
+            for (int j = j0; j < j1; ++j) {
+                double y = 256.0 * exp2(s_buf[j - j0] * M_LOG2E - r_buf[j - j0]);
+                double lo, hi;
+                e4m3_range(y, y * weight_rel_tol(noise, score_terms(&a, h, i, j)), &lo, &hi);
+                double step = (hi - lo) / 256.0 * exp2(r_buf[j - j0] - r);
+                if (step == 0.0) continue;
+                const double* vj = row(V, Hkv, d, j, g);
+                double vm = 0.0;
+                for (int c = 0; c < d; ++c) vm = fabs(vj[c]) > vm ? fabs(vj[c]) : vm;
+                sw += step;
+                swv += step * vm;
+            }
+            out[0] = (swv + sw * om) / l;
+            out[1] = sw / l;
+        }
+        free(s_buf);
+        free(r_buf);
+        free(O);
+    }
+    return ORC_OK;
+}
+
+/* Backward, one 32x32 block computed by bwd_block: for every visible element
+ * the most an evaluation within `noise` moves dS (tol_ds: the score's error
+ * through P, plus P times the error of dP, a dot product of the same kind;
+ * D is a plain FP32 sum whose error is far smaller) and the relative error of
+ * P (rel_p). */
+static void block_tolerances(const orc_bwd* w, int h, int q0, int q1, int k0, int k1,
+                             const double* P, const double* dP, const double* dS, double noise,
+                             double* tol_ds, double* rel_p)
+{
+    const orc_attn* a = w->a;
+    int d = a->d, g = kv_head(a, h);
+    for (int k = 0; k < 1024; ++k) tol_ds[k] = rel_p[k] = 0.0;
+    for (int i = q0; i < q1; ++i) {
+        const double* gi = row(w->G, a->Hq, d, i, h);
+        for (int j = k0; j < k1; ++j) {
+            if (a->causal && j > i) continue;
+            int e = (i - q0) * 32 + (j - k0);
+            const double* vj = row(a->V, a->Hkv, d, j, g);
+            double pterms = 0.0;
+            for (int c = 0; c < d; ++c) pterms += fabs(gi[c] * vj[c]);
+            rel_p[e] = weight_rel_tol(noise, score_terms(a, h, i, j));
+            tol_ds[e] = fabs(dS[e]) * rel_p[e] + P[e] * noise * pterms;
+        }
+    }
+}
+
+/* Exponents a block (or row) maximum amax could take when every entry may be
+ * off by up to tmax: [ceil_exp(amax - tmax), ceil_exp(amax + tmax)]. */
+static void exponent_range(double amax, double tmax, int* elo, int* ehi)
+{
+    *elo = orc_ceil_exponent(amax - tmax > 0.0 ? amax - tmax : 0.0);
+    *ehi = orc_ceil_exponent(amax + tmax);
+    if (amax - tmax <= 0.0) *elo = -127;
+}
+
+/* Range of dS^ results for dS within tol when the block exponent may be any
+ * of [elo, ehi] (at most a few values): the union of the per-exponent
+ * ranges, as an interval. */
+static void ds_range(double ds, double tol, int elo, int ehi, double* lo, double* hi)
+{
+    *lo = INFINITY;
+    *hi = -INFINITY;
+    if (ehi - elo > 3) elo = ehi - 3; /* below that the entry rounds to 0 or its neighbours */
+    for (int e = elo; e <= ehi; ++e) {
+        double a, b;
+        e4m3_range(ldexp(ds, -e), ldexp(tol, -e), &a, &b);
+        a = ldexp(a, e);
+        b = ldexp(b, e);
+        *lo = a < *lo ? a : *lo;
+        *hi = b > *hi ? b : *hi;
+    }
+}
+
+/* For the 32 query rows of the document-local block starting at q0 (head
+ * h): every visible key j whose dS^ of the dQ product could come out
+ * differently under an evaluation within `noise`, as (row i, key j, lo, hi),
+ * lo and hi the lowest and highest possible dS^ minus the value bwd_block
+ * chooses.  Writes at most `cap` entries; returns how many there are (call
+ * again with a larger cap if that is more), or a negative error. */
+int64_t orc_bwd_dq_ranges(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale,
+                          int causal, const double* Q, const double* K, const double* V,
+                          const double* Qs, const double* Ks, const double* G, const double* D,
+                          const double* LSE, int per_row_ds, double noise, int h, int q0,
+                          int64_t cap, int32_t* out_i, int32_t* out_j, double* out_lo,
+                          double* out_hi)
+{
+    if (check_attn_args(T, B, cu, Hq, Hkv, d) != ORC_OK) return ORC_EBADARG;
+    int b = doc_of(B, cu, q0);
+    if (b < 0 || (q0 - cu[b]) % 32 || h < 0 || h >= Hq) return ORC_EBADARG;
+    orc_attn a = {T, B, Hq, Hkv, d, causal, cu, scale, Q, K, V, Qs, Ks};
+    orc_bwd w = {&a, G, D, LSE, 0, per_row_ds};
+    int q1 = q0 + 32 < cu[b + 1] ? q0 + 32 : cu[b + 1];
+    int kend = causal ? q1 : cu[b + 1];
+    int nkb = (kend - cu[b] + 31) / 32;
+    /* per key block: up to 1024 entries, gathered in key order afterwards */
+    int32_t* cnt = (int32_t*)calloc((size_t)nkb + 1, sizeof(int32_t));
+    int32_t* ei = (int32_t*)malloc(sizeof(int32_t) * 1024 * (size_t)(nkb + 1));
+    int32_t* ej = (int32_t*)malloc(sizeof(int32_t) * 1024 * (size_t)(nkb + 1));
+    double* elo = (double*)malloc(sizeof(double) * 1024 * (size_t)(nkb + 1));
+    double* ehi = (double*)malloc(sizeof(double) * 1024 * (size_t)(nkb + 1));
+#pragma omp parallel
+    {
+        double* buf = (double*)malloc(sizeof(double) * 8 * 1024);
+        double *P = buf, *dP = buf + 1024, *dS = buf + 2048, *Pq = buf + 3072,
+               *dSk = buf + 4096, *dSq = buf + 5120, *tol = buf + 6144, *relp = buf + 7168;
+#pragma omp for schedule(dynamic)
+        for (int kb = 0; kb < nkb; ++kb) {
+            int k0 = cu[b] + 32 * kb;
+            int k1 = k0 + 32 < cu[b + 1] ? k0 + 32 : cu[b + 1];
+            bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq);
+            block_tolerances(&w, h, q0, q1, k0, k1, P, dP, dS, noise, tol, relp);
+            double amax = 0.0, tmax = 0.0;
+            for (int e = 0; e < 1024; ++e) {
+                amax = fabs(dS[e]) > amax ? fabs(dS[e]) : amax;
+                tmax = tol[e] > tmax ? tol[e] : tmax;
+            }
+            int xlo, xhi;
+            exponent_range(amax, tmax, &xlo, &xhi);
+            size_t o = (size_t)kb * 1024;
+            for (int i = q0; i < q1; ++i) {
+                int base = (i - q0) * 32;
+                int rlo = xlo, rhi = xhi;
+                if (per_row_ds) {
+                    double ra = 0.0, rt = 0.0;
+                    for (int j = k0; j < k1; ++j) {
+                        ra = fabs(dS[base + j - k0]) > ra ? fabs(dS[base + j - k0]) : ra;
+                        rt = tol[base + j - k0] > rt ? tol[base + j - k0] : rt;
                     }
-                    abs_k[(size_t)j * Hkv + g] = mk;
-                    abs_v[(size_t)j * Hkv + g] = mv;
+                    exponent_range(ra, rt, &rlo, &rhi);
+                }
+                for (int j = k0; j < k1; ++j) {
+                    if (causal && j > i) continue;
+                    int e = base + (j - k0);
+                    double lo, hi;
+                    ds_range(dS[e], tol[e], rlo, rhi, &lo, &hi);
+                    /* the oracle's own choice is always one of the results */
+                    lo = lo < dSq[e] ? lo : dSq[e];
+                    hi = hi > dSq[e] ? hi : dSq[e];
+                    if (lo == dSq[e] && hi == dSq[e]) continue;
+                    ei[o + cnt[kb]] = i;
+                    ej[o + cnt[kb]] = j;
+                    elo[o + cnt[kb]] = lo - dSq[e];
+                    ehi[o + cnt[kb]] = hi - dSq[e];
+                    ++cnt[kb];
+                }
+            }
+        }
+        free(buf);
+    }
+    int64_t n = 0;
+    for (int kb = 0; kb < nkb; ++kb)
+        for (int k = 0; k < cnt[kb]; ++k, ++n)
+            if (n < cap) {
+                size_t o = (size_t)kb * 1024 + k;
+                out_i[n] = ei[o];
+                out_j[n] = ej[o];
+                out_lo[n] = elo[o];
+                out_hi[n] = ehi[o];
+            }
+    free(cnt);
+    free(ei);
+    free(ej);
+    free(elo);
+    free(ehi);
+    return n;
+}
+
+/* The same for the dK and dV products of the 32 keys of the document-local
+ * block starting at k0 (kv head g): `which` 0 lists the probability operand
+ * P^ of dV, 1 the dS^ of dK (32x32 block exponents), over the group's q heads
+ * and the visible queries, as (head, query i, key j, lo, hi). */
+int64_t orc_bwd_dkdv_ranges(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale,
+                            int causal, const double* Q, const double* K, const double* V,
+                            const double* Qs, const double* Ks, const double* G, const double* D,
+                            const double* LSE, int per_row_ds, double noise, int g, int k0,
+                            int which, int64_t cap, int32_t* out_h, int32_t* out_i,
+                            int32_t* out_j, double* out_lo, double* out_hi)
+{
+    if (check_attn_args(T, B, cu, Hq, Hkv, d) != ORC_OK) return ORC_EBADARG;
+    int b = doc_of(B, cu, k0);
+    if (b < 0 || (k0 - cu[b]) % 32 || g < 0 || g >= Hkv || which < 0 || which > 1)
+        return ORC_EBADARG;
+    orc_attn a = {T, B, Hq, Hkv, d, causal, cu, scale, Q, K, V, Qs, Ks};
+    orc_bwd w = {&a, G, D, LSE, 0, per_row_ds};
+    int k1 = k0 + 32 < cu[b + 1] ? k0 + 32 : cu[b + 1];
+    int Gr = Hq / Hkv;
+    int qs = causal ? k0 : cu[b];
+    int nqb = (cu[b + 1] - qs + 31) / 32;
+    int nblk = Gr * nqb;
+    int32_t* cnt = (int32_t*)calloc((size_t)nblk + 1, sizeof(int32_t));
+    int32_t* eh = (int32_t*)malloc(sizeof(int32_t) * 1024 * (size_t)(nblk + 1));
+    int32_t* ei = (int32_t*)malloc(sizeof(int32_t) * 1024 * (size_t)(nblk + 1));
+    int32_t* ej = (int32_t*)malloc(sizeof(int32_t) * 1024 * (size_t)(nblk + 1));
+    double* elo = (double*)malloc(sizeof(double) * 1024 * (size_t)(nblk + 1));
+    double* ehi = (double*)malloc(sizeof(double) * 1024 * (size_t)(nblk + 1));
+#pragma omp parallel
+    {
+        double* buf = (double*)malloc(sizeof(double) * 8 * 1024);
+        double *P = buf, *dP = buf + 1024, *dS = buf + 2048, *Pq = buf + 3072,
+               *dSk = buf + 4096, *dSq = buf + 5120, *tol = buf + 6144, *relp = buf + 7168;
+#pragma omp for schedule(dynamic)
+        for (int x = 0; x < nblk; ++x) {
+            int h = g * Gr + x / nqb, q0 = qs + 32 * (x % nqb);
+            int q1 = q0 + 32 < cu[b + 1] ? q0 + 32 : cu[b + 1];
+            bwd_block(&w, h, q0, q1, k0, k1, P, dP, dS, Pq, dSk, dSq);
+            block_tolerances(&w, h, q0, q1, k0, k1, P, dP, dS, noise, tol, relp);
+            int xlo = 0, xhi = 0;
+            if (which == 1) {
+                double amax = 0.0, tmax = 0.0;
+                for (int e = 0; e < 1024; ++e) {
+                    amax = fabs(dS[e]) > amax ? fabs(dS[e]) : amax;
+                    tmax = tol[e] > tmax ? tol[e] : tmax;
+                }
+                exponent_range(amax, tmax, &xlo, &xhi);
+            }
+            size_t o = (size_t)x * 1024;
+            for (int i = q0; i < q1; ++i)
+                for (int j = k0; j < k1; ++j) {
+                    if (causal && j > i) continue;
+                    int e = (i - q0) * 32 + (j - k0);
+                    double lo, hi, ch;
+                    if (which == 0) {
+                        double y = 256.0 * P[e];
+                        e4m3_range(y, y * relp[e], &lo, &hi);
+                        lo /= 256.0;
+                        hi /= 256.0;
+                        ch = Pq[e];
+                    } else {
+                        ds_range(dS[e], tol[e], xlo, xhi, &lo, &hi);
+                        ch = dSk[e];
+                    }
+                    lo = lo < ch ? lo : ch;
+                    hi = hi > ch ? hi : ch;
+                    if (lo == ch && hi == ch) continue;
+                    eh[o + cnt[x]] = h;
+                    ei[o + cnt[x]] = i;
+                    ej[o + cnt[x]] = j;
+                    elo[o + cnt[x]] = lo - ch;
+                    ehi[o + cnt[x]] = hi - ch;
+                    ++cnt[x];
                 }
         }
         free(buf);
-        free(stp);
-        free(ak_sum);
-        free(av_sum);
     }
-    return ORC_OK;
+    int64_t n = 0;
+    for (int x = 0; x < nblk; ++x)
+        for (int k = 0; k < cnt[x]; ++k, ++n)
+            if (n < cap) {
+                size_t o = (size_t)x * 1024 + k;
+                out_h[n] = eh[o];
+                out_i[n] = ei[o];
+                out_j[n] = ej[o];
+                out_lo[n] = elo[o];
+                out_hi[n] = ehi[o];
+            }
+    free(cnt);
+    free(eh);
+    free(ei);
+    free(ej);
+    free(elo);
+    free(ehi);
+    return n;
 }

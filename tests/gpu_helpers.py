@@ -95,17 +95,31 @@ def oracle_operands(w, block=32):
     return q, k, v
 
 
+# Evaluation error of the GPU's dot products of E4M3 codes, as a fraction of
+# the sum of the absolute values of their terms: gfx950's FP8 matrix cores
+# keep about 12 bits below the largest product inside one instruction
+# (deviations from FP64 measured up to 2^-12.6 of that sum on random data),
+# and FP32 VALU work adds far less; 2^-12 leaves a factor 1.5.  It decides
+# which P^ / dS^ elements lie close enough to an E4M3 rounding midpoint that
+# either rounding is a correct result; it never widens a tolerance by itself.
+NOISE = 2.0 ** -12
+
+
+def fwd_ties(cu, ops, rows=None, **kw):
+    """The oracle's per-row tie bounds of the forward at NOISE, [Hq][T][2]."""
+    return oracle.fwd_ties(cu, ops, NOISE, mode=oracle.MODE_TILED, kblock=64, rows=rows, **kw)
+
+
 def check_fwd(got_O, got_LSE, ref_O64, ref_LSE, ties=None, tag=""):
     """Forward parity on matching row sets.  O: bf16 bits [n][d] vs FP64 [n][d];
     LSE: [n] f32 vs FP64; ties: [n][2] the oracle's rounding-tie bounds
     (|dO| and relative |dl| that flips of near-tie weights could cause).
     Tolerances: O cosine >= 0.9995; every row within 1e-2 max|O| plus its tie
-    bound; LSE within 1e-5 (1 + |LSE|) plus -ln(1 - tie_l), the larger of the
-    moves of ln l when l changes by a relative tie_l up (ln(1 + tie_l)) or
-    down (-ln(1 - tie_l)).  The GPU scores in
-    FP32 and the oracle in FP64, so a weight within FP32 noise of an E4M3
-    rounding midpoint may round either way; rows that need that allowance are
-    counted and reported."""
+    bound, and at most 5 % of the rows (or 2) needing the tie bound; LSE within
+    1e-5 (1 + |LSE|) plus -ln(1 - tie_l), the larger of the moves of ln l when
+    l changes by a relative tie_l up (ln(1 + tie_l)) or down (-ln(1 - tie_l)).
+    The reference is the oracle's tile loop at the kernel's 64-key step (the
+    weights are rounded against the running reference of each step)."""
     Og = oracle.bf16_to_float(got_O).reshape(-1, np.shape(got_O)[-1])
     Or = oracle.bf16_to_float(oracle.to_bf16(ref_O64)).reshape(Og.shape)
     tie = np.zeros((Og.shape[0], 2)) if ties is None else np.asarray(ties).reshape(-1, 2)
@@ -137,60 +151,179 @@ def check_fwd(got_O, got_LSE, ref_O64, ref_LSE, ties=None, tag=""):
     assert badl.size == 0
 
 
-def dq_tiles(cu, T, causal):
-    """Number of 128-key tiles whose FP16 partials reach each row's dQ."""
-    n = np.zeros(T, dtype=np.int64)
-    for s, e in zip(cu[:-1], cu[1:]):
-        s, e = int(s), int(e)
-        pos = np.arange(e - s)
-        n[s:e] = (pos // 128 + 1) if causal else ((e - s + 127) // 128)
-    return n
+def _closest_alternative(target, C, lo, hi):
+    """Smallest max-abs residual target - x C found over lo <= x <= hi (a
+    bounded least-squares solution: enough to show that a valid alternative
+    exists, which is all the check needs)."""
+    from scipy.optimize import lsq_linear
+    if len(C) == 0:
+        return float(np.abs(target).max())
+    C = np.asarray(C, dtype=np.float64)
+    lo, hi = np.asarray(lo, dtype=np.float64), np.asarray(hi, dtype=np.float64)
+    x = lsq_linear(C.T, target, bounds=(lo, hi), method="bvls").x
+    return float(np.abs(target - x @ C).max())
 
 
-def check_grad(got, ref64, tag, tie=None, rows=None, acc=None, ntiles=None, absm=None,
-               cos_min=0.995, row_max=5e-2):
-    """Gradient parity: cosine >= 0.995 and per-row max relative error <=
-    5e-2 (relative to the row's largest entry, floored at 1e-3 of the largest
-    entry overall), plus, per row, only what the arithmetic can explain:
-      - tie: the oracle's bound on what flips of near-tie P^ / dS^ elements
-        could move the row (FP32 vs FP64 evaluation), and
-      - for dQ, the FP16 accumulation of the per-128-key-tile partials that
-        the method prescribes: (n_tiles + 1) 2^-11 acc, acc being the sum
-        over tiles of each tile partial's largest magnitude, plus two bf16
-        roundings;
-      - the FP8 matrix cores' own rounding of the gradient product: 2^-11 of
-        the row's largest sum of absolute terms (absm).
-    Rows that need an allowance are counted and reported.  `rows` restricts
-    the check to a boolean [T][H] mask (sampled rows)."""
-    g = oracle.bf16_to_float(got)
+def check_grad(got, ref64, tag, alternatives=None, cos_min=0.995, row_max=5e-2, alt_max=1e-2,
+               max_alt_frac=0.05):
+    """Gradient parity on matching row sets: got bf16 bits (or float64
+    values) [n][d], ref64 float64 [n][d].  Every row must have max relative
+    error <= 5e-2 (relative to the row's largest reference entry, floored at
+    1e-3 of the largest entry overall), cosine >= 0.995 overall.
+
+    Several results are correct where an element of P^ or dS^ lies within the
+    GPU's evaluation error (NOISE) of an E4M3 rounding midpoint: the method
+    then allows either rounding (and the 32x32 block exponent can move when
+    the block maximum sits at a threshold).  A row beyond 5e-2 passes only if
+    such an alternative result explains it to within 1e-2 (alt_max, stricter
+    than the tolerance itself, so that the freedom of many near-midpoint
+    elements cannot absorb a real error): alternatives(k) returns
+    (C [m][d], lo [m], hi [m]) for row k, the valid results being ref + x C
+    with lo <= x <= hi.  At most 5 % of the rows (or 2) may need one.
+    Returns a dict of the row statistics, which is also logged."""
+    got = np.asarray(got)
+    g = oracle.bf16_to_float(got) if got.dtype == np.uint16 else got.astype(np.float64)
     r = oracle.bf16_to_float(oracle.to_bf16(ref64))
-    pick = (lambda x: None if x is None else np.asarray(x)[rows]) if rows is not None else \
-        (lambda x: x)
-    g, r, tie, acc, ntiles, absm = (pick(g), pick(r), pick(tie), pick(acc), pick(ntiles),
-                                    pick(absm))
-    g = g.reshape(-1, g.shape[-1])
-    r = r.reshape(-1, r.shape[-1])
+    d = g.shape[-1]
+    g, r = g.reshape(-1, d), r.reshape(-1, d)
     n = g.shape[0]
-    tie = np.zeros(n) if tie is None else np.asarray(tie, dtype=np.float64).ravel()
     rep = metrics.report(g, r)
     diff = np.abs(g - r).max(axis=1)
     rmax = np.abs(r).max(axis=1)
     denom = np.maximum(rmax, 1e-3 * rep["max_ref"])
-    base = row_max * denom
-    accb = np.zeros(n)
-    if acc is not None:
-        accb = (np.asarray(ntiles).ravel() + 1) * 2.0 ** -11 * np.asarray(acc).ravel() + \
-            2.0 ** -7 * rmax
-    mfma = np.zeros(n) if absm is None else 2.0 ** -11 * np.asarray(absm).ravel()
-    over = diff > base
-    log("%s: %s rows beyond %.0e: %d/%d (within the tie bound %d, within the FP16 "
-        "accumulation bound %d, within the MFMA rounding bound %d)" %
-        (tag, rep, row_max, int(over.sum()), n, int(np.sum(over & (diff <= base + tie))),
-         int(np.sum(over & (diff <= base + accb))), int(np.sum(over & (diff <= base + mfma)))))
+    err = diff / denom
+    over = np.nonzero(err > row_max)[0]
+    resolved, worst_alt, failed = 0, 0.0, []
+    for k in over:
+        if alternatives is None:
+            failed.append(k)
+            continue
+        C, lo, hi = alternatives(int(k))
+        res = _closest_alternative(g[k] - r[k], C, lo, hi) / denom[k]
+        worst_alt = max(worst_alt, res)
+        if res <= alt_max:
+            resolved += 1
+        else:
+            failed.append(k)
+    stats = dict(rows=n, p50=float(np.median(err)) if n else 0.0,
+                 p99=float(np.quantile(err, 0.99)) if n else 0.0,
+                 max=float(err.max()) if n else 0.0, beyond=int(over.size),
+                 resolved_by_alternative=resolved, worst_alternative_residual=worst_alt,
+                 cos=rep["cos"])
+    log("%s: %s per-row rel err p50 %.3g p99 %.3g max %.3g; rows beyond %.0e: %d/%d, "
+        "within %.0e of an alternative rounding: %d (worst residual %.3g)" %
+        (tag, rep, stats["p50"], stats["p99"], stats["max"], row_max, over.size, n, alt_max,
+         resolved, worst_alt))
+    for k in failed[:5]:
+        log("  row %d: rel err %.4g |d| %.4g rowmax %.4g" % (k, err[k], diff[k], rmax[k]))
     assert rep["cos"] >= cos_min, rep
-    bad = diff > base + tie + accb + mfma
-    for i in np.nonzero(bad)[0][:5]:
-        log("  row %d: |d| %.4g base %.4g tie %.4g acc %.4g mfma %.4g rowmax %.4g" %
-            (i, diff[i], base[i], tie[i], accb[i], mfma[i], rmax[i]))
-    assert not np.any(bad), "rows beyond tolerance + bounds: %s" % np.nonzero(bad)[0][:10]
-    return diff / denom
+    assert not failed, "rows beyond tolerance with no valid alternative: %s" % failed[:10]
+    assert over.size <= max(2, max_alt_frac * n), "too many rows needing an alternative"
+    return stats
+
+
+class Backward:
+    """References and alternatives for the gradient checks of one problem:
+    the oracle's microscaled backward on the GPU's own saved O / LSE (via D
+    and LSE), dQ through the method's FP16 accumulation (the GPU's prescale
+    exponents), dK and dV in FP64."""
+
+    def __init__(self, cu, ops, G, D, lse, kpre=None, scale=None, causal=True, per_row_ds=False):
+        self.cu, self.ops, self.G = np.asarray(cu, np.int32), ops, np.ascontiguousarray(G)
+        self.D = np.ascontiguousarray(D, dtype=np.float64)
+        self.lse = np.ascontiguousarray(lse, dtype=np.float64)
+        self.kpre = kpre
+        self.scale = oracle.default_scale(ops.d) if scale is None else scale
+        self.causal, self.per_row_ds = causal, per_row_ds
+        self.kw = dict(scale=self.scale, causal=causal, per_row_ds=per_row_ds)
+        self._ranges = {}
+
+    def _block_start(self, t):
+        b = int(np.searchsorted(self.cu, t, side="right") - 1)
+        while self.cu[b + 1] <= t:
+            b += 1
+        return int(self.cu[b]) + 32 * ((int(t) - int(self.cu[b])) // 32)
+
+    def dq(self, qblocks=None):
+        """dQ reference over the listed (q head, block start) pairs: the FP16
+        model when prescale exponents are given, else FP64."""
+        if self.kpre is None:
+            return oracle.bwd_dq(self.cu, self.ops, self.G, self.D, self.lse, qblocks=qblocks,
+                                 **self.kw)
+        return oracle.bwd_dq(self.cu, self.ops, self.G, self.D, self.lse, qblocks=qblocks,
+                             kpre=np.asarray(self.kpre, np.int32), **self.kw)[1]
+
+    def dkdv(self, kblocks=None):
+        return oracle.bwd_dkdv(self.cu, self.ops, self.G, self.D, self.lse, kblocks=kblocks,
+                               **self.kw)
+
+    def dq_alternatives(self, rows_th):
+        """alternatives() for dQ rows listed as (token, q head) in check order."""
+        ops, Hq, Hkv = self.ops, self.ops.Hq, self.ops.Hkv
+
+        def alt(k):
+            t, h = (int(x) for x in rows_th[k])
+            q0 = self._block_start(t)
+            key = ("q", h, q0)
+            if key not in self._ranges:
+                self._ranges[key] = oracle.dq_ranges(self.cu, ops, self.G, self.D, self.lse, h,
+                                                     q0, NOISE, **self.kw)
+            i, j, lo, hi = self._ranges[key]
+            sel = i == t
+            C = self.scale * ops.K[j[sel], h * Hkv // Hq]
+            return C, lo[sel], hi[sel]
+        return alt
+
+    def dkdv_alternatives(self, rows_tg, which):
+        """alternatives() for dV (which 0) or dK (which 1) rows listed as
+        (token, kv head)."""
+        ops = self.ops
+
+        def alt(k):
+            t, g = (int(x) for x in rows_tg[k])
+            k0 = self._block_start(t)
+            key = ("k", which, g, k0)
+            if key not in self._ranges:
+                self._ranges[key] = oracle.dkdv_ranges(self.cu, ops, self.G, self.D, self.lse, g,
+                                                       k0, which, NOISE, **self.kw)
+            h, i, j, lo, hi = self._ranges[key]
+            sel = j == t
+            C = self.G[i[sel], h[sel]] if which == 0 else self.scale * ops.Q[i[sel], h[sel]]
+            return C, lo[sel], hi[sel]
+        return alt
+
+    def check(self, got, tag, qmask=None, kmask=None, frame=None):
+        """Checks got = dict(dQ=..., dK=..., dV=...) (full [T][H][d] arrays of
+        bf16 bits) on the rows of qmask [T][Hq] / kmask [T][Hkv] (None: all
+        document rows).  frame maps a float64 gradient array to the frame the
+        oracle computes in (the rotated one for the Hadamard option)."""
+        T = self.ops.T
+        n = int(self.cu[-1])
+        if qmask is None:
+            qmask = np.zeros((T, self.ops.Hq), bool)
+            qmask[:n] = True
+        if kmask is None:
+            kmask = np.zeros((T, self.ops.Hkv), bool)
+            kmask[:n] = True
+        qb = sorted({(int(h), self._block_start(t)) for t, h in np.argwhere(qmask)})
+        kb = sorted({(int(g), self._block_start(t)) for t, g in np.argwhere(kmask)})
+        out = {}
+        fr = (lambda x: x) if frame is None else frame
+
+        def val(x):
+            return fr(oracle.bf16_to_float(x))
+        if "dQ" in got and qb:
+            ref = self.dq(np.array(qb, np.int32))
+            rows = np.argwhere(qmask)
+            out["dQ"] = check_grad(val(got["dQ"])[qmask], ref[qmask], tag + " dQ",
+                                   self.dq_alternatives(rows))
+        if kb and ("dK" in got or "dV" in got):
+            dK, dV = self.dkdv(np.array(kb, np.int32))
+            rows = np.argwhere(kmask)
+            if "dK" in got:
+                out["dK"] = check_grad(val(got["dK"])[kmask], dK[kmask], tag + " dK",
+                                       self.dkdv_alternatives(rows, 1))
+            if "dV" in got:
+                out["dV"] = check_grad(oracle.bf16_to_float(got["dV"])[kmask], dV[kmask],
+                                       tag + " dV", self.dkdv_alternatives(rows, 0))
+        return out

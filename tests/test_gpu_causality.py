@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_helpers import check_grad, dq_tiles, log, oracle_operands, run_gpu
+from tests.gpu_helpers import Backward, log, oracle_operands, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -45,9 +45,9 @@ def test_deterministic_dq_parity():
     gc, ge, D, _ = oracle.bwd_prep(w.cu, w.do, g["O"], k[1], v[1], w.Hkv)
     G = oracle.dequantize(gc, ge)
     lse = g["LSE"].astype(np.float64)
-    dQ, tq, _, aq = oracle.bwd_dq(w.cu, ops, G, D, lse, want_flags=True)
-    # FP32 accumulation: no FP16 accumulation allowance
-    check_grad(g["dQ"], dQ, "deterministic dQ", tq, absm=aq)
+    # FP32 accumulation in registers: the reference is the FP64 dQ (no FP16
+    # accumulation model)
+    Backward(w.cu, ops, G, D, lse).check(dict(dQ=g["dQ"]), "deterministic dQ")
     assert np.all(g["dQ"][int(w.cu[-1]):] == 0)
 
 
@@ -232,7 +232,5 @@ def test_sequence_prescale_control():
     log("sequence-wide prescale: earlier rows' exponent %d -> %d; per-row rule unchanged"
         % (int(a["ctl"]["kpre"][0, 0]), int(b["ctl"]["kpre"][0, 0])))
     w = b["w"]
-    dQ, tq, acc, aq = oracle.bwd_dq(w.cu, b["ops"], b["G"], b["D"],
-                                    b["ctl"]["LSE"].astype(np.float64), want_flags=True)
-    nt = np.repeat(dq_tiles(w.cu, w.T, True)[:, None], w.Hq, axis=1)
-    check_grad(b["ctl"]["dQ"], dQ, "dQ, sequence-wide prescale", tq, acc=acc, ntiles=nt, absm=aq)
+    Backward(w.cu, b["ops"], b["G"], b["D"], b["ctl"]["LSE"], kpre=b["ctl"]["kpre"]).check(
+        dict(dQ=b["ctl"]["dQ"]), "dQ, sequence-wide prescale")

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_helpers import (check_fwd, check_grad, dq_tiles, log, oracle_operands, run_gpu,
+from tests.gpu_helpers import (Backward, check_fwd, fwd_ties, log, oracle_operands, run_gpu,
                                run_gpu_exact)
 
 pytestmark = pytest.mark.gpu
@@ -23,6 +23,23 @@ def _sample_tokens(cu, rng, per_doc=6):
         toks += [s, min(s + 1, e - 1), min(s + 31, e - 1), min(s + 32, e - 1), e - 1]
         toks += list(rng.integers(s, e, size=per_doc))
     return sorted(set(toks))
+
+
+def _masks(w, qstarts, heads, nk=12, max_kheads=4):
+    """Rows of the sampled 32-query blocks (all heads listed) and of every
+    nk-th of those blocks' starts as key blocks (their kv heads)."""
+    qmask = np.zeros((w.T, w.Hq), dtype=bool)
+    for h in heads:
+        for t0 in qstarts:
+            b = int(np.searchsorted(w.cu, t0, side="right") - 1)
+            qmask[t0:min(t0 + 32, int(w.cu[b + 1])), h] = True
+    kheads = sorted(set(h * w.Hkv // w.Hq for h in heads))[:max_kheads]
+    kmask = np.zeros((w.T, w.Hkv), dtype=bool)
+    for hk in kheads:
+        for t0 in qstarts[:: max(1, len(qstarts) // nk)]:
+            b = int(np.searchsorted(w.cu, t0, side="right") - 1)
+            kmask[t0:min(t0 + 32, int(w.cu[b + 1])), hk] = True
+    return qmask, kmask
 
 
 @pytest.mark.timeout(600)
@@ -42,8 +59,8 @@ def test_full_size_sampled(name):
     heads = list(range(w.Hq)) if w.Hq <= 8 else list(rng.choice(w.Hq, 8, replace=False))
     rows = np.array([(h, t) for h in heads for t in toks], dtype=np.int32)
     ops = oracle.Operands.from_codes(q, k, v)
-    O, L, ties = oracle.attn_fwd(w.cu, ops, rows=rows, mode=oracle.MODE_TILED, kblock=64,
-                                   want_flags=True)
+    O, L = oracle.attn_fwd(w.cu, ops, rows=rows, mode=oracle.MODE_TILED, kblock=64)
+    ties = fwd_ties(w.cu, ops, rows=rows)
     mask = np.zeros((w.T, w.Hq), dtype=bool)
     mask[rows[:, 1], rows[:, 0]] = True
     check_fwd(g["O"][mask], g["LSE"].T[mask], O[mask], L.T[mask],
@@ -57,25 +74,8 @@ def test_full_size_sampled(name):
     log("prep ok")
     G = oracle.dequantize(gc, ge)
     lse = g["LSE"].astype(np.float64)
-    qstarts = oracle.doc_blocks(w.cu, toks)
-    qblocks = np.array([(h, t0) for h in heads for t0 in qstarts], dtype=np.int32)
-    dQ, tq, acc, aq = oracle.bwd_dq(w.cu, ops, G, D, lse, qblocks=qblocks, want_flags=True)
-    nt = np.repeat(dq_tiles(w.cu, w.T, True)[:, None], w.Hq, axis=1)
-    qmask = np.zeros((w.T, w.Hq), dtype=bool)
-    for h, t0 in qblocks:
-        b = int(np.searchsorted(w.cu, t0, side="right") - 1)
-        qmask[t0:min(t0 + 32, int(w.cu[b + 1])), h] = True
-    check_grad(g["dQ"], dQ, name + " dQ", tq, rows=qmask, acc=acc, ntiles=nt, absm=aq)
-    kheads = sorted(set(h * w.Hkv // w.Hq for h in heads))[:4]
-    kstarts = qstarts[:: max(1, len(qstarts) // 12)]
-    kblocks = np.array([(hk, t0) for hk in kheads for t0 in kstarts], dtype=np.int32)
-    dK, dV, tk, tv, ak, av = oracle.bwd_dkdv(w.cu, ops, G, D, lse, kblocks=kblocks, want_flags=True)
-    kmask = np.zeros((w.T, w.Hkv), dtype=bool)
-    for hk, t0 in kblocks:
-        b = int(np.searchsorted(w.cu, t0, side="right") - 1)
-        kmask[t0:min(t0 + 32, int(w.cu[b + 1])), hk] = True
-    check_grad(g["dK"], dK, name + " dK", tk, rows=kmask, absm=ak)
-    check_grad(g["dV"], dV, name + " dV", tv, rows=kmask, absm=av)
+    qmask, kmask = _masks(w, oracle.doc_blocks(w.cu, toks), heads)
+    Backward(w.cu, ops, G, D, lse, kpre=kpre).check(g, name, qmask=qmask, kmask=kmask)
 
 
 @pytest.mark.timeout(600)
@@ -101,8 +101,8 @@ def test_exact_option_full_size_sampled():
     heads = list(rng.choice(w.Hq, 6, replace=False))
     rows = np.array([(h, t) for h in heads for t in toks], dtype=np.int32)
     ops = oracle.Operands.from_codes(q, k, v, *v4)
-    O, L, ties = oracle.attn_fwd(w.cu, ops, rows=rows, mode=oracle.MODE_TILED, kblock=64,
-                                 want_flags=True)
+    O, L = oracle.attn_fwd(w.cu, ops, rows=rows, mode=oracle.MODE_TILED, kblock=64)
+    ties = fwd_ties(w.cu, ops, rows=rows)
     mask = np.zeros((w.T, w.Hq), dtype=bool)
     mask[rows[:, 1], rows[:, 0]] = True
     check_fwd(g["O"][mask], g["LSE"].T[mask], O[mask], L.T[mask],
@@ -115,25 +115,9 @@ def test_exact_option_full_size_sampled():
     log("prep ok")
     G = oracle.dequantize(gc, ge)
     lse = g["LSE"].astype(np.float64)
-    qstarts = oracle.doc_blocks(w.cu, toks)
-    qblocks = np.array([(h, t0) for h in heads for t0 in qstarts], dtype=np.int32)
-    dQ, tq, acc, aq = oracle.bwd_dq(w.cu, ops, G, D, lse, per_row_ds=True, qblocks=qblocks,
-                                    want_flags=True)
-    nt = np.repeat(dq_tiles(w.cu, w.T, True)[:, None], w.Hq, axis=1)
-    qmask = np.zeros((w.T, w.Hq), dtype=bool)
-    for h, t0 in qblocks:
-        qmask[t0:t0 + 32, h] = True
-    check_grad(g["dQ"], dQ, w.name + " dQ", tq, rows=qmask, acc=acc, ntiles=nt, absm=aq)
-    kheads = sorted(set(h * w.Hkv // w.Hq for h in heads))[:4]
-    kstarts = qstarts[:: max(1, len(qstarts) // 12)]
-    kblocks = np.array([(hk, t0) for hk in kheads for t0 in kstarts], dtype=np.int32)
-    dK, dV, tk, tv, ak, av = oracle.bwd_dkdv(w.cu, ops, G, D, lse, per_row_ds=True,
-                                             kblocks=kblocks, want_flags=True)
-    kmask = np.zeros((w.T, w.Hkv), dtype=bool)
-    for hk, t0 in kblocks:
-        kmask[t0:t0 + 32, hk] = True
-    check_grad(g["dK"], dK, w.name + " dK", tk, rows=kmask, absm=ak)
-    check_grad(g["dV"], dV, w.name + " dV", tv, rows=kmask, absm=av)
+    qmask, kmask = _masks(w, oracle.doc_blocks(w.cu, toks), heads)
+    Backward(w.cu, ops, G, D, lse, kpre=kpre, per_row_ds=True).check(g, w.name, qmask=qmask,
+                                                                      kmask=kmask)
 
 
 @pytest.mark.timeout(600)
@@ -166,8 +150,8 @@ def test_hadamard_full_size_sampled():
     toks = _sample_tokens(w.cu, rng, per_doc=6)
     heads = list(rng.choice(Hq, 5, replace=False))
     rows = np.array([(h, t) for h in heads for t in toks], dtype=np.int32)
-    O, L, ties = oracle.attn_fwd(w.cu, ops, scale=s, rows=rows, mode=oracle.MODE_TILED, kblock=64,
-                                 want_flags=True)
+    O, L = oracle.attn_fwd(w.cu, ops, scale=s, rows=rows, mode=oracle.MODE_TILED, kblock=64)
+    ties = fwd_ties(w.cu, ops, scale=s, rows=rows)
     Og, Lg = host(o).view(np.uint16), host(lse)
     mask = np.zeros((T, Hq), dtype=bool)
     mask[rows[:, 1], rows[:, 0]] = True
@@ -176,30 +160,13 @@ def test_hadamard_full_size_sampled():
     gc, ge, D, kpre = oracle.bwd_prep(w.cu, w.do, Og, rk[1], rv[1], Hkv, scale=s)
     G = oracle.dequantize(gc, ge)
     lse64 = Lg.astype(np.float64)
-    qstarts = oracle.doc_blocks(w.cu, toks)
-    qblocks = np.array([(h, t0) for h in heads for t0 in qstarts], dtype=np.int32)
-    dQr, tq, acc, aq = oracle.bwd_dq(w.cu, ops, G, D, lse64, scale=s, qblocks=qblocks, want_flags=True)
-    nt = np.repeat(dq_tiles(w.cu, T, True)[:, None], Hq, axis=1)
-    qmask = np.zeros((T, Hq), dtype=bool)
-    for h, t0 in qblocks:
-        b = int(np.searchsorted(w.cu, t0, side="right") - 1)
-        qmask[t0:min(t0 + 32, int(w.cu[b + 1])), h] = True
-    # rows are rotated back whole, so the sampled blocks' rows are exact;
-    # per-row allowances grow by at most d under the rotation
-    check_grad(host(dq).view(np.uint16), oracle.unrotate(dQr), "hadamard dQ", d * tq, rows=qmask,
-               acc=d * acc, ntiles=nt, absm=d * aq)
-    kheads = sorted(set(h * Hkv // Hq for h in heads))[:3]
-    kstarts = qstarts[:: max(1, len(qstarts) // 10)]
-    kblocks = np.array([(hk, t0) for hk in kheads for t0 in kstarts], dtype=np.int32)
-    dKr, dV, tk, tv, ak, av = oracle.bwd_dkdv(w.cu, ops, G, D, lse64, scale=s, kblocks=kblocks,
-                                              want_flags=True)
-    kmask = np.zeros((T, Hkv), dtype=bool)
-    for hk, t0 in kblocks:
-        b = int(np.searchsorted(w.cu, t0, side="right") - 1)
-        kmask[t0:min(t0 + 32, int(w.cu[b + 1])), hk] = True
-    check_grad(host(dk).view(np.uint16), oracle.unrotate(dKr), "hadamard dK", d * tk, rows=kmask,
-               absm=d * ak)
-    check_grad(host(dv).view(np.uint16), dV, "hadamard dV", tv, rows=kmask, absm=av)
+    qmask, kmask = _masks(w, oracle.doc_blocks(w.cu, toks), heads, nk=10, max_kheads=3)
+    # compared in the rotated frame the oracle computes in: the GPU's dQ and
+    # dK are dQ_r H and dK_r H with H H = d I, so dQ_r = dQ H / d
+    Hm = oracle.hadamard_matrix(d)
+    Backward(w.cu, ops, G, D, lse64, kpre=kpre, scale=s).check(
+        dict(dQ=host(dq).view(np.uint16), dK=host(dk).view(np.uint16), dV=host(dv).view(np.uint16)),
+        "hadamard", qmask=qmask, kmask=kmask, frame=lambda x: x @ Hm / d)
 
 
 @pytest.mark.timeout(600)
@@ -219,8 +186,8 @@ def test_noncausal_full_size_sampled():
     heads = list(rng.choice(w.Hq, 5, replace=False))
     rows = np.array([(h, t) for h in heads for t in toks], dtype=np.int32)
     ops = oracle.Operands.from_codes(q, k, v)
-    O, L, ties = oracle.attn_fwd(w.cu, ops, causal=False, rows=rows, mode=oracle.MODE_TILED, kblock=64,
-                                 want_flags=True)
+    O, L = oracle.attn_fwd(w.cu, ops, causal=False, rows=rows, mode=oracle.MODE_TILED, kblock=64)
+    ties = fwd_ties(w.cu, ops, causal=False, rows=rows)
     mask = np.zeros((w.T, w.Hq), dtype=bool)
     mask[rows[:, 1], rows[:, 0]] = True
     check_fwd(g["O"][mask], g["LSE"].T[mask], O[mask], L.T[mask], ties.transpose(1, 0, 2)[mask],
@@ -229,23 +196,6 @@ def test_noncausal_full_size_sampled():
     assert np.array_equal(g["gc"], gc) and np.array_equal(g["kpre"].astype(np.int32), kpre)
     G = oracle.dequantize(gc, ge)
     lse = g["LSE"].astype(np.float64)
-    qstarts = oracle.doc_blocks(w.cu, toks)
-    qblocks = np.array([(h, t0) for h in heads for t0 in qstarts[::2]], dtype=np.int32)
-    dQ, tq, acc, aq = oracle.bwd_dq(w.cu, ops, G, D, lse, causal=False, qblocks=qblocks, want_flags=True)
-    nt = np.repeat(dq_tiles(w.cu, w.T, False)[:, None], w.Hq, axis=1)
-    qmask = np.zeros((w.T, w.Hq), dtype=bool)
-    for h, t0 in qblocks:
-        b = int(np.searchsorted(w.cu, t0, side="right") - 1)
-        qmask[t0:min(t0 + 32, int(w.cu[b + 1])), h] = True
-    check_grad(g["dQ"], dQ, "non-causal dQ", tq, rows=qmask, acc=acc, ntiles=nt, absm=aq)
-    kheads = sorted(set(h * w.Hkv // w.Hq for h in heads))[:3]
-    kstarts = qstarts[:: max(1, len(qstarts) // 8)]
-    kblocks = np.array([(hk, t0) for hk in kheads for t0 in kstarts], dtype=np.int32)
-    dK, dV, tk, tv, ak, av = oracle.bwd_dkdv(w.cu, ops, G, D, lse, causal=False, kblocks=kblocks,
-                                             want_flags=True)
-    kmask = np.zeros((w.T, w.Hkv), dtype=bool)
-    for hk, t0 in kblocks:
-        b = int(np.searchsorted(w.cu, t0, side="right") - 1)
-        kmask[t0:min(t0 + 32, int(w.cu[b + 1])), hk] = True
-    check_grad(g["dK"], dK, "non-causal dK", tk, rows=kmask, absm=ak)
-    check_grad(g["dV"], dV, "non-causal dV", tv, rows=kmask, absm=av)
+    qmask, kmask = _masks(w, oracle.doc_blocks(w.cu, toks)[::2], heads, nk=4, max_kheads=3)
+    Backward(w.cu, ops, G, D, lse, kpre=kpre, causal=False).check(g, "non-causal", qmask=qmask,
+                                                                   kmask=kmask)

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_helpers import check_fwd, check_grad, dev, dq_tiles, host, log
+from tests.gpu_helpers import Backward, check_fwd, dev, fwd_ties, host, log
 
 pytestmark = pytest.mark.gpu
 
@@ -66,7 +66,8 @@ def test_rotated_forward_backward(case):
         assert np.array_equal(host(got[0]), ref[0]) and np.array_equal(host(got[1]), ref[1]), tag
     s = oracle.default_scale(d) / d
     ops = oracle.Operands.from_codes(rq, rk, rv)
-    O, L, ties = oracle.attn_fwd(w.cu, ops, scale=s, mode=oracle.MODE_TILED, kblock=64, want_flags=True)
+    O, L = oracle.attn_fwd(w.cu, ops, scale=s, mode=oracle.MODE_TILED, kblock=64)
+    ties = fwd_ties(w.cu, ops, scale=s)
     Og = host(o).view(np.uint16)
     check_fwd(Og.reshape(-1, d), host(lse).T.ravel(), O.reshape(-1, d), L.T.ravel(),
               ties.transpose(1, 0, 2).reshape(-1, 2), tag=name)
@@ -90,15 +91,13 @@ def test_rotated_forward_backward(case):
                           .astype(np.int32), kpre)
     G = oracle.dequantize(gc, ge)
     lse64 = host(lse).astype(np.float64)
-    dQr, tq, acc, aq = oracle.bwd_dq(w.cu, ops, G, D, lse64, scale=s, want_flags=True)
-    dKr, dV, tk, tv, ak, av = oracle.bwd_dkdv(w.cu, ops, G, D, lse64, scale=s, want_flags=True)
-    # back to the original coordinates; a row's max-norm error grows by at
-    # most d under the rotation, so the per-row allowances do too
-    dQ, dK = oracle.unrotate(dQr), oracle.unrotate(dKr)
-    nt = np.repeat(dq_tiles(w.cu, T, True)[:, None], Hq, axis=1)
-    check_grad(host(dq).view(np.uint16), dQ, name + " dQ", d * tq, acc=d * acc, ntiles=nt, absm=d * aq)
-    check_grad(host(dk).view(np.uint16), dK, name + " dK", d * tk, absm=d * ak)
-    check_grad(host(dv).view(np.uint16), dV, name + " dV", tv, absm=av)
+    # compared in the rotated frame the oracle computes in: the GPU's dQ and
+    # dK are dQ_r H and dK_r H, and H H = d I, so dQ_r = dQ H / d exactly in
+    # real arithmetic
+    Hm = oracle.hadamard_matrix(d)
+    Backward(w.cu, ops, G, D, lse64, kpre=kpre, scale=s).check(
+        dict(dQ=host(dq).view(np.uint16), dK=host(dk).view(np.uint16), dV=host(dv).view(np.uint16)),
+        name, frame=lambda x: x @ Hm / d)
     n = int(w.cu[-1])
     for t in (dq, dk, dv):
         assert np.all(host(t)[n:] == 0)

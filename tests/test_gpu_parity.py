@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_helpers import check_fwd, check_grad, dev, dq_tiles, host, log, oracle_operands, run_gpu
+from tests.gpu_helpers import Backward, check_fwd, dev, fwd_ties, host, log, oracle_operands, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -71,8 +71,8 @@ def _check_case(w, name):
         assert np.array_equal(g[tag + "e"], e), tag + " exps"
     # forward against the microscaled oracle
     ops = oracle.Operands.from_codes(q, k, v)
-    O, L, ties = oracle.attn_fwd(w.cu, ops, causal=causal, mode=oracle.MODE_TILED, kblock=64,
-                                   want_flags=True)
+    O, L = oracle.attn_fwd(w.cu, ops, causal=causal, mode=oracle.MODE_TILED, kblock=64)
+    ties = fwd_ties(w.cu, ops, causal=causal)
     check_fwd(g["O"].reshape(-1, d), g["LSE"].T.ravel(), O.reshape(-1, d), L.T.ravel(),
               ties.transpose(1, 0, 2).reshape(-1, 2), tag=name)
     # causal: the first token of every document sees only itself, so O equals
@@ -88,12 +88,7 @@ def _check_case(w, name):
     assert np.allclose(g["D"], D, rtol=1e-4, atol=1e-6 * np.abs(D).max())
     G = oracle.dequantize(gc, ge)
     lse = g["LSE"].astype(np.float64)
-    dQ, tq, acc, aq = oracle.bwd_dq(w.cu, ops, G, D, lse, causal=causal, want_flags=True)
-    dK, dV, tk, tv, ak, av = oracle.bwd_dkdv(w.cu, ops, G, D, lse, causal=causal, want_flags=True)
-    nt = np.repeat(dq_tiles(w.cu, w.T, causal)[:, None], Hq, axis=1)
-    check_grad(g["dQ"], dQ, name + " dQ", tq, acc=acc, ntiles=nt, absm=aq)
-    check_grad(g["dK"], dK, name + " dK", tk, absm=ak)
-    check_grad(g["dV"], dV, name + " dV", tv, absm=av)
+    Backward(w.cu, ops, G, D, lse, kpre=kpre, causal=causal).check(g, name)
     # padding rows
     n = int(w.cu[-1])
     assert np.all(g["O"][n:] == 0) and np.all(np.isinf(g["LSE"][:, n:]))
@@ -179,8 +174,8 @@ def _exact_case(name, lens, cap, Hq, Hkv, d, fp4, seed=5):
 def test_exact_forward(fp4, d):
     log("case exact forward fp4=%s d=%d" % (fp4, d))
     w, p, _, (o, lse), ops = _exact_case("exact", [160, 97], 270, 4, 2, d, fp4)
-    O, L, ties = oracle.attn_fwd(w.cu, ops, causal=True, mode=oracle.MODE_TILED, kblock=64,
-                                 want_flags=True)
+    O, L = oracle.attn_fwd(w.cu, ops, causal=True, mode=oracle.MODE_TILED, kblock=64)
+    ties = fwd_ties(w.cu, ops)
     check_fwd(host(o).view(np.uint16).reshape(-1, d), host(lse).T.ravel(), O.reshape(-1, d),
               L.T.ravel(), ties.transpose(1, 0, 2).reshape(-1, 2), tag="exact fp4=%s d=%d" % (fp4, d))
 
@@ -212,14 +207,10 @@ def test_exact_backward(d, fp4, lens=(230, 97, 40), cap=400):
                           .astype(np.int32), kpre)
     G = oracle.dequantize(gc, ge)
     lse64 = host(lse).astype(np.float64)
-    dQ, tq, acc, aq = oracle.bwd_dq(w.cu, ops, G, D, lse64, per_row_ds=True, want_flags=True)
-    dK, dV, tk, tv, ak, av = oracle.bwd_dkdv(w.cu, ops, G, D, lse64, per_row_ds=True,
-                                             want_flags=True)
-    nt = np.repeat(dq_tiles(w.cu, T, True)[:, None], Hq, axis=1)
     tag = "exact fp4=%s d=%d" % (fp4, d)
-    check_grad(host(dq).view(np.uint16), dQ, tag + " dQ", tq, acc=acc, ntiles=nt, absm=aq)
-    check_grad(host(dk).view(np.uint16), dK, tag + " dK", tk, absm=ak)
-    check_grad(host(dv).view(np.uint16), dV, tag + " dV", tv, absm=av)
+    Backward(w.cu, ops, G, D, lse64, kpre=kpre, per_row_ds=True).check(
+        dict(dQ=host(dq).view(np.uint16), dK=host(dk).view(np.uint16), dV=host(dv).view(np.uint16)),
+        tag)
     n = int(w.cu[-1])
     for t in (dq, dk, dv):
         assert np.all(host(t)[n:] == 0)

@@ -79,16 +79,22 @@ def test_blockwise_reference_equals_naive(causal, heads):
 
 def test_mirror_equals_reference_when_weights_are_representable():
     # scale ln 2 and integer dot products make every base-2 logit an integer,
-    # so every weight 2^(s2 - r) is a power of two >= 2^-12 and 256 p is an
-    # exact E4M3 value: the microscaled forward must then equal the reference
+    # so every weight 2^(s2 - r) is a power of two in [2^-17, 1] and 256 p,
+    # down to 2^-9 (the smallest E4M3 subnormal), is an exact E4M3 value: the
+    # microscaled forward must then equal the reference.  Each document's
+    # first key has logit 0 and its second -17, so every later row holds
+    # both ends: a boost of 128 would round 128 * 2^-17 (a tie) to 0, one of
+    # 512 would clip the largest weight to 448 / 512.
     rng = np.random.default_rng(4)
     T, d = 40, 4
     Q = np.zeros((T, 1, d))
     Q[:, 0, 0] = 1.0
     K = np.zeros((T, 1, d))
-    K[:, 0, 0] = rng.integers(-12, 1, T)
-    V = rng.integers(-8, 9, (T, 1, d)).astype(np.float64)
+    K[:, 0, 0] = rng.integers(-17, 1, T)
     cu = np.array([0, 17, 40], dtype=np.int32)
+    for s in cu[:-1]:
+        K[s, 0, 0], K[s + 1, 0, 0] = 0.0, -17.0
+    V = rng.integers(-8, 9, (T, 1, d)).astype(np.float64)
     ops = oracle.Operands(Q, K, V)
     Om, Lm = oracle.attn_fwd(cu, ops, scale=math.log(2), mode=oracle.MODE_ROUNDED)
     Or, Lr = oracle.attn_fwd(cu, ops, scale=math.log(2), mode=oracle.MODE_REFERENCE)

@@ -38,10 +38,33 @@ def _with_prescale(w, seq):
     r = mirror_pipeline(w)
     kp = (oracle.bwd_prescale_seq(w.cu, r["ge"], r["k"][1], r["v"][1], w.Hkv, w.d)
           if seq else r["kpre"])
-    dQ, dq16, tie, acc, absm = oracle.bwd_dq(w.cu, r["ops"], r["G"], r["D"],
-                                             r["LSE"].astype(np.float64), causal=w.causal,
-                                             kpre=kp, want_flags=True)
-    return r, kp, dQ, dq16, acc
+    lse = r["LSE"].astype(np.float64)
+    dQ, dq16 = oracle.bwd_dq(w.cu, r["ops"], r["G"], r["D"], lse, causal=w.causal, kpre=kp)
+    return r, kp, dQ, dq16, _tile_partial_magnitudes(w, r, lse)
+
+
+def _tile_partial_magnitudes(w, r, lse):
+    """Per row: the sum over its 128-key tiles of the largest magnitude of
+    the tile's dQ partial (scale sum_j dS^_ij K_j over the tile's keys), from
+    the oracle's 32x32 blocks."""
+    ops, scale = r["ops"], oracle.default_scale(w.d)
+    acc = np.zeros((w.T, w.Hq))
+    for h in range(w.Hq):
+        g = h * w.Hkv // w.Hq
+        for b in range(len(w.cu) - 1):
+            s0, s1 = int(w.cu[b]), int(w.cu[b + 1])
+            for q0 in range(s0, s1, 32):
+                n = min(32, s1 - q0)
+                part = np.zeros((32, w.d))
+                for k0 in range(s0, min(q0 + 32, s1), 32):
+                    kn = min(32, s1 - k0)
+                    blk = oracle.bwd_block(w.cu, ops, r["G"], r["D"], lse, h, q0, k0,
+                                           causal=w.causal)
+                    part += scale * blk["dSq"][:, :kn] @ ops.K[k0:k0 + kn, g]
+                    if (k0 - s0) // 32 % 4 == 3 or k0 + 32 >= min(q0 + 32, s1):
+                        acc[q0:q0 + n, h] += np.abs(part[:n]).max(axis=1)
+                        part[:] = 0.0
+    return acc
 
 
 def _scaled_rows(x, rows, factor):
