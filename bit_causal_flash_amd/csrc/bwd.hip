@@ -287,7 +287,7 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
             s_kq[buf][row] = r.ok ? r.pre + a.scale_exp : 0;
             // 8 - LSE log2 e: exp2 of the score term then yields 256 P; rows past
             // the document end get -inf, so their P is exactly zero
-            s_nlse[buf][row] = r.ok ? 8.f - r.lse * kLog2e : -INFINITY;
+            s_nlse[buf][row] = r.ok ? boosted_row_term(r.lse) : -INFINITY;
             s_delta[buf][row] = r.ok ? r.delta : 0.f;
             if constexpr (EXACT) {
                 // lane = query row: block maxima of the Q and dO exponents over
@@ -691,7 +691,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a)
     }
     const int eq = qvalid ? (int)a.q_exps[(size_t)h * T + qi] : 127;
     const int edo = qvalid ? (int)a.do_exps[(size_t)h * T + qi] : 127;
-    const float lse2 = qvalid ? a.lse_in[(size_t)h * T + qi] * kLog2e : INFINITY;
+    // 256 P = exp2(s c2 + 8 - LSE log2 e), formed as in the key-major kernel
+    const float nl = qvalid ? boosted_row_term(a.lse_in[(size_t)h * T + qi]) : -INFINITY;
     const float delta = qvalid ? a.delta[(size_t)h * T + qi] : 0.f;
 
     const int kend = a.causal ? min(q0 + 128, e) : e;
@@ -757,8 +758,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a)
                 for (int v = 0; v < 16; ++v) {
                     const int key = kt0 + 32 * t + 16 * g + v;
                     const bool vis = qvalid && key < e && (!a.causal || key <= qi);
-                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[t][v], c2, -lse2)) : 0.f;
-                    const float ds = p * (pacc[t][v] - delta);
+                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[t][v], c2, nl)) : 0.f;
+                    const float ds = p * (pacc[t][v] - delta);  // 256 dS
                     pacc[t][v] = ds;
                     amax[t] = fmaxf(amax[t], fabsf(ds));
                 }
@@ -766,13 +767,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a)
             v8i df;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const int et = ceil_exp448(wave_max_nonneg(amax[t]));
+                // block exponent of dS = that of 256 dS minus 8 (exact), and the
+                // codes of 256 dS over 2^(et + 8), as in the key-major kernel
+                const int et = ceil_exp448(wave_max_nonneg(amax[t]) * 0.00390625f);
                 dse[t] = et + 127;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     df[4 * t + q] = (int)cvt4_fp8(
-                        ldexpf(pacc[t][4 * q], -et), ldexpf(pacc[t][4 * q + 1], -et),
-                        ldexpf(pacc[t][4 * q + 2], -et), ldexpf(pacc[t][4 * q + 3], -et));
+                        ldexpf(pacc[t][4 * q], -et - 8), ldexpf(pacc[t][4 * q + 1], -et - 8),
+                        ldexpf(pacc[t][4 * q + 2], -et - 8), ldexpf(pacc[t][4 * q + 3], -et - 8));
             }
             // dQ^T += K^T dS^T: K read k-major from the token-major LDS tile
 #pragma unroll

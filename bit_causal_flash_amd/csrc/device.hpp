@@ -39,6 +39,15 @@ constexpr float kLn2 = 0.6931471805599453f;
 // MFMA).
 constexpr int kScaleMinus8 = 127 - 8;
 
+// The backward's per-row exponent term 8 - LSE log2(e), one FMA: exp2 of
+// s scale log2(e) plus it is 256 P.  Every kernel that rebuilds P forms it
+// this way, so that all of them round 256 P and 256 dS alike and one
+// quantized dS serves both dK and dQ.
+__device__ __forceinline__ float boosted_row_term(float lse)
+{
+    return __builtin_fmaf(-lse, kLog2e, 8.f);
+}
+
 __device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c, int scale_a,
                                         int scale_b)
 {

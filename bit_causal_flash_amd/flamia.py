@@ -249,6 +249,11 @@ def attn_fwd(p, q, k, v, stream=None, fp4=None):
     ws = torch.empty(max(flamia_attn_fwd_workspace_size(p), 1), dtype=torch.uint8, device=dev)
     f4 = None if fp4 is None else (fp4[0][0], fp4[0][1], fp4[1][0], fp4[1][1])
     flamia_attn_fwd(p, q[0], q[1], k[0], k[1], v[0], v[1], o, lse, ws, fp4=f4, stream=stream)
+    if stream is not None:
+        # the workspace was allocated on the current stream but is used on
+        # `stream`: keep the caching allocator from reusing it before that
+        # stream's kernels are done
+        ws.record_stream(stream)
     return o, lse
 
 
@@ -267,4 +272,85 @@ def attn_bwd(p, q, k, v, o, lse, dout, stream=None, workspace=None, fp4=None):
     f4 = None if fp4 is None else (fp4[0][0], fp4[0][1], fp4[1][0], fp4[1][1])
     flamia_attn_bwd(p, q[0], q[1], k[0], k[1], v[0], v[1], o, lse, dout, dq, dk, dv, workspace,
                     fp4=f4, stream=stream)
+    if stream is not None:
+        workspace.record_stream(stream)
     return dq, dk, dv, workspace
+
+
+# ---------------------------------------------------------------------------
+# PyTorch operator: quantize + forward, and the backward, as one autograd
+# Function (FLAMIA review section 9 "Reproduction notes and limitations": the
+# method ships as graph-capturable PyTorch operators taking bf16 in and
+# returning bf16 out).  torch supplies memory and the current stream only.
+# ---------------------------------------------------------------------------
+
+_ATTN_FN = None
+
+
+def _attn_function():
+    global _ATTN_FN
+    if _ATTN_FN is not None:
+        return _ATTN_FN
+    import torch
+
+    class FlamiaAttn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, cu_seqlens, flags, softmax_scale):
+            T, Hq, d = q.shape
+            Hkv = k.shape[1]
+            p = make_problem(cu_seqlens, T, Hq, Hkv, d, softmax_scale, flags)
+            mode = FLAMIA_SCALE_PER_TOKEN if flags & FLAMIA_EXACT else FLAMIA_SCALE_TOKBLOCK32
+            if flags & FLAMIA_HADAMARD:
+                mode |= FLAMIA_SCALE_ROTATE  # Q and K only (flamia_quantize_qkv)
+            (qc, qe), (kc, ke), (vc, ve) = quantize_qkv(p, q, k, v, mode)
+            views = ()
+            if flags & FLAMIA_FP4_SCORE:
+                views = quantize_nvfp4(p, q, Hq) + quantize_nvfp4(p, k, Hkv)
+            fp4 = None if not views else ((views[0], views[1]), (views[2], views[3]))
+            o, lse = attn_fwd(p, (qc, qe), (kc, ke), (vc, ve), fp4=fp4)
+            ctx.save_for_backward(cu_seqlens, qc, qe, kc, ke, vc, ve, o, lse, *views)
+            ctx.flags = flags
+            ctx.scale = softmax_scale
+            ctx.mark_non_differentiable(lse)
+            return o, lse
+
+        @staticmethod
+        def backward(ctx, dout, _dlse):
+            cu, qc, qe, kc, ke, vc, ve, o, lse, *views = ctx.saved_tensors
+            T, Hq, d = qc.shape
+            p = make_problem(cu, T, Hq, kc.shape[1], d, ctx.scale, ctx.flags)
+            fp4 = None if not views else ((views[0], views[1]), (views[2], views[3]))
+            dout = dout.to(torch.bfloat16).contiguous()
+            dq, dk, dv, _ = attn_bwd(p, (qc, qe), (kc, ke), (vc, ve), o, lse, dout, fp4=fp4)
+            return dq, dk, dv, None, None, None
+
+    _ATTN_FN = FlamiaAttn
+    return FlamiaAttn
+
+
+def attn(q, k, v, cu_seqlens, causal=True, exact=False, fp4_score=False, hadamard=False,
+         deterministic=False, softmax_scale=0.0, return_lse=False):
+    """Causal packed microscaled attention as a differentiable operator.
+
+    q: bf16 [T][Hq][d], k, v: bf16 [T][Hkv][d] (packed documents, rows past
+    cu_seqlens[-1] are padding), cu_seqlens: int32 [B + 1] on the same device.
+    The forward quantizes Q, K, V (token blocks, or per token with `exact`;
+    the E2M1 score views with `fp4_score`; Q and K rotated with `hadamard`)
+    and runs flamia_attn_fwd; the backward runs flamia_attn_bwd, which
+    quantizes dO itself.  Returns O (bf16 [T][Hq][d]), and with `return_lse`
+    also the natural-log LSE (float32 [Hq][T], not differentiable).  Raises
+    if the library is missing or the inputs are not bf16 GPU tensors: there
+    is no fallback path."""
+    import torch
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 3:
+            raise ValueError("%s must be a 3-d bfloat16 GPU tensor [T][H][d]" % name)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != q.device:
+        raise ValueError("cu_seqlens must be int32 on the device of q")
+    flags = (FLAMIA_CAUSAL if causal else 0) | (FLAMIA_EXACT if exact else 0) | \
+        (FLAMIA_FP4_SCORE if fp4_score else 0) | (FLAMIA_HADAMARD if hadamard else 0) | \
+        (FLAMIA_DETERMINISTIC if deterministic else 0)
+    load()
+    o, lse = _attn_function().apply(q.contiguous(), k.contiguous(), v.contiguous(),
+                                    cu_seqlens.contiguous(), flags, float(softmax_scale))
+    return (o, lse) if return_lse else o
