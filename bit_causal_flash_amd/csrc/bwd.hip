@@ -855,7 +855,7 @@ hipError_t launch_bwd(const AttnArgs& a, int D, int max_items, bool with_dq, hip
         return hipErrorInvalidDevice;
     const dim3 grid((unsigned)std::min<int64_t>((int64_t)max_items * a.Hkv, ncu));
 #define FLAMIA_BWD(DD, WQ, MM) \
-    hipExtLaunchKernelGGL((bwd_kernel<DD, WQ, MM>), grid, dim3(512), 0, stream, a.ev_start, a.ev_stop, 0, a)
+    FLAMIA_LAUNCH((bwd_kernel<DD, WQ, MM>), grid, dim3(512), stream, a.ev_start, a.ev_stop, a)
     if (D == 128) {
         if (a.mode == MODE_EXACT) {
             if (with_dq) FLAMIA_BWD(128, true, MODE_EXACT);

@@ -417,7 +417,7 @@ hipError_t launch_fwd(const AttnArgs& a, int D, int max_items, hipStream_t strea
     args.work_wgs = max_items * a.Hq;
     const dim3 grid((unsigned)(args.work_wgs + kFwdPadWgs));
 #define FLAMIA_FWD(DD, MM) \
-    hipExtLaunchKernelGGL((fwd_kernel<DD, MM>), grid, dim3(256), 0, stream, args.ev_start, args.ev_stop, 0, args)
+    FLAMIA_LAUNCH((fwd_kernel<DD, MM>), grid, dim3(256), stream, args.ev_start, args.ev_stop, args)
     if (D == 128) {
         if (a.mode == MODE_FP4) FLAMIA_FWD(128, MODE_FP4);
         else if (a.mode == MODE_EXACT) FLAMIA_FWD(128, MODE_EXACT);

@@ -8,6 +8,17 @@
 
 namespace flamia {
 
+// Launch with the caller's timing events when it asked for any (stamped from
+// the kernel's own dispatch), as a plain launch otherwise, which is what a
+// captured graph records.
+#define FLAMIA_LAUNCH(KERNEL, GRID, BLOCK, STREAM, EV0, EV1, ...)                             \
+    do {                                                                                      \
+        if ((EV0) != nullptr || (EV1) != nullptr)                                             \
+            hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, EV0, EV1, 0, __VA_ARGS__); \
+        else                                                                                  \
+            hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__);                  \
+    } while (0)
+
 // One tensor of a quantizer launch.
 struct QuantTensor {
     const uint16_t* x;   // bf16 [T][H][D]

@@ -473,8 +473,8 @@ hipError_t launch_nvfp4(const QuantArgs& a, int D, hipStream_t stream)
 {
     const size_t ng = (size_t)a.T * a.H * (D / 16);
     if (ng == 0) return hipSuccess;
-    hipExtLaunchKernelGGL(nvfp4_kernel, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, stream, a.ev_start,
-                          a.ev_stop, 0, a, D);
+    FLAMIA_LAUNCH(nvfp4_kernel, dim3((unsigned)((ng + 255) / 256)), dim3(256), stream, a.ev_start,
+                  a.ev_stop, a, D);
     return hipGetLastError();
 }
 
@@ -485,13 +485,13 @@ hipError_t launch_quant(const QuantArgs& a, int D, bool prep, hipStream_t stream
     bool rotate = false;
     for (int i = 0; i < a.ntensors; ++i) rotate = rotate || a.ten[i].rotate;
     if (D == 128) {
-        if (prep) hipExtLaunchKernelGGL((quant_kernel<128, true, false>), grid, dim3(256), 0, stream, a.ev_start, a.ev_stop, 0, a);
-        else if (rotate) hipExtLaunchKernelGGL((quant_kernel<128, false, true>), grid, dim3(256), 0, stream, a.ev_start, a.ev_stop, 0, a);
-        else hipExtLaunchKernelGGL((quant_kernel<128, false, false>), grid, dim3(256), 0, stream, a.ev_start, a.ev_stop, 0, a);
+        if (prep) FLAMIA_LAUNCH((quant_kernel<128, true, false>), grid, dim3(256), stream, a.ev_start, a.ev_stop, a);
+        else if (rotate) FLAMIA_LAUNCH((quant_kernel<128, false, true>), grid, dim3(256), stream, a.ev_start, a.ev_stop, a);
+        else FLAMIA_LAUNCH((quant_kernel<128, false, false>), grid, dim3(256), stream, a.ev_start, a.ev_stop, a);
     } else {
-        if (prep) hipExtLaunchKernelGGL((quant_kernel<64, true, false>), grid, dim3(256), 0, stream, a.ev_start, a.ev_stop, 0, a);
-        else if (rotate) hipExtLaunchKernelGGL((quant_kernel<64, false, true>), grid, dim3(256), 0, stream, a.ev_start, a.ev_stop, 0, a);
-        else hipExtLaunchKernelGGL((quant_kernel<64, false, false>), grid, dim3(256), 0, stream, a.ev_start, a.ev_stop, 0, a);
+        if (prep) FLAMIA_LAUNCH((quant_kernel<64, true, false>), grid, dim3(256), stream, a.ev_start, a.ev_stop, a);
+        else if (rotate) FLAMIA_LAUNCH((quant_kernel<64, false, true>), grid, dim3(256), stream, a.ev_start, a.ev_stop, a);
+        else FLAMIA_LAUNCH((quant_kernel<64, false, false>), grid, dim3(256), stream, a.ev_start, a.ev_stop, a);
     }
     return hipGetLastError();
 }
