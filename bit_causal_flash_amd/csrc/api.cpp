@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "flamia.h"
 #include "kernels.hpp"
@@ -180,6 +181,95 @@ void set_events(const flamia_problem* p, hipEvent_t& start, hipEvent_t& stop)
     stop = p->events ? (hipEvent_t)p->events->attn_stop : nullptr;
 }
 
+constexpr size_t kNoallocScratchBytes = size_t(4) << 20;
+
+}  // namespace
+
+// Scratch of the allocation-free forward (flamia_attn_fwd_noalloc): its work
+// list lives in this fixed device array instead of a caller's workspace.
+// Every GPU the library runs on holds its own copy until the process ends,
+// and every call on a GPU shares it (calls that overlap on one GPU race).
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+namespace {
+
+// The device address of `scratch` on each device, looked up once per device
+// with that device current.  (The name `scratch` in host code is a host-side
+// stand-in, not a device address.)
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+flamia_status scratch_of_current_device(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FLAMIA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FLAMIA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+            return FLAMIA_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return FLAMIA_OK;
+}
+
+flamia_status attn_fwd_impl(const flamia_problem* p, const uint8_t* q_codes,
+                              const uint8_t* q_exps, const uint8_t* k_codes,
+                              const uint8_t* k_exps, const uint8_t* v_codes,
+                              const uint8_t* v_exps, const uint8_t* q_fp4,
+                              const uint8_t* q_fp4_scales, const uint8_t* k_fp4,
+                              const uint8_t* k_fp4_scales, uint16_t* o, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream)
+{
+    Dims d;
+    flamia_status st = check_attn(p, &d);
+    if (st != FLAMIA_OK) return st;
+    st = check_fp4_pointers(p, q_fp4, q_fp4_scales, k_fp4, k_fp4_scales);
+    if (st != FLAMIA_OK) return st;
+    if (d.T == 0) return FLAMIA_OK;
+    if (!q_codes || !q_exps || !k_codes || !k_exps || !v_codes || !v_exps || !o || !lse)
+        return FLAMIA_ERR_INVALID_ARG;
+    const WorklistLayout wl = worklist_layout(d, kFwdTile, 0);
+    if (workspace == nullptr || workspace_bytes < wl.total) return FLAMIA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+
+    WorklistArgs w = make_worklist_args(d, p, kFwdTile, false, ws, wl);
+    hipError_t e = launch_worklist(w, s);
+    if (e != hipSuccess) return FLAMIA_ERR_HIP;
+
+    AttnArgs a = {};
+    a.T = (int)d.T;
+    a.B = (int)d.B;
+    a.Hq = (int)d.Hq;
+    a.Hkv = (int)d.Hkv;
+    a.causal = d.causal ? 1 : 0;
+    a.scale = d.scale;
+    a.c2 = d.scale * 1.4426950408889634f;
+    a.cu = p->cu_seqlens;
+    a.count = w.count;
+    a.items = w.items;
+    a.q_codes = q_codes;
+    a.q_exps = q_exps;
+    a.k_codes = k_codes;
+    a.k_exps = k_exps;
+    a.v_codes = v_codes;
+    a.v_exps = v_exps;
+    a.mode = operand_mode(p);
+    a.rotate = d.rotate ? 1 : 0;
+    a.q_fp4 = q_fp4;
+    a.q_fp4_scales = q_fp4_scales;
+    a.k_fp4 = k_fp4;
+    a.k_fp4_scales = k_fp4_scales;
+    a.o = o;
+    a.lse = lse;
+    set_events(p, a.ev_start, a.ev_stop);
+    return hip_status(launch_fwd(a, (int)d.d, w.max_items, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -293,50 +383,33 @@ flamia_status flamia_attn_fwd(const flamia_problem* p, const uint8_t* q_codes,
                               const uint8_t* k_fp4_scales, uint16_t* o, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream)
 {
+    return attn_fwd_impl(p, q_codes, q_exps, k_codes, k_exps, v_codes, v_exps, q_fp4, q_fp4_scales,
+                         k_fp4, k_fp4_scales, o, lse, workspace, workspace_bytes, stream);
+}
+
+size_t flamia_attn_fwd_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+flamia_status flamia_attn_fwd_noalloc(const flamia_problem* p, const uint8_t* q_codes,
+                                      const uint8_t* q_exps, const uint8_t* k_codes,
+                                      const uint8_t* k_exps, const uint8_t* v_codes,
+                                      const uint8_t* v_exps, const uint8_t* q_fp4,
+                                      const uint8_t* q_fp4_scales, const uint8_t* k_fp4,
+                                      const uint8_t* k_fp4_scales, uint16_t* o, float* lse,
+                                      void* stream)
+{
     Dims d;
     flamia_status st = check_attn(p, &d);
     if (st != FLAMIA_OK) return st;
-    st = check_fp4_pointers(p, q_fp4, q_fp4_scales, k_fp4, k_fp4_scales);
-    if (st != FLAMIA_OK) return st;
-    if (d.T == 0) return FLAMIA_OK;
-    if (!q_codes || !q_exps || !k_codes || !k_exps || !v_codes || !v_exps || !o || !lse)
-        return FLAMIA_ERR_INVALID_ARG;
-    const WorklistLayout wl = worklist_layout(d, kFwdTile, 0);
-    if (workspace == nullptr || workspace_bytes < wl.total) return FLAMIA_ERR_WORKSPACE;
-    hipStream_t s = (hipStream_t)stream;
-    uint8_t* ws = (uint8_t*)workspace;
-
-    WorklistArgs w = make_worklist_args(d, p, kFwdTile, false, ws, wl);
-    hipError_t e = launch_worklist(w, s);
-    if (e != hipSuccess) return FLAMIA_ERR_HIP;
-
-    AttnArgs a = {};
-    a.T = (int)d.T;
-    a.B = (int)d.B;
-    a.Hq = (int)d.Hq;
-    a.Hkv = (int)d.Hkv;
-    a.causal = d.causal ? 1 : 0;
-    a.scale = d.scale;
-    a.c2 = d.scale * 1.4426950408889634f;
-    a.cu = p->cu_seqlens;
-    a.count = w.count;
-    a.items = w.items;
-    a.q_codes = q_codes;
-    a.q_exps = q_exps;
-    a.k_codes = k_codes;
-    a.k_exps = k_exps;
-    a.v_codes = v_codes;
-    a.v_exps = v_exps;
-    a.mode = operand_mode(p);
-    a.rotate = d.rotate ? 1 : 0;
-    a.q_fp4 = q_fp4;
-    a.q_fp4_scales = q_fp4_scales;
-    a.k_fp4 = k_fp4;
-    a.k_fp4_scales = k_fp4_scales;
-    a.o = o;
-    a.lse = lse;
-    set_events(p, a.ev_start, a.ev_stop);
-    return hip_status(launch_fwd(a, (int)d.d, w.max_items, s));
+    // the work list must fit the fixed scratch: rejected before any launch
+    if (d.T > 0 && worklist_layout(d, kFwdTile, 0).total > kNoallocScratchBytes)
+        return FLAMIA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (d.T > 0) {
+        st = scratch_of_current_device(&ws);
+        if (st != FLAMIA_OK) return st;
+    }
+    return attn_fwd_impl(p, q_codes, q_exps, k_codes, k_exps, v_codes, v_exps, q_fp4, q_fp4_scales,
+                         k_fp4, k_fp4_scales, o, lse, ws, kNoallocScratchBytes, stream);
 }
 
 size_t flamia_attn_bwd_workspace_size(const flamia_problem* p)

@@ -37,6 +37,8 @@ EXPORTED = [
     "flamia_quantize_qkv",
     "flamia_attn_fwd_workspace_size",
     "flamia_attn_fwd",
+    "flamia_attn_fwd_noalloc_scratch_bytes",
+    "flamia_attn_fwd_noalloc",
     "flamia_attn_bwd_workspace_size",
     "flamia_attn_bwd",
     "flamia_attn_bwd_workspace_layout",
@@ -94,6 +96,10 @@ def load():
     lib.flamia_attn_fwd_workspace_size.argtypes = [P]
     lib.flamia_attn_fwd.restype = ctypes.c_int
     lib.flamia_attn_fwd.argtypes = [P] + [vp] * 12 + [vp, sz, vp]
+    lib.flamia_attn_fwd_noalloc_scratch_bytes.restype = sz
+    lib.flamia_attn_fwd_noalloc_scratch_bytes.argtypes = []
+    lib.flamia_attn_fwd_noalloc.restype = ctypes.c_int
+    lib.flamia_attn_fwd_noalloc.argtypes = [P] + [vp] * 12 + [vp]
     lib.flamia_attn_bwd_workspace_size.restype = sz
     lib.flamia_attn_bwd_workspace_size.argtypes = [P]
     lib.flamia_attn_bwd.restype = ctypes.c_int
@@ -187,6 +193,19 @@ def flamia_attn_fwd(p, q_codes, q_exps, k_codes, k_exps, v_codes, v_exps, o, lse
         ctypes.byref(p), _ptr(q_codes), _ptr(q_exps), _ptr(k_codes), _ptr(k_exps), _ptr(v_codes),
         _ptr(v_exps), _ptr(q4), _ptr(q4s), _ptr(k4), _ptr(k4s), _ptr(o), _ptr(lse),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def flamia_attn_fwd_noalloc(p, q_codes, q_exps, k_codes, k_exps, v_codes, v_exps, o, lse,
+                            fp4=None, stream=None):
+    q4, q4s, k4, k4s = fp4 if fp4 is not None else (None, None, None, None)
+    _check("flamia_attn_fwd_noalloc", load().flamia_attn_fwd_noalloc(
+        ctypes.byref(p), _ptr(q_codes), _ptr(q_exps), _ptr(k_codes), _ptr(k_exps), _ptr(v_codes),
+        _ptr(v_exps), _ptr(q4), _ptr(q4s), _ptr(k4), _ptr(k4s), _ptr(o), _ptr(lse),
+        _stream(stream)))
+
+
+def flamia_attn_noalloc_scratch_bytes() -> int:
+    return int(load().flamia_attn_fwd_noalloc_scratch_bytes())
 
 
 def flamia_attn_bwd(p, q_codes, q_exps, k_codes, k_exps, v_codes, v_exps, o, lse, dout, dq, dk,

@@ -36,8 +36,9 @@
  *   - Rows t >= cu_seqlens[B] are padding: codes 0, exponent byte 127,
  *     O = 0, LSE = +inf, dQ = dK = dV = 0.
  *   - GQA: q head h reads kv head floor(h * Hkv / Hq) (contiguous groups).
- *   - Thread-safety: no global mutable state; concurrent calls on different
- *     streams with disjoint outputs and workspaces are safe.
+ *   - Thread-safety: no global mutable state (except the fixed scratch array
+ *     of flamia_attn_fwd_noalloc, described there); concurrent calls on
+ *     different streams with disjoint outputs and workspaces are safe.
  */
 #ifndef FLAMIA_H
 #define FLAMIA_H
@@ -217,6 +218,36 @@ flamia_status flamia_attn_fwd(const flamia_problem* p, const uint8_t* q_codes,
                               const uint8_t* q_fp4_scales, const uint8_t* k_fp4,
                               const uint8_t* k_fp4_scales, uint16_t* o, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation and results as flamia_attn_fwd, with the work list in
+ * a fixed device array of the library instead of a caller's workspace.
+ *   - The array holds flamia_attn_fwd_noalloc_scratch_bytes() bytes (4 MiB):
+ *     a problem whose forward workspace (flamia_attn_fwd_workspace_size)
+ *     exceeds it returns FLAMIA_ERR_WORKSPACE before any launch.  4 MiB
+ *     covers, for instance, any document count up to 2^18 tokens, or up to
+ *     2^20 tokens in at most 2^16 documents.
+ *   - Each GPU the library runs on holds its own array until the process
+ *     ends; the call uses the one of the current device, so `stream` must
+ *     belong to it.  The array's device address is looked up on the first
+ *     call on each device (no allocation; make that first call outside a
+ *     graph capture).
+ *   - Every call on a GPU shares that GPU's array and leaves it holding the
+ *     last call's work list: calls that overlap on one GPU (several streams,
+ *     or several threads) race and must be ordered by the caller.
+ *   - Nothing is allocated or freed; the other arguments are as for
+ *     flamia_attn_fwd.
+ */
+size_t flamia_attn_fwd_noalloc_scratch_bytes(void);
+flamia_status flamia_attn_fwd_noalloc(const flamia_problem* p, const uint8_t* q_codes,
+                                      const uint8_t* q_exps, const uint8_t* k_codes,
+                                      const uint8_t* k_exps, const uint8_t* v_codes,
+                                      const uint8_t* v_exps, const uint8_t* q_fp4,
+                                      const uint8_t* q_fp4_scales, const uint8_t* k_fp4,
+                                      const uint8_t* k_fp4_scales, uint16_t* o, float* lse,
+                                      void* stream);
 
 /*
  * Backward (review section 5 Algorithm 1 steps 09-16; jaehun.me sections
