@@ -18,7 +18,8 @@ using namespace flamia;
 
 constexpr size_t kAlign = 256;
 constexpr int kFwdTile = 128;  // queries per forward work item
-constexpr int kBwdTile = 128;  // keys per backward work item
+constexpr int kBwdTile = 128;  // keys per backward work item (exact-scale modes)
+constexpr int kBwdWideTile = 256;  // keys per backward work item (token-block operands)
 constexpr uint32_t kKnownFlags =
     FLAMIA_CAUSAL | FLAMIA_EXACT | FLAMIA_FP4_SCORE | FLAMIA_DETERMINISTIC | FLAMIA_HADAMARD |
     FLAMIA_DQ_PRESCALE_SEQUENCE;
@@ -489,8 +490,11 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
         if (e != hipSuccess) return FLAMIA_ERR_HIP;
     }
 
+    // token-block operands: 256-key tiles (the layout is sized for the larger
+    // item count of 128-key tiles)
+    const bool wide = operand_mode(p) == MODE_BLOCK;
     const WorklistLayout wl = worklist_layout(d, kBwdTile, wl_base[0]);
-    WorklistArgs w = make_worklist_args(d, p, kBwdTile, true, ws, wl);
+    WorklistArgs w = make_worklist_args(d, p, wide ? kBwdWideTile : kBwdTile, true, ws, wl);
     e = launch_worklist(w, s);
     if (e != hipSuccess) return FLAMIA_ERR_HIP;
 
@@ -534,7 +538,8 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     a.k_fp4 = k_fp4;
     a.k_fp4_scales = k_fp4_scales;
     set_events(p, a.ev_start, a.ev_stop);
-    e = launch_bwd(a, (int)d.d, w.max_items, !d.deterministic, s);
+    e = wide ? launch_bwd_wide(a, (int)d.d, w.max_items, !d.deterministic, s)
+             : launch_bwd(a, (int)d.d, w.max_items, !d.deterministic, s);
     if (e != hipSuccess) return FLAMIA_ERR_HIP;
     a.ev_start = a.ev_stop = nullptr;
     if (d.deterministic) {

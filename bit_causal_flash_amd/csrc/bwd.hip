@@ -605,6 +605,385 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
     }  // tickets
 }
 
+// Adds one 32 x 32 dQ tile, the accumulator of a 32x32x64 MFMA (lane =
+// column, VGPR v = row 8 (v / 4) + 4 g + v % 4), into the FP16 accumulator
+// with packed atomics of two adjacent columns: neighbour lanes swap one value
+// of each VGPR pair (v, v + 1), which holds rows (R, R + 1), so that the even
+// lane adds columns (c, c + 1) of row R and the odd lane the same columns of
+// row R + 1.  Rows >= nrows are skipped.
+template <bool CHECK>
+__device__ __forceinline__ void dq_tile_atomics(const v16f& acc, _Float16* tile, size_t rs, int lane,
+                                                int nrows)
+{
+    const bool odd = lane & 1;
+    const int g = lane >> 5;
+    const int col = (lane & 31) & ~1;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int v = 2 * p;
+        const float x = acc[v], y = acc[v + 1];
+        const float send = odd ? x : y;
+        const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
+        const float lo = odd ? recv : x;
+        const float hi = odd ? y : recv;
+        const int row = 8 * (v / 4) + 4 * g + (v % 4) + (odd ? 1 : 0);
+        if (!CHECK || row < nrows)
+            __builtin_amdgcn_global_atomic_fadd_v2f16((h2*)(tile + (size_t)row * rs + col),
+                                                      __builtin_convertvector(v2f{lo, hi}, h2));
+    }
+}
+
+// The per-query statistics of one 64-query tile (lane = query, rows past the
+// document end clamped to its last row and marked invalid).
+struct QStats {
+    int eq, edo, pre, ok;
+    float lse, delta;
+};
+
+__device__ __forceinline__ void load_qstats(const AttnArgs& a, QStats& r, int h, int qb, int e, int tid)
+{
+    const int t = qb + (tid & 63);
+    r.ok = t < e;
+    const size_t i = (size_t)h * a.T + min(t, e - 1);
+    r.eq = a.q_exps[i];
+    r.edo = a.do_exps[i];
+    r.lse = a.lse_in[i];
+    r.delta = a.delta[i];
+    r.pre = a.prescale[i];
+}
+
+// Backward over document-local 256-key tiles (token-block operands).  A
+// workgroup of 8 waves owns 256 keys of one kv head; wave w owns keys
+// 32 w .. 32 w + 31 in every role: for each 64-query tile it forms S and dP
+// for them (one 32-query half at a time), P, dS and their codes, and
+// contracts those codes with the tile's dO and Q into its keys' dV and dK,
+// accumulated over the head dim in registers across the whole loop (the GQA
+// head reduction without atomics).  dS^ also goes key-major to LDS, where the
+// tile's dQ = dS^ K^ over all 256 keys is formed one step later, one FP16
+// partial per query row and 256-key tile (half the atomic payload of 128-key
+// tiles).
+//
+// The two waves that share a SIMD run their steps shifted against each
+// other, so that one wave's exponentials overlap the other's matrix
+// products: waves 0-3 form the scores of query tile j and contract them;
+// waves 4-7 first form and add (packed FP16 atomics) the dQ of tile j - 1,
+// then do the same as waves 0-3.  Only waves 0-3 fetch the next Q / dO tile
+// (at D = 128 straight into LDS, global_load_lds), so no load ever waits
+// behind an atomic (vector memory counters complete in order).  Q / dO tiles
+// are double-buffered (tile j in use, j + 1 landing), dS^ double-buffered;
+// one barrier per step orders the LDS traffic.
+template <int D, bool WITH_DQ>
+__global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
+{
+    using CT = CodeTile<D>;
+    constexpr int NKEY = 256;
+    constexpr int SPITCH = 64 + 16;  // dS^ tile, key-major: [256 keys][64 queries]
+    constexpr int NKS = D / 64;
+    constexpr int NDT = D / 32;
+    constexpr int CPR = D / 16;
+    constexpr bool DMA = CT::SWZ;    // D = 128: Q / dO tiles by direct global -> LDS loads
+    __shared__ __attribute__((aligned(16))) uint8_t s_kt[NKEY * CT::PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_vt[NKEY * CT::PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[2][64 * CT::PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_do[2][64 * CT::PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ds[2][NKEY * SPITCH];
+    __shared__ int s_eq[2][64], s_edo[2][64];
+    // the rows' prescale exponents are read by the dQ of tile j - 1 while tile
+    // j + 1's are staged: three slots (tile % 3)
+    __shared__ int s_kq[3][64];
+    __shared__ __attribute__((aligned(16))) float s_nlse[2][64];
+    __shared__ __attribute__((aligned(16))) float s_delta[2][64];
+    __shared__ int s_dsexp[2][2][8];  // [buffer][query half][key block]
+    __shared__ int s_ekb[8];
+    __shared__ int s_ticket[2];
+
+    const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
+    const size_t T = (size_t)a.T;
+    int* const next_ticket = a.tickets;
+    const int ntickets = *a.count * Hkv;
+    if (threadIdx.x == 0) s_ticket[0] = atomicAdd(next_ticket, 1);
+    __syncthreads();
+    for (int slot = 0;; slot ^= 1) {
+        const int ticket = __builtin_amdgcn_readfirstlane(s_ticket[slot]);
+        if (ticket >= ntickets) break;  // uniform: every thread read the slot after a barrier
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, wave = wave_id(), g = lane >> 5;
+        if (tid == 0) s_ticket[slot ^ 1] = atomicAdd(next_ticket, 1);
+        const int item = ticket / Hkv, hk = ticket % Hkv;
+        const int b = a.items[2 * item], kt = a.items[2 * item + 1];
+        const int s = a.cu[b], e = a.cu[b + 1];
+        const int k0 = s + NKEY * kt;
+        const int kw0 = k0 + 32 * wave;
+        const int kj = kw0 + (lane & 31);
+        const bool kvalid = kj < e;
+        const bool wave_keys = kw0 < e;
+        const float c2 = a.c2;
+        const int krow = 32 * wave + (lane & 31);
+
+        // the item's K and V tiles, token-major
+        for (int c = tid; c < NKEY * CPR; c += 512) {
+            const int row = c / CPR, col = 16 * (c % CPR);
+            const int t = k0 + row;
+            v4i kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+            if (t < e) {
+                kv = *(const v4i*)(a.k_codes + ((size_t)t * Hkv + hk) * D + col);
+                vv = *(const v4i*)(a.v_codes + ((size_t)t * Hkv + hk) * D + col);
+            }
+            *(v4i*)(s_kt + CT::off(row, col)) = kv;
+            *(v4i*)(s_vt + CT::off(row, col)) = vv;
+        }
+        const int ek = kvalid ? (int)a.k_exps[(size_t)hk * T + kj] : 127;
+        const int ev = kvalid ? (int)a.v_exps[(size_t)hk * T + kj] : 127;
+        if (tid < 8) s_ekb[tid] = (k0 + 32 * tid < e) ? (int)a.k_exps[(size_t)hk * T + k0 + 32 * tid] : 127;
+
+        // iterations: q heads of the group (outer) x 64-query tiles that see the keys
+        const int qt_lo = a.causal ? (NKEY / 64) * kt : 0;
+        const int nqt = (e - s + 63) / 64 - qt_lo;
+        const int niter = G * nqt;
+        auto tile_head = [&](int j) { return hk * G + j / nqt; };
+        auto tile_base = [&](int j) { return s + 64 * (qt_lo + j % nqt); };
+
+        // Q / dO tile j into buffer j & 1 (threads 0-255).  D = 128: wave w
+        // fills rows 16 w .. + 15 of each tile with two direct loads of 1 KB
+        // (eight rows), lane L writing LDS bytes 16 L .. + 15 of its block:
+        // row + L / 8, physical chunk L % 8, i.e. logical chunk (L % 8) ^
+        // tile_swizzle(row).  D = 64: through registers.
+        using Tile = QTile<D, 256>;
+        Tile nxt;
+        QStats st;
+        auto fetch = [&](int j) {
+            const int h = tile_head(j), qb = tile_base(j);
+            if constexpr (DMA) {
+                const int buf = j & 1;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int rb = 16 * wave + 8 * i;
+                    const int row = rb + (lane >> 3);
+                    const int c = (lane & 7) ^ tile_swizzle(row);
+                    const size_t src = ((size_t)min(qb + row, e - 1) * Hq + h) * D + 16 * c;
+                    __builtin_amdgcn_global_load_lds(a.q_codes + src, (lds_void*)&s_q[buf][rb * 128], 16, 0, 0);
+                    __builtin_amdgcn_global_load_lds(a.do_codes + src, (lds_void*)&s_do[buf][rb * 128], 16, 0, 0);
+                }
+                load_qstats(a, st, h, qb, e, tid);
+            } else {
+                load_qtile<D, 256, MODE_BLOCK>(a, nxt, h, qb, e, tid);
+            }
+        };
+        auto stage = [&](int j) {
+            const int buf = j & 1;
+            int eq, edo, pre, ok;
+            float lse, delta;
+            if constexpr (DMA) {
+                eq = st.eq; edo = st.edo; pre = st.pre; ok = st.ok; lse = st.lse; delta = st.delta;
+            } else {
+#pragma unroll
+                for (int k = 0; k < Tile::NC; ++k) {
+                    const int c = tid + 256 * k;
+                    const bool isq = c < 4 * D;
+                    const int cc = isq ? c : c - 4 * D;
+                    const int row = cc / CPR, col = 16 * (cc % CPR);
+                    *(v4i*)((isq ? s_q[buf] : s_do[buf]) + CT::off(row, col)) = nxt.c[k];
+                }
+                eq = nxt.eq; edo = nxt.edo; pre = nxt.pre; ok = nxt.ok; lse = nxt.lse; delta = nxt.delta;
+            }
+            const int row = tid & 63;
+            s_eq[buf][row] = ok ? eq : 127;
+            s_edo[buf][row] = ok ? edo : 127;
+            s_kq[j % 3][row] = ok ? pre + a.scale_exp : 0;
+            // 8 - LSE log2 e: exp2 of the score term then yields 256 P; rows past
+            // the document end get -inf, so their P is exactly zero
+            s_nlse[buf][row] = ok ? boosted_row_term(lse) : -INFINITY;
+            s_delta[buf][row] = ok ? delta : 0.f;
+        };
+        if (wave < 4) {
+            fetch(0);
+            stage(0);
+        }
+        // every load issued so far has landed (vmcnt(0)), so that inside the
+        // loop only the prefetch of the next tile is outstanding
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        lds_barrier();
+
+        v16f dk[NDT], dv[NDT];
+#pragma unroll
+        for (int i = 0; i < NDT; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dk[i][v] = dv[i][v] = 0.f;
+
+        // Tile j for the wave's keys: S, dP, P, dS, their codes (the k layout
+        // of the dV / dK products: bytes 0-15 query half 0, 16-31 half 1), the
+        // key-major dS^ rows of the tile's dQ product, then dV^T += dO^T P^ and
+        // dK^T += Q^T dS^ over the tile's 64 queries.
+        auto step = [&](int j) {
+            // lane-derived offsets are recomputed in every step (an opaque
+            // read of the thread index), not held across the loop next to the
+            // dK / dV accumulators
+            int lane = threadIdx.x;
+            asm volatile("" : "+v"(lane));
+            lane &= 63;
+            const int g = lane >> 5;
+            const int krow = 32 * wave + (lane & 31);
+            const int kj = kw0 + (lane & 31);
+            const bool kvalid = kj < e;
+            const int pb = j & 1;
+            const int qb = tile_base(j);
+            const uint8_t* sq = s_q[pb];
+            const uint8_t* sg = s_do[pb];
+            v8i pc = {0, 0, 0, 0, 0, 0, 0, 0}, dc = pc;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                v4i pf = {0, 0, 0, 0}, df = {0, 0, 0, 0};
+                int dse = 127;
+                const bool active = wave_keys && (!a.causal || qb + 32 * t + 31 >= kw0);
+                if (active) {
+                    const int qr = perm_row(t, lane & 31);
+                    v16f sacc, pacc;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = 0.f;
+                    const int eqr = s_eq[pb][qr], edr = s_edo[pb][qr];
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        sacc = mfma_f8(tile_row_operand<D>(sq, qr, 64 * ks, lane),
+                                       tile_row_operand<D>(s_kt, krow, 64 * ks, lane), sacc, eqr, ek);
+                        pacc = mfma_f8(tile_row_operand<D>(sg, qr, 64 * ks, lane),
+                                       tile_row_operand<D>(s_vt, krow, 64 * ks, lane), pacc, edr, ev);
+                    }
+                    // keep the scheduler from hoisting the next operands above
+                    // the element-wise work (register pressure)
+                    __builtin_amdgcn_sched_barrier(0);
+                    // element v of lane group g is query qb + 32 t + 16 g + v
+                    const float* nl = &s_nlse[pb][32 * t + 16 * g];
+                    const float* dl = &s_delta[pb][32 * t + 16 * g];
+                    const bool full = kw0 + 32 <= e && (!a.causal || qb + 32 * t >= kw0 + 31);
+                    float amax;
+                    if (full) {
+                        amax = softmax_grad<false>(sacc, pacc, nl, dl, c2, 0);
+                    } else {
+                        const int lim = a.causal ? kj - qb - 32 * t - 16 * g : (kvalid ? -1 : 16);
+                        amax = softmax_grad<true>(sacc, pacc, nl, dl, c2, lim);
+                    }
+                    // block exponent of dS = that of 256 dS minus 8 (exact)
+                    const int et = ceil_exp448(wave_max_nonneg(amax) * 0.00390625f);
+                    dse = et + 127;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        pf[q] = (int)cvt4_fp8(sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]);
+                        df[q] = (int)cvt4_fp8(ldexpf(pacc[4 * q], -et - 8), ldexpf(pacc[4 * q + 1], -et - 8),
+                                              ldexpf(pacc[4 * q + 2], -et - 8), ldexpf(pacc[4 * q + 3], -et - 8));
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    pc[4 * t + q] = pf[q];
+                    dc[4 * t + q] = df[q];
+                }
+                *(v4i*)(s_ds[pb] + krow * SPITCH + 32 * t + 16 * g) = df;
+                if (lane == 0) s_dsexp[pb][t][wave] = dse;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (wave_keys && (!a.causal || qb + 63 >= kw0)) {
+                // the dS block exponents of this wave's key block, per query
+                // half (lane group g supplies k block g's scale); the same
+                // wave wrote them above
+                const int dsg = s_dsexp[pb][g][wave];
+                const int sdo = s_edo[pb][32 * g];
+                const int sqe = s_eq[pb][32 * g];
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    dv[dt] = mfma_f8(tile_tr_operand<D>(sg, 0, 32 * dt, lane), pc, dv[dt], sdo, kScaleMinus8);
+                    dk[dt] = mfma_f8(tile_tr_operand<D>(sq, 0, 32 * dt, lane), dc, dk[dt], sqe, dsg);
+                }
+            }
+        };
+
+        // dQ of tile jp over the 256 keys: wave 4 + i forms the 32 x 32 tiles
+        // (query half ct, head-dim tile i % NDT) and adds them to the FP16
+        // accumulator.  The row's prescale 2^(k_i + f) rides in the A
+        // operand's block scale; the finalize applies 2^-(k_i + f) and the rest
+        // of the softmax scale.
+        auto dq = [&](int jp) {
+            int lane = threadIdx.x;
+            asm volatile("" : "+v"(lane));
+            lane &= 63;
+            const int g = lane >> 5;
+            const int pb = jp & 1;
+            const int qb = tile_base(jp), h = tile_head(jp);
+            const int wi = wave - 4;
+#pragma unroll 1
+            for (int ct = 0; ct < 2; ++ct) {
+                if (NDT == 2 && ct != (wi >> 1)) continue;  // D = 64: one tile per wave
+                const int dt = wi % NDT;
+                const int nrows = e - (qb + 32 * ct);
+                if (nrows <= 0) continue;
+                const int qrow = 32 * ct + (lane & 31);
+                const int kq = s_kq[jp % 3][qrow];
+                v16f acc;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < NKEY / 64; ++ks) {
+                    if (k0 + 64 * ks >= e) break;
+                    const int kb = 2 * ks + g;
+                    const int sa = min(max(s_dsexp[pb][ct][kb] + kq, 0), 254);
+                    acc = mfma_f8(lds_tr_operand(s_ds[pb] + 64 * ks * SPITCH, SPITCH, 0, 32 * ct, lane),
+                                  tile_tr_operand<D>(s_kt, 64 * ks, 32 * dt, lane), acc, sa, s_ekb[kb]);
+                }
+                _Float16* tile = a.dq_acc + ((size_t)(qb + 32 * ct) * Hq + h) * D + 32 * dt;
+                if (nrows >= 32) dq_tile_atomics<false>(acc, tile, (size_t)Hq * D, lane, nrows);
+                else dq_tile_atomics<true>(acc, tile, (size_t)Hq * D, lane, nrows);
+            }
+        };
+
+        // both loops pass the same number of barriers
+        if (wave < 4) {
+            for (int j = 0; j <= niter; ++j) {
+                // fetch tile j + 1 (the last steps reload the last tile, unused)
+                if (j + 1 < niter) fetch(j + 1);
+                if (j < niter) step(j);
+                if (j + 1 < niter) {
+                    stage(j + 1);
+                    // the direct loads count in vmcnt: they have landed once it is zero
+                    if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0x0F70);
+                }
+                lds_barrier();
+            }
+        } else {
+            for (int j = 0; j <= niter; ++j) {
+                if constexpr (WITH_DQ) {
+                    if (j >= 1) dq(j - 1);
+                }
+                if (j < niter) step(j);
+                lds_barrier();
+            }
+        }
+
+        // rotated Q and K: dK = dK_r H (the Sylvester matrix, unnormalised;
+        // the softmax scale already carries the 1 / d)
+        if (a.rotate) fwht_cols<NDT>(dk, lane);
+        if (kvalid) {
+            uint16_t* krp = a.dk + ((size_t)kj * Hkv + hk) * D;
+            uint16_t* vrp = a.dv + ((size_t)kj * Hkv + hk) * D;
+            const float sc = a.scale;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    v2i wk, wv;
+                    wk.x = (int)pack_bf16x2(dk[dt][4 * q] * sc, dk[dt][4 * q + 1] * sc);
+                    wk.y = (int)pack_bf16x2(dk[dt][4 * q + 2] * sc, dk[dt][4 * q + 3] * sc);
+                    wv.x = (int)pack_bf16x2(dv[dt][4 * q], dv[dt][4 * q + 1]);
+                    wv.y = (int)pack_bf16x2(dv[dt][4 * q + 2], dv[dt][4 * q + 3]);
+                    *(v2i*)(krp + 32 * dt + 8 * q + 4 * g) = wk;
+                    *(v2i*)(vrp + 32 * dt + 8 * q + 4 * g) = wv;
+                }
+        }
+        // item boundary: every wave is done with this item's LDS before the next
+        // item's first writes, and the next ticket is visible
+        __syncthreads();
+    }  // tickets
+}
+
 // Query-major dQ for the deterministic backward: a workgroup (4 waves x 32
 // queries) owns a 128-query tile of one document and one q head and walks
 // the visible keys in 64-key steps, recomputing S and dP exactly as the
@@ -877,6 +1256,27 @@ hipError_t launch_bwd(const AttnArgs& a, int D, int max_items, bool with_dq, hip
         }
     }
 #undef FLAMIA_BWD
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_wide(const AttnArgs& a, int D, int max_items, bool with_dq, hipStream_t stream)
+{
+    if (max_items <= 0) return hipSuccess;
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+        return hipErrorInvalidDevice;
+    const dim3 grid((unsigned)std::min<int64_t>((int64_t)max_items * a.Hkv, ncu));
+#define FLAMIA_BWDW(DD, WQ) \
+    FLAMIA_LAUNCH((bwd_wide_kernel<DD, WQ>), grid, dim3(512), stream, a.ev_start, a.ev_stop, a)
+    if (D == 128) {
+        if (with_dq) FLAMIA_BWDW(128, true);
+        else FLAMIA_BWDW(128, false);
+    } else {
+        if (with_dq) FLAMIA_BWDW(64, true);
+        else FLAMIA_BWDW(64, false);
+    }
+#undef FLAMIA_BWDW
     return hipGetLastError();
 }
 

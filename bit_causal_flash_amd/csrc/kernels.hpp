@@ -111,6 +111,8 @@ struct AttnArgs {
 
 hipError_t launch_fwd(const AttnArgs& a, int D, int max_items, hipStream_t stream);
 hipError_t launch_bwd(const AttnArgs& a, int D, int max_items, bool with_dq, hipStream_t stream);
+// token-block operands only: 256-key tiles (work list built with tile 256)
+hipError_t launch_bwd_wide(const AttnArgs& a, int D, int max_items, bool with_dq, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnArgs& a, int D, int max_items, hipStream_t stream);
 hipError_t launch_bwd_finalize(const AttnArgs& a, int D, bool dq_from_acc, hipStream_t stream);
 

@@ -4,8 +4,8 @@
 // sorted across the packed row, built without host synchronisation).
 //
 // Forward items are (document, 128-query tile), cost = number of 64-key steps
-// the tile visits.  Backward items are (document, 128-key tile), cost =
-// number of 64-query tiles visited.  One 1024-thread workgroup performs a
+// the tile visits.  Backward items are (document, key tile of 128 or 256
+// keys), cost = number of 64-query tiles visited.  One 1024-thread workgroup performs a
 // counting sort by cost: per-document item counts are scanned, every item
 // finds its document by binary search and bumps a cost histogram, the
 // histogram is scanned from the largest cost down, and items are scattered
@@ -51,8 +51,8 @@ __device__ __forceinline__ int item_cost(const WorklistArgs& a, int n, int m)
 {
     const int steps64 = (n + 63) / 64;
     if (a.backward) {
-        // query tiles of 64 visited by key tile m (keys [128 m, 128 m + 128))
-        return a.causal ? steps64 - 2 * m : steps64;
+        // query tiles of 64 visited by key tile m (keys [tile m, tile (m + 1)))
+        return a.causal ? steps64 - (a.tile / 64) * m : steps64;
     }
     // 64-key steps visited by query tile m (queries [128 m, 128 m + 128))
     return a.causal ? (min(a.tile * (m + 1), n) + 63) / 64 : steps64;

@@ -430,14 +430,14 @@ def _pairs(heads, starts):
 
 
 def bwd_dq(cu, ops: Operands, G, D, LSE, scale=None, causal=True, mode=MODE_ROUNDED,
-           per_row_ds=False, qblocks=None, kpre=None):
+           per_row_ds=False, qblocks=None, kpre=None, dq_tile=256):
     """dQ (float64 [T][Hq][d]) for the listed (q head, block start) pairs
     (default: every block of every head).  G: dequantized dO; D: [Hq][T];
     LSE: [Hq][T] natural log as saved by a forward.  With kpre (int32
     [Hq][T] prescale exponents) returns (dQ, dQ16): dQ16 is the same
-    gradient through the method's FP16 accumulation (per 128-key tile
-    partials boosted by 2^(kpre + f), rounded to FP16, summed in FP16 in tile
-    order)."""
+    gradient through the method's FP16 accumulation (partials per
+    document-relative tile of dq_tile keys boosted by 2^(kpre + f), rounded
+    to FP16, summed in FP16 in tile order)."""
     cu = _c(cu, np.int32)
     T, Hq, Hkv, d = ops.T, ops.Hq, ops.Hkv, ops.d
     scale = default_scale(d) if scale is None else scale
@@ -451,7 +451,7 @@ def bwd_dq(cu, ops: Operands, G, D, LSE, scale=None, causal=True, mode=MODE_ROUN
         T, len(cu) - 1, _p(cu), Hq, Hkv, d, ctypes.c_double(scale), int(bool(causal)),
         *ops.ptrs(), _p(_c(G, np.float64)), _p(_c(D, np.float64)), _p(_c(LSE, np.float64)),
         mode, int(bool(per_row_ds)), ctypes.c_int64(qblocks.shape[0]), _p(qblocks), _p(dQ),
-        _p(kp), _p(dq16)))
+        _p(kp), _p(dq16), int(dq_tile)))
     return (dQ, dq16) if kpre is not None else dQ
 
 

@@ -837,17 +837,20 @@ int orc_bwd_block(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, doubl
  * first token of a block.  dQ: [T][Hq][d], accumulated into.
  * With kpre (int32 [Hq][T]) and dq16, also the method's FP16 accumulation of
  * dQ ([R] S4 and [K] S3.3: FP16 partials with a power-of-two row prescale):
- * per document-relative 128-key tile the partial sum_j dS^_ij K^_j times
- * 2^(kpre_i + f), where 2^f <= scale < 2^(f + 1), is rounded to FP16 and
- * added into an FP16 accumulator (rounded again), tiles in key order; dq16 =
- * accumulator * scale / 2^(kpre_i + f). */
+ * per document-relative tile of `dq_tile` keys (a multiple of 32: the
+ * implementation's key tile, as the forward's key step is a parameter) the
+ * partial sum_j dS^_ij K^_j times 2^(kpre_i + f), where 2^f <= scale <
+ * 2^(f + 1), is rounded to FP16 and added into an FP16 accumulator (rounded
+ * again), tiles in key order; dq16 = accumulator * scale / 2^(kpre_i + f). */
 int orc_bwd_dq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double scale, int causal,
                const double* Q, const double* K, const double* V, const double* Qs,
                const double* Ks, const double* G, const double* D, const double* LSE, int mode,
                int per_row_ds, int64_t n, const int32_t* qblocks, double* dQ,
-               const int32_t* kpre, double* dq16)
+               const int32_t* kpre, double* dq16, int dq_tile)
 {
     if (check_attn_args(T, B, cu, Hq, Hkv, d) != ORC_OK) return ORC_EBADARG;
+    if (dq_tile < 32 || dq_tile % 32) return ORC_EBADARG;
+    const int tile_blocks = dq_tile / 32;
     if (check_blocks(B, cu, n, qblocks, Hq) != ORC_OK) return ORC_EBADARG;
     orc_attn a = {T, B, Hq, Hkv, d, causal, cu, scale, Q, K, V, Qs, Ks};
     orc_bwd w = {&a, G, D, LSE, mode, per_row_ds};
@@ -881,8 +884,9 @@ int orc_bwd_dq(int T, int B, const int32_t* cu, int Hq, int Hkv, int d, double s
                         part[(i - q0) * d + c] += acc;
                     }
                 }
-                /* the FP16 model: one partial per 128-key tile */
-                if (kpre && dq16 && (((k0 - cu[b]) / 32) % 4 == 3 || k0 + 32 >= kend)) {
+                /* the FP16 model: one partial per key tile */
+                if (kpre && dq16 &&
+                    (((k0 - cu[b]) / 32) % tile_blocks == tile_blocks - 1 || k0 + 32 >= kend)) {
                     for (int i = q0; i < q1; ++i) {
                         int kp = kpre[(size_t)h * T + i] + fexp;
                         for (int c = 0; c < d; ++c) {

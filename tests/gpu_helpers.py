@@ -228,13 +228,17 @@ class Backward:
     and LSE), dQ through the method's FP16 accumulation (the GPU's prescale
     exponents), dK and dV in FP64."""
 
-    def __init__(self, cu, ops, G, D, lse, kpre=None, scale=None, causal=True, per_row_ds=False):
+    def __init__(self, cu, ops, G, D, lse, kpre=None, scale=None, causal=True, per_row_ds=False,
+                 dq_tile=None):
         self.cu, self.ops, self.G = np.asarray(cu, np.int32), ops, np.ascontiguousarray(G)
         self.D = np.ascontiguousarray(D, dtype=np.float64)
         self.lse = np.ascontiguousarray(lse, dtype=np.float64)
         self.kpre = kpre
         self.scale = oracle.default_scale(ops.d) if scale is None else scale
         self.causal, self.per_row_ds = causal, per_row_ds
+        # the key tile of the kernel's FP16 dQ partials: 256 with token-block
+        # operands, 128 in the exact-scale modes
+        self.dq_tile = dq_tile if dq_tile is not None else (128 if per_row_ds else 256)
         self.kw = dict(scale=self.scale, causal=causal, per_row_ds=per_row_ds)
         self._ranges = {}
 
@@ -251,7 +255,8 @@ class Backward:
             return oracle.bwd_dq(self.cu, self.ops, self.G, self.D, self.lse, qblocks=qblocks,
                                  **self.kw)
         return oracle.bwd_dq(self.cu, self.ops, self.G, self.D, self.lse, qblocks=qblocks,
-                             kpre=np.asarray(self.kpre, np.int32), **self.kw)[1]
+                             kpre=np.asarray(self.kpre, np.int32), dq_tile=self.dq_tile,
+                             **self.kw)[1]
 
     def dkdv(self, kblocks=None):
         return oracle.bwd_dkdv(self.cu, self.ops, self.G, self.D, self.lse, kblocks=kblocks,

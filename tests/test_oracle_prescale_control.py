@@ -39,7 +39,8 @@ def _with_prescale(w, seq):
     kp = (oracle.bwd_prescale_seq(w.cu, r["ge"], r["k"][1], r["v"][1], w.Hkv, w.d)
           if seq else r["kpre"])
     lse = r["LSE"].astype(np.float64)
-    dQ, dq16 = oracle.bwd_dq(w.cu, r["ops"], r["G"], r["D"], lse, causal=w.causal, kpre=kp)
+    dQ, dq16 = oracle.bwd_dq(w.cu, r["ops"], r["G"], r["D"], lse, causal=w.causal, kpre=kp,
+                             dq_tile=128)
     return r, kp, dQ, dq16, _tile_partial_magnitudes(w, r, lse)
 
 
