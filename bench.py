@@ -46,7 +46,7 @@ def log(*a):
 def traffic_file(workload):
     """rocprofv3 FETCH_SIZE / WRITE_SIZE record of the backward main kernel on
     `workload`, valid only for the sources it was measured on."""
-    return os.path.join(ROOT, "profiles", "bwd_kernel_%s_traffic.json" % workload)
+    return os.path.join(ROOT, "profiles", "bwd_main_kernel_%s_traffic.json" % workload)
 
 
 class Hip:
@@ -412,7 +412,8 @@ def main():
         "seeds": hs["seeds"],
         "tflops_range": hs["tflops_range"],
         "pct_fp8_peak": hs["pct_fp8_peak"],
-        "roofline": {"kernel": "bwd_kernel", "bound": "mfma", "achieved": round(bwd_tflops, 2),
+        "roofline": {"kernel": ("bwd_kernel<%d, true, %d>" % (d, 2 if st.fp4 else 1)) if exact
+                     else "bwd_wide_kernel<%d, true>" % d, "bound": "mfma", "achieved": round(bwd_tflops, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bwd_tflops / FP8_PEAK_TFLOPS, 4),
                      "traffic": None if args.hadamard else measured_traffic(w.name)},
