@@ -663,15 +663,15 @@ __device__ __forceinline__ void load_qstats(const AttnArgs& a, QStats& r, int h,
 // partial per query row and 256-key tile (half the atomic payload of 128-key
 // tiles).
 //
-// The two waves that share a SIMD run their steps shifted against each
-// other, so that one wave's exponentials overlap the other's matrix
-// products: waves 0-3 form the scores of query tile j and contract them;
-// waves 4-7 first form and add (packed FP16 atomics) the dQ of tile j - 1,
-// then do the same as waves 0-3.  Only waves 0-3 fetch the next Q / dO tile
-// (at D = 128 straight into LDS, global_load_lds), so no load ever waits
-// behind an atomic (vector memory counters complete in order).  Q / dO tiles
-// are double-buffered (tile j in use, j + 1 landing), dS^ double-buffered;
-// one barrier per step orders the LDS traffic.
+// Each step every wave first forms and adds (packed FP16 atomics) its 32 x 32
+// tile of the dQ of query tile j - 1 (D = 64: waves 4-7 only), then forms
+// the scores of tile j for its keys and contracts them.  Waves 0-3 also
+// fetch the next Q / dO tile (at D = 128 straight into LDS,
+// global_load_lds), issued before their atomics: vector memory counters
+// complete in order, and the wait for the fetch at the end of the step then
+// also covers atomics issued a whole step earlier.  Q / dO tiles are
+// double-buffered (tile j in use, j + 1 landing), dS^ double-buffered; one
+// barrier per step orders the LDS traffic.
 template <int D, bool WITH_DQ>
 __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
 {
@@ -897,49 +897,52 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
             }
         };
 
-        // dQ of tile jp over the 256 keys: wave 4 + i forms the 32 x 32 tiles
-        // (query half ct, head-dim tile i % NDT) and adds them to the FP16
-        // accumulator.  The row's prescale 2^(k_i + f) rides in the A
-        // operand's block scale; the finalize applies 2^-(k_i + f) and the rest
-        // of the softmax scale.
-        auto dq = [&](int jp) {
+        // dQ of tile jp over the 256 keys: the 2 NDT output tiles of 32 x 32
+        // (query half ct = ti / NDT, head-dim tile dt = ti % NDT), one per
+        // wave (D = 128: all eight waves; D = 64: waves 4-7), each added to
+        // the FP16 accumulator.  The row's prescale 2^(k_i + f) rides in the
+        // A operand's block scale; the finalize applies 2^-(k_i + f) and the
+        // rest of the softmax scale.
+        auto dq = [&](int jp, int ti) {
             int lane = threadIdx.x;
             asm volatile("" : "+v"(lane));
             lane &= 63;
             const int g = lane >> 5;
             const int pb = jp & 1;
             const int qb = tile_base(jp), h = tile_head(jp);
-            const int wi = wave - 4;
-#pragma unroll 1
-            for (int ct = 0; ct < 2; ++ct) {
-                if (NDT == 2 && ct != (wi >> 1)) continue;  // D = 64: one tile per wave
-                const int dt = wi % NDT;
-                const int nrows = e - (qb + 32 * ct);
-                if (nrows <= 0) continue;
-                const int qrow = 32 * ct + (lane & 31);
-                const int kq = s_kq[jp % 3][qrow];
-                v16f acc;
+            const int ct = ti / NDT, dt = ti % NDT;
+            const int nrows = e - (qb + 32 * ct);
+            if (nrows <= 0) return;
+            const int qrow = 32 * ct + (lane & 31);
+            const int kq = s_kq[jp % 3][qrow];
+            v16f acc;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+            for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
-                for (int ks = 0; ks < NKEY / 64; ++ks) {
-                    if (k0 + 64 * ks >= e) break;
-                    const int kb = 2 * ks + g;
-                    const int sa = min(max(s_dsexp[pb][ct][kb] + kq, 0), 254);
-                    acc = mfma_f8(lds_tr_operand(s_ds[pb] + 64 * ks * SPITCH, SPITCH, 0, 32 * ct, lane),
-                                  tile_tr_operand<D>(s_kt, 64 * ks, 32 * dt, lane), acc, sa, s_ekb[kb]);
-                }
-                _Float16* tile = a.dq_acc + ((size_t)(qb + 32 * ct) * Hq + h) * D + 32 * dt;
-                if (nrows >= 32) dq_tile_atomics<false>(acc, tile, (size_t)Hq * D, lane, nrows);
-                else dq_tile_atomics<true>(acc, tile, (size_t)Hq * D, lane, nrows);
+            for (int ks = 0; ks < NKEY / 64; ++ks) {
+                if (k0 + 64 * ks >= e) break;
+                const int kb = 2 * ks + g;
+                const int sa = min(max(s_dsexp[pb][ct][kb] + kq, 0), 254);
+                acc = mfma_f8(lds_tr_operand(s_ds[pb] + 64 * ks * SPITCH, SPITCH, 0, 32 * ct, lane),
+                              tile_tr_operand<D>(s_kt, 64 * ks, 32 * dt, lane), acc, sa, s_ekb[kb]);
             }
+            _Float16* tile = a.dq_acc + ((size_t)(qb + 32 * ct) * Hq + h) * D + 32 * dt;
+            if (nrows >= 32) dq_tile_atomics<false>(acc, tile, (size_t)Hq * D, lane, nrows);
+            else dq_tile_atomics<true>(acc, tile, (size_t)Hq * D, lane, nrows);
         };
+        // D = 128: every wave owns one dQ output tile; waves 0-3 add theirs
+        // after issuing the next tile's fetch, so that their final wait for
+        // the fetch also covers atomics issued a whole step earlier
+        constexpr bool DQ_ALL = NDT == 4;
 
         // both loops pass the same number of barriers
         if (wave < 4) {
             for (int j = 0; j <= niter; ++j) {
                 // fetch tile j + 1 (the last steps reload the last tile, unused)
                 if (j + 1 < niter) fetch(j + 1);
+                if constexpr (WITH_DQ && DQ_ALL) {
+                    if (j >= 1) dq(j - 1, wave);
+                }
                 if (j < niter) step(j);
                 if (j + 1 < niter) {
                     stage(j + 1);
@@ -951,7 +954,7 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
         } else {
             for (int j = 0; j <= niter; ++j) {
                 if constexpr (WITH_DQ) {
-                    if (j >= 1) dq(j - 1);
+                    if (j >= 1) dq(j - 1, DQ_ALL ? wave : wave - 4);
                 }
                 if (j < niter) step(j);
                 lds_barrier();
