@@ -633,6 +633,33 @@ __device__ __forceinline__ void dq_tile_atomics(const v16f& acc, _Float16* tile,
     }
 }
 
+// The same addition with fewer vector instructions: VGPRs v, v + 1 (rows
+// r, r + 1 of the lane's column c) are converted as one FP16 pair, neighbour
+// lanes swap pairs (DPP) and v_perm regroups them, so that the even lane of
+// a pair adds (row r; columns c, c + 1) and the odd lane (row r + 1;
+// columns c - 1, c).  Each row pair's address is a uniform base (scalar
+// arithmetic) plus the lane's constant offset.  Rows >= nrows are skipped.
+template <bool CHECK>
+__device__ __forceinline__ void dq_tile_atomics_pk(const v16f& acc, _Float16* tile, size_t rs, int lane,
+                                                   int nrows)
+{
+    const bool odd = lane & 1;
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+    const int lrow = 4 * (lane >> 5) + (odd ? 1 : 0);
+    const uint32_t lane_off = (uint32_t)(((size_t)lrow * rs + (lane & 30)) * 2);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int v = 2 * p;
+        const int r0 = 8 * (v / 4) + (v % 4);
+        const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{acc[v], acc[v + 1]}, h2));
+        const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0xB1, 0xF, 0xF, false);
+        const uint32_t out = __builtin_amdgcn_perm(y, w, sel);
+        char* base = (char*)(tile + (size_t)r0 * rs);
+        if (!CHECK || r0 + lrow < nrows)
+            __builtin_amdgcn_global_atomic_fadd_v2f16((h2*)(base + lane_off), __builtin_bit_cast(h2, out));
+    }
+}
+
 // The per-query statistics of one 64-query tile (lane = query, rows past the
 // document end clamped to its last row and marked invalid).
 struct QStats {
@@ -927,8 +954,8 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                               tile_tr_operand<D>(s_kt, 64 * ks, 32 * dt, lane), acc, sa, s_ekb[kb]);
             }
             _Float16* tile = a.dq_acc + ((size_t)(qb + 32 * ct) * Hq + h) * D + 32 * dt;
-            if (nrows >= 32) dq_tile_atomics<false>(acc, tile, (size_t)Hq * D, lane, nrows);
-            else dq_tile_atomics<true>(acc, tile, (size_t)Hq * D, lane, nrows);
+            if (nrows >= 32) dq_tile_atomics_pk<false>(acc, tile, (size_t)Hq * D, lane, nrows);
+            else dq_tile_atomics_pk<true>(acc, tile, (size_t)Hq * D, lane, nrows);
         };
         // D = 128: every wave owns one dQ output tile; waves 0-3 add theirs
         // after issuing the next tile's fetch, so that their final wait for
