@@ -474,10 +474,9 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
                                 for (int q = 0; q < 4; ++q) {
                                     pf[q] = (int)cvt4_fp8(sacc[t][4 * q], sacc[t][4 * q + 1],
                                                           sacc[t][4 * q + 2], sacc[t][4 * q + 3]);
-                                    df[q] = (int)cvt4_fp8(ldexpf(pacc[t][4 * q], -et - 8),
-                                                          ldexpf(pacc[t][4 * q + 1], -et - 8),
-                                                          ldexpf(pacc[t][4 * q + 2], -et - 8),
-                                                          ldexpf(pacc[t][4 * q + 3], -et - 8));
+                                    df[q] = (int)cvt4_fp8_div(pacc[t][4 * q], pacc[t][4 * q + 1],
+                                                              pacc[t][4 * q + 2], pacc[t][4 * q + 3],
+                                                              ds_code_divisor(et));
                                 }
                             }
                         }
@@ -896,8 +895,8 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         pf[q] = (int)cvt4_fp8(sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]);
-                        df[q] = (int)cvt4_fp8(ldexpf(pacc[4 * q], -et - 8), ldexpf(pacc[4 * q + 1], -et - 8),
-                                              ldexpf(pacc[4 * q + 2], -et - 8), ldexpf(pacc[4 * q + 3], -et - 8));
+                        df[q] = (int)cvt4_fp8_div(pacc[4 * q], pacc[4 * q + 1], pacc[4 * q + 2],
+                                                  pacc[4 * q + 3], ds_code_divisor(et));
                     }
                 }
 #pragma unroll
@@ -1182,9 +1181,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a)
                 dse[t] = et + 127;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    df[4 * t + q] = (int)cvt4_fp8(
-                        ldexpf(pacc[t][4 * q], -et - 8), ldexpf(pacc[t][4 * q + 1], -et - 8),
-                        ldexpf(pacc[t][4 * q + 2], -et - 8), ldexpf(pacc[t][4 * q + 3], -et - 8));
+                    df[4 * t + q] = (int)cvt4_fp8_div(pacc[t][4 * q], pacc[t][4 * q + 1], pacc[t][4 * q + 2],
+                                                      pacc[t][4 * q + 3], ds_code_divisor(et));
             }
             // dQ^T += K^T dS^T: K read k-major from the token-major LDS tile
 #pragma unroll

@@ -92,6 +92,24 @@ __device__ __forceinline__ uint32_t cvt4_fp8(float a, float b, float c, float d)
     return (uint32_t)w;
 }
 
+// Four floats divided by the power of two `scale` -> four E4M3 codes.  The
+// scaled conversion divides exactly before it rounds: measured bit-identical
+// to rounding ldexpf(x, -k) for scale = 2^k on 2^20 pairs (midpoints and
+// E4M3-subnormal results included), one instruction per two codes instead of
+// one per code plus the conversion.
+__device__ __forceinline__ uint32_t cvt4_fp8_div(float a, float b, float c, float d, float scale)
+{
+    typedef short s2 __attribute__((ext_vector_type(2)));
+    const s2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s2{0, 0}, a, b, scale, false);
+    const s2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, c, d, scale, true);
+    return __builtin_bit_cast(uint32_t, w);
+}
+
+// 2^(e + 8) as the divisor of cvt4_fp8_div for a dS block exponent e (the
+// codes of 256 dS scaled by 2^(-e-8)); e + 8 stays within [-119, 121] for
+// finite inputs, the clamp only keeps non-finite ones representable.
+__device__ __forceinline__ float ds_code_divisor(int e) { return ldexpf(1.f, min(e + 8, 127)); }
+
 // Sum of the four E4M3 values packed in w.
 __device__ __forceinline__ float sum4_fp8(uint32_t w)
 {
