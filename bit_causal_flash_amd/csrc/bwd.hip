@@ -946,7 +946,9 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
             for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < NKEY / 64; ++ks) {
-                if (k0 + 64 * ks >= e) break;
+                // an item's first key is inside its document: the first block
+                // always runs, so the zero accumulator is never needed
+                if (ks > 0 && k0 + 64 * ks >= e) break;
                 const int kb = 2 * ks + g;
                 const int sa = min(max(s_dsexp[pb][ct][kb] + kq, 0), 254);
                 acc = mfma_f8(lds_tr_operand(s_ds[pb] + 64 * ks * SPITCH, SPITCH, 0, 32 * ct, lane),
