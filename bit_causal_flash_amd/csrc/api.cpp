@@ -490,9 +490,10 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
         if (e != hipSuccess) return FLAMIA_ERR_HIP;
     }
 
-    // token-block operands: 256-key tiles (the layout is sized for the larger
-    // item count of 128-key tiles)
-    const bool wide = operand_mode(p) == MODE_BLOCK;
+    // 256-key tiles for token-block operands and for per-token operands at
+    // d = 64; per-token operands at d = 128 keep 128-key tiles (the layout is
+    // sized for the larger item count of 128-key tiles)
+    const bool wide = operand_mode(p) == MODE_BLOCK || d.d == 64;
     const WorklistLayout wl = worklist_layout(d, kBwdTile, wl_base[0]);
     WorklistArgs w = make_worklist_args(d, p, wide ? kBwdWideTile : kBwdTile, true, ws, wl);
     e = launch_worklist(w, s);

@@ -698,16 +698,21 @@ __device__ __forceinline__ void load_qstats(const AttnArgs& a, QStats& r, int h,
 // also covers atomics issued a whole step earlier.  Q / dO tiles are
 // double-buffered (tile j in use, j + 1 landing), dS^ double-buffered; one
 // barrier per step orders the LDS traffic.
-template <int D, bool WITH_DQ>
+template <int D, bool WITH_DQ, int MODE>
 __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
 {
     using CT = CodeTile<D>;
     constexpr int NKEY = 256;
     constexpr int SPITCH = 64 + 16;  // dS^ tile, key-major: [256 keys][64 queries]
+    constexpr int PITCH16 = 2 * D + 16;
     constexpr int NKS = D / 64;
+    constexpr int NKH = D / 16;
     constexpr int NDT = D / 32;
     constexpr int CPR = D / 16;
     constexpr bool DMA = CT::SWZ;    // D = 128: Q / dO tiles by direct global -> LDS loads
+    constexpr bool EXACT = MODE != MODE_BLOCK;
+    constexpr bool FP4 = MODE == MODE_FP4;
+    static_assert(!EXACT || D == 64, "per-token operands: 256-key tiles at d = 64 only");
     __shared__ __attribute__((aligned(16))) uint8_t s_kt[NKEY * CT::PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t s_vt[NKEY * CT::PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t s_q[2][64 * CT::PITCH];
@@ -722,6 +727,14 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
     __shared__ int s_dsexp[2][2][8];  // [buffer][query half][key block]
     __shared__ int s_ekb[8];
     __shared__ int s_ticket[2];
+    // per-token operands: the dQ copy's per-(row, key block) exponents, the
+    // Q / dO exponent maxima per 32-query half and the rows' fold factors;
+    // E2M1 score view: the FP16 expansion of the Q view
+    __shared__ __attribute__((aligned(16))) int s_er[EXACT ? 2 : 1][8][EXACT ? 64 : 1];
+    __shared__ int s_eqb[2][2], s_egb[2][2];
+    __shared__ __attribute__((aligned(16))) float s_fq[EXACT ? 2 : 1][64];
+    __shared__ __attribute__((aligned(16))) float s_fg[EXACT ? 2 : 1][64];
+    __shared__ __attribute__((aligned(16))) uint8_t s_q16[FP4 ? 2 : 1][FP4 ? 64 * PITCH16 : 16];
 
     const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
     const size_t T = (size_t)a.T;
@@ -761,7 +774,28 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
         }
         const int ek = kvalid ? (int)a.k_exps[(size_t)hk * T + kj] : 127;
         const int ev = kvalid ? (int)a.v_exps[(size_t)hk * T + kj] : 127;
-        if (tid < 8) s_ekb[tid] = (k0 + 32 * tid < e) ? (int)a.k_exps[(size_t)hk * T + k0 + 32 * tid] : 127;
+        // K block exponents of the dQ MFMA; with per-token exponents the
+        // maximum over the wave's 32 keys, and this key's fold factor
+        float fk = 1.f;
+        if constexpr (EXACT) {
+            const uint32_t ekb = half_wave_max_u32(kvalid ? (uint32_t)ek : 0u);
+            fk = kvalid ? ldexpf(1.f, ek - (int)ekb) : 0.f;
+            if (lane == 0) s_ekb[wave] = (int)ekb;
+        } else {
+            if (tid < 8)
+                s_ekb[tid] = (k0 + 32 * tid < e) ? (int)a.k_exps[(size_t)hk * T + k0 + 32 * tid] : 127;
+        }
+        // E2M1 score view: this lane's key row, expanded to FP16 (B operand of S)
+        h8 kh[FP4 ? NKH : 1];
+        if constexpr (FP4) {
+            const size_t row = (size_t)min(kj, e - 1) * Hkv + hk;
+#pragma unroll
+            for (int ks = 0; ks < NKH; ++ks) {
+                const uint32_t c = *(const uint32_t*)(a.k_fp4 + row * (D / 2) + 8 * ks + 4 * g);
+                const float sc = __builtin_amdgcn_cvt_f32_fp8((int)a.k_fp4_scales[row * (D / 16) + ks], 0);
+                kh[ks] = fp4x8_to_f16(c, sc);
+            }
+        }
 
         // iterations: q heads of the group (outer) x 64-query tiles that see the keys
         const int qt_lo = a.causal ? (NKEY / 64) * kt : 0;
@@ -793,7 +827,7 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                 }
                 load_qstats(a, st, h, qb, e, tid);
             } else {
-                load_qtile<D, 256, MODE_BLOCK>(a, nxt, h, qb, e, tid);
+                load_qtile<D, 256, MODE>(a, nxt, h, qb, e, tid);
             }
         };
         auto stage = [&](int j) {
@@ -821,6 +855,26 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
             // the document end get -inf, so their P is exactly zero
             s_nlse[buf][row] = ok ? boosted_row_term(lse) : -INFINITY;
             s_delta[buf][row] = ok ? delta : 0.f;
+            if constexpr (EXACT) {
+                // lane = query row: the Q and dO exponent maxima over each
+                // 32-query half (the dK / dV MFMA scales) and the rows' fold
+                // factors
+                const uint32_t eqr = ok ? (uint32_t)eq : 0u, egr = ok ? (uint32_t)edo : 0u;
+                const uint32_t eqb = half_wave_max_u32(eqr), egb = half_wave_max_u32(egr);
+                s_eqb[buf][row >> 5] = (int)eqb;
+                s_egb[buf][row >> 5] = (int)egb;
+                s_fq[buf][row] = ok ? ldexpf(1.f, (int)eqr - (int)eqb) : 0.f;
+                s_fg[buf][row] = ok ? ldexpf(1.f, (int)egr - (int)egb) : 0.f;
+            }
+            if constexpr (FP4) {
+                // the Q row's features (tid % 4) D / 4 .. + D / 4 - 1 as FP16
+                uint8_t* dst = &s_q16[buf][(tid >> 2) * PITCH16 + 2 * (tid & 3) * (D / 4)];
+#pragma unroll
+                for (int q = 0; q < D / 32; ++q) {
+                    const float sc = __builtin_amdgcn_cvt_f32_fp8((int)((nxt.q4s >> (8 * (q / 2))) & 0xff), 0);
+                    *(h8*)(dst + 16 * q) = fp4x8_to_f16((uint32_t)nxt.q4[q], sc);
+                }
+            }
         };
         if (wave < 4) {
             fetch(0);
@@ -859,7 +913,7 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
             v8i pc = {0, 0, 0, 0, 0, 0, 0, 0}, dc = pc;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                v4i pf = {0, 0, 0, 0}, df = {0, 0, 0, 0};
+                v4i pf = {0, 0, 0, 0}, df = {0, 0, 0, 0}, dr = {0, 0, 0, 0};
                 int dse = 127;
                 const bool active = wave_keys && (!a.causal || qb + 32 * t + 31 >= kw0);
                 if (active) {
@@ -868,10 +922,19 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = 0.f;
                     const int eqr = s_eq[pb][qr], edr = s_edo[pb][qr];
+                    if constexpr (FP4) {
+                        // S from the E2M1 views, expanded to exact FP16
+#pragma unroll
+                        for (int ks = 0; ks < NKH; ++ks)
+                            sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                *(const h8*)(s_q16[pb] + qr * PITCH16 + 2 * (16 * ks + 8 * g)), kh[ks], sacc, 0,
+                                0, 0);
+                    }
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) {
-                        sacc = mfma_f8(tile_row_operand<D>(sq, qr, 64 * ks, lane),
-                                       tile_row_operand<D>(s_kt, krow, 64 * ks, lane), sacc, eqr, ek);
+                        if constexpr (!FP4)
+                            sacc = mfma_f8(tile_row_operand<D>(sq, qr, 64 * ks, lane),
+                                           tile_row_operand<D>(s_kt, krow, 64 * ks, lane), sacc, eqr, ek);
                         pacc = mfma_f8(tile_row_operand<D>(sg, qr, 64 * ks, lane),
                                        tile_row_operand<D>(s_vt, krow, 64 * ks, lane), pacc, edr, ev);
                     }
@@ -892,19 +955,64 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                     // block exponent of dS = that of 256 dS minus 8 (exact)
                     const int et = ceil_exp448(wave_max_nonneg(amax) * 0.00390625f);
                     dse = et + 127;
+                    if constexpr (EXACT) {
+                        // the dQ copy's per-row exponents: each query row's
+                        // largest |dS| over the wave's 32 keys, one row per lane
+                        // after a transpose-reduce, then all 16 rows of the lane
+                        // group back from LDS (the same wave's write)
+                        uint32_t ab[16];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        pf[q] = (int)cvt4_fp8(sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]);
-                        df[q] = (int)cvt4_fp8_div(pacc[4 * q], pacc[4 * q + 1], pacc[4 * q + 2],
-                                                  pacc[4 * q + 3], ds_code_divisor(et));
+                        for (int v = 0; v < 16; ++v) ab[v] = __float_as_uint(fabsf(pacc[v]));
+                        const int erl = ceil_exp448(__uint_as_float(row_max_transpose(ab, lane)) * 0.00390625f);
+                        int* erow = &s_er[pb][wave][32 * t + 16 * g];
+                        if ((lane & 16) == 0) erow[rev4(lane & 15)] = erl + 127;
+                        int er[16];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const v4i e4 = *(const v4i*)(erow + 4 * q);
+                            er[4 * q] = e4.x - 127;
+                            er[4 * q + 1] = e4.y - 127;
+                            er[4 * q + 2] = e4.z - 127;
+                            er[4 * q + 3] = e4.w - 127;
+                        }
+                        // folded operands: P^ x 2^(e_dO - block max) for dV, dS x
+                        // 2^(e_Q - block max) for dK (block exponent et), dS x
+                        // 2^(e_K - block max) for dQ (the row exponents)
+                        const float* fg = &s_fg[pb][32 * t + 16 * g];
+                        const float* fq = &s_fq[pb][32 * t + 16 * g];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            float pv[4], dv4[4], rv[4];
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) {
+                                const int v = 4 * q + k;
+                                pv[k] = sacc[v] * fg[v];
+                                dv4[k] = pacc[v] * fq[v];
+                                rv[k] = ldexpf(pacc[v] * fk, -er[v] - 8);
+                            }
+                            pf[q] = (int)cvt4_fp8(pv[0], pv[1], pv[2], pv[3]);
+                            df[q] = (int)cvt4_fp8_div(dv4[0], dv4[1], dv4[2], dv4[3], ds_code_divisor(et));
+                            dr[q] = (int)cvt4_fp8(rv[0], rv[1], rv[2], rv[3]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            pf[q] = (int)cvt4_fp8(sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]);
+                            df[q] = (int)cvt4_fp8_div(pacc[4 * q], pacc[4 * q + 1], pacc[4 * q + 2],
+                                                      pacc[4 * q + 3], ds_code_divisor(et));
+                        }
                     }
+                } else if constexpr (EXACT) {
+                    if ((lane & 16) == 0) s_er[pb][wave][32 * t + 16 * g + (lane & 15)] = 127;
                 }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     pc[4 * t + q] = pf[q];
                     dc[4 * t + q] = df[q];
                 }
-                *(v4i*)(s_ds[pb] + krow * SPITCH + 32 * t + 16 * g) = df;
+                // the dQ product's key-major rows (per-token operands: the
+                // K-folded copy with per-row exponents)
+                *(v4i*)(s_ds[pb] + krow * SPITCH + 32 * t + 16 * g) = EXACT ? dr : df;
                 if (lane == 0) s_dsexp[pb][t][wave] = dse;
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -913,8 +1021,10 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                 // half (lane group g supplies k block g's scale); the same
                 // wave wrote them above
                 const int dsg = s_dsexp[pb][g][wave];
-                const int sdo = s_edo[pb][32 * g];
-                const int sqe = s_eq[pb][32 * g];
+                // per-token operands: the block maxima the fold factors are
+                // relative to
+                const int sdo = EXACT ? s_egb[pb][g] : s_edo[pb][32 * g];
+                const int sqe = EXACT ? s_eqb[pb][g] : s_eq[pb][32 * g];
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
                     dv[dt] = mfma_f8(tile_tr_operand<D>(sg, 0, 32 * dt, lane), pc, dv[dt], sdo, kScaleMinus8);
@@ -950,7 +1060,7 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                 // always runs, so the zero accumulator is never needed
                 if (ks > 0 && k0 + 64 * ks >= e) break;
                 const int kb = 2 * ks + g;
-                const int sa = min(max(s_dsexp[pb][ct][kb] + kq, 0), 254);
+                const int sa = min(max((EXACT ? s_er[pb][kb][qrow] : s_dsexp[pb][ct][kb]) + kq, 0), 254);
                 acc = mfma_f8(lds_tr_operand(s_ds[pb] + 64 * ks * SPITCH, SPITCH, 0, 32 * ct, lane),
                               tile_tr_operand<D>(s_kt, 64 * ks, 32 * dt, lane), acc, sa, s_ekb[kb]);
             }
@@ -1297,14 +1407,19 @@ hipError_t launch_bwd_wide(const AttnArgs& a, int D, int max_items, bool with_dq
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
         return hipErrorInvalidDevice;
     const dim3 grid((unsigned)std::min<int64_t>((int64_t)max_items * a.Hkv, ncu));
-#define FLAMIA_BWDW(DD, WQ) \
-    FLAMIA_LAUNCH((bwd_wide_kernel<DD, WQ>), grid, dim3(512), stream, a.ev_start, a.ev_stop, a)
-    if (D == 128) {
-        if (with_dq) FLAMIA_BWDW(128, true);
-        else FLAMIA_BWDW(128, false);
+#define FLAMIA_BWDW(DD, WQ, MM) \
+    FLAMIA_LAUNCH((bwd_wide_kernel<DD, WQ, MM>), grid, dim3(512), stream, a.ev_start, a.ev_stop, a)
+    if (a.mode != MODE_BLOCK) {
+        // per-token operands: d = 64, dQ by atomics (no deterministic form)
+        if (D != 64 || !with_dq) return hipErrorInvalidValue;
+        if (a.mode == MODE_FP4) FLAMIA_BWDW(64, true, MODE_FP4);
+        else FLAMIA_BWDW(64, true, MODE_EXACT);
+    } else if (D == 128) {
+        if (with_dq) FLAMIA_BWDW(128, true, MODE_BLOCK);
+        else FLAMIA_BWDW(128, false, MODE_BLOCK);
     } else {
-        if (with_dq) FLAMIA_BWDW(64, true);
-        else FLAMIA_BWDW(64, false);
+        if (with_dq) FLAMIA_BWDW(64, true, MODE_BLOCK);
+        else FLAMIA_BWDW(64, false, MODE_BLOCK);
     }
 #undef FLAMIA_BWDW
     return hipGetLastError();

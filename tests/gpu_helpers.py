@@ -236,9 +236,9 @@ class Backward:
         self.kpre = kpre
         self.scale = oracle.default_scale(ops.d) if scale is None else scale
         self.causal, self.per_row_ds = causal, per_row_ds
-        # the key tile of the kernel's FP16 dQ partials: 256 with token-block
-        # operands, 128 in the exact-scale modes
-        self.dq_tile = dq_tile if dq_tile is not None else (128 if per_row_ds else 256)
+        # the key tile of the kernel's FP16 dQ partials: 256, except 128 with
+        # per-token operands at d = 128
+        self.dq_tile = dq_tile if dq_tile is not None else (128 if per_row_ds and ops.d == 128 else 256)
         self.kw = dict(scale=self.scale, causal=causal, per_row_ds=per_row_ds)
         self._ranges = {}
 
