@@ -1090,11 +1090,15 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                 lds_barrier();
             }
         } else {
+            // the reverse order of waves 0-3 (step first, then the dQ of the
+            // previous tile, whose dS^ sits in the other buffer), so that the
+            // two waves of a SIMD are in different phases: one's matrix
+            // products overlap the other's element-wise work
             for (int j = 0; j <= niter; ++j) {
+                if (j < niter) step(j);
                 if constexpr (WITH_DQ) {
                     if (j >= 1) dq(j - 1, DQ_ALL ? wave : wave - 4);
                 }
-                if (j < niter) step(j);
                 lds_barrier();
             }
         }
