@@ -110,6 +110,24 @@ __device__ __forceinline__ float softmax_grad(v16f& sacc, v16f& pacc, const floa
     return amax;
 }
 
+// The same with pacc already holding dP - D (the dP product accumulated
+// onto -D).
+template <bool MASK>
+__device__ __forceinline__ float softmax_grad_c(v16f& sacc, v16f& pacc, const float* nl, float c2, int lim)
+{
+    float amax = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        float p = __builtin_amdgcn_exp2f(fmaf(sacc[v], c2, nl[v]));
+        if (MASK) p = (v >= lim) ? p : 0.f;
+        const float ds = p * pacc[v];
+        sacc[v] = p;
+        pacc[v] = ds;
+        amax = fmaxf(amax, fabsf(ds));
+    }
+    return amax;
+}
+
 // Adds a 32 x 64 dQ region, the accumulators acc0 / acc1 of two
 // horizontally adjacent 32x32x64 MFMA tiles (lane = column, VGPR v = row
 // 8 (v / 4) + 4 g + v % 4), into the FP16 accumulator so that every packed
@@ -723,7 +741,7 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
     // j + 1's are staged: three slots (tile % 3)
     __shared__ int s_kq[3][64];
     __shared__ __attribute__((aligned(16))) float s_nlse[2][64];
-    __shared__ __attribute__((aligned(16))) float s_delta[2][64];
+    __shared__ __attribute__((aligned(16))) float s_ndelta[2][64];  // -D
     __shared__ int s_dsexp[2][2][8];  // [buffer][query half][key block]
     __shared__ int s_ekb[8];
     __shared__ int s_ticket[2];
@@ -854,7 +872,7 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
             // 8 - LSE log2 e: exp2 of the score term then yields 256 P; rows past
             // the document end get -inf, so their P is exactly zero
             s_nlse[buf][row] = ok ? boosted_row_term(lse) : -INFINITY;
-            s_delta[buf][row] = ok ? delta : 0.f;
+            s_ndelta[buf][row] = ok ? -delta : 0.f;
             if constexpr (EXACT) {
                 // lane = query row: the Q and dO exponent maxima over each
                 // 32-query half (the dK / dV MFMA scales) and the rows' fold
@@ -918,9 +936,20 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                 const bool active = wave_keys && (!a.causal || qb + 32 * t + 31 >= kw0);
                 if (active) {
                     const int qr = perm_row(t, lane & 31);
+                    // element v of lane group g is query qb + 32 t + 16 g + v.
+                    // The dP product accumulates onto -D, so that pacc ends as
+                    // dP - D without a subtraction per element.
                     v16f sacc, pacc;
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) sacc[v] = pacc[v] = 0.f;
+                    for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float4 x = *(const float4*)&s_ndelta[pb][32 * t + 16 * g + 4 * i];
+                        pacc[4 * i] = x.x;
+                        pacc[4 * i + 1] = x.y;
+                        pacc[4 * i + 2] = x.z;
+                        pacc[4 * i + 3] = x.w;
+                    }
                     const int eqr = s_eq[pb][qr], edr = s_edo[pb][qr];
                     if constexpr (FP4) {
                         // S from the E2M1 views, expanded to exact FP16
@@ -941,16 +970,14 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                     // keep the scheduler from hoisting the next operands above
                     // the element-wise work (register pressure)
                     __builtin_amdgcn_sched_barrier(0);
-                    // element v of lane group g is query qb + 32 t + 16 g + v
                     const float* nl = &s_nlse[pb][32 * t + 16 * g];
-                    const float* dl = &s_delta[pb][32 * t + 16 * g];
                     const bool full = kw0 + 32 <= e && (!a.causal || qb + 32 * t >= kw0 + 31);
                     float amax;
                     if (full) {
-                        amax = softmax_grad<false>(sacc, pacc, nl, dl, c2, 0);
+                        amax = softmax_grad_c<false>(sacc, pacc, nl, c2, 0);
                     } else {
                         const int lim = a.causal ? kj - qb - 32 * t - 16 * g : (kvalid ? -1 : 16);
-                        amax = softmax_grad<true>(sacc, pacc, nl, dl, c2, lim);
+                        amax = softmax_grad_c<true>(sacc, pacc, nl, c2, lim);
                     }
                     // block exponent of dS = that of 256 dS minus 8 (exact)
                     const int et = ceil_exp448(wave_max_nonneg(amax) * 0.00390625f);
@@ -1264,8 +1291,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int krow = perm_row(t, lane & 31);
+                // the dP product accumulates onto -D (lane = query), as in the
+                // key-major kernel, so both form dP - D the same way
 #pragma unroll
-                for (int v = 0; v < 16; ++v) sacc[t][v] = pacc[t][v] = 0.f;
+                for (int v = 0; v < 16; ++v) {
+                    sacc[t][v] = 0.f;
+                    pacc[t][v] = -delta;
+                }
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
                     sacc[t] = mfma_f8(row_operand(sk + krow * PITCH + 64 * ks, lane), qf[ks],
@@ -1283,7 +1315,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(AttnArgs a)
                     const int key = kt0 + 32 * t + 16 * g + v;
                     const bool vis = qvalid && key < e && (!a.causal || key <= qi);
                     const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[t][v], c2, nl)) : 0.f;
-                    const float ds = p * (pacc[t][v] - delta);  // 256 dS
+                    const float ds = p * pacc[t][v];  // 256 dS
                     pacc[t][v] = ds;
                     amax[t] = fmaxf(amax[t], fabsf(ds));
                 }
