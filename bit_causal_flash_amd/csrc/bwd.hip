@@ -731,10 +731,11 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
     constexpr bool EXACT = MODE != MODE_BLOCK;
     constexpr bool FP4 = MODE == MODE_FP4;
     static_assert(!EXACT || D == 64, "per-token operands: 256-key tiles at d = 64 only");
-    __shared__ __attribute__((aligned(16))) uint8_t s_kt[NKEY * CT::PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t s_vt[NKEY * CT::PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t s_q[2][64 * CT::PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t s_do[2][64 * CT::PITCH];
+    // code tiles 128-byte aligned (swz_row_operand addresses them by XOR)
+    __shared__ __attribute__((aligned(128))) uint8_t s_kt[NKEY * CT::PITCH];
+    __shared__ __attribute__((aligned(128))) uint8_t s_vt[NKEY * CT::PITCH];
+    __shared__ __attribute__((aligned(128))) uint8_t s_q[2][64 * CT::PITCH];
+    __shared__ __attribute__((aligned(128))) uint8_t s_do[2][64 * CT::PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t s_ds[2][NKEY * SPITCH];
     __shared__ int s_eq[2][64], s_edo[2][64];
     // the rows' prescale exponents are read by the dQ of tile j - 1 while tile
@@ -959,13 +960,28 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                                 *(const h8*)(s_q16[pb] + qr * PITCH16 + 2 * (16 * ks + 8 * g)), kh[ks], sacc, 0,
                                 0, 0);
                     }
+                    if constexpr (CT::SWZ) {
+                        // Q / dO rows qr and K / V rows krow: one address per
+                        // pair of tiles, the rest XOR and immediate offsets
+                        const uint32_t qa = swz_row_addr(sq, qr, lane);
+                        const uint32_t ka = swz_row_addr(s_kt, krow, lane);
+                        const int dqg = (int)(lds_addr(s_do[0]) - lds_addr(s_q[0]));
+                        const int dkv = (int)(lds_addr(s_vt) - lds_addr(s_kt));
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) {
-                        if constexpr (!FP4)
-                            sacc = mfma_f8(tile_row_operand<D>(sq, qr, 64 * ks, lane),
-                                           tile_row_operand<D>(s_kt, krow, 64 * ks, lane), sacc, eqr, ek);
-                        pacc = mfma_f8(tile_row_operand<D>(sg, qr, 64 * ks, lane),
-                                       tile_row_operand<D>(s_vt, krow, 64 * ks, lane), pacc, edr, ev);
+                        for (int ks = 0; ks < NKS; ++ks) {
+                            sacc = mfma_f8(swz_row_operand(qa, ks, 0), swz_row_operand(ka, ks, 0), sacc, eqr, ek);
+                            pacc = mfma_f8(swz_row_operand(qa, ks, dqg), swz_row_operand(ka, ks, dkv), pacc, edr,
+                                           ev);
+                        }
+                    } else {
+#pragma unroll
+                        for (int ks = 0; ks < NKS; ++ks) {
+                            if constexpr (!FP4)
+                                sacc = mfma_f8(tile_row_operand<D>(sq, qr, 64 * ks, lane),
+                                               tile_row_operand<D>(s_kt, krow, 64 * ks, lane), sacc, eqr, ek);
+                            pacc = mfma_f8(tile_row_operand<D>(sg, qr, 64 * ks, lane),
+                                           tile_row_operand<D>(s_vt, krow, 64 * ks, lane), pacc, edr, ev);
+                        }
                     }
                     // keep the scheduler from hoisting the next operands above
                     // the element-wise work (register pressure)
@@ -1052,10 +1068,20 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                 // relative to
                 const int sdo = EXACT ? s_egb[pb][g] : s_edo[pb][32 * g];
                 const int sqe = EXACT ? s_eqb[pb][g] : s_eq[pb][32 * g];
+                if constexpr (CT::SWZ) {
+                    const uint32_t ta = swz_tr_addr(sq, lane);
+                    const int dqg = (int)(lds_addr(s_do[0]) - lds_addr(s_q[0]));
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    dv[dt] = mfma_f8(tile_tr_operand<D>(sg, 0, 32 * dt, lane), pc, dv[dt], sdo, kScaleMinus8);
-                    dk[dt] = mfma_f8(tile_tr_operand<D>(sq, 0, 32 * dt, lane), dc, dk[dt], sqe, dsg);
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        dv[dt] = mfma_f8(swz_tr_operand(ta, 0, dt, dqg), pc, dv[dt], sdo, kScaleMinus8);
+                        dk[dt] = mfma_f8(swz_tr_operand(ta, 0, dt, 0), dc, dk[dt], sqe, dsg);
+                    }
+                } else {
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        dv[dt] = mfma_f8(tile_tr_operand<D>(sg, 0, 32 * dt, lane), pc, dv[dt], sdo, kScaleMinus8);
+                        dk[dt] = mfma_f8(tile_tr_operand<D>(sq, 0, 32 * dt, lane), dc, dk[dt], sqe, dsg);
+                    }
                 }
             }
         };
@@ -1088,8 +1114,10 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                 if (ks > 0 && k0 + 64 * ks >= e) break;
                 const int kb = 2 * ks + g;
                 const int sa = min(max((EXACT ? s_er[pb][kb][qrow] : s_dsexp[pb][ct][kb]) + kq, 0), 254);
-                acc = mfma_f8(lds_tr_operand(s_ds[pb] + 64 * ks * SPITCH, SPITCH, 0, 32 * ct, lane),
-                              tile_tr_operand<D>(s_kt, 64 * ks, 32 * dt, lane), acc, sa, s_ekb[kb]);
+                const v8i kop = CT::SWZ ? swz_tr_operand(swz_tr_addr(s_kt, lane), 64 * ks, dt, 0)
+                                        : tile_tr_operand<D>(s_kt, 64 * ks, 32 * dt, lane);
+                acc = mfma_f8(lds_tr_operand(s_ds[pb] + 64 * ks * SPITCH, SPITCH, 0, 32 * ct, lane), kop, acc, sa,
+                              s_ekb[kb]);
             }
             _Float16* tile = a.dq_acc + ((size_t)(qb + 32 * ct) * Hq + h) * D + 32 * dt;
             if (nrows >= 32) dq_tile_atomics_pk<false>(acc, tile, (size_t)Hq * D, lane, nrows);

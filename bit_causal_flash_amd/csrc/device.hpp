@@ -207,6 +207,72 @@ struct CodeTile {
     }
 };
 
+// 32-bit LDS address of a pointer into a __shared__ array, and a 16-byte
+// LDS read at such an address.
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ v4i lds_read16(uint32_t addr)
+{
+    return *(const __attribute__((address_space(3))) v4i*)(uintptr_t)addr;
+}
+
+// The swizzle permutes the 16-byte chunk indices of a row by XOR, so the
+// four chunks a lane reads for the row operand of `row` (bytes 64 ks +
+// 32 h + 16 g, g = lane / 32) lie at one address XOR (64 ks + 32 h) in a
+// 128-byte-aligned tile.  swz_row_addr gives that address (ks = h = 0).
+__device__ __forceinline__ uint32_t swz_row_addr(const uint8_t* tile, int row, int lane)
+{
+    return lds_addr(tile) + (uint32_t)(row * 128 + 16 * ((lane >> 5) ^ tile_swizzle(row)));
+}
+
+// tile_row_operand at byte column 64 ks from a swz_row_addr a0, read from
+// the tile `delta` bytes after the one a0 was taken in (delta a multiple
+// of 128, so it commutes with the XOR and becomes an immediate offset).
+__device__ __forceinline__ v8i swz_row_operand(uint32_t a0, int ks, int delta)
+{
+    const v4i a = lds_read16((a0 ^ (uint32_t)(64 * ks)) + (uint32_t)delta);
+    const v4i b = lds_read16((a0 ^ (uint32_t)(64 * ks + 32)) + (uint32_t)delta);
+    v8i o;
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    return o;
+}
+
+// tile_tr_operand by the same XOR addressing: swz_tr_addr is the lane's base
+// address (row0 = 0, col0 = 0) in a 128-byte-aligned tile, swz_tr_operand
+// the operand at rows row0 .. row0 + 63 (row0 a multiple of 32) and columns
+// 32 dt .. 32 dt + 31 of the tile `delta` bytes after that one (delta a
+// multiple of 128).
+__device__ __forceinline__ uint32_t swz_tr_addr(const uint8_t* tile, int lane)
+{
+    const int grp = lane >> 4, l16 = lane & 15, g = grp >> 1, r = l16 >> 1;
+    const int sw = (r & 6) | g;
+    return lds_addr(tile) + (uint32_t)((r + 16 * g) * 128 + ((((grp & 1) ^ sw) << 4) | (8 * (l16 & 1))));
+}
+
+__device__ __forceinline__ v2i lds_read_tr8_at(uint32_t addr)
+{
+    lds_i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) lds_i32x2*)(uintptr_t)addr);
+    v2i out;
+    out.x = r[0];
+    out.y = r[1];
+    return out;
+}
+
+__device__ __forceinline__ v8i swz_tr_operand(uint32_t a0, int row0, int dt, int delta)
+{
+    const uint32_t b = (a0 ^ (uint32_t)(32 * dt)) + (uint32_t)(row0 * 128 + delta);
+    const v2i x = lds_read_tr8_at(b), y = lds_read_tr8_at(b + 8 * 128);
+    const v2i z = lds_read_tr8_at(b + 32 * 128), w = lds_read_tr8_at(b + 40 * 128);
+    v8i o;
+    o[0] = x.x; o[1] = x.y; o[2] = y.x; o[3] = y.y;
+    o[4] = z.x; o[5] = z.y; o[6] = w.x; o[7] = w.y;
+    return o;
+}
+
 // row_operand of row `row` of a code tile, from byte column col0.
 template <int D>
 __device__ __forceinline__ v8i tile_row_operand(const uint8_t* tile, int row, int col0, int lane)
