@@ -209,8 +209,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
     constexpr int CPR = D / 16;        // 16-byte chunks per row
     constexpr bool FP4 = MODE == MODE_FP4;
     constexpr bool FOLD = MODE != MODE_BLOCK;
-    __shared__ __attribute__((aligned(16))) uint8_t s_k[2][FP4 ? 64 * PITCH16 : 64 * CT::PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t s_v[2][64 * CT::PITCH];
+    // 128-byte aligned: at D = 128 the swizzled tiles are addressed by XOR
+    __shared__ __attribute__((aligned(128))) uint8_t s_k[2][FP4 ? 64 * PITCH16 : 64 * CT::PITCH];
+    __shared__ __attribute__((aligned(128))) uint8_t s_v[2][64 * CT::PITCH];
     __shared__ int s_ek[2][64];
     __shared__ int s_ev[2][2];
     __shared__ __attribute__((aligned(16))) float s_vf[2][FOLD ? 64 : 1];
@@ -361,7 +362,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
                     const int ek = s_ek[cur][krow];
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
-                        sacc[t] = mfma_f8(tile_row_operand<D>(sk, krow, 64 * ks, lane), qf[ks],
+                        sacc[t] = mfma_f8(CT::SWZ ? swz_row_operand(swz_row_addr(sk, krow, lane), ks, 0)
+                                                  : tile_row_operand<D>(sk, krow, 64 * ks, lane),
+                                          qf[ks],
                                           sacc[t], ek, eq);
                 }
             }
@@ -379,7 +382,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
             const int sv_exp = s_ev[cur][g];
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
-                oacc[dt] = mfma_f8(tile_tr_operand<D>(sv, 0, 32 * dt, lane), pf, oacc[dt],
+                oacc[dt] = mfma_f8(CT::SWZ ? swz_tr_operand(swz_tr_addr(sv, lane), 0, dt, 0)
+                                           : tile_tr_operand<D>(sv, 0, 32 * dt, lane),
+                                   pf, oacc[dt],
                                    sv_exp, sp);
         }
         stage(nxt, cur ^ 1);
