@@ -10,8 +10,8 @@ Timing: each seed's step is captured once in a HIP graph and replayed; W
 untimed replays, then K replays each bracketed by hipEvents on the stream;
 the seed's figure is the median of the K.  Three seeds; the reported value
 is the median seed's, with the seeds' range alongside.  Kernel durations
-(roofline) come from a separate eager pass on the same stream, whose events
-the library stamps from the kernels' own dispatch.
+(roofline) come from a separate eager pass on the same stream, with events
+that the library records just before and after each kernel's launch.
 
 Prints one JSON line.  value = algorithmic FLOPs of attention fwd+bwd
 (14 d Hq x visible pairs; a multiply-add counts 2) per second of the step.
@@ -250,8 +250,9 @@ def time_replays(hip, stream, step, K, W):
 
 
 def kernel_times(hip, stream, st, K):
-    """Eager pass of K steps with the library stamping the forward and the
-    backward main kernels' own dispatch; then the quantizer kernels alone,
+    """Eager pass of K steps with the library recording events around the
+    forward and the backward main kernels' launches; then the quantizer
+    kernels alone,
     with a forward queued ahead of each so the GPU never waits on a launch.
     Returns mean kernel milliseconds."""
     import torch
@@ -412,8 +413,9 @@ def main():
         "seeds": hs["seeds"],
         "tflops_range": hs["tflops_range"],
         "pct_fp8_peak": hs["pct_fp8_peak"],
-        "roofline": {"kernel": ("bwd_kernel<%d, true, %d>" % (d, 2 if st.fp4 else 1)) if exact
-                     else "bwd_wide_kernel<%d, true>" % d, "bound": "mfma", "achieved": round(bwd_tflops, 2),
+        "roofline": {"kernel": ("bwd_kernel<%d, true, %d>" if exact and d == 128 else
+                                "bwd_wide_kernel<%d, true, %d>") % (d, (2 if st.fp4 else 1) if exact else 0),
+                     "bound": "mfma", "achieved": round(bwd_tflops, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bwd_tflops / FP8_PEAK_TFLOPS, 4),
                      "traffic": None if args.hadamard else measured_traffic(w.name)},

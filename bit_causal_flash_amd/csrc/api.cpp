@@ -175,7 +175,7 @@ int prescale_c(const Dims& d)
 flamia_status hip_status(hipError_t e) { return e == hipSuccess ? FLAMIA_OK : FLAMIA_ERR_HIP; }
 
 // The caller's timing events, if any, for the launch of the call's main
-// kernel (stamped from its dispatch, see AttnArgs).
+// kernel (recorded around its launch, see AttnArgs).
 void set_events(const flamia_problem* p, hipEvent_t& start, hipEvent_t& stop)
 {
     start = p->events ? (hipEvent_t)p->events->attn_start : nullptr;

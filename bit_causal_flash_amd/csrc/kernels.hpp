@@ -8,15 +8,16 @@
 
 namespace flamia {
 
-// Launch with the caller's timing events when it asked for any (stamped from
-// the kernel's own dispatch), as a plain launch otherwise, which is what a
-// captured graph records.
-#define FLAMIA_LAUNCH(KERNEL, GRID, BLOCK, STREAM, EV0, EV1, ...)                             \
-    do {                                                                                      \
-        if ((EV0) != nullptr || (EV1) != nullptr)                                             \
-            hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, EV0, EV1, 0, __VA_ARGS__); \
-        else                                                                                  \
-            hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__);                  \
+// A plain launch, bracketed by the caller's timing events when it asked for
+// them (recorded on the same stream just before and after the launch).  The
+// launch itself is the same either way: stamping the dispatch instead
+// (hipExtLaunchKernel with events) was measured to slow the kernel down, by
+// up to half of its time for the short d = 64 backward.
+#define FLAMIA_LAUNCH(KERNEL, GRID, BLOCK, STREAM, EV0, EV1, ...)             \
+    do {                                                                      \
+        if ((EV0) != nullptr) (void)hipEventRecord(EV0, STREAM);              \
+        hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__);      \
+        if ((EV1) != nullptr) (void)hipEventRecord(EV1, STREAM);              \
     } while (0)
 
 // One tensor of a quantizer launch.
@@ -48,7 +49,7 @@ struct QuantArgs {
     float* delta;             // [H][T]
     int8_t* prescale;         // [H][T]
     _Float16* dq_acc;         // [T][H][D]
-    // optional: stamped with the start / end of the launch's kernel
+    // optional: recorded just before / after the launch of the kernel
     hipEvent_t ev_start, ev_stop;
 };
 
@@ -103,9 +104,8 @@ struct AttnArgs {
     const int8_t* prescale;
     _Float16* dq_acc;
     uint16_t *dq, *dk, *dv;
-    // optional: stamped with the start / end of the forward kernel or of the
-    // backward main kernel (hipExtLaunchKernel: no extra packets in the
-    // stream, unlike hipEventRecord around the launch)
+    // optional: recorded just before / after the launch of the forward kernel
+    // or of the backward main kernel
     hipEvent_t ev_start, ev_stop;
 };
 

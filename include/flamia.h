@@ -100,12 +100,12 @@ enum {
                                     for causality tests only. */
 };
 
-/* Optional timing hook: hipEvent_t handles that the library has stamped with
- * the start and the end of the quantizer kernel of flamia_quantize_tokblock
- * and flamia_quantize_qkv, the forward kernel of flamia_attn_fwd or the
- * backward main kernel of flamia_attn_bwd (taken from the kernel's own
- * dispatch, hipExtLaunchKernel: no separate event packets enter the
- * stream).  Either may be NULL.  The caller owns the events. */
+/* Optional timing hook: hipEvent_t handles that the library records on the
+ * call's stream just before and just after the launch of the quantizer
+ * kernel of flamia_quantize_tokblock and flamia_quantize_qkv, the forward
+ * kernel of flamia_attn_fwd or the backward main kernel of flamia_attn_bwd,
+ * so that their elapsed time is that kernel's.  The launch is the same with
+ * or without them.  Either may be NULL.  The caller owns the events. */
 typedef struct {
     void* attn_start;
     void* attn_stop;
