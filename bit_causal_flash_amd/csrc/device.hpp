@@ -195,6 +195,25 @@ typedef __attribute__((address_space(3))) void lds_void;  // LDS pointer of dire
 
 __device__ __forceinline__ int tile_swizzle(int row) { return (row & 6) | ((row >> 4) & 1); }
 
+// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4,
+// lane L's bytes landing at dst + 16 L), issued as inline assembly.  The
+// compiler does not see this LDS write, so it adds no vmcnt(0) wait before
+// later LDS reads that it cannot tell apart from the destination (with the
+// builtin, each step's first read of the current tile waited for the next
+// tile's prefetch).  The caller orders every read of the destination after
+// a wait of its own (wait_vm0_asm) and a barrier.  m0 is set here; no other code
+// of these kernels keeps a value in it.
+__device__ __forceinline__ void dma16_opaque(const void* src, lds_void* dst)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
+}
+
+// Waits for every vector memory operation, the direct loads above included,
+// as inline assembly: the compiler does not count those loads, and drops a
+// builtin wait that its own count makes look redundant.
+__device__ __forceinline__ void wait_vm0_asm() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
+
 template <int D>
 struct CodeTile {
     static constexpr bool SWZ = D == 128;

@@ -284,9 +284,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
                 const int row = rb + (lane >> 3);
                 const int c = (lane & 7) ^ tile_swizzle(row);
                 const size_t src = ((size_t)min(kt0 + row, e - 1) * Hkv + hk) * D + 16 * c;
-                if constexpr (!FP4)
-                    __builtin_amdgcn_global_load_lds(a.k_codes + src, (lds_void*)&s_k[buf][rb * 128], 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(a.v_codes + src, (lds_void*)&s_v[buf][rb * 128], 16, 0, 0);
+                if constexpr (!FP4) dma16_opaque(a.k_codes + src, (lds_void*)&s_k[buf][rb * 128]);
+                dma16_opaque(a.v_codes + src, (lds_void*)&s_v[buf][rb * 128]);
             }
         }
     };
@@ -330,7 +329,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
     dma(s, 0);
     stage(nxt, 0);
     // every load issued so far has landed (vmcnt(0)), so that inside the loop
-    // only the prefetch of the next step is outstanding
+    // only the prefetch of the next step is outstanding; the builtin wait
+    // (free after the asm one) tells the compiler that the Q fragments have
+    // landed, so it puts no wait for them inside the loop
+    if constexpr (DMA) wait_vm0_asm();
     __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
 
@@ -389,7 +391,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
         }
         stage(nxt, cur ^ 1);
         // the direct loads count in vmcnt: they have landed once it is zero
-        if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0x0F70);
+        // (a wait the compiler cannot drop: it does not see the asm loads)
+        if constexpr (DMA) wait_vm0_asm();
         lds_barrier();
     }
 
