@@ -746,13 +746,14 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
     __shared__ int s_dsexp[2][2][8];  // [buffer][query half][key block]
     __shared__ int s_ekb[8];
     __shared__ int s_ticket[2];
-    // per-token operands: the dQ copy's per-(row, key block) exponents, the
-    // Q / dO exponent maxima per 32-query half and the rows' fold factors;
-    // E2M1 score view: the FP16 expansion of the Q view
+    // per-token operands: the dQ copy's per-(row, key block) exponents and
+    // their code multipliers 2^(-e - 8), the Q / dO exponent maxima per
+    // 32-query half and the rows' Q fold factors; E2M1 score view: the FP16
+    // expansion of the Q view
     __shared__ __attribute__((aligned(16))) int s_er[EXACT ? 2 : 1][8][EXACT ? 64 : 1];
+    __shared__ __attribute__((aligned(16))) float s_rm[EXACT ? 2 : 1][8][EXACT ? 64 : 1];
     __shared__ int s_eqb[2][2], s_egb[2][2];
     __shared__ __attribute__((aligned(16))) float s_fq[EXACT ? 2 : 1][64];
-    __shared__ __attribute__((aligned(16))) float s_fg[EXACT ? 2 : 1][64];
     __shared__ __attribute__((aligned(16))) uint8_t s_q16[FP4 ? 2 : 1][FP4 ? 64 * PITCH16 : 16];
 
     const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
@@ -795,10 +796,13 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
         const int ev = kvalid ? (int)a.v_exps[(size_t)hk * T + kj] : 127;
         // K block exponents of the dQ MFMA; with per-token exponents the
         // maximum over the wave's 32 keys, and this key's fold factor
-        float fk = 1.f;
+        // 2^(e_K - max) as the divisor 2^(max - e_K) of the scaled conversion
+        // (capped at 2^127, where every code is zero anyway; 1 past the
+        // document end, where dS is zero)
+        float fkdiv = 1.f;
         if constexpr (EXACT) {
             const uint32_t ekb = half_wave_max_u32(kvalid ? (uint32_t)ek : 0u);
-            fk = kvalid ? ldexpf(1.f, ek - (int)ekb) : 0.f;
+            fkdiv = kvalid ? ldexpf(1.f, min((int)ekb - ek, 127)) : 1.f;
             if (lane == 0) s_ekb[wave] = (int)ekb;
         } else {
             if (tid < 8)
@@ -868,22 +872,30 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
             }
             const int row = tid & 63;
             s_eq[buf][row] = ok ? eq : 127;
-            s_edo[buf][row] = ok ? edo : 127;
             s_kq[j % 3][row] = ok ? pre + a.scale_exp : 0;
-            // 8 - LSE log2 e: exp2 of the score term then yields 256 P; rows past
-            // the document end get -inf, so their P is exactly zero
-            s_nlse[buf][row] = ok ? boosted_row_term(lse) : -INFINITY;
-            s_ndelta[buf][row] = ok ? -delta : 0.f;
             if constexpr (EXACT) {
                 // lane = query row: the Q and dO exponent maxima over each
-                // 32-query half (the dK / dV MFMA scales) and the rows' fold
-                // factors
+                // 32-query half (the dK / dV MFMA scales) and the rows' Q fold
+                // factors.  The dO fold 2^(e_dO - max) of P^ enters through the
+                // exponent term, 2^(8 + e_dO - max - LSE log2 e), which makes
+                // P 2^(e_dO - max) times larger; dP - D is made as much smaller
+                // by taking the half's maximum as the dO rows' scale of the dP
+                // product and D scaled to match, so dS itself is unchanged.
                 const uint32_t eqr = ok ? (uint32_t)eq : 0u, egr = ok ? (uint32_t)edo : 0u;
                 const uint32_t eqb = half_wave_max_u32(eqr), egb = half_wave_max_u32(egr);
+                const int lfg = (int)egr - (int)egb;
                 s_eqb[buf][row >> 5] = (int)eqb;
                 s_egb[buf][row >> 5] = (int)egb;
+                s_edo[buf][row] = (int)egb;
                 s_fq[buf][row] = ok ? ldexpf(1.f, (int)eqr - (int)eqb) : 0.f;
-                s_fg[buf][row] = ok ? ldexpf(1.f, (int)egr - (int)egb) : 0.f;
+                s_nlse[buf][row] = ok ? boosted_row_term(lse, lfg) : -INFINITY;
+                s_ndelta[buf][row] = ok ? ldexpf(-delta, -lfg) : 0.f;
+            } else {
+                s_edo[buf][row] = ok ? edo : 127;
+                // 8 - LSE log2 e: exp2 of the score term then yields 256 P; rows
+                // past the document end get -inf, so their P is exactly zero
+                s_nlse[buf][row] = ok ? boosted_row_term(lse) : -INFINITY;
+                s_ndelta[buf][row] = ok ? -delta : 0.f;
             }
             if constexpr (FP4) {
                 // the Q row's features (tid % 4) D / 4 .. + D / 4 - 1 as FP16
@@ -995,47 +1007,45 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                         const int lim = a.causal ? kj - qb - 32 * t - 16 * g : (kvalid ? -1 : 16);
                         amax = softmax_grad_c<true>(sacc, pacc, nl, c2, lim);
                     }
+                    if constexpr (EXACT) {
+                        // the dQ copy's per-row exponents: each query row's
+                        // largest |256 dS| over the wave's 32 keys, one row per
+                        // lane pair after a transpose-reduce (the block maximum
+                        // is the largest of them), published in LDS as the dQ
+                        // product's row scale and as the multiplier 2^(-e - 8)
+                        // of the codes
+                        const float rmax = row_absmax_transpose(pacc, lane);
+                        amax = rmax;
+                        const int erl = ceil_exp448(rmax * 0.00390625f);
+                        if ((lane & 1) == 0) {
+                            const int r = 32 * t + 16 * g + ((lane >> 1) & 15);
+                            s_er[pb][wave][r] = erl + 127;
+                            s_rm[pb][wave][r] = ldexpf(1.f, -erl - 8);
+                        }
+                    }
                     // block exponent of dS = that of 256 dS minus 8 (exact)
                     const int et = ceil_exp448(wave_max_nonneg(amax) * 0.00390625f);
                     dse = et + 127;
                     if constexpr (EXACT) {
-                        // the dQ copy's per-row exponents: each query row's
-                        // largest |dS| over the wave's 32 keys, one row per lane
-                        // after a transpose-reduce, then all 16 rows of the lane
-                        // group back from LDS (the same wave's write)
-                        uint32_t ab[16];
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) ab[v] = __float_as_uint(fabsf(pacc[v]));
-                        const int erl = ceil_exp448(__uint_as_float(row_max_transpose(ab, lane)) * 0.00390625f);
-                        int* erow = &s_er[pb][wave][32 * t + 16 * g];
-                        if ((lane & 16) == 0) erow[rev4(lane & 15)] = erl + 127;
-                        int er[16];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const v4i e4 = *(const v4i*)(erow + 4 * q);
-                            er[4 * q] = e4.x - 127;
-                            er[4 * q + 1] = e4.y - 127;
-                            er[4 * q + 2] = e4.z - 127;
-                            er[4 * q + 3] = e4.w - 127;
-                        }
-                        // folded operands: P^ x 2^(e_dO - block max) for dV, dS x
-                        // 2^(e_Q - block max) for dK (block exponent et), dS x
-                        // 2^(e_K - block max) for dQ (the row exponents)
-                        const float* fg = &s_fg[pb][32 * t + 16 * g];
+                        // folded operands: P^ already carries 2^(e_dO - block
+                        // max) (from the exponent term); dS x 2^(e_Q - block max)
+                        // for dK (block exponent et); dS x 2^(e_K - block max)
+                        // for dQ, coded against the row exponents (the
+                        // conversion divides by 2^(block max - e_K))
                         const float* fq = &s_fq[pb][32 * t + 16 * g];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            float pv[4], dv4[4], rv[4];
+                            const float4 f = *(const float4*)(fq + 4 * q);
+                            pf[q] = (int)cvt4_fp8(sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]);
+                            df[q] = (int)cvt4_fp8_div(pacc[4 * q] * f.x, pacc[4 * q + 1] * f.y, pacc[4 * q + 2] * f.z,
+                                                      pacc[4 * q + 3] * f.w, ds_code_divisor(et));
+                        }
+                        const float* rm = &s_rm[pb][wave][32 * t + 16 * g];
 #pragma unroll
-                            for (int k = 0; k < 4; ++k) {
-                                const int v = 4 * q + k;
-                                pv[k] = sacc[v] * fg[v];
-                                dv4[k] = pacc[v] * fq[v];
-                                rv[k] = ldexpf(pacc[v] * fk, -er[v] - 8);
-                            }
-                            pf[q] = (int)cvt4_fp8(pv[0], pv[1], pv[2], pv[3]);
-                            df[q] = (int)cvt4_fp8_div(dv4[0], dv4[1], dv4[2], dv4[3], ds_code_divisor(et));
-                            dr[q] = (int)cvt4_fp8(rv[0], rv[1], rv[2], rv[3]);
+                        for (int q = 0; q < 4; ++q) {
+                            const float4 m = *(const float4*)(rm + 4 * q);
+                            dr[q] = (int)cvt4_fp8_div(pacc[4 * q] * m.x, pacc[4 * q + 1] * m.y, pacc[4 * q + 2] * m.z,
+                                                      pacc[4 * q + 3] * m.w, fkdiv);
                         }
                     } else {
 #pragma unroll

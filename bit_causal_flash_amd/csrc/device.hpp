@@ -48,6 +48,13 @@ __device__ __forceinline__ float boosted_row_term(float lse)
     return __builtin_fmaf(-lse, kLog2e, 8.f);
 }
 
+// The same term for 2^k times 256 P (k a small integer): one rounding of
+// 8 + k - LSE log2(e).
+__device__ __forceinline__ float boosted_row_term(float lse, int k)
+{
+    return __builtin_fmaf(-lse, kLog2e, (float)(8 + k));
+}
+
 __device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c, int scale_a,
                                         int scale_b)
 {
@@ -59,21 +66,16 @@ __device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& 
 // [-127, 127].  Pure integer work on the float's bits.
 __device__ __forceinline__ int ceil_exp448(float amax)
 {
-    uint32_t u = __float_as_uint(amax) & 0x7fffffffu;
-    if (u == 0) return 0;
-    int E;
-    uint32_t frac;
-    uint32_t bexp = u >> 23;
-    if (bexp != 0) {
-        E = (int)bexp - 127;
-        frac = u & 0x7fffffu;
-    } else {  // float subnormal: normalise the mantissa
-        int lz = __clz(u) - 8;  // leading zeros inside the 24-bit field
-        E = -126 - lz;
-        frac = (u << lz) & 0x7fffffu;
-    }
+    // branch-free: a float subnormal's mantissa is normalised by its
+    // leading-zero count inside the 24-bit field, which is 0 for normal floats
+    const uint32_t u = __float_as_uint(amax) & 0x7fffffffu;
+    const uint32_t bexp = u >> 23;
+    const int lz = max(__clz(u) - 8, 0);
+    const int E = (int)bexp - 127 - lz + (bexp == 0 ? 1 : 0);
+    const uint32_t frac = (u << lz) & 0x7fffffu;
     int e = E - 8 + (frac > 0x600000u ? 1 : 0);
-    return e < -127 ? -127 : (e > 127 ? 127 : e);
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    return u == 0 ? 0 : e;
 }
 
 // Two floats -> two E4M3 codes in the low 16 bits (x in byte 0).
@@ -372,13 +374,16 @@ __device__ __forceinline__ float sum_xor32(float x)
 }
 
 // Largest unsigned value over the wave, returned wave-uniform: DPP within
-// each 16-lane row, then the four row maxima through v_readlane.
+// each 16-lane row, then the four row maxima through v_readlane.  The DPP
+// moves here and in the reductions below set bound_ctrl: their patterns read
+// inside the lane's own row, so it changes no result, and it lets the
+// compiler fold each move into its maximum.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t u)
 {
-    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, false));  // row_half_mirror
-    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x140, 0xF, 0xF, false));  // row_mirror
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, true));  // row_half_mirror
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x140, 0xF, 0xF, true));  // row_mirror
     const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)u, 0);
     const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)u, 16);
     const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)u, 32);
@@ -424,10 +429,10 @@ __device__ __forceinline__ h8 fp4x8_to_f16(uint32_t codes, float scale)
 // Largest over each 32-lane half of the wave (unsigned), in every lane of it.
 __device__ __forceinline__ uint32_t half_wave_max_u32(uint32_t u)
 {
-    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, false));  // row_half_mirror
-    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x140, 0xF, 0xF, false));  // row_mirror
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, true));  // row_half_mirror
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x140, 0xF, 0xF, true));  // row_mirror
     // v_permlane16_swap hands every lane, across its two results, the value
     // of its own 16-lane row and of the neighbouring row in its half
     const auto pr = __builtin_amdgcn_permlane16_swap(u, u, false, false);
@@ -449,24 +454,68 @@ __device__ __forceinline__ uint32_t row_max_transpose(const uint32_t (&x)[16], i
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const uint32_t send = b0 ? x[k] : x[k + 8], keep = b0 ? x[k + 8] : x[k];
-        y[k] = max(keep, (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false));
+        y[k] = max(keep, (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, true));
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const uint32_t send = b1 ? y[k] : y[k + 4], keep = b1 ? y[k + 4] : y[k];
-        z[k] = max(keep, (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, false));
+        z[k] = max(keep, (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, true));
     }
     // row_ror:4 pairs lane i with lane i - 4 (mod 16): the same low two
     // bits, the other bit 2
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const uint32_t send = b2 ? z[k] : z[k + 2], keep = b2 ? z[k + 2] : z[k];
-        w[k] = max(keep, (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x124, 0xF, 0xF, false));
+        w[k] = max(keep, (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x124, 0xF, 0xF, true));
     }
     const uint32_t send = b3 ? w[0] : w[1], keep = b3 ? w[1] : w[0];
-    const uint32_t u = max(keep, (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x128, 0xF, 0xF, false));
+    const uint32_t u = max(keep, (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x128, 0xF, 0xF, true));
     const auto pr = __builtin_amdgcn_permlane16_swap(u, u, false, false);
     return max((uint32_t)pr[0], (uint32_t)pr[1]);
+}
+
+// max(a, b from the DPP lane pattern CTRL).  Every pattern used with it reads
+// inside the lane's own 16-lane row, so bound_ctrl (a zero from a disabled
+// source lane, the identity of a maximum over non-negative values) changes
+// no result; it lets the compiler fold the lane move into the maximum.
+template <int CTRL>
+__device__ __forceinline__ uint32_t max_dpp_u32(uint32_t a, uint32_t b)
+{
+    return max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)b, CTRL, 0xF, 0xF, true));
+}
+
+// Row maxima of |x| over a 32 x 32 block in the MFMA C layout (element v of
+// lane c of half g is row 16 g + v, column c), the same transpose-reduce in
+// another order, on the bit patterns of |x| (non-negative floats order like
+// their bits).  Bit 4 of the lane goes first, by v_permlane16_swap: it
+// exchanges the odd 16-lane rows of its first operand with the even rows of
+// its second, so one swap and one maximum reduce two values over lanes 16
+// apart with no select, the lanes of the lower row keeping value k and those
+// of the upper row value k + 8.  Bits 3, 2 and 1 then halve the values with
+// DPP partners (row_ror:8 = lane ^ 8; row_half_mirror = lane ^ 7, which at
+// that point holds the same rows as lane ^ 4; quad_perm [2,3,0,1] =
+// lane ^ 2), and bit 0 combines lanes 1 apart.  Lane l of half g returns the
+// largest |x| of row 16 g + ((l >> 1) & 15); lanes l and l ^ 1 return the
+// same row.
+__device__ __forceinline__ float row_absmax_transpose(const v16f& x, int lane)
+{
+    const bool b1 = lane & 2, b2 = lane & 4, b3 = lane & 8;
+    uint32_t a[16], y[8], z[4], w[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) a[v] = __float_as_uint(x[v]) & 0x7fffffffu;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const auto pr = __builtin_amdgcn_permlane16_swap(a[k], a[k + 8], false, false);
+        y[k] = max((uint32_t)pr[0], (uint32_t)pr[1]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        z[k] = max_dpp_u32<0x128>(b3 ? y[k + 4] : y[k], b3 ? y[k] : y[k + 4]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+        w[k] = max_dpp_u32<0x141>(b2 ? z[k + 2] : z[k], b2 ? z[k] : z[k + 2]);
+    const uint32_t u = max_dpp_u32<0x4E>(b1 ? w[1] : w[0], b1 ? w[0] : w[1]);
+    return __uint_as_float(max_dpp_u32<0xB1>(u, u));
 }
 
 // Walsh-Hadamard transform (Sylvester matrix, unnormalised) of a row of D
