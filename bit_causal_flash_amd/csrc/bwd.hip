@@ -1007,24 +1007,30 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                         const int lim = a.causal ? kj - qb - 32 * t - 16 * g : (kvalid ? -1 : 16);
                         amax = softmax_grad_c<true>(sacc, pacc, nl, c2, lim);
                     }
+                    // block exponent of dS = that of 256 dS minus 8 (exact)
+                    int et;
                     if constexpr (EXACT) {
                         // the dQ copy's per-row exponents: each query row's
                         // largest |256 dS| over the wave's 32 keys, one row per
-                        // lane pair after a transpose-reduce (the block maximum
-                        // is the largest of them), published in LDS as the dQ
-                        // product's row scale and as the multiplier 2^(-e - 8)
-                        // of the codes
+                        // lane pair after a transpose-reduce, published in LDS as
+                        // the dQ product's row scale and as the multiplier
+                        // 2^(-e - 8) of the codes.  The exponent rule is
+                        // monotone on non-zero maxima, so the block exponent is
+                        // the largest row exponent over the non-zero rows (an
+                        // all-zero row has exponent 0 and takes no part; an
+                        // all-zero block has exponent 0).
                         const float rmax = row_absmax_transpose(pacc, lane);
-                        amax = rmax;
                         const int erl = ceil_exp448(rmax * 0.00390625f);
                         if ((lane & 1) == 0) {
                             const int r = 32 * t + 16 * g + ((lane >> 1) & 15);
                             s_er[pb][wave][r] = erl + 127;
                             s_rm[pb][wave][r] = ldexpf(1.f, -erl - 8);
                         }
+                        const int eb = (int)wave_max_u32(rmax == 0.f ? 0u : (uint32_t)(erl + 128));
+                        et = eb == 0 ? 0 : eb - 128;
+                    } else {
+                        et = ceil_exp448(wave_max_nonneg(amax) * 0.00390625f);
                     }
-                    // block exponent of dS = that of 256 dS minus 8 (exact)
-                    const int et = ceil_exp448(wave_max_nonneg(amax) * 0.00390625f);
                     dse = et + 127;
                     if constexpr (EXACT) {
                         // folded operands: P^ already carries 2^(e_dO - block
