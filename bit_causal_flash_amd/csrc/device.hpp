@@ -204,11 +204,14 @@ __device__ __forceinline__ int tile_swizzle(int row) { return (row & 6) | ((row 
 // builtin, each step's first read of the current tile waited for the next
 // tile's prefetch).  The caller orders every read of the destination after
 // a wait of its own (wait_vm0_asm) and a barrier.  m0 is set here; no other code
-// of these kernels keeps a value in it.
+// of these kernels keeps a value in it.  An LDS-DMA load that reads m0
+// right after a scalar write of m0 needs one wait state on this chip
+// family, which the compiler cannot insert inside an asm block: hence the
+// s_nop between the two.
 __device__ __forceinline__ void dma16_opaque(const void* src, lds_void* dst)
 {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
 }
 
 // Waits for every vector memory operation, the direct loads above included,
