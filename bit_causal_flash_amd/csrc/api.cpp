@@ -20,6 +20,11 @@ constexpr size_t kAlign = 256;
 constexpr int kFwdTile = 128;  // queries per forward work item
 constexpr int kBwdTile = 128;  // keys per backward work item (exact-scale modes)
 constexpr int kBwdWideTile = 256;  // keys per backward work item (token-block operands)
+// The 256-key backward splits its costliest items in two (see the work-list
+// kernel); each split (item, kv head) pair keeps two FP32 slots of its raw
+// dK / dV (256 keys x d x 2 tensors).  The slots take at most this many bytes.
+constexpr size_t kSplitSlotBytes = (size_t)64 << 20;
+constexpr int64_t kSplitMinIters = 64;
 constexpr uint32_t kKnownFlags =
     FLAMIA_CAUSAL | FLAMIA_EXACT | FLAMIA_FP4_SCORE | FLAMIA_DETERMINISTIC | FLAMIA_HADAMARD |
     FLAMIA_DQ_PRESCALE_SEQUENCE;
@@ -115,15 +120,24 @@ WorklistLayout worklist_layout(const Dims& d, int tile, size_t base)
     w.cursor = o;
     o = align_up(o + 4 * (size_t)(max_cost(d) + 1));
     w.count = o;
-    o = align_up(o + 4);
+    o = align_up(o + 4 * 3);
     w.items = o;
     o = align_up(o + 8 * (size_t)max_items(d, tile));
     w.total = o;
     return w;
 }
 
-// The public part of the backward workspace layout, plus where its work list
-// starts.
+// Split pairs of the 256-key backward (item x kv head) that the slots can
+// hold, and the bytes of one pair's two slots.
+size_t split_pair_bytes(const Dims& d) { return 2 * 2 * (size_t)kBwdWideTile * d.d * 4; }
+int64_t split_pairs(const Dims& d)
+{
+    return std::min<int64_t>(max_items(d, kBwdWideTile) * d.Hkv,
+                             (int64_t)(kSplitSlotBytes / split_pair_bytes(d)));
+}
+
+// The public part of the backward workspace layout, plus where its work lists
+// (and, after them, the split pairs' counters and slots) start.
 flamia_bwd_workspace_layout bwd_layout(const Dims& d, size_t* worklist_base = nullptr)
 {
     flamia_bwd_workspace_layout l;
@@ -142,14 +156,16 @@ flamia_bwd_workspace_layout bwd_layout(const Dims& d, size_t* worklist_base = nu
     if (worklist_base) *worklist_base = o;
     o = worklist_layout(d, kBwdTile, o).total;
     if (worklist_base) worklist_base[1] = o;  // query-tile list of the deterministic dQ kernel
-    l.total = worklist_layout(d, kFwdTile, o).total;
+    o = worklist_layout(d, kFwdTile, o).total;
+    if (worklist_base) worklist_base[2] = o;  // the split pairs' slots
+    l.total = o + split_pairs(d) * split_pair_bytes(d);
     return l;
 }
 
 WorklistArgs make_worklist_args(const Dims& d, const flamia_problem* p, int tile, bool backward,
                                 uint8_t* ws, const WorklistLayout& w)
 {
-    WorklistArgs a;
+    WorklistArgs a = {};
     a.B = (int)d.B;
     a.T = (int)d.T;
     a.tile = tile;
@@ -455,7 +471,7 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     if (!q_codes || !q_exps || !k_codes || !k_exps || !v_codes || !v_exps || !o || !lse ||
         !dout || !dq || !dk || !dv)
         return FLAMIA_ERR_INVALID_ARG;
-    size_t wl_base[2] = {0, 0};
+    size_t wl_base[3] = {0, 0, 0};
     const flamia_bwd_workspace_layout L = bwd_layout(d, wl_base);
     if (workspace == nullptr || workspace_bytes < L.total) return FLAMIA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
@@ -496,6 +512,16 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     const bool wide = operand_mode(p) == MODE_BLOCK || d.d == 64;
     const WorklistLayout wl = worklist_layout(d, kBwdTile, wl_base[0]);
     WorklistArgs w = make_worklist_args(d, p, wide ? kBwdWideTile : kBwdTile, true, ws, wl);
+    if (wide) {
+        w.split_wgs = bwd_wide_workgroups(2 * (int64_t)w.max_items * d.Hkv);
+        if (w.split_wgs <= 0) return FLAMIA_ERR_HIP;
+        w.split_cap = (int)(split_pairs(d) / d.Hkv);
+        w.split_hkv = (int)d.Hkv;
+        // a ticket of an item of cost c takes (Hq / Hkv) c iterations; split
+        // only tickets of at least kSplitMinIters
+        const int64_t G = d.Hq / d.Hkv;
+        w.split_min_cost = (int)((kSplitMinIters + G - 1) / G);
+    }
     e = launch_worklist(w, s);
     if (e != hipSuccess) return FLAMIA_ERR_HIP;
 
@@ -529,6 +555,7 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
     a.delta = q.delta;
     a.prescale = q.prescale;
     a.dq_acc = q.dq_acc;
+    a.dkv_part = (float*)(ws + wl_base[2]);
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
@@ -553,6 +580,7 @@ flamia_status flamia_attn_bwd(const flamia_problem* p, const uint8_t* q_codes,
         aq.items = wqa.items;
         if (launch_bwd_dq(aq, (int)d.d, wqa.max_items, s) != hipSuccess) return FLAMIA_ERR_HIP;
     }
+    if (wide && launch_bwd_pairs(a, (int)d.d, (int)split_pairs(d), s) != hipSuccess) return FLAMIA_ERR_HIP;
     return hip_status(launch_bwd_finalize(a, (int)d.d, !d.deterministic, s));
 }
 

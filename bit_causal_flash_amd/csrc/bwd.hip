@@ -696,6 +696,36 @@ __device__ __forceinline__ void load_qstats(const AttnArgs& a, QStats& r, int h,
     r.pre = a.prescale[i];
 }
 
+// Writes one wave's dK and dV rows (lane = key kj, accumulators of the
+// 32 x 32 MFMA layout over the head dim) as bf16: dK times the softmax scale,
+// and, with rotated Q and K, dK = dK_r H (the Sylvester matrix,
+// unnormalised; the scale already carries the 1 / d).  Keys past the
+// document end are not written.
+template <int D>
+__device__ __forceinline__ void store_dkdv(const AttnArgs& a, v16f (&dk)[D / 32], v16f (&dv)[D / 32], int kj,
+                                           int e, int hk, int lane)
+{
+    constexpr int NDT = D / 32;
+    const int g = lane >> 5;
+    if (a.rotate) fwht_cols<NDT>(dk, lane);
+    if (kj >= e) return;
+    uint16_t* krp = a.dk + ((size_t)kj * a.Hkv + hk) * D;
+    uint16_t* vrp = a.dv + ((size_t)kj * a.Hkv + hk) * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v2i wk, wv;
+            wk.x = (int)pack_bf16x2(dk[dt][4 * q] * sc, dk[dt][4 * q + 1] * sc);
+            wk.y = (int)pack_bf16x2(dk[dt][4 * q + 2] * sc, dk[dt][4 * q + 3] * sc);
+            wv.x = (int)pack_bf16x2(dv[dt][4 * q], dv[dt][4 * q + 1]);
+            wv.y = (int)pack_bf16x2(dv[dt][4 * q + 2], dv[dt][4 * q + 3]);
+            *(v2i*)(krp + 32 * dt + 8 * q + 4 * g) = wk;
+            *(v2i*)(vrp + 32 * dt + 8 * q + 4 * g) = wv;
+        }
+}
+
 // Backward over document-local 256-key tiles (token-block operands).  A
 // workgroup of 8 waves owns 256 keys of one kv head; wave w owns keys
 // 32 w .. 32 w + 31 in every role: for each 64-query tile it forms S and dP
@@ -759,7 +789,11 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
     const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
     const size_t T = (size_t)a.T;
     int* const next_ticket = a.tickets;
-    const int ntickets = *a.count * Hkv;
+    // the count[2] costliest items are split into two tickets per kv head
+    // (tickets 2 p, 2 p + 1 for pair p = item x Hkv + kv head), the rest take
+    // one ticket per kv head
+    const int npairs = a.count[2] * Hkv;
+    const int ntickets = *a.count * Hkv + npairs;
     if (threadIdx.x == 0) s_ticket[0] = atomicAdd(next_ticket, 1);
     __syncthreads();
     for (int slot = 0;; slot ^= 1) {
@@ -769,7 +803,9 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
         asm volatile("" : "+v"(tid));
         const int lane = tid & 63, wave = wave_id(), g = lane >> 5;
         if (tid == 0) s_ticket[slot ^ 1] = atomicAdd(next_ticket, 1);
-        const int item = ticket / Hkv, hk = ticket % Hkv;
+        const int pair = ticket < 2 * npairs ? ticket >> 1 : ticket - npairs;
+        const int half = ticket < 2 * npairs ? (ticket & 1) : -1;  // -1: whole item
+        const int item = pair / Hkv, hk = pair % Hkv;
         const int b = a.items[2 * item], kt = a.items[2 * item + 1];
         const int s = a.cu[b], e = a.cu[b + 1];
         const int k0 = s + NKEY * kt;
@@ -823,7 +859,10 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
         // iterations: q heads of the group (outer) x 64-query tiles that see the keys
         const int qt_lo = a.causal ? (NKEY / 64) * kt : 0;
         const int nqt = (e - s + 63) / 64 - qt_lo;
-        const int niter = G * nqt;
+        // a split item's halves take iterations [0, n / 2) and [n / 2, n)
+        const int nall = G * nqt;
+        const int jlo = half == 1 ? nall / 2 : 0;
+        const int niter = half == 0 ? nall / 2 : nall;
         auto tile_head = [&](int j) { return hk * G + j / nqt; };
         auto tile_base = [&](int j) { return s + 64 * (qt_lo + j % nqt); };
 
@@ -908,8 +947,8 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
             }
         };
         if (wave < 4) {
-            fetch(0);
-            stage(0);
+            fetch(jlo);
+            stage(jlo);
         }
         // every load issued so far has landed (vmcnt(0)), so that inside the
         // loop only the prefetch of the next tile is outstanding
@@ -1146,11 +1185,11 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
 
         // both loops pass the same number of barriers
         if (wave < 4) {
-            for (int j = 0; j <= niter; ++j) {
+            for (int j = jlo; j <= niter; ++j) {
                 // fetch tile j + 1 (the last steps reload the last tile, unused)
                 if (j + 1 < niter) fetch(j + 1);
                 if constexpr (WITH_DQ && DQ_ALL) {
-                    if (j >= 1) dq(j - 1, wave);
+                    if (j > jlo) dq(j - 1, wave);
                 }
                 if (j < niter) step(j);
                 if (j + 1 < niter) {
@@ -1165,39 +1204,74 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
             // previous tile, whose dS^ sits in the other buffer), so that the
             // two waves of a SIMD are in different phases: one's matrix
             // products overlap the other's element-wise work
-            for (int j = 0; j <= niter; ++j) {
+            for (int j = jlo; j <= niter; ++j) {
                 if (j < niter) step(j);
                 if constexpr (WITH_DQ) {
-                    if (j >= 1) dq(j - 1, DQ_ALL ? wave : wave - 4);
+                    if (j > jlo) dq(j - 1, DQ_ALL ? wave : wave - 4);
                 }
                 lds_barrier();
             }
         }
 
-        // rotated Q and K: dK = dK_r H (the Sylvester matrix, unnormalised;
-        // the softmax scale already carries the 1 / d)
-        if (a.rotate) fwht_cols<NDT>(dk, lane);
-        if (kvalid) {
-            uint16_t* krp = a.dk + ((size_t)kj * Hkv + hk) * D;
-            uint16_t* vrp = a.dv + ((size_t)kj * Hkv + hk) * D;
-            const float sc = a.scale;
+        // a split item: each half stores its raw accumulators in its slot
+        // (16-byte chunk c of thread t at float4 index 512 c + t) and the
+        // pair kernel, launched next, adds the two and writes the outputs
+        if (half >= 0) {
+            float4* mine = (float4*)a.dkv_part + (size_t)(2 * pair + half) * (8 * NDT) * 512;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    v2i wk, wv;
-                    wk.x = (int)pack_bf16x2(dk[dt][4 * q] * sc, dk[dt][4 * q + 1] * sc);
-                    wk.y = (int)pack_bf16x2(dk[dt][4 * q + 2] * sc, dk[dt][4 * q + 3] * sc);
-                    wv.x = (int)pack_bf16x2(dv[dt][4 * q], dv[dt][4 * q + 1]);
-                    wv.y = (int)pack_bf16x2(dv[dt][4 * q + 2], dv[dt][4 * q + 3]);
-                    *(v2i*)(krp + 32 * dt + 8 * q + 4 * g) = wk;
-                    *(v2i*)(vrp + 32 * dt + 8 * q + 4 * g) = wv;
+                    mine[(4 * dt + q) * 512 + tid] =
+                        make_float4(dk[dt][4 * q], dk[dt][4 * q + 1], dk[dt][4 * q + 2], dk[dt][4 * q + 3]);
+                    mine[(4 * NDT + 4 * dt + q) * 512 + tid] =
+                        make_float4(dv[dt][4 * q], dv[dt][4 * q + 1], dv[dt][4 * q + 2], dv[dt][4 * q + 3]);
                 }
+        } else {
+            store_dkdv<D>(a, dk, dv, kj, e, hk, lane);
         }
         // item boundary: every wave is done with this item's LDS before the next
         // item's first writes, and the next ticket is visible
         __syncthreads();
     }  // tickets
+}
+
+// The split items of the 256-key backward: workgroup p (512 threads, the
+// thread layout of bwd_wide_kernel) adds the two halves' raw dK / dV
+// accumulators of pair p = item x Hkv + kv head, slot 0 then slot 1, and
+// writes the outputs.  The launch covers the most pairs the slots hold;
+// workgroups past count[2] x Hkv return at once.
+template <int D>
+__global__ __launch_bounds__(512) void bwd_pair_kernel(AttnArgs a)
+{
+    constexpr int NDT = D / 32;
+    constexpr int NC = 8 * NDT;  // float4 chunks of dk, then dv, per thread
+    const int pair = blockIdx.x;
+    if (pair >= a.count[2] * a.Hkv) return;
+    const int item = pair / a.Hkv, hk = pair % a.Hkv;
+    const int b = a.items[2 * item], kt = a.items[2 * item + 1];
+    const int e = a.cu[b + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int kj = a.cu[b] + 256 * kt + 32 * wave + (lane & 31);
+    const float4* s0 = (const float4*)a.dkv_part + (size_t)(2 * pair) * NC * 512;
+    const float4* s1 = s0 + (size_t)NC * 512;
+    v16f dk[NDT], dv[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ck = (4 * dt + q) * 512 + tid, cv = (4 * NDT + 4 * dt + q) * 512 + tid;
+            const float4 x0 = s0[ck], x1 = s1[ck], y0 = s0[cv], y1 = s1[cv];
+            dk[dt][4 * q] = x0.x + x1.x;
+            dk[dt][4 * q + 1] = x0.y + x1.y;
+            dk[dt][4 * q + 2] = x0.z + x1.z;
+            dk[dt][4 * q + 3] = x0.w + x1.w;
+            dv[dt][4 * q] = y0.x + y1.x;
+            dv[dt][4 * q + 1] = y0.y + y1.y;
+            dv[dt][4 * q + 2] = y0.z + y1.z;
+            dv[dt][4 * q + 3] = y0.w + y1.w;
+        }
+    store_dkdv<D>(a, dk, dv, kj, e, hk, lane);
 }
 
 // Query-major dQ for the deterministic backward: a workgroup (4 waves x 32
@@ -1479,14 +1553,22 @@ hipError_t launch_bwd(const AttnArgs& a, int D, int max_items, bool with_dq, hip
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_wide(const AttnArgs& a, int D, int max_items, bool with_dq, hipStream_t stream)
+int bwd_wide_workgroups(int64_t tickets)
 {
-    if (max_items <= 0) return hipSuccess;
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
-        return hipErrorInvalidDevice;
-    const dim3 grid((unsigned)std::min<int64_t>((int64_t)max_items * a.Hkv, ncu));
+        return 0;
+    return (int)std::min<int64_t>(tickets, ncu);
+}
+
+hipError_t launch_bwd_wide(const AttnArgs& a, int D, int max_items, bool with_dq, hipStream_t stream)
+{
+    if (max_items <= 0) return hipSuccess;
+    // split items add up to one more ticket per item and kv head
+    const int wgs = bwd_wide_workgroups(2 * (int64_t)max_items * a.Hkv);
+    if (wgs <= 0) return hipErrorInvalidDevice;
+    const dim3 grid((unsigned)wgs);
 #define FLAMIA_BWDW(DD, WQ, MM) \
     FLAMIA_LAUNCH((bwd_wide_kernel<DD, WQ, MM>), grid, dim3(512), stream, a.ev_start, a.ev_stop, a)
     if (a.mode != MODE_BLOCK) {
@@ -1502,6 +1584,14 @@ hipError_t launch_bwd_wide(const AttnArgs& a, int D, int max_items, bool with_dq
         else FLAMIA_BWDW(64, false, MODE_BLOCK);
     }
 #undef FLAMIA_BWDW
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_pairs(const AttnArgs& a, int D, int max_pairs, hipStream_t stream)
+{
+    if (max_pairs <= 0) return hipSuccess;
+    if (D == 128) hipLaunchKernelGGL(bwd_pair_kernel<128>, dim3(max_pairs), dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL(bwd_pair_kernel<64>, dim3(max_pairs), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 

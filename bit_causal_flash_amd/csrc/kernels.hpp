@@ -68,8 +68,15 @@ struct WorklistArgs {
     int32_t* doc_off;    // [B + 1]
     int32_t* hist;       // [max_cost + 1]
     int32_t* cursor;     // [max_cost + 1]
-    int32_t* count;      // [1]
+    int32_t* count;      // [3]: items, the persistent grid's ticket counter, items split in two
     int32_t* items;      // [max_items][2] = (doc, tile)
+    // Backward 256-key list: the costliest items (a prefix of the order) are
+    // split into two tickets per kv head when one ticket would take more
+    // than half of a workgroup's average share.  split_cap: most items that
+    // may be split (0: none); split_wgs: workgroups of the persistent grid;
+    // split_hkv: tickets per item; split_min_cost: the least cost of an item
+    // worth splitting.
+    int split_cap, split_wgs, split_hkv, split_min_cost;
 };
 
 hipError_t launch_worklist(const WorklistArgs& a, hipStream_t stream);
@@ -91,6 +98,11 @@ struct AttnArgs {
     const int32_t* count;
     const int32_t* items;
     int32_t* tickets;   // backward: the persistent grid's ticket counter (count + 1, zeroed with the list)
+    // backward, 256-key tiles: count[2] leading items are split into two
+    // tickets per kv head (halves of the iteration range); each half writes
+    // its raw dK / dV accumulators to its slot of dkv_part (slots 2 p, 2 p + 1
+    // of pair p = item x Hkv + kv head), which bwd_pair_kernel adds up
+    float* dkv_part;
     const uint8_t *q_codes, *q_exps, *k_codes, *k_exps, *v_codes, *v_exps;
     // E2M1 score views (MODE_FP4): codes [T][H][D/2], E4M3 scales [T][H][D/16]
     const uint8_t *q_fp4, *q_fp4_scales, *k_fp4, *k_fp4_scales;
@@ -114,6 +126,10 @@ hipError_t launch_bwd(const AttnArgs& a, int D, int max_items, bool with_dq, hip
 // token-block operands only: 256-key tiles (work list built with tile 256)
 hipError_t launch_bwd_wide(const AttnArgs& a, int D, int max_items, bool with_dq, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnArgs& a, int D, int max_items, hipStream_t stream);
+// workgroups of the persistent 256-key backward grid for up to `tickets` tickets
+int bwd_wide_workgroups(int64_t tickets);
+// dK / dV of the split pairs of the 256-key backward (after its main kernel)
+hipError_t launch_bwd_pairs(const AttnArgs& a, int D, int max_pairs, hipStream_t stream);
 hipError_t launch_bwd_finalize(const AttnArgs& a, int D, bool dq_from_acc, hipStream_t stream);
 
 }  // namespace flamia

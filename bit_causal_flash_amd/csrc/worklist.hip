@@ -10,7 +10,8 @@
 // finds its document by binary search and bumps a cost histogram, the
 // histogram is scanned from the largest cost down, and items are scattered
 // into their buckets (order inside a bucket is unspecified; it affects only
-// scheduling, never results).
+// scheduling, never results).  For the persistent backward it also decides
+// how many of the costliest items are split into two tickets.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -122,6 +123,25 @@ __global__ __launch_bounds__(kThreads) void worklist_kernel(WorklistArgs a)
     __syncthreads();
     __threadfence_block();
 
+    // 3b. (backward) items split in two, only when there are fewer than
+    // eight tickets per workgroup (with more, the cost-ordered queue already
+    // balances the grid and halves only add per-ticket work): those whose
+    // tickets cost more than half of a workgroup's average share of all
+    // tickets, i.e. cost c > Hkv sum(c) / (2 workgroups), and at least
+    // split_min_cost (a half must outweigh the slots it writes and reads).
+    // They are the leading buckets, so their number is the start of bucket
+    // thr - 1 (read before the scatter moves the cursors); at most split_cap.
+    int nsplit = 0;
+    if (a.split_cap > 0 && (int64_t)nitems * a.split_hkv < 8 * (int64_t)a.split_wgs) {
+        int part = 0;
+        for (int c = tid; c <= a.max_cost; c += kThreads) part += c * hist[c];
+        int total;
+        (void)block_exclusive_scan(part, s_tmp, &total);
+        const int64_t thr = max<int64_t>(max(a.split_min_cost, 2),
+                                         (int64_t)a.split_hkv * total / (2 * (int64_t)a.split_wgs) + 1);
+        nsplit = thr > a.max_cost ? 0 : min(cursor[thr - 1], a.split_cap);
+    }
+
     // 4. scatter
     for (int i = tid; i < nitems; i += kThreads) {
         int lo = 0, hi = a.B - 1;
@@ -137,10 +157,12 @@ __global__ __launch_bounds__(kThreads) void worklist_kernel(WorklistArgs a)
         a.items[2 * pos] = lo;
         a.items[2 * pos + 1] = m;
     }
-    // count[1]: the ticket counter of the persistent backward, taken from 0
+    // count[1]: the ticket counter of the persistent backward, taken from 0;
+    // count[2]: the number of leading items split in two
     if (tid == 0) {
         a.count[0] = nitems;
         a.count[1] = 0;
+        a.count[2] = nsplit;
     }
 }
 

@@ -37,6 +37,19 @@ def test_deterministic_backward_is_bitwise_repeatable():
         assert np.array_equal(a[k], b[k]), k
 
 
+def test_split_backward_is_bitwise_repeatable():
+    """Long tickets split in two (8 q heads per kv head): dK and dV are the
+    pair kernel's sum of the halves' slots, so they repeat bitwise in both
+    modes; with FLAMIA_DETERMINISTIC so does everything else."""
+    w = workloads.make("split", 3, 1536, [700, 300, 520], 8, 1, 128)
+    a, b = run_gpu(w), run_gpu(w)
+    for k in ("O", "LSE", "dK", "dV"):
+        assert np.array_equal(a[k], b[k]), k
+    a, b = run_gpu(w, flags=DET), run_gpu(w, flags=DET)
+    for k in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.array_equal(a[k], b[k]), k
+
+
 def test_deterministic_dq_parity():
     w = _make([257, 64, 130], 460, Hq=4, Hkv=1, d=64)
     g = run_gpu(w, flags=DET)

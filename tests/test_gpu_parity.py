@@ -21,6 +21,13 @@ SMALL = [
     # document and padding rows
     ("empty_docs_d64", [0, 50, 0, 0, 33, 1, 0], 100, 2, 1, 64, True),
     ("empty_docs_noncausal_d128", [0, 70, 0, 40, 0], 128, 2, 2, 128, False),
+    # few, long backward tickets (8 q heads per kv head): the 256-key backward
+    # splits the items of cost >= 8 query tiles (64 iterations) into two
+    # halves whose dK / dV slots the pair kernel adds up -- the first key
+    # tiles of the 700- and 520-token documents, every key tile of the
+    # 600-token one
+    ("split_gqa_d128", [700, 300, 520], 1536, 8, 1, 128, True),
+    ("split_noncausal_d64", [600, 150], 760, 8, 1, 64, False),
 ]
 
 

@@ -117,9 +117,10 @@ def make(name: str, seed: int, T: int, lens, Hq: int, Hkv: int, d: int, flags: i
 
 # The named workloads.  "tiny" is the small case the oracle finishes in
 # seconds; "long_doc" is the headline single-GPU workload; packed MHA, packed
-# GQA and the exact option are parity cases timed alongside; the two 65,536-
-# token rows are the packed shapes the pages time a training call on, kept as
-# context rows.
+# GQA and the exact option are parity cases timed alongside; the two exact-
+# shape rows split the exact option's cost (scale policy, score view); the
+# two 65,536-token rows are the packed shapes the pages time a training call
+# on, kept as context rows.
 def tiny(seed: int = 0) -> Workload:
     """One 256-token document, 1/1 heads, d = 64, causal, N(0, 1)."""
     return make("tiny", seed, 256, [256], 1, 1, 64)
@@ -151,6 +152,20 @@ def exact_option(seed: int = 0) -> Workload:
                 flags=FLAG_CAUSAL | FLAG_EXACT | FLAG_FP4_SCORE)
 
 
+def exact_shape_block(seed: int = 0) -> Workload:
+    """The exact option's shape and inputs (8 documents x 2048, 16/4 heads,
+    d = 64) with token-block operands and FP8 scores: the baseline the
+    exact-scale and score-view costs are measured against."""
+    return make("exact_shape_block", seed, 16384, [2048] * 8, 16, 4, 64)
+
+
+def exact_shape_no_fp4(seed: int = 0) -> Workload:
+    """The exact option without the E2M1 score view: per-token operand scales
+    and per-query-row dS exponents, FP8 scores."""
+    return make("exact_shape_no_fp4", seed, 16384, [2048] * 8, 16, 4, 64,
+                flags=FLAG_CAUSAL | FLAG_EXACT)
+
+
 def docs_16x4096(seed: int = 0) -> Workload:
     """16 documents x 4096 tokens (65,536), 16/16 heads, d = 128, causal,
     N(0, 1); dO ~ 1e-2 N(0, 1)."""
@@ -169,6 +184,8 @@ NAMED = {
     "packed_gqa": packed_gqa,
     "long_doc": long_doc,
     "exact_option": exact_option,
+    "exact_shape_block": exact_shape_block,
+    "exact_shape_no_fp4": exact_shape_no_fp4,
     "docs_16x4096": docs_16x4096,
     "docs_8192_224x256": docs_8192_224x256,
 }
