@@ -112,7 +112,9 @@ __device__ __forceinline__ uint32_t cvt4_fp8_div(float a, float b, float c, floa
 // finite inputs, the clamp only keeps non-finite ones representable.
 __device__ __forceinline__ float ds_code_divisor(int e) { return ldexpf(1.f, min(e + 8, 127)); }
 
-// Sum of the four E4M3 values packed in w.
+// Sum of the four E4M3 values packed in w.  (Widening pairs to bf16 and
+// adding them with bf16 dot products takes fewer instructions but was
+// measured slower in the forward.)
 __device__ __forceinline__ float sum4_fp8(uint32_t w)
 {
     v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
@@ -212,6 +214,15 @@ __device__ __forceinline__ void dma16_opaque(const void* src, lds_void* dst)
 {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
+}
+
+// The same load addressed by a uniform 64-bit base (an SGPR pair) plus the
+// lane's 32-bit byte offset: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void dma16_opaque_s(const void* base, uint32_t off, lds_void* dst)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(m0)
+                 : "memory", "m0");
 }
 
 // Waits for every vector memory operation, the direct loads above included,

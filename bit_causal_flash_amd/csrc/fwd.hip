@@ -84,6 +84,17 @@ __device__ __forceinline__ void load_kvtile(const AttnArgs& a, KVTile<D, MODE>& 
             r.k4s = ssrc[0];
         }
     }
+    if (kt0 + 64 <= e) {
+        // a whole step inside the document (every step but a document's last):
+        // a uniform base and the lane's offset, nothing to clamp
+        const uint8_t* ke = a.k_exps + (size_t)hk * T + kt0;
+        const uint8_t* ve = a.v_exps + (size_t)hk * T + kt0;
+        r.kok = r.vok = 1;
+        r.ek = ke[tid & 63];
+        r.ev = ve[32 * (tid & 1)];
+        if constexpr (MODE != MODE_BLOCK) r.evk = ve[tid & 63];
+        return;
+    }
     const int tk = kt0 + (tid & 63);
     const int tv = kt0 + 32 * (tid & 1);
     r.kok = tk < e;
@@ -166,7 +177,7 @@ __device__ __forceinline__ int online_softmax(v16f (&sacc)[2], v16f (&oacc)[NDT]
                 pf[4 * t + q] = (int)w;
             }
         }
-    // the row sum is exact in FP32 (multiples of 2^-9 below 2^14), and so is
+    // the row sum is exact in FP32 (multiples of 2^-9 below 2^15), and so is
     // its product with the power of two
     l = fmaf(lsum, ldexpf(1.f, rel - 8), l);
     return kScaleMinus8 + rel;
@@ -276,16 +287,34 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
     // 16 L .. 16 L + 15 of its block: row + L / 8, physical chunk L % 8, so it
     // fetches the logical chunk (L % 8) ^ tile_swizzle(row).
     constexpr bool DMA = CT::SWZ;
+    // the lane's byte offsets of its two rows from the step's first row
+    uint32_t dma_off[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = 16 * wave + 8 * i + (lane >> 3);
+        dma_off[i] = (uint32_t)(row * Hkv * D + 16 * ((lane & 7) ^ tile_swizzle(row)));
+    }
     auto dma = [&](int kt0, int buf) {
         if constexpr (DMA) {
+            if (kt0 + 64 <= e) {
+                // every row inside the document: a uniform base plus the offsets
+                const size_t base = ((size_t)kt0 * Hkv + hk) * D;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int rb = 16 * wave + 8 * i;
-                const int row = rb + (lane >> 3);
-                const int c = (lane & 7) ^ tile_swizzle(row);
-                const size_t src = ((size_t)min(kt0 + row, e - 1) * Hkv + hk) * D + 16 * c;
-                if constexpr (!FP4) dma16_opaque(a.k_codes + src, (lds_void*)&s_k[buf][rb * 128]);
-                dma16_opaque(a.v_codes + src, (lds_void*)&s_v[buf][rb * 128]);
+                for (int i = 0; i < 2; ++i) {
+                    const int rb = 16 * wave + 8 * i;
+                    if constexpr (!FP4) dma16_opaque_s(a.k_codes + base, dma_off[i], (lds_void*)&s_k[buf][rb * 128]);
+                    dma16_opaque_s(a.v_codes + base, dma_off[i], (lds_void*)&s_v[buf][rb * 128]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int rb = 16 * wave + 8 * i;
+                    const int row = rb + (lane >> 3);
+                    const int c = (lane & 7) ^ tile_swizzle(row);
+                    const size_t src = ((size_t)min(kt0 + row, e - 1) * Hkv + hk) * D + 16 * c;
+                    if constexpr (!FP4) dma16_opaque(a.k_codes + src, (lds_void*)&s_k[buf][rb * 128]);
+                    dma16_opaque(a.v_codes + src, (lds_void*)&s_v[buf][rb * 128]);
+                }
             }
         }
     };
