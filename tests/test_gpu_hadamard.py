@@ -39,6 +39,9 @@ CASES = [
     # name, lens, capacity, Hq, Hkv, d
     ("had_gqa_d128", [190, 333, 40], 600, 4, 2, 128),
     ("had_mha_d64", [256, 97, 5], 380, 2, 2, 64),
+    # 8 q heads per kv head: the backward splits its longest tickets, and the
+    # pair kernel un-rotates dK after adding the halves
+    ("had_split_gqa_d128", [700, 300, 520], 1536, 8, 1, 128),
 ]
 
 
