@@ -270,7 +270,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
 
     const int kend = a.causal ? min(q0 + 128, e) : e;
     const int nsteps = (kend - s + 63) / 64;
-    const int kend_w = a.causal ? min(qw + 32, e) : e;
+    // keys the wave's queries can see; none when all of its queries lie past
+    // the document end (the last tile of a document): such a wave only
+    // helps stage the K/V tiles
+    const int kend_w = qw >= e ? s : (a.causal ? min(qw + 32, e) : e);
 
     v16f oacc[NDT];
 #pragma unroll
