@@ -191,14 +191,13 @@ EXACT_BWD = [(64, False), (64, True), (128, False)]
 
 
 @pytest.mark.parametrize("d,fp4", EXACT_BWD, ids=["exact_d64", "exact_fp4_d64", "exact_d128"])
-def test_exact_backward(d, fp4, lens=(230, 97, 40), cap=400):
+def test_exact_backward(d, fp4, lens=(230, 97, 40), cap=400, Hq=4, Hkv=2):
     """Exact-scale backward: per-token dO, folded exponents and per-(query
     row, 32-key block) dS exponents for dQ, against the oracle's per-row dS
     backward on the same per-token operands."""
     import torch
     from bit_causal_flash_amd import flamia as F
-    log("case exact backward fp4=%s d=%d" % (fp4, d))
-    Hq, Hkv = 4, 2
+    log("case exact backward fp4=%s d=%d Hq=%d Hkv=%d" % (fp4, d, Hq, Hkv))
     w, p, (q, k, v, f4, x), (o, lse), ops = _exact_case("exact_bwd", list(lens), cap, Hq, Hkv,
                                                         d, fp4, seed=9)
     dq, dk, dv, ws = F.attn_bwd(p, q, k, v, o, lse, x["do"].view(torch.bfloat16), fp4=f4)
@@ -227,6 +226,13 @@ def test_exact_backward_empty_documents():
     """The exact-scale path (E2M1 score view) with empty documents between and
     after the others."""
     test_exact_backward(64, True, lens=(0, 61, 0, 140, 0), cap=220)
+
+
+def test_exact_backward_split_tickets():
+    """The exact-scale path (E2M1 score view) with 8 q heads per kv head, so
+    that the backward splits its longest tickets and the pair kernel adds the
+    halves' dK / dV."""
+    test_exact_backward(64, True, lens=(700, 300, 520), cap=1536, Hq=8, Hkv=1)
 
 
 @pytest.mark.parametrize("mode", ["tokblock", "per_token", "rotated"])
