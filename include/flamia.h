@@ -271,7 +271,7 @@ flamia_status flamia_attn_fwd_noalloc(const flamia_problem* p, const uint8_t* q_
  *              at the offsets flamia_attn_bwd_workspace_layout reports, and
  *              (at most 64 MB) FP32 dK / dV halves of work items the call
  *              splits in two when they are few and long; the halves are added
- *              in a fixed order, so results do not depend on the split.
+ *              in a fixed order, so repeated calls give identical dK and dV.
  * FLAMIA_HADAMARD: Q and K codes of the rotated rows; the gradient products
  * use them at softmax scale / d, and dQ, dK are taken back to the original
  * coordinates (times H_d) before they are written.
