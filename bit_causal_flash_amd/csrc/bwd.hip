@@ -624,38 +624,12 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
 
 // Adds one 32 x 32 dQ tile, the accumulator of a 32x32x64 MFMA (lane =
 // column, VGPR v = row 8 (v / 4) + 4 g + v % 4), into the FP16 accumulator
-// with packed atomics of two adjacent columns: neighbour lanes swap one value
-// of each VGPR pair (v, v + 1), which holds rows (R, R + 1), so that the even
-// lane adds columns (c, c + 1) of row R and the odd lane the same columns of
-// row R + 1.  Rows >= nrows are skipped.
-template <bool CHECK>
-__device__ __forceinline__ void dq_tile_atomics(const v16f& acc, _Float16* tile, size_t rs, int lane,
-                                                int nrows)
-{
-    const bool odd = lane & 1;
-    const int g = lane >> 5;
-    const int col = (lane & 31) & ~1;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int v = 2 * p;
-        const float x = acc[v], y = acc[v + 1];
-        const float send = odd ? x : y;
-        const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
-        const float lo = odd ? recv : x;
-        const float hi = odd ? y : recv;
-        const int row = 8 * (v / 4) + 4 * g + (v % 4) + (odd ? 1 : 0);
-        if (!CHECK || row < nrows)
-            __builtin_amdgcn_global_atomic_fadd_v2f16((h2*)(tile + (size_t)row * rs + col),
-                                                      __builtin_convertvector(v2f{lo, hi}, h2));
-    }
-}
-
-// The same addition with fewer vector instructions: VGPRs v, v + 1 (rows
-// r, r + 1 of the lane's column c) are converted as one FP16 pair, neighbour
-// lanes swap pairs (DPP) and v_perm regroups them, so that the even lane of
-// a pair adds (row r; columns c, c + 1) and the odd lane (row r + 1;
-// columns c - 1, c).  Each row pair's address is a uniform base (scalar
-// arithmetic) plus the lane's constant offset.  Rows >= nrows are skipped.
+// with packed atomics of two adjacent columns: VGPRs v, v + 1 (rows r, r + 1
+// of the lane's column c) are converted as one FP16 pair, neighbour lanes
+// swap pairs (DPP) and v_perm regroups them, so that the even lane of a pair
+// adds (row r; columns c, c + 1) and the odd lane (row r + 1; columns c - 1,
+// c).  Each row pair's address is a uniform base (scalar arithmetic) plus the
+// lane's constant offset.  Rows >= nrows are skipped.
 template <bool CHECK>
 __device__ __forceinline__ void dq_tile_atomics_pk(const v16f& acc, _Float16* tile, size_t rs, int lane,
                                                    int nrows)
@@ -814,7 +788,6 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
         const bool kvalid = kj < e;
         const bool wave_keys = kw0 < e;
         const float c2 = a.c2;
-        const int krow = 32 * wave + (lane & 31);
 
         // the item's K and V tiles, token-major
         for (int c = tid; c < NKEY * CPR; c += 512) {
