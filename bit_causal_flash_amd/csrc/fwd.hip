@@ -205,6 +205,12 @@ __device__ void fwd_padding(const AttnArgs& a, int wg)
     }
 }
 
+// compile-time buffer index of a forward step
+template <int V>
+struct StepBuf {
+    static constexpr int value = V;
+};
+
 template <int D, int MODE>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
 {
@@ -368,8 +374,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
     __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
 
-    for (int st = 0; st < nsteps; ++st) {
-        const int cur = st & 1;
+    // One 64-key step; the buffer index is a compile-time constant (the loop
+    // below takes two steps per trip), so every LDS operand address is a
+    // loop-invariant lane base plus an immediate offset.
+    auto step = [&](int st, auto cur_c) __attribute__((always_inline)) {
+        constexpr int cur = decltype(cur_c)::value;
         const int kt0 = s + 64 * st;
         // prefetch the next step (the last step reloads its own, unused)
         const int kn0 = min(kt0 + 64, s + 64 * (nsteps - 1));
@@ -396,7 +405,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
                     const int ek = s_ek[cur][krow];
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
-                        sacc[t] = mfma_f8(CT::SWZ ? swz_row_operand(swz_row_addr(sk, krow, lane), ks, 0)
+                        sacc[t] = mfma_f8(CT::SWZ ? swz_row_operand(swz_row_addr(s_k[0], krow, lane), ks,
+                                                                    cur * (int)sizeof(s_k[0]))
                                                   : tile_row_operand<D>(sk, krow, 64 * ks, lane),
                                           qf[ks],
                                           sacc[t], ek, eq);
@@ -416,7 +426,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
             const int sv_exp = s_ev[cur][g];
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
-                oacc[dt] = mfma_f8(CT::SWZ ? swz_tr_operand(swz_tr_addr(sv, lane), 0, dt, 0)
+                oacc[dt] = mfma_f8(CT::SWZ ? swz_tr_operand(swz_tr_addr(s_v[0], lane), 0, dt, cur * (int)sizeof(s_v[0]))
                                            : tile_tr_operand<D>(sv, 0, 32 * dt, lane),
                                    pf, oacc[dt],
                                    sv_exp, sp);
@@ -426,6 +436,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(AttnArgs a)
         // (a wait the compiler cannot drop: it does not see the asm loads)
         if constexpr (DMA) wait_vm0_asm();
         lds_barrier();
+    };
+    for (int st = 0; st < nsteps; st += 2) {
+        step(st, StepBuf<0>{});
+        if (st + 1 < nsteps) step(st + 1, StepBuf<1>{});
     }
 
     l = sum_xor32(l);
