@@ -934,6 +934,19 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
 #pragma unroll
             for (int v = 0; v < 16; ++v) dk[i][v] = dv[i][v] = 0.f;
 
+        // D = 128: the lane bases of the swizzled operand reads of the step
+        // (Q rows of either query half and the transposed Q tile in buffer 0,
+        // the wave's K rows), held across the loop; buffer 1 is 8 KB on, an
+        // offset that commutes with the XOR addressing
+        uint32_t qa0[2] = {0u, 0u}, ka0 = 0u, ta0 = 0u;
+        if constexpr (CT::SWZ) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) qa0[t] = swz_row_addr(s_q[0], perm_row(t, lane & 31), lane);
+            ka0 = swz_row_addr(s_kt, 32 * wave + (lane & 31), lane);
+            ta0 = swz_tr_addr(s_q[0], lane);
+        }
+        constexpr uint32_t QBUF = sizeof(s_q[0]);
+
         // Tile j for the wave's keys: S, dP, P, dS, their codes (the k layout
         // of the dV / dK products: bytes 0-15 query half 0, 16-31 half 1), the
         // key-major dS^ rows of the tile's dQ product, then dV^T += dO^T P^ and
@@ -987,8 +1000,8 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                     if constexpr (CT::SWZ) {
                         // Q / dO rows qr and K / V rows krow: one address per
                         // pair of tiles, the rest XOR and immediate offsets
-                        const uint32_t qa = swz_row_addr(sq, qr, lane);
-                        const uint32_t ka = swz_row_addr(s_kt, krow, lane);
+                        const uint32_t qa = qa0[t] + pb * QBUF;
+                        const uint32_t ka = ka0;
                         const int dqg = (int)(lds_addr(s_do[0]) - lds_addr(s_q[0]));
                         const int dkv = (int)(lds_addr(s_vt) - lds_addr(s_kt));
 #pragma unroll
@@ -1097,7 +1110,7 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                 const int sdo = EXACT ? s_egb[pb][g] : s_edo[pb][32 * g];
                 const int sqe = EXACT ? s_eqb[pb][g] : s_eq[pb][32 * g];
                 if constexpr (CT::SWZ) {
-                    const uint32_t ta = swz_tr_addr(sq, lane);
+                    const uint32_t ta = ta0 + pb * QBUF;
                     const int dqg = (int)(lds_addr(s_do[0]) - lds_addr(s_q[0]));
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
