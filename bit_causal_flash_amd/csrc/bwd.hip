@@ -628,16 +628,23 @@ __global__ __launch_bounds__(512) void bwd_kernel(AttnArgs a)
 // of the lane's column c) are converted as one FP16 pair, neighbour lanes
 // swap pairs (DPP) and v_perm regroups them, so that the even lane of a pair
 // adds (row r; columns c, c + 1) and the odd lane (row r + 1; columns c - 1,
-// c).  Each row pair's address is a uniform base (scalar arithmetic) plus the
-// lane's constant offset.  Rows >= nrows are skipped.
+// c).  The atomics are buffer atomics on a resource based at the tile's first
+// row: each row pair's byte offset is a scalar (soffset), the lane's a
+// constant VGPR, so no atomic needs 64-bit vector address arithmetic.  Rows
+// >= nrows are skipped.
 template <bool CHECK>
-__device__ __forceinline__ void dq_tile_atomics_pk(const v16f& acc, _Float16* tile, size_t rs, int lane,
+__device__ __forceinline__ void dq_tile_atomics_pk(const v16f& acc, _Float16* tile, uint32_t rs_bytes, int lane,
                                                    int nrows)
 {
+    // recomputed per call: the row offsets are a few scalar multiplies, not
+    // eight values held across the loop
+    asm volatile("" : "+s"(rs_bytes));
     const bool odd = lane & 1;
     const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
     const int lrow = 4 * (lane >> 5) + (odd ? 1 : 0);
-    const uint32_t lane_off = (uint32_t)(((size_t)lrow * rs + (lane & 30)) * 2);
+    const uint32_t lane_off = (uint32_t)lrow * rs_bytes + 2 * (uint32_t)(lane & 30);
+    // raw buffer (stride 0), no range limit; data format word of gfx9
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(tile, 0, -1, 0x00020000);
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         const int v = 2 * p;
@@ -645,9 +652,12 @@ __device__ __forceinline__ void dq_tile_atomics_pk(const v16f& acc, _Float16* ti
         const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{acc[v], acc[v + 1]}, h2));
         const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0xB1, 0xF, 0xF, false);
         const uint32_t out = __builtin_amdgcn_perm(y, w, sel);
-        char* base = (char*)(tile + (size_t)r0 * rs);
+        // (readfirstlane: the offset stays a scalar where the row checks
+        // make the control flow merge)
+        const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)r0 * rs_bytes);
         if (!CHECK || r0 + lrow < nrows)
-            __builtin_amdgcn_global_atomic_fadd_v2f16((h2*)(base + lane_off), __builtin_bit_cast(h2, out));
+            (void)__builtin_amdgcn_raw_ptr_buffer_atomic_fadd_v2f16(__builtin_bit_cast(h2, out), rsrc, lane_off, soff,
+                                                                    0);
     }
 }
 
@@ -1161,8 +1171,9 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                               s_ekb[kb]);
             }
             _Float16* tile = a.dq_acc + ((size_t)(qb + 32 * ct) * Hq + h) * D + 32 * dt;
-            if (nrows >= 32) dq_tile_atomics_pk<false>(acc, tile, (size_t)Hq * D, lane, nrows);
-            else dq_tile_atomics_pk<true>(acc, tile, (size_t)Hq * D, lane, nrows);
+            const uint32_t rs_bytes = (uint32_t)(Hq * D * 2);
+            if (nrows >= 32) dq_tile_atomics_pk<false>(acc, tile, rs_bytes, lane, nrows);
+            else dq_tile_atomics_pk<true>(acc, tile, rs_bytes, lane, nrows);
         };
         // D = 128: every wave owns one dQ output tile; waves 0-3 add theirs
         // after issuing the next tile's fetch, so that their final wait for
