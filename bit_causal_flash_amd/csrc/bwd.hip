@@ -956,6 +956,14 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
             ta0 = swz_tr_addr(s_q[0], lane);
         }
         constexpr uint32_t QBUF = sizeof(s_q[0]);
+        // and of the dQ product's reads: the transposed K tile, the dS^ tile
+        // (buffer 0)
+        uint32_t kta0 = 0u, dsa0 = 0u;
+        if constexpr (CT::SWZ) {
+            kta0 = swz_tr_addr(s_kt, lane);
+            dsa0 = lds_tr_addr(s_ds[0], SPITCH, lane);
+        }
+        constexpr uint32_t DSBUF = sizeof(s_ds[0]);
 
         // Tile j for the wave's keys: S, dP, P, dS, their codes (the k layout
         // of the dV / dK products: bytes 0-15 query half 0, 16-31 half 1), the
@@ -1165,10 +1173,15 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                 if (ks > 0 && k0 + 64 * ks >= e) break;
                 const int kb = 2 * ks + g;
                 const int sa = min(max((EXACT ? s_er[pb][kb][qrow] : s_dsexp[pb][ct][kb]) + kq, 0), 254);
-                const v8i kop = CT::SWZ ? swz_tr_operand(swz_tr_addr(s_kt, lane), 64 * ks, dt, 0)
-                                        : tile_tr_operand<D>(s_kt, 64 * ks, 32 * dt, lane);
-                acc = mfma_f8(lds_tr_operand(s_ds[pb] + 64 * ks * SPITCH, SPITCH, 0, 32 * ct, lane), kop, acc, sa,
-                              s_ekb[kb]);
+                if constexpr (CT::SWZ) {
+                    const v8i kop = swz_tr_operand(kta0, 64 * ks, dt, 0);
+                    const v8i dop = lds_tr_operand_at(dsa0 + pb * DSBUF + 64 * ks * SPITCH + 32 * ct, SPITCH);
+                    acc = mfma_f8(dop, kop, acc, sa, s_ekb[kb]);
+                } else {
+                    const v8i kop = tile_tr_operand<D>(s_kt, 64 * ks, 32 * dt, lane);
+                    acc = mfma_f8(lds_tr_operand(s_ds[pb] + 64 * ks * SPITCH, SPITCH, 0, 32 * ct, lane), kop, acc,
+                                  sa, s_ekb[kb]);
+                }
             }
             _Float16* tile = a.dq_acc + ((size_t)(qb + 32 * ct) * Hq + h) * D + 32 * dt;
             const uint32_t rs_bytes = (uint32_t)(Hq * D * 2);

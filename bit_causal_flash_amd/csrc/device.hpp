@@ -173,6 +173,29 @@ __device__ __forceinline__ v8i lds_tr_operand(const uint8_t* tile, int pitch, in
     return o;
 }
 
+// The same operand from a precomputed lane address: lds_tr_addr gives the
+// lane's base (row0 = 0, col0 = 0) in `tile`, and the operand at row0, col0
+// is lds_tr_operand_at(base + row0 * pitch + col0, pitch).
+__device__ __forceinline__ uint32_t lds_tr_addr(const uint8_t* tile, int pitch, int lane)
+{
+    const int grp = lane >> 4, l16 = lane & 15, g = grp >> 1;
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)tile +
+           (uint32_t)(((l16 >> 1) + 16 * g) * pitch + 16 * (grp & 1) + 8 * (l16 & 1));
+}
+
+__device__ __forceinline__ v8i lds_tr_operand_at(uint32_t addr, int pitch)
+{
+    typedef __attribute__((address_space(3))) lds_i32x2 lds_p;
+    const lds_i32x2 a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_p*)(uintptr_t)addr);
+    const lds_i32x2 b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_p*)(uintptr_t)(addr + 8 * pitch));
+    const lds_i32x2 c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_p*)(uintptr_t)(addr + 32 * pitch));
+    const lds_i32x2 d = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_p*)(uintptr_t)(addr + 40 * pitch));
+    v8i o;
+    o[0] = a[0]; o[1] = a[1]; o[2] = b[0]; o[3] = b[1];
+    o[4] = c[0]; o[5] = c[1]; o[6] = d[0]; o[7] = d[1];
+    return o;
+}
+
 // MFMA operand whose k axis runs over 64 consecutive bytes of one row (the
 // head dim, or keys of a dS row): bytes 0..15 = row[16g .. 16g+16),
 // bytes 16..31 = row[32 + 16g .. 32 + 16g + 16).
