@@ -853,7 +853,10 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
         // fills rows 16 w .. + 15 of each tile with two direct loads of 1 KB
         // (eight rows), lane L writing LDS bytes 16 L .. + 15 of its block:
         // row + L / 8, physical chunk L % 8, i.e. logical chunk (L % 8) ^
-        // tile_swizzle(row).  D = 64: through registers.
+        // tile_swizzle(row).  The loads are inline assembly: with the builtin
+        // the compiler waits for them (vmcnt(0)) before the first LDS read of
+        // the dQ product that follows, which only reads other tiles; the step
+        // ends with an asm wait instead.  D = 64: through registers.
         using Tile = QTile<D, 256>;
         Tile nxt;
         QStats st;
@@ -867,8 +870,8 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                     const int row = rb + (lane >> 3);
                     const int c = (lane & 7) ^ tile_swizzle(row);
                     const size_t src = ((size_t)min(qb + row, e - 1) * Hq + h) * D + 16 * c;
-                    __builtin_amdgcn_global_load_lds(a.q_codes + src, (lds_void*)&s_q[buf][rb * 128], 16, 0, 0);
-                    __builtin_amdgcn_global_load_lds(a.do_codes + src, (lds_void*)&s_do[buf][rb * 128], 16, 0, 0);
+                    dma16_opaque(a.q_codes + src, (lds_void*)&s_q[buf][rb * 128]);
+                    dma16_opaque(a.do_codes + src, (lds_void*)&s_do[buf][rb * 128]);
                 }
                 load_qstats(a, st, h, qb, e, tid);
             } else {
@@ -935,6 +938,7 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
         }
         // every load issued so far has landed (vmcnt(0)), so that inside the
         // loop only the prefetch of the next tile is outstanding
+        wait_vm0_asm();
         __builtin_amdgcn_s_waitcnt(0x0F70);
         lds_barrier();
 
@@ -1204,8 +1208,13 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
                 if (j < niter) step(j);
                 if (j + 1 < niter) {
                     stage(j + 1);
-                    // the direct loads count in vmcnt: they have landed once it is zero
-                    if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0x0F70);
+                    // the direct loads count in vmcnt: they have landed once it
+                    // is zero (an asm wait, which the compiler cannot drop: it
+                    // does not count the asm loads)
+                    if constexpr (DMA) {
+                        wait_vm0_asm();
+                        __builtin_amdgcn_s_waitcnt(0x0F70);
+                    }
                 }
                 lds_barrier();
             }
