@@ -799,7 +799,21 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(AttnArgs a)
         const bool wave_keys = kw0 < e;
         const float c2 = a.c2;
 
-        // the item's K and V tiles, token-major
+        // the item's K and V tiles, token-major.  D = 128 and every key inside
+        // the document: direct loads into the swizzled tiles (wave w fills
+        // rows 32 w .. + 31 with four loads of eight rows each), landing by the
+        // asm wait before the loop together with the first Q / dO tile, so the
+        // item start waits for one memory round trip, not two
+        if (DMA && k0 + NKEY <= e) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rb = 32 * wave + 8 * i;
+                const int row = rb + (lane >> 3);
+                const size_t src = ((size_t)(k0 + row) * Hkv + hk) * D + 16 * ((lane & 7) ^ tile_swizzle(row));
+                dma16_opaque(a.k_codes + src, (lds_void*)&s_kt[rb * 128]);
+                dma16_opaque(a.v_codes + src, (lds_void*)&s_vt[rb * 128]);
+            }
+        } else
         for (int c = tid; c < NKEY * CPR; c += 512) {
             const int row = c / CPR, col = 16 * (c % CPR);
             const int t = k0 + row;
