@@ -14,10 +14,16 @@ from tests.gpu_helpers import (Backward, check_fwd, fwd_ties, log, oracle_operan
 pytestmark = pytest.mark.gpu
 
 
-def _sample_tokens(cu, rng, per_doc=6):
+def _sample_tokens(cu, rng, per_doc=6, max_docs=None):
+    """Sampled query tokens: each document's start, its first block
+    boundary and end, and random interior positions; with max_docs, only the
+    first document and max_docs - 1 others drawn at random."""
+    docs = list(range(len(cu) - 1))
+    if max_docs is not None and len(docs) > max_docs:
+        docs = [0] + sorted(rng.choice(docs[1:], max_docs - 1, replace=False).tolist())
     toks = []
-    for s, e in zip(cu[:-1], cu[1:]):
-        s, e = int(s), int(e)
+    for b in docs:
+        s, e = int(cu[b]), int(cu[b + 1])
         if e <= s:
             continue
         toks += [s, min(s + 1, e - 1), min(s + 31, e - 1), min(s + 32, e - 1), e - 1]
@@ -43,7 +49,7 @@ def _masks(w, qstarts, heads, nk=12, max_kheads=4):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["tiny", "packed_mha", "packed_gqa", "long_doc"])
+@pytest.mark.parametrize("name", ["tiny", "packed_mha", "packed_gqa", "long_doc", "docs_8192_224x256"])
 def test_full_size_sampled(name):
     log("workload %s" % name)
     w = workloads.NAMED[name](0)
@@ -55,7 +61,10 @@ def test_full_size_sampled(name):
         assert np.array_equal(g[tag + "e"], e), tag + " exps"
     log("codes bit-exact")
     rng = np.random.default_rng(1)
-    toks = _sample_tokens(w.cu, rng, per_doc=8 if name != "long_doc" else 40)
+    # the 8192 + 224 x 256 shape (most backward items a whole 256-token
+    # document): the long document and 23 of the short ones
+    toks = _sample_tokens(w.cu, rng, per_doc=8 if name != "long_doc" else 40,
+                          max_docs=24 if name == "docs_8192_224x256" else None)
     heads = list(range(w.Hq)) if w.Hq <= 8 else list(rng.choice(w.Hq, 8, replace=False))
     rows = np.array([(h, t) for h in heads for t in toks], dtype=np.int32)
     ops = oracle.Operands.from_codes(q, k, v)
