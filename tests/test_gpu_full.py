@@ -49,7 +49,8 @@ def _masks(w, qstarts, heads, nk=12, max_kheads=4):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["tiny", "packed_mha", "packed_gqa", "long_doc", "docs_8192_224x256"])
+@pytest.mark.parametrize("name", ["tiny", "packed_mha", "packed_gqa", "long_doc", "docs_16x4096",
+                                  "docs_8192_224x256"])
 def test_full_size_sampled(name):
     log("workload %s" % name)
     w = workloads.NAMED[name](0)
